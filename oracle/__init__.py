@@ -1,0 +1,187 @@
+"""CPU oracle for NVFP4 (g16) W4A16 GEMV and the MoE expert-slot variant.
+
+TEST INFRASTRUCTURE ONLY. Only the test suite, ``__graft_entry__.smoke()``
+and the benchmark's ``cpu_baseline`` leg may import this package. It shares no
+code with the GPU library and never imports it.
+
+The arithmetic lives in ``nvfp4_oracle.c`` (plain C, fp32 quantisation
+decisions, fp64 dot products); this module only marshals numpy arrays.
+Definitions and their sources are documented in ``nvfp4_oracle.h``.
+"""
+import ctypes
+import os
+
+import numpy as np
+
+from . import build as _build
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_lib = None
+
+_u8p = ctypes.POINTER(ctypes.c_uint8)
+_u16p = ctypes.POINTER(ctypes.c_uint16)
+_i32p = ctypes.POINTER(ctypes.c_int32)
+_i64p = ctypes.POINTER(ctypes.c_int64)
+_f32p = ctypes.POINTER(ctypes.c_float)
+_f64p = ctypes.POINTER(ctypes.c_double)
+_i64 = ctypes.c_int64
+
+
+def lib():
+    """Load the oracle library, building it first if it is not built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_build.LIB):
+            _build.build()
+        L = ctypes.CDLL(_build.LIB)
+        L.oracle_e2m1_value.restype = ctypes.c_double
+        L.oracle_e2m1_value.argtypes = [ctypes.c_uint]
+        L.oracle_e4m3_value.restype = ctypes.c_double
+        L.oracle_e4m3_value.argtypes = [ctypes.c_uint]
+        L.oracle_e4m3_encode.restype = ctypes.c_uint
+        L.oracle_e4m3_encode.argtypes = [ctypes.c_float]
+        L.oracle_e2m1_encode.restype = ctypes.c_uint
+        L.oracle_e2m1_encode.argtypes = [ctypes.c_float]
+        L.oracle_bf16_from_double.restype = ctypes.c_uint16
+        L.oracle_bf16_from_double.argtypes = [ctypes.c_double]
+        L.oracle_pack.restype = ctypes.c_int
+        L.oracle_pack.argtypes = [_f32p, _i64, _i64, _u8p, _u8p, _f32p, _f32p]
+        L.oracle_dequant.restype = ctypes.c_int
+        L.oracle_dequant.argtypes = [_u8p, _u8p, ctypes.c_float, _i64, _i64, _f32p]
+        L.oracle_gemv.restype = ctypes.c_int
+        L.oracle_gemv.argtypes = [_u8p, _u8p, ctypes.c_float, _u16p, _i64, _i64,
+                                  _i64, _i64p, _i64, _f64p, _f64p]
+        L.oracle_moe.restype = ctypes.c_int
+        L.oracle_moe.argtypes = [_u8p, _u8p, _f32p, _u8p, _u8p, _f32p, _u16p,
+                                 _i32p, _f32p, _i64, _i64, _i64, _i64, _i64,
+                                 _f64p, _f64p, _u16p]
+        _lib = L
+    return _lib
+
+
+def _ptr(a, t):
+    return a.ctypes.data_as(t)
+
+
+def _c(a, dtype):
+    a = np.ascontiguousarray(a)
+    if a.dtype != dtype:
+        raise TypeError(f"expected {dtype}, got {a.dtype}")
+    return a
+
+
+def _check(rc, what):
+    if rc != 0:
+        raise ValueError(f"oracle {what} failed with status {rc}")
+
+
+# ---------------------------------------------------------------- elements
+
+def e2m1_value(code: int) -> float:
+    return lib().oracle_e2m1_value(code)
+
+
+def e4m3_value(byte: int) -> float:
+    return lib().oracle_e4m3_value(byte)
+
+
+def e4m3_encode(r: float) -> int:
+    return lib().oracle_e4m3_encode(float(np.float32(r)))
+
+
+def e2m1_encode(t: float) -> int:
+    return lib().oracle_e2m1_encode(float(np.float32(t)))
+
+
+def bf16_from_double(v: float) -> int:
+    return lib().oracle_bf16_from_double(float(v))
+
+
+# ------------------------------------------------------------------- pack
+
+def pack(W, gscale_override=None):
+    """fp32 W[N,K] -> (codes u8[N,K/2], scales u8[N,K/16], g float32)."""
+    W = _c(W, np.float32)
+    N, K = W.shape
+    codes = np.empty((N, K // 2), np.uint8)
+    scales = np.empty((N, K // 16), np.uint8)
+    g = np.zeros(1, np.float32)
+    ov = None
+    if gscale_override is not None:
+        ov = np.array([gscale_override], np.float32)
+    rc = lib().oracle_pack(_ptr(W, _f32p), N, K, _ptr(codes, _u8p),
+                           _ptr(scales, _u8p), _ptr(g, _f32p),
+                           _ptr(ov, _f32p) if ov is not None else None)
+    _check(rc, "pack")
+    return codes, scales, np.float32(g[0])
+
+
+def dequant(codes, scales, g):
+    codes = _c(codes, np.uint8)
+    scales = _c(scales, np.uint8)
+    N, K = codes.shape[0], codes.shape[1] * 2
+    out = np.empty((N, K), np.float32)
+    rc = lib().oracle_dequant(_ptr(codes, _u8p), _ptr(scales, _u8p),
+                              float(np.float32(g)), N, K, _ptr(out, _f32p))
+    _check(rc, "dequant")
+    return out
+
+
+# ------------------------------------------------------------------- gemv
+
+def gemv(codes, scales, g, x_bits, rows=None):
+    """y, absdot (fp64, [M, N] or [M, len(rows)]) for bf16 x given as uint16."""
+    codes = _c(codes, np.uint8)
+    scales = _c(scales, np.uint8)
+    x_bits = _c(x_bits, np.uint16)
+    N, K = codes.shape[0], codes.shape[1] * 2
+    M = x_bits.shape[0]
+    if x_bits.shape[1] != K:
+        raise ValueError("x has the wrong K")
+    if rows is not None:
+        rows = _c(np.asarray(rows, np.int64), np.int64)
+        cnt = rows.shape[0]
+    else:
+        cnt = N
+    y = np.empty((M, cnt), np.float64)
+    ad = np.empty((M, cnt), np.float64)
+    rc = lib().oracle_gemv(_ptr(codes, _u8p), _ptr(scales, _u8p),
+                           float(np.float32(g)), _ptr(x_bits, _u16p), M, N, K,
+                           _ptr(rows, _i64p) if rows is not None else None,
+                           cnt, _ptr(y, _f64p), _ptr(ad, _f64p))
+    _check(rc, "gemv")
+    return y, ad
+
+
+# -------------------------------------------------------------------- moe
+
+def moe(w13_codes, w13_scales, w13_g, w2_codes, w2_scales, w2_g, x_bits,
+        ids, gate_w, want_h=False):
+    """y, bound (fp64 [M, H]) and optionally h bits (uint16 [M*topk, I])."""
+    w13_codes = _c(w13_codes, np.uint8)
+    w13_scales = _c(w13_scales, np.uint8)
+    w2_codes = _c(w2_codes, np.uint8)
+    w2_scales = _c(w2_scales, np.uint8)
+    w13_g = _c(w13_g, np.float32)
+    w2_g = _c(w2_g, np.float32)
+    x_bits = _c(x_bits, np.uint16)
+    ids = _c(ids, np.int32)
+    gate_w = _c(gate_w, np.float32)
+    E, twoI, Hh = w13_codes.shape
+    H = Hh * 2
+    I = twoI // 2
+    M, topk = ids.shape
+    if w2_codes.shape != (E, H, I // 2) or x_bits.shape != (M, H):
+        raise ValueError("inconsistent MoE shapes")
+    y = np.empty((M, H), np.float64)
+    bound = np.empty((M, H), np.float64)
+    h = np.empty((M * topk, I), np.uint16) if want_h else None
+    rc = lib().oracle_moe(_ptr(w13_codes, _u8p), _ptr(w13_scales, _u8p),
+                          _ptr(w13_g, _f32p), _ptr(w2_codes, _u8p),
+                          _ptr(w2_scales, _u8p), _ptr(w2_g, _f32p),
+                          _ptr(x_bits, _u16p), _ptr(ids, _i32p),
+                          _ptr(gate_w, _f32p), M, E, H, I, topk,
+                          _ptr(y, _f64p), _ptr(bound, _f64p),
+                          _ptr(h, _u16p) if h is not None else None)
+    _check(rc, "moe")
+    return (y, bound, h) if want_h else (y, bound)
