@@ -1,0 +1,310 @@
+#!/usr/bin/env python3
+"""Benchmark: achieved HBM GB/s and % of the HBM roofline of the NVFP4 g16
+W4A16 GEMV on one MI355X.
+
+Headline leg (``value``): the LM-head-sized GEMV, M=1, N=151936, K=4096 (the
+llama.cpp trace page's output.weight at one token). A step is one GEMV call.
+Secondary legs, measured the same way and reported in the same JSON line:
+  m8   - the stress GEMV pair at M=8 (12288x4096 and 4096x12288, Student-t
+         weights with 1% zero blocks), one step = both calls;
+  moe  - the 288-expert MoE expert-slot pass at M=8 (and M=1), top-8.
+Throughput counts algorithmic bytes (codes + scales + tensor scale + x + y;
+for the MoE every distinct expert's weights once) per second, inputs already
+resident in HBM. Weight copies are rotated so that each call reads memory
+the previous calls did not (the 256 MB MALL cannot serve repeats).
+
+Timing: W warm-up steps, then exactly K steps between two device
+synchronisations (wall clock -> ms_per_step, value). Inside the timed region
+HIP events on the launch stream bracket every launch; their mean is the
+kernel's average duration used for ``roofline.achieved``.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--legs ...]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import platform
+import subprocess
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0      # MI355X published HBM3E bandwidth
+METRIC = "achieved HBM GB/s and % of roofline, NVFP4 W4A16 GEMV at M=1 and M=8"
+MIN_ROTATION_BYTES = 1 << 30
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def git_sha():
+    try:
+        return subprocess.run(["git", "rev-parse", "--short", "HEAD"], cwd=ROOT,
+                              capture_output=True, text=True, timeout=10).stdout.strip() or None
+    except Exception:
+        return None
+
+
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor() or None
+
+
+def timed_steps(torch, step, steps, warmup, nkernels):
+    """Run `warmup` untimed steps, then exactly `steps` timed ones. step(i,
+    ev) launches the step's kernels; ev(j) returns the (start, end) event
+    pair to record around kernel j. Returns wall ms per step and the mean
+    event duration (ms) of every kernel position."""
+    for i in range(warmup):
+        step(i, None)
+    torch.cuda.synchronize()
+    evs = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+            for _ in range(nkernels)] for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        step(warmup + i, lambda j, _i=i: evs[_i][j])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    per_kernel = [float(np.mean([evs[i][j][0].elapsed_time(evs[i][j][1])
+                                 for i in range(steps)])) for j in range(nkernels)]
+    return (t1 - t0) * 1e3 / steps, per_kernel
+
+
+def rec(ev, j, which):
+    if ev is not None:
+        ev(j)[which].record()
+
+
+# ------------------------------------------------------------------- legs
+
+def leg_lm_head(torch, nv, workloads, traffic, steps, warmup, want_cpu):
+    import oracle
+    M, N, K = 1, 151936, 4096
+    log(f"[bench] lm head: generating W {N}x{K}")
+    W = workloads.dense_weights(3, 0, 0, N, K)
+    Wd = torch.from_numpy(W).cuda()
+    codes, scales, g = nv.pack(Wd)
+    del Wd
+    x_bits = workloads.x_bf16(3, 0, 0, M, K)
+    x = torch.from_numpy(x_bits.view(np.int16)).cuda().view(torch.bfloat16)
+    wbytes = traffic.weight_bytes(N, K)
+    R = max(2, -(-MIN_ROTATION_BYTES // wbytes))
+    copies = [(codes, scales, g)] + [(codes.clone(), scales.clone(), g.clone())
+                                     for _ in range(R - 1)]
+    y = torch.empty((M, N), dtype=torch.float32, device="cuda")
+
+    def step(i, ev):
+        c, s, gg = copies[i % R]
+        rec(ev, 0, 0)
+        nv.gemv_into(c, s, gg, x, y)
+        rec(ev, 0, 1)
+
+    ms, (kms,) = timed_steps(torch, step, steps, warmup, 1)
+    B = traffic.gemv_bytes(M, N, K)
+    out = {
+        "bytes_per_step": B, "ms_per_step": ms, "kernel_us": kms * 1e3,
+        "gbs_wall": B / (ms * 1e-3) / 1e9, "gbs_kernel": B / (kms * 1e-3) / 1e9,
+        "tokens_per_s": M / (ms * 1e-3), "rotate_copies": R,
+    }
+    # parity of the timed configuration: pack bit-exact, sampled rows in tolerance
+    log("[bench] lm head: oracle pack + sampled-row parity")
+    t = time.perf_counter()
+    c0, s0, g0 = oracle.pack(W)
+    pack_s = time.perf_counter() - t
+    del W
+    torch.cuda.synchronize()
+    pack_ok = bool(np.array_equal(codes.cpu().numpy(), c0) and
+                   np.array_equal(scales.cpu().numpy(), s0) and
+                   np.float32(g.cpu().numpy()[0]) == g0)
+    nv.gemv_into(codes, scales, g, x, y)
+    yh = y.cpu().numpy()
+    rows = np.random.default_rng(0).choice(N, 2048, replace=False)
+    yr, ad = oracle.gemv(c0, s0, g0, x_bits, rows=rows)
+    worst = float((np.abs(yh[:, rows] - yr) / (1e-3 * ad + 1e-6)).max())
+    out["parity"] = {"pack_bit_exact": pack_ok, "sampled_rows": int(len(rows)),
+                     "max_err_over_tol": worst, "ok": pack_ok and worst <= 1.0}
+    if want_cpu:
+        out["cpu_baseline"] = cpu_baseline(c0, s0, g0, x_bits, B, M)
+        out["cpu_baseline"]["pack_s"] = pack_s
+    return out
+
+
+def cpu_baseline(c0, s0, g0, x_bits, B, M):
+    """The oracle as it stands (fp64, OpenMP over rows) on the host cores:
+    the full 151936 x 4096 M=1 GEMV, repeated until about 10 s have passed."""
+    import oracle
+    threads = int(os.environ.get("OMP_NUM_THREADS") or os.cpu_count() or 1)
+    times = []
+    t_end = time.perf_counter() + 10.0
+    while len(times) < 2 or (time.perf_counter() < t_end and len(times) < 50):
+        t = time.perf_counter()
+        oracle.gemv(c0, s0, g0, x_bits)
+        times.append(time.perf_counter() - t)
+    tm = float(np.median(times))
+    return {"value": B / tm / 1e9, "unit": "GB/s", "cores": threads, "kind": "oracle",
+            "sample": f"full 151936x4096 M=1 GEMV, {len(times)} runs, median {tm:.3f} s",
+            "tokens_per_s": M / tm, "cpu": cpu_model(), "host_cpus": os.cpu_count()}
+
+
+def leg_m8(torch, nv, workloads, traffic, steps, warmup):
+    M = 8
+    mats = [(0, 12288, 4096), (1, 4096, 12288)]
+    packed, B, wb = [], 0, 0
+    for i, N, K in mats:
+        log(f"[bench] m8: generating W {N}x{K} (Student-t)")
+        W = workloads.dense_weights(5, 0, i, N, K)
+        c, s, g = nv.pack(torch.from_numpy(W).cuda())
+        x = torch.from_numpy(workloads.x_bf16(5, 0, i, M, K).view(np.int16)).cuda().view(
+            torch.bfloat16)
+        y = torch.empty((M, N), dtype=torch.float32, device="cuda")
+        packed.append((c, s, g, x, y))
+        B += traffic.gemv_bytes(M, N, K)
+        wb += traffic.weight_bytes(N, K)
+    R = max(2, -(-MIN_ROTATION_BYTES // wb))
+    copies = [packed] + [[(c.clone(), s.clone(), g.clone(), x, y) for c, s, g, x, y in packed]
+                         for _ in range(R - 1)]
+
+    def step(i, ev):
+        for j, (c, s, g, x, y) in enumerate(copies[i % R]):
+            rec(ev, j, 0)
+            nv.gemv_into(c, s, g, x, y)
+            rec(ev, j, 1)
+
+    ms, kms = timed_steps(torch, step, steps, warmup, 2)
+    kt = sum(kms)
+    return {"workload": "stress_m8_t3 (12288x4096 + 4096x12288)", "M": M,
+            "bytes_per_step": B, "ms_per_step": ms, "kernel_us": [k * 1e3 for k in kms],
+            "gbs_wall": B / (ms * 1e-3) / 1e9, "gbs_kernel": B / (kt * 1e-3) / 1e9,
+            "frac_of_peak": B / (kt * 1e-3) / 1e9 / HBM_PEAK_GBS,
+            "tokens_per_s": M / (ms * 1e-3), "rotate_copies": R}
+
+
+def leg_moe(torch, nv, workloads, traffic, steps, warmup, M):
+    E, H, I, topk = 288, 4096, 1536, 8
+    log(f"[bench] moe M={M}: generating {E} experts on the device")
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(4_000 + M)
+    c13 = torch.empty((E, 2 * I, H // 2), dtype=torch.uint8, device="cuda")
+    s13 = torch.empty((E, 2 * I, H // 16), dtype=torch.uint8, device="cuda")
+    g13 = torch.empty((E,), dtype=torch.float32, device="cuda")
+    c2 = torch.empty((E, H, I // 2), dtype=torch.uint8, device="cuda")
+    s2 = torch.empty((E, H, I // 16), dtype=torch.uint8, device="cuda")
+    g2 = torch.empty((E,), dtype=torch.float32, device="cuda")
+    for e in range(E):
+        w = torch.randn((2 * I, H), generator=gen, device="cuda") * 0.02
+        nv.pack_into(w, c13[e], s13[e], g13[e:e + 1])
+        w = torch.randn((H, I), generator=gen, device="cuda") * 0.02
+        nv.pack_into(w, c2[e], s2[e], g2[e:e + 1])
+    del w
+    nb = 16
+    batches = []
+    for b in range(nb):
+        ids, gw = workloads.moe_routing(4, b, M, E, topk)
+        x = torch.from_numpy(workloads.x_bf16(4, b, 0, M, H).view(np.int16)).cuda().view(
+            torch.bfloat16)
+        batches.append((torch.from_numpy(ids).cuda(), torch.from_numpy(gw).cuda(), x,
+                        len(set(ids.ravel().tolist()))))
+    ws = torch.empty(nv.moe_workspace_bytes(M, H, I, topk), dtype=torch.uint8, device="cuda")
+    y = torch.empty((M, H), dtype=torch.float32, device="cuda")
+
+    def step(i, ev):
+        ids, gw, x, _ = batches[i % nb]
+        rec(ev, 0, 0)
+        nv.moe_gemv_into(c13, s13, g13, c2, s2, g2, x, ids, gw, y, ws)
+        rec(ev, 0, 1)
+
+    ms, (kms,) = timed_steps(torch, step, steps, warmup, 1)
+    # bytes of the steps actually timed (each step's own distinct-expert count)
+    Bs = [traffic.moe_bytes(M, H, I, topk, batches[(warmup + i) % nb][3]) for i in range(steps)]
+    B = float(np.mean(Bs))
+    D = float(np.mean([batches[(warmup + i) % nb][3] for i in range(steps)]))
+    return {"workload": f"moe_288x(3072x4096,4096x1536)_top8_m{M}", "M": M,
+            "distinct_experts_mean": D, "bytes_per_step": B, "ms_per_step": ms,
+            "pass_us": kms * 1e3, "gbs_wall": B / (ms * 1e-3) / 1e9,
+            "gbs_pass": B / (kms * 1e-3) / 1e9,
+            "frac_of_peak": B / (kms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+            "tokens_per_s": M / (ms * 1e-3), "rotating_batches": nb}
+
+
+# ------------------------------------------------------------------- main
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--legs", default="lm_head,m8,moe",
+                    help="comma list of lm_head, m8, moe (lm_head is the headline)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU only: --gpus {args.gpus} (WORLD_SIZE {world}) is not "
+              "supported; the GEMV is sharded by output rows across GPUs and each GPU's share "
+              "is this single-GPU kernel at a smaller N.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import nvfp4_block_scaled_gemv_amd as nv
+    from nvfp4_block_scaled_gemv_amd import traffic
+    import workloads
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    nv.lib()   # fail loudly if the HIP library is not built
+    legs = [s.strip() for s in args.legs.split(",") if s.strip()]
+    props = torch.cuda.get_device_properties(0)
+    result = {
+        "metric": METRIC, "value": None, "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": None, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "lm_head_m1_151936x4096", "M": 1, "N": 151936, "K": 4096,
+                   "weights": "nvfp4 g16 from N(0,0.02) fp32, packed on the GPU",
+                   "x": "bf16 N(0,1)", "y": "fp32"},
+    }
+    if "lm_head" in legs:
+        lm = leg_lm_head(torch, nv, workloads, traffic, args.steps, args.warmup,
+                         not args.no_cpu_baseline)
+        result["value"] = lm["gbs_wall"]
+        result["ms_per_step"] = lm["ms_per_step"]
+        result["tokens_per_s"] = lm["tokens_per_s"]
+        result["frac_of_peak_wall"] = lm["gbs_wall"] / HBM_PEAK_GBS
+        result["roofline"] = {"bound": "hbm", "achieved": lm["gbs_kernel"],
+                              "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                              "frac": lm["gbs_kernel"] / HBM_PEAK_GBS, "traffic": None,
+                              "kernel": "nvfp4::k_gemv<1, 4>",
+                              "kernel_avg_us": lm["kernel_us"],
+                              "bytes_per_launch": lm["bytes_per_step"]}
+        result["config"]["rotate_copies"] = lm["rotate_copies"]
+        result["parity"] = lm["parity"]
+        if "cpu_baseline" in lm:
+            result["cpu_baseline"] = lm["cpu_baseline"]
+    if "m8" in legs:
+        result["m8"] = leg_m8(torch, nv, workloads, traffic, args.steps, args.warmup)
+    if "moe" in legs:
+        result["moe"] = {f"m{M}": leg_moe(torch, nv, workloads, traffic, args.steps,
+                                          args.warmup, M) for M in (1, 8)}
+    result["env"] = {"gpu": props.name, "cus": props.multi_processor_count,
+                     "hip": torch.version.hip, "torch": torch.__version__, "git": git_sha(),
+                     "argv": sys.argv[1:]}
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,193 @@
+/*
+ * nvfp4_gemv.h -- C ABI of the MI355X (gfx950) NVFP4 g16 W4A16 small-M GEMV
+ * library: weight packing, bit-exact dequantisation, the weight-streaming
+ * GEMV y[M,N] = x[M,K] . W[N,K]^T for M <= 8, and the MoE expert-slot variant
+ * (gather top-k experts by id, SwiGLU, combine by gate weight).
+ *
+ * The operations are the ones the GLM-5.3-Flash-NVFP4 blueprint pages
+ * describe for their decode step:
+ *  - weight format "nvfp4/g16" with activation "bf16" (blueprint page,
+ *    Precision table, 322 weighted nodes): E2M1 4-bit codes, one unsigned
+ *    E4M3 scale per 16 consecutive weights of a row ("E2M1 + UE4M3/16",
+ *    card.json performance[6].note) and one fp32 tensor scale;
+ *  - per-node steps "act bf16, weight nvfp4/g16->bf16, mma bf16*bf16,
+ *    accumulate f32, scale f32" (graph.json node "l0.kda.q");
+ *  - the MoE slot GEMV over 8 experts (card.json performance[33],
+ *    w4a16_gemv_sw_moe), the union of expert ids over the rows
+ *    (performance[31], performance[64]), silu_mul to bf16 (graph.json node
+ *    "l3.moe.experts_act") and the f32 combine by gate weight (graph.json node
+ *    "l3.moe.blend"). The element bit layouts are OCP MX v1.0 E2M1 / E4M3.
+ *
+ * Conventions for every entry point:
+ *  - every pointer is a DEVICE pointer of the current HIP device; arrays are
+ *    row-major and contiguous; the caller owns (allocates and frees) every
+ *    buffer. The library allocates no device memory and keeps no mutable
+ *    global state.
+ *  - shapes are checked on the host before anything is launched; on a failed
+ *    check nothing is launched, the call returns the error code and
+ *    nvfp4_last_error() describes it. Device data (ids, scales, the tensor
+ *    scale) is not inspected on the host.
+ *  - work is enqueued on `stream` (0 = the null stream) and the call returns
+ *    without synchronising. A launch failure returns NVFP4_ERR_HIP.
+ *  - outputs must not overlap inputs (checked: NVFP4_ERR_ALIAS).
+ *  - results are deterministic: no floating-point atomics, fixed reduction
+ *    order for a given shape.
+ *
+ * NVFP4 g16 storage of a weight matrix W[N, K] (N output rows, K inputs;
+ * K % 32 == 0 for the GEMV, K % 16 == 0 for pack/dequant):
+ *  - codes  uint8[N, K/2]:  byte j of row n holds element 2j in bits 3..0
+ *                           and element 2j+1 in bits 7..4 (E2M1, sign in
+ *                           the nibble's bit 3);
+ *  - scales uint8[N, K/16]: E4M3 (sign bit 0) scale of elements
+ *                           16b .. 16b+15 of the row;
+ *  - gscale float[1]:       fp32 tensor scale g.
+ *  The dequantised weight is w[n,k] = e2m1(code) * e4m3(scale) * g.
+ */
+#ifndef NVFP4_GEMV_H
+#define NVFP4_GEMV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define NVFP4_ABI_VERSION 1
+
+/* Largest number of activation rows (tokens) one GEMV / MoE call takes. */
+#define NVFP4_MAX_M 8
+/* Largest number of expert slots per token in the MoE call. */
+#define NVFP4_MAX_TOPK 16
+
+typedef enum nvfp4_status {
+  NVFP4_OK = 0,
+  NVFP4_ERR_NULL = 1,        /* a required pointer is NULL */
+  NVFP4_ERR_SHAPE = 2,       /* negative size or a divisibility rule broken */
+  NVFP4_ERR_ALIGN = 3,       /* a pointer is not aligned as documented */
+  NVFP4_ERR_UNSUPPORTED = 4, /* M > NVFP4_MAX_M, topk > NVFP4_MAX_TOPK, ... */
+  NVFP4_ERR_WORKSPACE = 5,   /* workspace NULL or smaller than required */
+  NVFP4_ERR_HIP = 6,         /* a HIP call or kernel launch failed */
+  NVFP4_ERR_ALIAS = 7        /* an output overlaps an input */
+} nvfp4_status;
+
+/* NVFP4_ABI_VERSION of the loaded library. */
+int nvfp4_abi_version(void);
+
+/* Static text for a status code (never NULL). */
+const char* nvfp4_status_string(int status);
+
+/* Detail of the last failing call on the calling thread ("" if none). The
+   text stays valid until the next library call on the same thread. */
+const char* nvfp4_last_error(void);
+
+/*
+ * nvfp4_pack -- quantise fp32 W[N, K] to NVFP4 g16 (blueprint page Precision
+ * table "nvfp4/g16"; card.json performance[6].note "E2M1 + UE4M3/16"), with
+ * the two-level recipe of the workload: tensor scale g = max|W| / (6 * 448)
+ * (g = 1 for an all-zero W), block scale = E4M3(amax_block / (6 g)), element
+ * code = E2M1(w / (s g)). Both encodings round to nearest, ties to the even
+ * code, and saturate (448 and 6); negative values that round to 0 become +0.
+ * All arithmetic is IEEE fp32 (correctly rounded divisions, no contraction),
+ * so the result is bit-for-bit reproducible on any IEEE host.
+ *
+ *   W              float[N, K], 16-byte aligned. Finite values required; the
+ *                  result for NaN/Inf input is unspecified (no fault).
+ *   N, K           N >= 0, K >= 0, K % 16 == 0.
+ *   codes          uint8[N, K/2] out, 8-byte aligned.
+ *   scales         uint8[N, K/16] out.
+ *   gscale         float[1] out: g.
+ *   gscale_override NULL, or a device float[1] holding g to use instead of
+ *                  max|W| / 2688 (must be finite and > 0; not checked).
+ *   stream         HIP stream.
+ * Errors: NULL, SHAPE, ALIGN, ALIAS, HIP.
+ */
+nvfp4_status nvfp4_pack(const float* W, int64_t N, int64_t K, uint8_t* codes,
+                        uint8_t* scales, float* gscale, const float* gscale_override,
+                        hipStream_t stream);
+
+/*
+ * nvfp4_dequant -- W_out[n, k] = (e2m1 * s) * g in fp32: the product e2m1 * s
+ * is exact and the only rounding is the multiply by g ("weight
+ * nvfp4/g16->bf16" step of graph.json node "l0.kda.q", here to fp32).
+ *
+ *   codes   uint8[N, K/2], 16-byte aligned;  scales uint8[N, K/16];
+ *   gscale  float[1];  N >= 0, K >= 0, K % 32 == 0;
+ *   W_out   float[N, K] out, 16-byte aligned.
+ * Errors: NULL, SHAPE, ALIGN, ALIAS, HIP.
+ */
+nvfp4_status nvfp4_dequant(const uint8_t* codes, const uint8_t* scales,
+                           const float* gscale, int64_t N, int64_t K, float* W_out,
+                           hipStream_t stream);
+
+/*
+ * nvfp4_gemv -- the W4A16 small-M GEMV of graph.json node "l0.kda.q" (steps
+ * act bf16 / weight nvfp4/g16->bf16 / mma / accumulate f32 / scale f32):
+ *
+ *   y[m, n] = g * sum_k e2m1(c[n,k]) * e4m3(s[n, k/16]) * x[m, k]
+ *
+ * with fp32 accumulation and the tensor scale applied once at the end.
+ * Accuracy: |y - y_exact| <= 1e-3 * sum_k |w * x| + 1e-6.
+ *
+ *   codes   uint8[N, K/2], 16-byte aligned;  scales uint8[N, K/16], 2-byte
+ *           aligned;  gscale float[1];
+ *   x       bf16[M, K] given as uint16 bit patterns, 16-byte aligned;
+ *   M       0 <= M <= NVFP4_MAX_M;  N >= 0;  K >= 0, K % 32 == 0;
+ *   y       float[M, N] out, 4-byte aligned (M == 0 or N == 0: nothing is
+ *           launched; K == 0: y is set to zero).
+ * Errors: NULL, SHAPE, ALIGN, UNSUPPORTED (M > 8), ALIAS, HIP.
+ */
+nvfp4_status nvfp4_gemv(const uint8_t* codes, const uint8_t* scales,
+                        const float* gscale, const uint16_t* x, int64_t M,
+                        int64_t N, int64_t K, float* y, hipStream_t stream);
+
+/*
+ * nvfp4_moe_workspace_bytes -- device workspace that nvfp4_moe_gemv needs for
+ * the given sizes (the row-union tables, the bf16 SwiGLU activations
+ * h[M*topk, I] and the per-slot fp32 outputs [M*topk, H]).
+ */
+size_t nvfp4_moe_workspace_bytes(int64_t M, int64_t H, int64_t I, int64_t topk);
+
+/*
+ * nvfp4_moe_gemv -- MoE expert slots, W4A16 (card.json performance[33]
+ * w4a16_gemv_sw_moe; performance[31] row union; graph.json nodes
+ * "l3.moe.experts_act" and "l3.moe.blend"). For token m and slot j < topk:
+ *
+ *   e  = expert_ids[m, j]            (an id outside [0, E) adds nothing)
+ *   a  = g13[e] * W13[e] . x[m]      (2I values, fp32 accumulation)
+ *   h  = bf16( silu(a[0:I]) * a[I:2I] ),  silu(v) = v / (1 + exp(-v))
+ *   y[m] += gate_w[m, j] * ( g2[e] * W2[e] . h )
+ *
+ * Each distinct expert of the batch is streamed once (the union of ids over
+ * the M rows is built on the device, no host sync). The combine sums the
+ * slots of a token in slot order (deterministic).
+ *
+ *   w13_codes  uint8[E, 2I, H/2] (rows 0..I-1 gate, I..2I-1 up), 16-byte
+ *              aligned; w13_scales uint8[E, 2I, H/16], 2-byte aligned;
+ *              w13_gscale float[E];
+ *   w2_codes   uint8[E, H, I/2], 16-byte aligned; w2_scales uint8[E, H, I/16],
+ *              2-byte aligned; w2_gscale float[E];
+ *   x          bf16[M, H] (uint16 bits), 16-byte aligned;
+ *   expert_ids int32[M, topk];  gate_w float[M, topk];
+ *   M          0 <= M <= NVFP4_MAX_M; 1 <= topk <= NVFP4_MAX_TOPK; E >= 1;
+ *              H % 32 == 0, I % 32 == 0, H > 0, I > 0;
+ *   y          float[M, H] out, 16-byte aligned;
+ *   workspace  device buffer of at least nvfp4_moe_workspace_bytes(M, H, I,
+ *              topk) bytes, 256-byte aligned; overwritten; must not be shared
+ *              by calls that may run concurrently.
+ * Errors: NULL, SHAPE, ALIGN, UNSUPPORTED, WORKSPACE, ALIAS, HIP.
+ */
+nvfp4_status nvfp4_moe_gemv(const uint8_t* w13_codes, const uint8_t* w13_scales,
+                            const float* w13_gscale, const uint8_t* w2_codes,
+                            const uint8_t* w2_scales, const float* w2_gscale,
+                            const uint16_t* x, const int32_t* expert_ids,
+                            const float* gate_w, int64_t M, int64_t E, int64_t H,
+                            int64_t I, int64_t topk, float* y, void* workspace,
+                            size_t workspace_bytes, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* NVFP4_GEMV_H */

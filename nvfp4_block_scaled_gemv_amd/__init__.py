@@ -1,0 +1,215 @@
+"""NVFP4 g16 W4A16 small-M GEMV for MI355X (gfx950): a thin Python binding.
+
+Every function here marshals torch tensors into the C ABI declared in
+``include/nvfp4_gemv.h`` and calls ``libnvfp4_gemv.so``; all computation runs
+in the library's HIP kernels on the tensors' device, on the current torch
+stream. PyTorch only provides device memory and streams. There is no CPU
+fallback: if the library is not built, every call raises.
+
+Functions (same names as the C entry points, without the prefix):
+  pack(W[, gscale_override])             -> codes, scales, gscale
+  dequant(codes, scales, gscale)         -> W_hat (fp32)
+  gemv(codes, scales, gscale, x)         -> y (fp32 [M, N])
+  moe_workspace_bytes(M, H, I, topk)     -> int
+  moe_gemv(w13..., w2..., x, ids, gate_w[, workspace]) -> y (fp32 [M, H])
+The ``*_into`` variants write into caller-provided outputs.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+from . import traffic  # noqa: F401  (algorithmic byte model, pure Python)
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libnvfp4_gemv.so")
+HEADER_PATH = os.path.join(os.path.dirname(_HERE), "include", "nvfp4_gemv.h")
+
+MAX_M = 8
+MAX_TOPK = 16
+
+_VP = ctypes.c_void_p
+_I64 = ctypes.c_int64
+_lib = None
+
+
+class Nvfp4Error(RuntimeError):
+    def __init__(self, fn: str, status: int, detail: str):
+        super().__init__(f"{fn} failed: status {status} ({detail})")
+        self.status = status
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded C library (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(
+                f"{LIB_PATH} is not built; run "
+                "`python -m nvfp4_block_scaled_gemv_amd.build` (no CPU fallback exists)")
+        L = ctypes.CDLL(LIB_PATH)
+        L.nvfp4_abi_version.restype = ctypes.c_int
+        L.nvfp4_abi_version.argtypes = []
+        L.nvfp4_status_string.restype = ctypes.c_char_p
+        L.nvfp4_status_string.argtypes = [ctypes.c_int]
+        L.nvfp4_last_error.restype = ctypes.c_char_p
+        L.nvfp4_last_error.argtypes = []
+        L.nvfp4_pack.restype = ctypes.c_int
+        L.nvfp4_pack.argtypes = [_VP, _I64, _I64, _VP, _VP, _VP, _VP, _VP]
+        L.nvfp4_dequant.restype = ctypes.c_int
+        L.nvfp4_dequant.argtypes = [_VP, _VP, _VP, _I64, _I64, _VP, _VP]
+        L.nvfp4_gemv.restype = ctypes.c_int
+        L.nvfp4_gemv.argtypes = [_VP, _VP, _VP, _VP, _I64, _I64, _I64, _VP, _VP]
+        L.nvfp4_moe_workspace_bytes.restype = ctypes.c_size_t
+        L.nvfp4_moe_workspace_bytes.argtypes = [_I64, _I64, _I64, _I64]
+        L.nvfp4_moe_gemv.restype = ctypes.c_int
+        L.nvfp4_moe_gemv.argtypes = [_VP] * 9 + [_I64] * 5 + [_VP, _VP, ctypes.c_size_t, _VP]
+        _lib = L
+    return _lib
+
+
+def _check(fn: str, status: int) -> None:
+    if status != 0:
+        L = lib()
+        detail = (L.nvfp4_last_error() or b"").decode() or \
+            L.nvfp4_status_string(status).decode()
+        raise Nvfp4Error(fn, status, detail)
+
+
+def _stream(t: torch.Tensor) -> int:
+    return torch.cuda.current_stream(t.device).cuda_stream
+
+
+def _p(t) -> int | None:
+    return None if t is None else t.data_ptr()
+
+
+def _dev(*ts):
+    d = None
+    for t in ts:
+        if t is None:
+            continue
+        if not t.is_cuda:
+            raise ValueError("tensors must be on a HIP device")
+        if not t.is_contiguous():
+            raise ValueError("tensors must be contiguous")
+        if d is None:
+            d = t.device
+        elif t.device != d:
+            raise ValueError("tensors must be on one device")
+    return d
+
+
+def _dtype(t, *dts, name="tensor"):
+    if t.dtype not in dts:
+        raise TypeError(f"{name} must be one of {dts}, got {t.dtype}")
+
+
+# ------------------------------------------------------------------ pack
+
+def pack_into(W, codes, scales, gscale, gscale_override=None) -> None:
+    _dev(W, codes, scales, gscale, gscale_override)
+    _dtype(W, torch.float32, name="W")
+    N, K = W.shape
+    _check("nvfp4_pack", lib().nvfp4_pack(_p(W), N, K, _p(codes), _p(scales), _p(gscale),
+                                          _p(gscale_override), _stream(W)))
+
+
+def pack(W: torch.Tensor, gscale_override: torch.Tensor | None = None):
+    """fp32 W[N, K] -> (codes u8[N, K/2], scales u8[N, K/16], gscale f32[1])."""
+    N, K = W.shape
+    codes = torch.empty((N, K // 2), dtype=torch.uint8, device=W.device)
+    scales = torch.empty((N, K // 16), dtype=torch.uint8, device=W.device)
+    gscale = torch.empty((1,), dtype=torch.float32, device=W.device)
+    pack_into(W, codes, scales, gscale, gscale_override)
+    return codes, scales, gscale
+
+
+# --------------------------------------------------------------- dequant
+
+def dequant_into(codes, scales, gscale, out) -> None:
+    _dev(codes, scales, gscale, out)
+    N, K = codes.shape[0], codes.shape[1] * 2
+    _check("nvfp4_dequant", lib().nvfp4_dequant(_p(codes), _p(scales), _p(gscale), N, K,
+                                                _p(out), _stream(codes)))
+
+
+def dequant(codes, scales, gscale) -> torch.Tensor:
+    N, K = codes.shape[0], codes.shape[1] * 2
+    out = torch.empty((N, K), dtype=torch.float32, device=codes.device)
+    dequant_into(codes, scales, gscale, out)
+    return out
+
+
+# ------------------------------------------------------------------ gemv
+
+def gemv_into(codes, scales, gscale, x, y) -> None:
+    """y[M, N] (fp32) = g * decode(W) . x^T for bf16 x[M, K]."""
+    _dev(codes, scales, gscale, x, y)
+    _dtype(x, torch.bfloat16, torch.int16, torch.uint16, name="x")
+    _dtype(y, torch.float32, name="y")
+    N, K = codes.shape[0], codes.shape[1] * 2
+    M = x.shape[0]
+    if x.shape[1] != K or tuple(y.shape) != (M, N):
+        raise ValueError(f"shape mismatch: codes {tuple(codes.shape)}, x {tuple(x.shape)}, "
+                         f"y {tuple(y.shape)}")
+    _check("nvfp4_gemv", lib().nvfp4_gemv(_p(codes), _p(scales), _p(gscale), _p(x), M, N, K,
+                                          _p(y), _stream(codes)))
+
+
+def gemv(codes, scales, gscale, x) -> torch.Tensor:
+    y = torch.empty((x.shape[0], codes.shape[0]), dtype=torch.float32, device=codes.device)
+    gemv_into(codes, scales, gscale, x, y)
+    return y
+
+
+# ------------------------------------------------------------------- moe
+
+def moe_workspace_bytes(M: int, H: int, I: int, topk: int) -> int:
+    return int(lib().nvfp4_moe_workspace_bytes(M, H, I, topk))
+
+
+def moe_gemv_into(w13_codes, w13_scales, w13_gscale, w2_codes, w2_scales, w2_gscale,
+                  x, expert_ids, gate_w, y, workspace) -> None:
+    _dev(w13_codes, w13_scales, w13_gscale, w2_codes, w2_scales, w2_gscale, x,
+         expert_ids, gate_w, y, workspace)
+    _dtype(x, torch.bfloat16, torch.int16, torch.uint16, name="x")
+    _dtype(expert_ids, torch.int32, name="expert_ids")
+    _dtype(gate_w, torch.float32, name="gate_w")
+    E, twoI, Hh = w13_codes.shape
+    H, I = Hh * 2, twoI // 2
+    M, topk = expert_ids.shape
+    if tuple(w2_codes.shape) != (E, H, I // 2) or tuple(x.shape) != (M, H) \
+            or tuple(gate_w.shape) != (M, topk) or tuple(y.shape) != (M, H):
+        raise ValueError("inconsistent MoE shapes")
+    _check("nvfp4_moe_gemv", lib().nvfp4_moe_gemv(
+        _p(w13_codes), _p(w13_scales), _p(w13_gscale), _p(w2_codes), _p(w2_scales),
+        _p(w2_gscale), _p(x), _p(expert_ids), _p(gate_w), M, E, H, I, topk, _p(y),
+        _p(workspace), workspace.numel() * workspace.element_size(), _stream(x)))
+
+
+def moe_gemv(w13_codes, w13_scales, w13_gscale, w2_codes, w2_scales, w2_gscale, x,
+             expert_ids, gate_w, workspace: torch.Tensor | None = None) -> torch.Tensor:
+    E, twoI, Hh = w13_codes.shape
+    H, I = Hh * 2, twoI // 2
+    M, topk = expert_ids.shape
+    if workspace is None:
+        workspace = torch.empty(max(moe_workspace_bytes(M, H, I, topk), 256),
+                                dtype=torch.uint8, device=x.device)
+    y = torch.empty((M, H), dtype=torch.float32, device=x.device)
+    moe_gemv_into(w13_codes, w13_scales, w13_gscale, w2_codes, w2_scales, w2_gscale, x,
+                  expert_ids, gate_w, y, workspace)
+    return y
+
+
+def moe_workspace_layout(M: int, H: int, I: int, topk: int) -> dict:
+    """Byte offsets inside the MoE workspace (for inspecting the bf16 SwiGLU
+    activations h[M*topk, I] after a call)."""
+    def a256(v):
+        return (v + 255) & ~255
+    S = M * topk
+    h_off = a256((S + 1) * 4)
+    o_off = a256(h_off + S * I * 2)
+    return {"union": 0, "h": h_off, "o": o_off, "total": a256(o_off + S * H * 4)}

@@ -1,0 +1,51 @@
+"""Build libnvfp4_gemv.so (the HIP kernels and the C ABI) for gfx950 in-tree.
+
+hipcc flags:
+  -ffp-contract=off                          no implicit FMA: the pack's fp32
+                                             steps round exactly as written
+  -fhip-fp32-correctly-rounded-divide-sqrt   IEEE division in the pack
+  -Xclang -target-feature -Xclang -packed-fp32-ops
+                                             no packed fp32 instructions
+"""
+import glob
+import os
+import subprocess
+import sys
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+CSRC = os.path.join(HERE, "csrc")
+LIB = os.path.join(HERE, "libnvfp4_gemv.so")
+ARCH = "gfx950"
+
+FLAGS = [
+    f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
+    "-ffp-contract=off", "-fhip-fp32-correctly-rounded-divide-sqrt",
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-Wall", "-Wno-unused-function",
+]
+
+
+def sources():
+    return sorted(glob.glob(os.path.join(CSRC, "*.hip")))
+
+
+def build(verbose: bool = False) -> str:
+    hipcc = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+    cmd = [hipcc, *FLAGS, "-o", LIB + ".tmp", *sources()]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    # hipcc's host pass does not know the packed-fp32 feature and says so
+    noise = "'-packed-fp32-ops' is not a recognized feature for this target"
+    err = "\n".join(l for l in res.stderr.splitlines() if noise not in l)
+    if res.returncode != 0:
+        sys.stderr.write(err + "\n")
+        raise RuntimeError(f"hipcc failed with status {res.returncode}")
+    if verbose and err.strip():
+        sys.stderr.write(err + "\n")
+    os.replace(LIB + ".tmp", LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    print(build(verbose=True))

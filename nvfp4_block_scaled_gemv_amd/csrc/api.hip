@@ -1,0 +1,183 @@
+// api.hip -- the extern "C" boundary: host-side argument checks, then the
+// launches on the caller's stream. No allocation, no synchronisation.
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "../../include/nvfp4_gemv.h"
+#include "internal.h"
+
+static_assert(NVFP4_MAX_M == NVFP4_MAX_M_INTERNAL, "M limit mismatch");
+static_assert(NVFP4_MAX_TOPK == NVFP4_MAX_TOPK_INTERNAL, "topk limit mismatch");
+
+namespace {
+
+thread_local char g_last_error[512] = "";
+
+nvfp4_status fail(nvfp4_status st, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
+  va_end(ap);
+  return st;
+}
+
+void clear_error() { g_last_error[0] = '\0'; }
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+// [a, a + na) and [b, b + nb) share a byte.
+bool overlap(const void* a, size_t na, const void* b, size_t nb) {
+  if (!a || !b || na == 0 || nb == 0) return false;
+  const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+  return x < y + nb && y < x + na;
+}
+
+nvfp4_status hip_result(hipError_t e, const char* what) {
+  if (e != hipSuccess)
+    return fail(NVFP4_ERR_HIP, "%s: %s (%s)", what, hipGetErrorName(e), hipGetErrorString(e));
+  return NVFP4_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int nvfp4_abi_version(void) { return NVFP4_ABI_VERSION; }
+
+const char* nvfp4_status_string(int status) {
+  switch (status) {
+    case NVFP4_OK: return "ok";
+    case NVFP4_ERR_NULL: return "null pointer";
+    case NVFP4_ERR_SHAPE: return "invalid shape";
+    case NVFP4_ERR_ALIGN: return "misaligned pointer";
+    case NVFP4_ERR_UNSUPPORTED: return "unsupported size";
+    case NVFP4_ERR_WORKSPACE: return "workspace too small";
+    case NVFP4_ERR_HIP: return "HIP error";
+    case NVFP4_ERR_ALIAS: return "output overlaps an input";
+    default: return "unknown status";
+  }
+}
+
+const char* nvfp4_last_error(void) { return g_last_error; }
+
+nvfp4_status nvfp4_pack(const float* W, int64_t N, int64_t K, uint8_t* codes,
+                        uint8_t* scales, float* gscale, const float* gscale_override,
+                        hipStream_t stream) {
+  clear_error();
+  if (N < 0 || K < 0 || (K % 16) != 0)
+    return fail(NVFP4_ERR_SHAPE, "nvfp4_pack: need N >= 0, K >= 0, K %% 16 == 0 (N=%lld K=%lld)",
+                (long long)N, (long long)K);
+  const size_t numel = (size_t)N * (size_t)K;
+  if (!gscale || (numel && (!W || !codes || !scales)))
+    return fail(NVFP4_ERR_NULL, "nvfp4_pack: W, codes, scales and gscale must be non-NULL");
+  if (!aligned(W, 16) || !aligned(codes, 8) || !aligned(gscale, 4) ||
+      (gscale_override && !aligned(gscale_override, 4)))
+    return fail(NVFP4_ERR_ALIGN, "nvfp4_pack: W must be 16-byte, codes 8-byte, gscale 4-byte aligned");
+  const size_t wb = numel * 4, cb = numel / 2, sb = numel / 16;
+  if (overlap(codes, cb, W, wb) || overlap(scales, sb, W, wb) || overlap(gscale, 4, W, wb) ||
+      overlap(codes, cb, scales, sb) || overlap(codes, cb, gscale, 4) ||
+      overlap(scales, sb, gscale, 4) || overlap(gscale, 4, gscale_override, 4))
+    return fail(NVFP4_ERR_ALIAS, "nvfp4_pack: outputs overlap each other or an input");
+  return hip_result(nvfp4::launch_pack(W, N, K, codes, scales, gscale, gscale_override, stream),
+                    "nvfp4_pack launch");
+}
+
+nvfp4_status nvfp4_dequant(const uint8_t* codes, const uint8_t* scales, const float* gscale,
+                           int64_t N, int64_t K, float* W_out, hipStream_t stream) {
+  clear_error();
+  if (N < 0 || K < 0 || (K % 32) != 0)
+    return fail(NVFP4_ERR_SHAPE, "nvfp4_dequant: need N >= 0, K >= 0, K %% 32 == 0 (N=%lld K=%lld)",
+                (long long)N, (long long)K);
+  const size_t numel = (size_t)N * (size_t)K;
+  if (numel == 0) return NVFP4_OK;
+  if (!codes || !scales || !gscale || !W_out)
+    return fail(NVFP4_ERR_NULL, "nvfp4_dequant: NULL pointer");
+  if (!aligned(codes, 16) || !aligned(W_out, 16) || !aligned(gscale, 4))
+    return fail(NVFP4_ERR_ALIGN, "nvfp4_dequant: codes and W_out must be 16-byte aligned");
+  if (overlap(W_out, numel * 4, codes, numel / 2) || overlap(W_out, numel * 4, scales, numel / 16) ||
+      overlap(W_out, numel * 4, gscale, 4))
+    return fail(NVFP4_ERR_ALIAS, "nvfp4_dequant: W_out overlaps an input");
+  return hip_result(nvfp4::launch_dequant(codes, scales, gscale, N, K, W_out, stream),
+                    "nvfp4_dequant launch");
+}
+
+nvfp4_status nvfp4_gemv(const uint8_t* codes, const uint8_t* scales, const float* gscale,
+                        const uint16_t* x, int64_t M, int64_t N, int64_t K, float* y,
+                        hipStream_t stream) {
+  clear_error();
+  if (M < 0 || N < 0 || K < 0 || (K % 32) != 0)
+    return fail(NVFP4_ERR_SHAPE, "nvfp4_gemv: need M, N, K >= 0 and K %% 32 == 0 (M=%lld N=%lld K=%lld)",
+                (long long)M, (long long)N, (long long)K);
+  if (M > NVFP4_MAX_M)
+    return fail(NVFP4_ERR_UNSUPPORTED, "nvfp4_gemv: M=%lld exceeds %d", (long long)M, NVFP4_MAX_M);
+  if (M == 0 || N == 0) return NVFP4_OK;
+  if (!y) return fail(NVFP4_ERR_NULL, "nvfp4_gemv: y is NULL");
+  if (!aligned(y, 4)) return fail(NVFP4_ERR_ALIGN, "nvfp4_gemv: y must be 4-byte aligned");
+  const size_t yb = (size_t)M * (size_t)N * 4;
+  if (K == 0) return hip_result(nvfp4::launch_fill_zero(y, (size_t)M * (size_t)N, stream),
+                                "nvfp4_gemv zero fill");
+  if (!codes || !scales || !gscale || !x) return fail(NVFP4_ERR_NULL, "nvfp4_gemv: NULL input");
+  if (!aligned(codes, 16) || !aligned(scales, 2) || !aligned(x, 16) || !aligned(gscale, 4))
+    return fail(NVFP4_ERR_ALIGN,
+                "nvfp4_gemv: codes and x must be 16-byte, scales 2-byte, gscale 4-byte aligned");
+  const size_t nk = (size_t)N * (size_t)K;
+  if (overlap(y, yb, codes, nk / 2) || overlap(y, yb, scales, nk / 16) ||
+      overlap(y, yb, gscale, 4) || overlap(y, yb, x, (size_t)M * (size_t)K * 2))
+    return fail(NVFP4_ERR_ALIAS, "nvfp4_gemv: y overlaps an input");
+  return hip_result(nvfp4::launch_gemv(codes, scales, gscale, x, (int)M, N, K, y, stream),
+                    "nvfp4_gemv launch");
+}
+
+size_t nvfp4_moe_workspace_bytes(int64_t M, int64_t H, int64_t I, int64_t topk) {
+  if (M < 0 || H < 0 || I < 0 || topk < 0) return 0;
+  return nvfp4::moe_layout(M, H, I, topk).total;
+}
+
+nvfp4_status nvfp4_moe_gemv(const uint8_t* w13_codes, const uint8_t* w13_scales,
+                            const float* w13_gscale, const uint8_t* w2_codes,
+                            const uint8_t* w2_scales, const float* w2_gscale, const uint16_t* x,
+                            const int32_t* expert_ids, const float* gate_w, int64_t M, int64_t E,
+                            int64_t H, int64_t I, int64_t topk, float* y, void* workspace,
+                            size_t workspace_bytes, hipStream_t stream) {
+  clear_error();
+  if (M < 0 || E < 1 || H <= 0 || I <= 0 || topk < 1 || (H % 32) != 0 || (I % 32) != 0)
+    return fail(NVFP4_ERR_SHAPE,
+                "nvfp4_moe_gemv: need M >= 0, E >= 1, topk >= 1, H, I > 0 and multiples of 32 "
+                "(M=%lld E=%lld H=%lld I=%lld topk=%lld)",
+                (long long)M, (long long)E, (long long)H, (long long)I, (long long)topk);
+  if (M > NVFP4_MAX_M || topk > NVFP4_MAX_TOPK)
+    return fail(NVFP4_ERR_UNSUPPORTED, "nvfp4_moe_gemv: M=%lld (max %d), topk=%lld (max %d)",
+                (long long)M, NVFP4_MAX_M, (long long)topk, NVFP4_MAX_TOPK);
+  if (M == 0) return NVFP4_OK;
+  if (!w13_codes || !w13_scales || !w13_gscale || !w2_codes || !w2_scales || !w2_gscale || !x ||
+      !expert_ids || !gate_w || !y)
+    return fail(NVFP4_ERR_NULL, "nvfp4_moe_gemv: NULL pointer");
+  const size_t need = nvfp4::moe_layout(M, H, I, topk).total;
+  if (!workspace || workspace_bytes < need)
+    return fail(NVFP4_ERR_WORKSPACE, "nvfp4_moe_gemv: workspace of %zu bytes needed, %zu given",
+                need, workspace ? workspace_bytes : (size_t)0);
+  if (!aligned(w13_codes, 16) || !aligned(w2_codes, 16) || !aligned(w13_scales, 2) ||
+      !aligned(w2_scales, 2) || !aligned(x, 16) || !aligned(y, 16) || !aligned(workspace, 256) ||
+      !aligned(expert_ids, 4) || !aligned(gate_w, 4) || !aligned(w13_gscale, 4) ||
+      !aligned(w2_gscale, 4))
+    return fail(NVFP4_ERR_ALIGN, "nvfp4_moe_gemv: alignment rule broken (see nvfp4_gemv.h)");
+  const size_t e13 = (size_t)E * 2 * (size_t)I * (size_t)H, e2 = (size_t)E * (size_t)H * (size_t)I;
+  const size_t yb = (size_t)M * (size_t)H * 4, S = (size_t)(M * topk);
+  const void* ins[] = {w13_codes, w13_scales, w13_gscale, w2_codes, w2_scales,
+                       w2_gscale, x,          expert_ids, gate_w};
+  const size_t insz[] = {e13 / 2, e13 / 16, (size_t)E * 4, e2 / 2, e2 / 16,
+                         (size_t)E * 4, (size_t)M * (size_t)H * 2, S * 4, S * 4};
+  for (int i = 0; i < 9; ++i) {
+    if (overlap(y, yb, ins[i], insz[i]) || overlap(workspace, need, ins[i], insz[i]))
+      return fail(NVFP4_ERR_ALIAS, "nvfp4_moe_gemv: y or workspace overlaps input %d", i);
+  }
+  if (overlap(y, yb, workspace, need))
+    return fail(NVFP4_ERR_ALIAS, "nvfp4_moe_gemv: y overlaps the workspace");
+  return hip_result(nvfp4::launch_moe(w13_codes, w13_scales, w13_gscale, w2_codes, w2_scales,
+                                      w2_gscale, x, expert_ids, gate_w, (int)M, E, H, I,
+                                      (int)topk, y, workspace, stream),
+                    "nvfp4_moe_gemv launch");
+}
+
+}  // extern "C"

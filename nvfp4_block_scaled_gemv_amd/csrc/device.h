@@ -1,0 +1,118 @@
+// device.h -- gfx950 device helpers for NVFP4 g16: element decode through the
+// CDNA4 conversion instructions, fp32 encoders for the pack kernel, and
+// wavefront reductions.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace nvfp4 {
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float float2_t __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+
+// 128-bit load with the non-temporal hint: streamed weights are read once.
+__device__ __forceinline__ u32x4_t load_stream(const void* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
+}
+
+// ------------------------------------------------------------------ decode
+
+// Two E2M1 codes (byte `sel` of `word`; low nibble -> .x) to bf16. The scale
+// operand of v_cvt_scalef32_pk_bf16_fp4 only contributes its exponent, so it
+// is always 1.0 here and block scales are applied to fp32 partial sums.
+template <int SEL>
+__device__ __forceinline__ bf16x2_t e2m1x2_to_bf16(uint32_t word) {
+  return __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(word, 1.0f, SEL);
+}
+
+template <int SEL>
+__device__ __forceinline__ float2_t e2m1x2_to_f32(uint32_t word) {
+  return __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(word, 1.0f, SEL);
+}
+
+// UE4M3 scale byte `sel` of `word` to fp32 (v_cvt_f32_fp8 decodes the OCP
+// E4M3FN format on gfx950; exact for every byte).
+template <int SEL>
+__device__ __forceinline__ float e4m3_to_f32(uint32_t word) {
+  return __builtin_amdgcn_cvt_f32_fp8(word, SEL);
+}
+
+// bf16 dot of two pairs accumulated into fp32: a.x*b.x + a.y*b.y + c.
+__device__ __forceinline__ float dot2(bf16x2_t a, bf16x2_t b, float c) {
+  return __builtin_amdgcn_fdot2_f32_bf16(a, b, c, false);
+}
+
+__device__ __forceinline__ bf16x2_t as_bf16x2(uint32_t u) {
+  bf16x2_t r;
+  __builtin_memcpy(&r, &u, 4);
+  return r;
+}
+
+// ------------------------------------------------------------------ encode
+// Round-to-nearest-even onto the E4M3 grid by integer manipulation of the
+// fp32 bit pattern, saturating at 448 (0x7E). Non-positive and NaN inputs
+// give 0x00 (a block scale is never negative).
+__device__ __forceinline__ uint32_t e4m3_encode(float r) {
+  if (!(r > 0.0f)) return 0u;
+  if (r > 448.0f) return 0x7Eu;
+  const uint32_t u = __float_as_uint(r);
+  const int exp = (int)(u >> 23) - 127;   // unbiased exponent of r
+  const uint32_t man = u & 0x7FFFFFu;
+  if (exp < -6) {
+    // E4M3 subnormal range: integer multiple of 2^-9. r = (2^23 + man) *
+    // 2^(exp - 23), so r * 2^9 = (2^23 + man) >> (14 - exp) with RNE.
+    if (exp < -10) return 0u;              // below 2^-10: rounds to zero
+    const uint32_t sig = man | 0x800000u;  // exp >= -10: r is an fp32 normal
+    const int sh = 14 - exp;               // 21 .. 24
+    const uint32_t q = sig >> sh;
+    const uint32_t rem = sig & ((1u << sh) - 1u);
+    const uint32_t half = 1u << (sh - 1);
+    return q + ((rem > half || (rem == half && (q & 1u))) ? 1u : 0u);
+  }
+  // normal range: keep 3 mantissa bits with RNE; a carry bumps the exponent
+  const uint32_t keep = man >> 20;
+  const uint32_t rem = man & 0xFFFFFu;
+  const uint32_t up = (rem > 0x80000u || (rem == 0x80000u && (keep & 1u))) ? 1u : 0u;
+  const uint32_t code = ((uint32_t)(exp + 7) << 3) + keep + up;
+  return code > 0x7Eu ? 0x7Eu : code;
+}
+
+// E2M1 code of t by comparison with the decision points between adjacent
+// magnitudes (0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5); a point exactly on a
+// boundary goes to the neighbour with the even code. Magnitudes above 5 give
+// 6 (saturating). A negative t whose magnitude rounds to 0 gives +0.
+__device__ __forceinline__ uint32_t e2m1_encode(float t) {
+  const float a = fabsf(t);
+  uint32_t mag;
+  if (a <= 0.25f) mag = 0u;
+  else if (a < 0.75f) mag = 1u;
+  else if (a <= 1.25f) mag = 2u;
+  else if (a < 1.75f) mag = 3u;
+  else if (a <= 2.5f) mag = 4u;
+  else if (a < 3.5f) mag = 5u;
+  else if (a <= 5.0f) mag = 6u;
+  else mag = 7u;
+  return (t < 0.0f && mag != 0u) ? (mag | 8u) : mag;
+}
+
+// --------------------------------------------------------------- reductions
+
+// Sum over the 64 lanes of a wavefront; every lane receives the total.
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
+  return v;
+}
+
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    uint32_t o = __shfl_xor(v, off, 64);
+    v = o > v ? o : v;
+  }
+  return v;
+}
+
+}  // namespace nvfp4

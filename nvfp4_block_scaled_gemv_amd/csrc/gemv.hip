@@ -1,0 +1,86 @@
+// gemv.hip -- dense NVFP4 g16 W4A16 GEMV for 1 <= M <= 8 on gfx950:
+//   y[m, n] = g * sum_k e2m1(c[n,k]) * s[n, k/16] * x[m, k]
+// (graph.json node "l0.kda.q": act bf16, weight nvfp4/g16 -> bf16,
+// accumulate f32, scale f32). Bandwidth-bound: every weight byte is read
+// from HBM exactly once; x (at most 8 x K bf16) stays in the caches.
+#include "gemv_core.h"
+#include "internal.h"
+
+namespace nvfp4 {
+
+constexpr int kWavesPerBlock = 4;
+
+// Each wavefront takes groups of R consecutive rows, striding over the grid.
+template <int M, int R>
+__global__ __launch_bounds__(256) void k_gemv(const uint8_t* __restrict__ codes,
+                                              const uint8_t* __restrict__ scales,
+                                              const float* __restrict__ gscale,
+                                              const uint16_t* __restrict__ x, int64_t N,
+                                              int64_t K, float* __restrict__ y) {
+  const int lane = threadIdx.x & 63;
+  const int64_t wave = (int64_t)blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6);
+  const int64_t nwaves = (int64_t)gridDim.x * kWavesPerBlock;
+  const float g = *gscale;
+  const uint16_t* xs[M];
+#pragma unroll
+  for (int m = 0; m < M; ++m) xs[m] = x + (int64_t)m * K;
+
+  for (int64_t n0 = wave * R; n0 < N; n0 += nwaves * R) {
+    int64_t rows[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) rows[r] = (n0 + r < N) ? (n0 + r) : (N - 1);
+    float acc[R][M];
+    wave_row_dots<M, R>(codes, scales, K, rows, xs, M, acc);
+    // lane (r * M + m) stores one result
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+#pragma unroll
+      for (int m = 0; m < M; ++m)
+        if (lane == r * M + m && n0 + r < N) y[(int64_t)m * N + n0 + r] = acc[r][m] * g;
+  }
+}
+
+__global__ void k_fill_zero(float* y, size_t n) {
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
+       i += (size_t)gridDim.x * blockDim.x)
+    y[i] = 0.0f;
+}
+
+hipError_t launch_fill_zero(float* y, size_t n, hipStream_t stream) {
+  if (n) {
+    const size_t want = (n + 255) / 256;
+    hipLaunchKernelGGL(k_fill_zero, dim3((unsigned)(want < 1024 ? want : 1024)), dim3(256),
+                       0, stream, y, n);
+  }
+  return hipGetLastError();
+}
+
+template <int M, int R>
+static void launch_m(const uint8_t* codes, const uint8_t* scales, const float* gscale,
+                     const uint16_t* x, int64_t N, int64_t K, float* y, hipStream_t stream) {
+  const int64_t groups = (N + R - 1) / R;
+  const int64_t want = (groups + kWavesPerBlock - 1) / kWavesPerBlock;
+  const int64_t cap = 256 * 8;   // 8 workgroups (32 wavefronts) per CU
+  const unsigned grid = (unsigned)(want < cap ? want : cap);
+  hipLaunchKernelGGL((k_gemv<M, R>), dim3(grid), dim3(256), 0, stream, codes, scales, gscale,
+                     x, N, K, y);
+}
+
+hipError_t launch_gemv(const uint8_t* codes, const uint8_t* scales, const float* gscale,
+                       const uint16_t* x, int M, int64_t N, int64_t K, float* y,
+                       hipStream_t stream) {
+  switch (M) {
+    case 1: launch_m<1, 4>(codes, scales, gscale, x, N, K, y, stream); break;
+    case 2: launch_m<2, 4>(codes, scales, gscale, x, N, K, y, stream); break;
+    case 3: launch_m<3, 4>(codes, scales, gscale, x, N, K, y, stream); break;
+    case 4: launch_m<4, 4>(codes, scales, gscale, x, N, K, y, stream); break;
+    case 5: launch_m<5, 4>(codes, scales, gscale, x, N, K, y, stream); break;
+    case 6: launch_m<6, 4>(codes, scales, gscale, x, N, K, y, stream); break;
+    case 7: launch_m<7, 4>(codes, scales, gscale, x, N, K, y, stream); break;
+    case 8: launch_m<8, 4>(codes, scales, gscale, x, N, K, y, stream); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace nvfp4

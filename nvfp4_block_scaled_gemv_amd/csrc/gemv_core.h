@@ -1,0 +1,88 @@
+// gemv_core.h -- the wavefront-level NVFP4 g16 x bf16 dot-product engine used
+// by the dense GEMV and by both MoE sweeps.
+//
+// Layout of the work: one wavefront owns R weight rows at a time. The K axis
+// of a row is cut into 32-element chunks (16 code bytes = one 128-bit load,
+// plus 2 scale bytes); lane l takes chunks l, l+64, l+128, ... so that each
+// wavefront load instruction reads 1 KiB of contiguous codes. A chunk is
+// decoded once (v_cvt_scalef32_pk_bf16_fp4, exact) and reused for every
+// activation row; per 16-element block and activation row, 8 bf16 pair dots
+// (v_dot2_f32_bf16) give a block partial that is multiplied by the block's
+// E4M3 scale and accumulated in fp32. Lanes are summed at the end.
+#pragma once
+
+#include "device.h"
+
+namespace nvfp4 {
+
+// out[r][m] = sum_k e2m1(c[row_r, k]) * s[row_r, k/16] * x_m[k]  (no tensor
+// scale), for r < R and m < ns (ns <= MS; entries m >= ns are left at 0).
+// Every lane of the wavefront receives the totals. `rows[r]` must be valid
+// row indices (callers clamp ragged tails and drop the duplicate results).
+template <int MS, int R>
+__device__ __forceinline__ void wave_row_dots(const uint8_t* __restrict__ codes,
+                                              const uint8_t* __restrict__ scales,
+                                              int64_t K, const int64_t (&rows)[R],
+                                              const uint16_t* const (&xs)[MS], int ns,
+                                              float (&out)[R][MS]) {
+  const int lane = threadIdx.x & 63;
+  const int64_t C = K >> 5;        // chunks per row
+  const int64_t cb = K >> 1;       // code bytes per row
+  const int64_t sb = K >> 4;       // scale bytes per row
+#pragma unroll
+  for (int r = 0; r < R; ++r)
+#pragma unroll
+    for (int m = 0; m < MS; ++m) out[r][m] = 0.0f;
+
+  for (int64_t c = lane; c < C; c += 64) {
+    u32x4_t q[R];
+    uint32_t sw[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      q[r] = load_stream(codes + rows[r] * cb + c * 16);
+      sw[r] = *reinterpret_cast<const uint16_t*>(scales + rows[r] * sb + c * 2);
+    }
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+      bf16x2_t wd[R][8];
+      float s[R];
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        const uint32_t w0 = b ? q[r].z : q[r].x;
+        const uint32_t w1 = b ? q[r].w : q[r].y;
+        wd[r][0] = e2m1x2_to_bf16<0>(w0);
+        wd[r][1] = e2m1x2_to_bf16<1>(w0);
+        wd[r][2] = e2m1x2_to_bf16<2>(w0);
+        wd[r][3] = e2m1x2_to_bf16<3>(w0);
+        wd[r][4] = e2m1x2_to_bf16<0>(w1);
+        wd[r][5] = e2m1x2_to_bf16<1>(w1);
+        wd[r][6] = e2m1x2_to_bf16<2>(w1);
+        wd[r][7] = e2m1x2_to_bf16<3>(w1);
+        s[r] = b ? e4m3_to_f32<1>(sw[r]) : e4m3_to_f32<0>(sw[r]);
+      }
+#pragma unroll
+      for (int m = 0; m < MS; ++m) {
+        if (m < ns) {
+          const uint4* xp = reinterpret_cast<const uint4*>(xs[m] + c * 32 + b * 16);
+          const uint4 xa = xp[0], xb = xp[1];
+          const bf16x2_t xv[8] = {as_bf16x2(xa.x), as_bf16x2(xa.y), as_bf16x2(xa.z),
+                                  as_bf16x2(xa.w), as_bf16x2(xb.x), as_bf16x2(xb.y),
+                                  as_bf16x2(xb.z), as_bf16x2(xb.w)};
+#pragma unroll
+          for (int r = 0; r < R; ++r) {
+            float p = 0.0f;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) p = dot2(wd[r][j], xv[j], p);
+            out[r][m] = __builtin_fmaf(p, s[r], out[r][m]);
+          }
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int r = 0; r < R; ++r)
+#pragma unroll
+    for (int m = 0; m < MS; ++m) out[r][m] = wave_sum(out[r][m]);
+}
+
+}  // namespace nvfp4

@@ -1,0 +1,42 @@
+// internal.h -- launchers shared between the kernels and the C ABI layer.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+// Limits of one call (the public header exports the same values).
+#define NVFP4_MAX_M_INTERNAL 8
+#define NVFP4_MAX_TOPK_INTERNAL 16
+
+namespace nvfp4 {
+
+hipError_t launch_pack(const float* W, int64_t N, int64_t K, uint8_t* codes,
+                       uint8_t* scales, float* gscale, const float* override_g,
+                       hipStream_t stream);
+
+hipError_t launch_dequant(const uint8_t* codes, const uint8_t* scales, const float* gscale,
+                          int64_t N, int64_t K, float* out, hipStream_t stream);
+
+hipError_t launch_gemv(const uint8_t* codes, const uint8_t* scales, const float* gscale,
+                       const uint16_t* x, int M, int64_t N, int64_t K, float* y,
+                       hipStream_t stream);
+
+hipError_t launch_fill_zero(float* y, size_t n, hipStream_t stream);
+
+// MoE workspace layout (byte offsets from the workspace base, 256-aligned).
+struct MoeLayout {
+  size_t union_off;   // int32: [0] = number of distinct experts, [1..S] ids
+  size_t h_off;       // uint16 bf16 h[S, I]
+  size_t o_off;       // float per-slot outputs [S, H]
+  size_t total;
+};
+MoeLayout moe_layout(int64_t M, int64_t H, int64_t I, int64_t topk);
+
+hipError_t launch_moe(const uint8_t* w13_codes, const uint8_t* w13_scales,
+                      const float* w13_gscale, const uint8_t* w2_codes,
+                      const uint8_t* w2_scales, const float* w2_gscale, const uint16_t* x,
+                      const int32_t* ids, const float* gate_w, int M, int64_t E, int64_t H,
+                      int64_t I, int topk, float* y, void* workspace, hipStream_t stream);
+
+}  // namespace nvfp4

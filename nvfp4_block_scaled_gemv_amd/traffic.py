@@ -1,0 +1,38 @@
+"""Algorithmic HBM bytes of one call: what the method must move, used for the
+achieved-bandwidth and roofline figures.
+
+The blueprint's card.json prices every W4A16 GEMV row at
+  N*K*bits/8 + M*K*2 + M*N*2  bytes (floor_us = bytes / 249 GB/s),
+with 4.5 bits per weight (a 4-bit code plus one 8-bit scale per 16 weights);
+``pages_floor_us`` reproduces the printed floors. This library returns fp32
+y, so its own per-call count is
+  gemv_bytes = N*K/2 (codes) + N*K/16 (scales) + 4 (g) + M*K*2 (x) + M*N*4 (y).
+"""
+from __future__ import annotations
+
+
+def gemv_bytes(M: int, N: int, K: int) -> int:
+    return N * K // 2 + N * K // 16 + 4 + M * K * 2 + M * N * 4
+
+
+def weight_bytes(N: int, K: int) -> int:
+    return N * K // 2 + N * K // 16
+
+
+def moe_bytes(M: int, H: int, I: int, topk: int, distinct: int) -> int:
+    """One MoE call: every distinct expert's gate|up [2I, H] and down [H, I]
+    weights plus its two tensor scales, x, ids and gate weights, the bf16
+    SwiGLU activations (written and read) and the per-slot fp32 outputs
+    (written and read) and y."""
+    S = M * topk
+    per_expert = weight_bytes(2 * I, H) + weight_bytes(H, I) + 8
+    return (distinct * per_expert + M * H * 2 + S * 8 + 2 * S * I * 2
+            + 2 * S * H * 4 + M * H * 4)
+
+
+def pages_floor_us(M: float, N: int, K: int, experts: float, bits: float,
+                   act_bytes_per_elem: float, out_elems: int,
+                   bw_bytes_per_s: float = 249e9) -> float:
+    """The blueprint's floor for one kernel row, in microseconds."""
+    b = experts * N * K * bits / 8 + M * K * act_bytes_per_elem + out_elems * 2
+    return b / bw_bytes_per_s * 1e6

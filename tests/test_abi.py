@@ -1,0 +1,108 @@
+"""The C ABI boundary on the CPU: the library loads, exports every entry point
+include/nvfp4_gemv.h declares, and rejects bad arguments on the host before
+any HIP call (only argument checks run here; nothing is launched)."""
+import ctypes
+import re
+
+import pytest
+
+import nvfp4_block_scaled_gemv_amd as nv
+
+OK, ERR_NULL, ERR_SHAPE, ERR_ALIGN, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP, ERR_ALIAS = range(8)
+
+# Fake, never-dereferenced device addresses: every call below fails its host
+# checks before it could touch them.
+A = 0x7F0000000000
+B = 0x7F0100000000
+
+
+@pytest.fixture(scope="module")
+def L():
+    return nv.lib()
+
+
+def declared_functions():
+    text = open(nv.HEADER_PATH).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(nvfp4_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol(L):
+    names = declared_functions()
+    assert {"nvfp4_pack", "nvfp4_dequant", "nvfp4_gemv", "nvfp4_moe_gemv",
+            "nvfp4_moe_workspace_bytes", "nvfp4_abi_version", "nvfp4_status_string",
+            "nvfp4_last_error"} <= set(names)
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_version_and_status_strings(L):
+    assert L.nvfp4_abi_version() == 1
+    for s in range(8):
+        assert L.nvfp4_status_string(s)
+    assert L.nvfp4_status_string(99) == b"unknown status"
+
+
+def _err(L):
+    return L.nvfp4_last_error().decode()
+
+
+def test_gemv_rejects_bad_shapes(L):
+    assert L.nvfp4_gemv(A, A, A, A, 1, 16, 48, B, None) == ERR_SHAPE       # K % 32
+    assert "K % 32" in _err(L)
+    assert L.nvfp4_gemv(A, A, A, A, -1, 16, 64, B, None) == ERR_SHAPE
+    assert L.nvfp4_gemv(A, A, A, A, 9, 16, 64, B, None) == ERR_UNSUPPORTED
+    assert L.nvfp4_gemv(A, A, A, A, 0, 16, 64, B, None) == OK              # nothing to do
+    assert L.nvfp4_gemv(A, A, A, A, 2, 0, 64, B, None) == OK
+
+
+def test_gemv_rejects_null_and_misaligned(L):
+    assert L.nvfp4_gemv(None, A, A, A, 1, 16, 64, B, None) == ERR_NULL
+    assert L.nvfp4_gemv(A, A, A, A, 1, 16, 64, None, None) == ERR_NULL
+    assert L.nvfp4_gemv(A + 8, A, A, A, 1, 16, 64, B, None) == ERR_ALIGN   # codes 16B
+    assert L.nvfp4_gemv(A, A + 1, A, A, 1, 16, 64, B, None) == ERR_ALIGN   # scales 2B
+    assert L.nvfp4_gemv(A, A, A, A + 4, 1, 16, 64, B, None) == ERR_ALIGN   # x 16B
+    assert L.nvfp4_gemv(A, A, A, A, 1, 16, 64, B + 2, None) == ERR_ALIGN   # y 4B
+
+
+def test_gemv_rejects_aliasing(L):
+    # y overlapping x
+    codes, scales, g, x = A, A + 0x10000, A + 0x20000, A + 0x30000
+    assert L.nvfp4_gemv(codes, scales, g, x, 1, 16, 64, x + 16, None) == ERR_ALIAS
+    assert L.nvfp4_gemv(codes, scales, g, x, 1, 16, 64, codes, None) == ERR_ALIAS
+
+
+def test_pack_and_dequant_checks(L):
+    assert L.nvfp4_pack(A, 4, 24, A, A, A, None, None) == ERR_SHAPE
+    assert L.nvfp4_pack(A, 4, 32, A, A, None, None, None) == ERR_NULL
+    assert L.nvfp4_pack(A + 4, 4, 32, B, B + 0x1000, B + 0x2000, None, None) == ERR_ALIGN
+    assert L.nvfp4_pack(A, 4, 32, A + 64, B, B + 0x1000, None, None) == ERR_ALIAS
+    assert L.nvfp4_dequant(A, A, A, 4, 16, B, None) == ERR_SHAPE             # K % 32
+    assert L.nvfp4_dequant(A, A, A, 0, 32, B, None) == OK
+    assert L.nvfp4_dequant(A, A, A, 4, 32, A + 8, None) == ERR_ALIGN
+    assert L.nvfp4_dequant(A, A + 0x1000, A + 0x2000, 4, 32, A, None) == ERR_ALIAS
+
+
+def test_moe_checks(L):
+    ws = nv.moe_workspace_bytes(8, 4096, 1536, 8)
+    assert ws == nv.moe_workspace_layout(8, 4096, 1536, 8)["total"]
+    assert ws >= 64 * 1536 * 2 + 64 * 4096 * 4
+    args = [A + i * 0x10000000 for i in range(9)]
+    f = L.nvfp4_moe_gemv
+    assert f(*args, 1, 4, 64, 48, 2, B, B + 0x1000000, ws, None) == ERR_SHAPE   # I % 32
+    assert f(*args, 9, 4, 64, 64, 2, B, B + 0x1000000, ws, None) == ERR_UNSUPPORTED
+    assert f(*args, 1, 4, 64, 64, 17, B, B + 0x1000000, ws, None) == ERR_UNSUPPORTED
+    assert f(*args, 1, 0, 64, 64, 2, B, B + 0x1000000, ws, None) == ERR_SHAPE
+    need = nv.moe_workspace_bytes(1, 64, 64, 2)
+    assert f(*args, 1, 4, 64, 64, 2, B, B + 0x1000000, need - 1, None) == ERR_WORKSPACE
+    assert f(*args, 1, 4, 64, 64, 2, B, None, need, None) == ERR_WORKSPACE
+    assert f(*args, 1, 4, 64, 64, 2, B, B + 0x1000000 + 64, need, None) == ERR_ALIGN
+    assert f(*args, 1, 4, 64, 64, 2, args[6], B + 0x1000000, need, None) == ERR_ALIAS
+    assert f(*args, 0, 4, 64, 64, 2, B, B + 0x1000000, need, None) == OK
+
+
+def test_binding_raises_without_device_tensors():
+    import torch
+    with pytest.raises(ValueError):
+        nv.gemv(torch.zeros(4, 16, dtype=torch.uint8), torch.zeros(4, 2, dtype=torch.uint8),
+                torch.ones(1), torch.zeros(1, 32, dtype=torch.bfloat16))

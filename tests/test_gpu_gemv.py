@@ -1,0 +1,156 @@
+"""GPU GEMV against the oracle within |y - y_ref| <= 1e-3 sum|w x| + 1e-6:
+every workload at full size (the LM head on sampled rows), ragged and edge
+shapes, arbitrary codes and scales, determinism and stream use."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+import nvfp4_block_scaled_gemv_amd as nv
+from gpu_util import check_tol, dev, dev_x, host, say
+
+pytestmark = pytest.mark.gpu
+
+
+def run_gpu(codes, scales, g, x_bits):
+    return host(nv.gemv(dev(codes), dev(scales), dev(np.array([g], np.float32)), dev_x(x_bits)))
+
+
+def packed_pair(W):
+    """Oracle pack (for the oracle) and GPU pack (for the GPU), which must be
+    identical byte for byte."""
+    c0, s0, g0 = oracle.pack(W)
+    c1, s1, g1 = nv.pack(dev(W))
+    assert np.array_equal(host(c1), c0) and np.array_equal(host(s1), s0)
+    assert np.float32(host(g1)[0]) == g0
+    return (c0, s0, g0), (c1, s1, g1)
+
+
+def test_closed_form_all_ones():
+    for K in (32, 4096, 12288):
+        N, M = 77, 3
+        codes = np.full((N, K // 2), 0x22, np.uint8)
+        scales = np.full((N, K // 16), 0x38, np.uint8)
+        x = np.full((M, K), 0x3F80, np.uint16)
+        y = run_gpu(codes, scales, 1.0, x)
+        assert np.all(y == K), (K, y.min(), y.max())
+
+
+@pytest.mark.parametrize("M", list(range(1, 9)))
+@pytest.mark.parametrize("N,K", [(1, 32), (3, 64), (37, 96), (257, 2048), (1001, 2080),
+                                 (130, 4096), (64, 12288)])
+def test_random_storage_shapes(M, N, K):
+    say(f"[gemv] random storage M={M} N={N} K={K}")
+    codes, scales = workloads.random_nvfp4(9, M, N * 7 + K, N, K)
+    x = workloads.x_bf16(9, M, N * 7 + K, M, K)
+    g = np.float32(0.0123)
+    y = run_gpu(codes, scales, g, x)
+    y_ref, ad = oracle.gemv(codes, scales, g, x)
+    check_tol(y, y_ref, ad, f"M={M} N={N} K={K}")
+
+
+@pytest.mark.parametrize("M", [1, 2, 5, 8])
+def test_subnormal_and_max_scales(M):
+    N, K = 200, 1024
+    for lo, hi in [(0x00, 0x07), (0x70, 0x7E), (0x78, 0x7E)]:
+        codes, scales = workloads.random_nvfp4(9, 100 + M, lo, N, K, lo, hi)
+        x = workloads.x_bf16(9, 100 + M, lo, M, K)
+        y = run_gpu(codes, scales, 1.0, x)
+        y_ref, ad = oracle.gemv(codes, scales, 1.0, x)
+        check_tol(y, y_ref, ad, f"scales {lo:#x}-{hi:#x}")
+
+
+def test_workload_1_single_gemv():
+    W = workloads.dense_weights(1, 0, 0, 1024, 4096)
+    (c0, s0, g0), (c1, s1, g1) = packed_pair(W)
+    x = workloads.x_bf16(1, 0, 0, 1, 4096)
+    y = host(nv.gemv(c1, s1, g1, dev_x(x)))
+    y_ref, ad = oracle.gemv(c0, s0, g0, x)
+    r = check_tol(y, y_ref, ad, "workload 1")
+    say(f"  max err / tol = {r:.3e}")
+
+
+@pytest.mark.parametrize("i", range(len(workloads.DECODE_LAYER)))
+def test_workload_2_decode_layer(i):
+    name, N, K = workloads.DECODE_LAYER[i]
+    say(f"[gemv] decode layer {name} {N}x{K} M=5")
+    W = workloads.dense_weights(2, 0, i, N, K)
+    (c0, s0, g0), (c1, s1, g1) = packed_pair(W)
+    x = workloads.x_bf16(2, 0, i, 5, K)
+    y = host(nv.gemv(c1, s1, g1, dev_x(x)))
+    y_ref, ad = oracle.gemv(c0, s0, g0, x)
+    check_tol(y, y_ref, ad, name)
+
+
+@pytest.mark.parametrize("i,N,K", [(0, 12288, 4096), (1, 4096, 12288)])
+def test_workload_5_stress_m8(i, N, K):
+    say(f"[gemv] stress t3 {N}x{K} M=8")
+    W = workloads.dense_weights(5, 0, i, N, K)
+    (c0, s0, g0), (c1, s1, g1) = packed_pair(W)
+    zb = workloads.zero_block_ids(5, 0, i, N, K)
+    assert np.all(s0.ravel()[zb] == 0)
+    x = workloads.x_bf16(5, 0, i, 8, K)
+    y = host(nv.gemv(c1, s1, g1, dev_x(x)))
+    y_ref, ad = oracle.gemv(c0, s0, g0, x)
+    check_tol(y, y_ref, ad, f"stress {N}x{K}")
+
+
+def test_workload_3_lm_head_sampled_rows():
+    """Full 151936 x 4096 at M=1, in the launch the benchmark times; the
+    oracle computes a sample of rows (first, last, random) one by one."""
+    N, K = 151936, 4096
+    W = workloads.dense_weights(3, 0, 0, N, K)
+    (c0, s0, g0), (c1, s1, g1) = packed_pair(W)
+    del W
+    x = workloads.x_bf16(3, 0, 0, 1, K)
+    y = host(nv.gemv(c1, s1, g1, dev_x(x)))
+    rows = np.unique(np.concatenate([[0, 1, N - 2, N - 1],
+                                     np.random.default_rng(5).choice(N, 3000, replace=False)]))
+    y_ref, ad = oracle.gemv(c0, s0, g0, x, rows=rows)
+    check_tol(y[:, rows], y_ref, ad, "lm head")
+    assert np.all(np.isfinite(y))
+
+
+def test_empty_and_zero_k():
+    c = torch.zeros((4, 16), dtype=torch.uint8, device="cuda")
+    s = torch.zeros((4, 2), dtype=torch.uint8, device="cuda")
+    g = torch.ones(1, device="cuda")
+    y = torch.full((0, 4), 7.0, device="cuda")
+    nv.gemv_into(c, s, g, torch.zeros((0, 32), dtype=torch.bfloat16, device="cuda"), y)
+    # K == 0: y becomes zero
+    c0 = torch.zeros((5, 0), dtype=torch.uint8, device="cuda")
+    s0 = torch.zeros((5, 0), dtype=torch.uint8, device="cuda")
+    y = torch.full((2, 5), 7.0, device="cuda")
+    nv.gemv_into(c0, s0, g, torch.zeros((2, 0), dtype=torch.bfloat16, device="cuda"), y)
+    assert torch.all(y == 0)
+    # N == 0: nothing launched
+    y = torch.empty((3, 0), device="cuda")
+    nv.gemv_into(torch.zeros((0, 16), dtype=torch.uint8, device="cuda"),
+                 torch.zeros((0, 2), dtype=torch.uint8, device="cuda"), g,
+                 torch.zeros((3, 32), dtype=torch.bfloat16, device="cuda"), y)
+
+
+def test_rejects_m9():
+    c = torch.zeros((4, 16), dtype=torch.uint8, device="cuda")
+    s = torch.zeros((4, 2), dtype=torch.uint8, device="cuda")
+    with pytest.raises(nv.Nvfp4Error) as e:
+        nv.gemv(c, s, torch.ones(1, device="cuda"),
+                torch.zeros((9, 32), dtype=torch.bfloat16, device="cuda"))
+    assert e.value.status == 4
+
+
+def test_deterministic_and_on_side_stream():
+    N, K, M = 3000, 4096, 4
+    codes, scales = workloads.random_nvfp4(9, 1, 1, N, K)
+    x = workloads.x_bf16(9, 1, 1, M, K)
+    cd, sd, gd, xd = dev(codes), dev(scales), dev(np.array([0.5], np.float32)), dev_x(x)
+    y1 = nv.gemv(cd, sd, gd, xd)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        y2 = nv.gemv(cd, sd, gd, xd)
+    torch.cuda.current_stream().wait_stream(side)
+    assert np.array_equal(host(y1), host(y2))
+    y_ref, ad = oracle.gemv(codes, scales, 0.5, x)
+    check_tol(host(y2), y_ref, ad, "side stream")

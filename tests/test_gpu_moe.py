@@ -1,0 +1,109 @@
+"""GPU MoE expert slots against the oracle: the 288-expert workload at full
+per-expert size (M = 1 and M = 8; only routed experts are generated, the
+rest stay zero), union sharing, duplicates, invalid ids and topk limits."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+import nvfp4_block_scaled_gemv_amd as nv
+from gpu_util import check_tol, dev, dev_x, host, say
+
+pytestmark = pytest.mark.gpu
+
+
+def build_experts(wl, rep, E, H, I, used):
+    """Oracle-packed (host) and GPU-packed (device) stacks; experts outside
+    `used` are all-zero storage with g = 1. The two packs must agree."""
+    hc13 = np.zeros((E, 2 * I, H // 2), np.uint8)
+    hs13 = np.zeros((E, 2 * I, H // 16), np.uint8)
+    hg13 = np.ones(E, np.float32)
+    hc2 = np.zeros((E, H, I // 2), np.uint8)
+    hs2 = np.zeros((E, H, I // 16), np.uint8)
+    hg2 = np.ones(E, np.float32)
+    dc13, ds13, dg13 = dev(hc13), dev(hs13), dev(hg13)
+    dc2, ds2, dg2 = dev(hc2), dev(hs2), dev(hg2)
+    for e in sorted(set(int(v) for v in used)):
+        w13, w2 = workloads.moe_expert_weights(wl, rep, e, H, I)
+        hc13[e], hs13[e], hg13[e] = oracle.pack(w13)
+        hc2[e], hs2[e], hg2[e] = oracle.pack(w2)
+        nv.pack_into(dev(w13), dc13[e], ds13[e], dg13[e:e + 1])
+        nv.pack_into(dev(w2), dc2[e], ds2[e], dg2[e:e + 1])
+    for a, b in [(hc13, dc13), (hs13, ds13), (hg13, dg13), (hc2, dc2), (hs2, ds2), (hg2, dg2)]:
+        assert np.array_equal(host(b), a)
+    return (hc13, hs13, hg13, hc2, hs2, hg2), (dc13, ds13, dg13, dc2, ds2, dg2)
+
+
+def run_both(hw, dw, x, ids, gw, H, I, want_h=False):
+    ws = torch.empty(nv.moe_workspace_bytes(ids.shape[0], H, I, ids.shape[1]),
+                     dtype=torch.uint8, device="cuda")
+    y = host(nv.moe_gemv(*dw, dev_x(x), dev(ids), dev(gw), workspace=ws))
+    res = oracle.moe(*hw, x, ids, gw, want_h=want_h)
+    return y, res, ws
+
+
+@pytest.mark.parametrize("M", [1, 8])
+def test_moe_workload_4_full_size(M):
+    E, H, I, topk = 288, 4096, 1536, 8
+    ids, gw = workloads.moe_routing(4, 0, M, E, topk)
+    say(f"[moe] M={M} distinct experts={len(set(ids.ravel()))}")
+    hw, dw = build_experts(4, 0, E, H, I, ids.ravel())
+    x = workloads.x_bf16(4, 0, 0, M, H)
+    y, (y_ref, bound, h_ref), ws = run_both(hw, dw, x, ids, gw, H, I, want_h=True)
+    r = check_tol(y, y_ref, bound, f"moe M={M}")
+    say(f"  max err / tol = {r:.3e}")
+    # stage 1: the bf16 SwiGLU activations agree except for rare one-ulp
+    # rounding flips (fp32 vs fp64 gate/up sums)
+    lay = nv.moe_workspace_layout(M, H, I, topk)
+    h = host(ws[lay["h"]:lay["h"] + M * topk * I * 2].view(torch.int16)).view(np.uint16)
+    h = h.reshape(M * topk, I)
+    same = np.mean(h == h_ref)
+    ulp = np.abs(h.astype(np.int32) - h_ref.astype(np.int32))
+    say(f"  h bit-equal fraction {same:.6f}, max ulp diff {ulp.max()}")
+    assert same > 0.999
+
+
+def test_moe_shared_experts_union():
+    """All 8 rows route to the same 8 experts (each expert streamed once for
+    8 slots), in different slot orders."""
+    E, H, I, topk, M = 16, 512, 256, 8, 8
+    base = np.array([3, 9, 0, 15, 7, 1, 12, 4], np.int32)
+    g = np.random.default_rng(1)
+    ids = np.stack([g.permutation(base) for _ in range(M)]).astype(np.int32)
+    gw = g.dirichlet(np.ones(topk), size=M).astype(np.float32)
+    hw, dw = build_experts(40, 0, E, H, I, base)
+    x = workloads.x_bf16(40, 0, 0, M, H)
+    y, (y_ref, bound), _ = run_both(hw, dw, x, ids, gw, H, I)
+    check_tol(y, y_ref, bound, "shared union")
+
+
+def test_moe_duplicates_invalid_ids_and_limits():
+    E, H, I = 6, 256, 128
+    hw, dw = build_experts(41, 0, E, H, I, range(E))
+    cases = {
+        "dup_in_row": np.array([[2, 2, 5], [1, 1, 1]], np.int32),
+        "invalid": np.array([[-1, 3, 6], [1000, -7, 0]], np.int32),
+        "all_invalid": np.array([[-1, 6, 99]], np.int32),
+        "topk1": np.array([[4], [0], [5]], np.int32),
+        "topk16": np.tile(np.arange(16, dtype=np.int32) % E, (2, 1)),
+        "m8": np.random.default_rng(2).integers(0, E, size=(8, 4)).astype(np.int32),
+    }
+    for name, ids in cases.items():
+        say(f"[moe] {name} ids={ids.tolist()}")
+        M, topk = ids.shape
+        gw = np.random.default_rng(M * 31 + topk).random((M, topk)).astype(np.float32)
+        x = workloads.x_bf16(41, M, topk, M, H)
+        y, (y_ref, bound), _ = run_both(hw, dw, x, ids, gw, H, I)
+        check_tol(y, y_ref, bound, name)
+        if name == "all_invalid":
+            assert np.all(y == 0)
+
+
+def test_moe_empty_batch():
+    E, H, I = 2, 64, 32
+    hw, dw = build_experts(42, 0, E, H, I, [])
+    y = nv.moe_gemv(*dw, torch.zeros((0, H), dtype=torch.bfloat16, device="cuda"),
+                    torch.zeros((0, 2), dtype=torch.int32, device="cuda"),
+                    torch.zeros((0, 2), dtype=torch.float32, device="cuda"))
+    assert y.shape == (0, H)

@@ -1,0 +1,35 @@
+"""The algorithmic byte model against the floors the blueprint prints
+(card.json performance[i].floor_us), and the per-workload totals."""
+import pytest
+
+from conftest import golden_rows
+from nvfp4_block_scaled_gemv_amd import traffic
+
+
+def test_pages_floors_reproduce():
+    rows = golden_rows("roofline_floors.txt")
+    assert len(rows) == 6
+    for idx, M, N, K, experts, bits, act, out, floor in rows:
+        got = traffic.pages_floor_us(float(M), int(N), int(K), float(experts), float(bits),
+                                     float(act), int(out))
+        assert abs(got - float(floor)) < 0.0015, (idx, got, floor)
+
+
+def test_gemv_bytes_workloads():
+    assert traffic.gemv_bytes(1, 1024, 4096) == 2_371_588
+    assert traffic.gemv_bytes(1, 151936, 4096) == 350_676_484
+    layer = [(4096, 4096), (1024, 4096), (1024, 4096), (4096, 4096), (12288, 4096),
+             (12288, 4096), (4096, 12288)]
+    assert sum(traffic.gemv_bytes(5, n, k) for n, k in layer) == 109_674_524
+    assert traffic.gemv_bytes(8, 12288, 4096) == 28_770_308
+    assert traffic.gemv_bytes(8, 4096, 12288) == 28_639_236
+
+
+def test_weight_bytes_are_4p5_bits():
+    assert traffic.weight_bytes(3072, 4096) * 8 == 3072 * 4096 * 4.5
+
+
+def test_moe_bytes_counts_distinct_experts():
+    one = traffic.moe_bytes(1, 4096, 1536, 8, 8)
+    assert one > 8 * (traffic.weight_bytes(3072, 4096) + traffic.weight_bytes(4096, 1536))
+    assert traffic.moe_bytes(8, 4096, 1536, 8, 58) < traffic.moe_bytes(8, 4096, 1536, 8, 64)

@@ -176,3 +176,13 @@ def moe_expert_weights(workload: int, rep: int, e: int, H: int, I: int,
     w13 = normal_weights(workload, rep, 2 * e, 2 * I, H, threads=threads)
     w2 = normal_weights(workload, rep, 2 * e + 1, H, I, threads=threads)
     return w13, w2
+
+
+def random_nvfp4(workload: int, rep: int, stream: int, N: int, K: int,
+                 scale_lo: int = 0x00, scale_hi: int = 0x7E):
+    """Arbitrary NVFP4 storage (not produced by a pack): uniform code bytes
+    (every nibble 0..15) and uniform scale bytes in [scale_lo, scale_hi]."""
+    g = rng(workload, rep, (1 << 23) + stream)
+    codes = g.integers(0, 256, size=(N, K // 2), dtype=np.uint8)
+    scales = g.integers(scale_lo, scale_hi + 1, size=(N, K // 16), dtype=np.uint8)
+    return codes, scales
