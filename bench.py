@@ -14,9 +14,10 @@ resident in HBM. Weight copies are rotated so that each call reads memory
 the previous calls did not (the 256 MB MALL cannot serve repeats).
 
 Timing: W warm-up steps, then exactly K steps between two device
-synchronisations (wall clock -> ms_per_step, value). Inside the timed region
-HIP events on the launch stream bracket every launch; their mean is the
-kernel's average duration used for ``roofline.achieved``.
+synchronisations (wall clock -> ms_per_step, value). Two HIP events on the
+launch stream bracket the timed launches; their elapsed time over K is the
+kernel's average launch duration (gaps between back-to-back launches
+included) used for ``roofline.achieved``.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--legs ...]
 """
@@ -64,30 +65,24 @@ def cpu_model():
     return platform.processor() or None
 
 
-def timed_steps(torch, step, steps, warmup, nkernels):
-    """Run `warmup` untimed steps, then exactly `steps` timed ones. step(i,
-    ev) launches the step's kernels; ev(j) returns the (start, end) event
-    pair to record around kernel j. Returns wall ms per step and the mean
-    event duration (ms) of every kernel position."""
+def timed_steps(torch, step, steps, warmup):
+    """Run `warmup` untimed steps, then exactly `steps` timed ones between two
+    device synchronisations. Two HIP events on the launch stream (torch's
+    current stream, which every call of the library uses) bracket the timed
+    launches. Returns (wall ms per step, event ms per step)."""
     for i in range(warmup):
-        step(i, None)
-    torch.cuda.synchronize()
-    evs = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-            for _ in range(nkernels)] for _ in range(steps)]
+        step(i)
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
+    e0.record()
     for i in range(steps):
-        step(warmup + i, lambda j, _i=i: evs[_i][j])
+        step(warmup + i)
+    e1.record()
     torch.cuda.synchronize()
     t1 = time.perf_counter()
-    per_kernel = [float(np.mean([evs[i][j][0].elapsed_time(evs[i][j][1])
-                                 for i in range(steps)])) for j in range(nkernels)]
-    return (t1 - t0) * 1e3 / steps, per_kernel
-
-
-def rec(ev, j, which):
-    if ev is not None:
-        ev(j)[which].record()
+    return (t1 - t0) * 1e3 / steps, e0.elapsed_time(e1) / steps
 
 
 # ------------------------------------------------------------------- legs
@@ -108,16 +103,14 @@ def leg_lm_head(torch, nv, workloads, traffic, steps, warmup, want_cpu):
                                      for _ in range(R - 1)]
     y = torch.empty((M, N), dtype=torch.float32, device="cuda")
 
-    def step(i, ev):
+    def step(i):
         c, s, gg = copies[i % R]
-        rec(ev, 0, 0)
         nv.gemv_into(c, s, gg, x, y)
-        rec(ev, 0, 1)
 
-    ms, (kms,) = timed_steps(torch, step, steps, warmup, 1)
+    ms, kms = timed_steps(torch, step, steps, warmup)
     B = traffic.gemv_bytes(M, N, K)
     out = {
-        "bytes_per_step": B, "ms_per_step": ms, "kernel_us": kms * 1e3,
+        "bytes_per_step": B, "ms_per_step": ms, "kernel_us_events": kms * 1e3,
         "gbs_wall": B / (ms * 1e-3) / 1e9, "gbs_kernel": B / (kms * 1e-3) / 1e9,
         "tokens_per_s": M / (ms * 1e-3), "rotate_copies": R,
     }
@@ -179,16 +172,13 @@ def leg_m8(torch, nv, workloads, traffic, steps, warmup):
     copies = [packed] + [[(c.clone(), s.clone(), g.clone(), x, y) for c, s, g, x, y in packed]
                          for _ in range(R - 1)]
 
-    def step(i, ev):
-        for j, (c, s, g, x, y) in enumerate(copies[i % R]):
-            rec(ev, j, 0)
+    def step(i):
+        for c, s, g, x, y in copies[i % R]:
             nv.gemv_into(c, s, g, x, y)
-            rec(ev, j, 1)
 
-    ms, kms = timed_steps(torch, step, steps, warmup, 2)
-    kt = sum(kms)
+    ms, kt = timed_steps(torch, step, steps, warmup)
     return {"workload": "stress_m8_t3 (12288x4096 + 4096x12288)", "M": M,
-            "bytes_per_step": B, "ms_per_step": ms, "kernel_us": [k * 1e3 for k in kms],
+            "bytes_per_step": B, "ms_per_step": ms, "step_us_events": kt * 1e3,
             "gbs_wall": B / (ms * 1e-3) / 1e9, "gbs_kernel": B / (kt * 1e-3) / 1e9,
             "frac_of_peak": B / (kt * 1e-3) / 1e9 / HBM_PEAK_GBS,
             "tokens_per_s": M / (ms * 1e-3), "rotate_copies": R}
@@ -222,13 +212,11 @@ def leg_moe(torch, nv, workloads, traffic, steps, warmup, M):
     ws = torch.empty(nv.moe_workspace_bytes(M, H, I, topk), dtype=torch.uint8, device="cuda")
     y = torch.empty((M, H), dtype=torch.float32, device="cuda")
 
-    def step(i, ev):
+    def step(i):
         ids, gw, x, _ = batches[i % nb]
-        rec(ev, 0, 0)
         nv.moe_gemv_into(c13, s13, g13, c2, s2, g2, x, ids, gw, y, ws)
-        rec(ev, 0, 1)
 
-    ms, (kms,) = timed_steps(torch, step, steps, warmup, 1)
+    ms, kms = timed_steps(torch, step, steps, warmup)
     # bytes of the steps actually timed (each step's own distinct-expert count)
     Bs = [traffic.moe_bytes(M, H, I, topk, batches[(warmup + i) % nb][3]) for i in range(steps)]
     B = float(np.mean(Bs))
@@ -289,7 +277,7 @@ def main():
                               "peak": HBM_PEAK_GBS, "unit": "GB/s",
                               "frac": lm["gbs_kernel"] / HBM_PEAK_GBS, "traffic": None,
                               "kernel": "nvfp4::k_gemv<1, 4>",
-                              "kernel_avg_us": lm["kernel_us"],
+                              "kernel_avg_us": lm["kernel_us_events"],
                               "bytes_per_launch": lm["bytes_per_step"]}
         result["config"]["rotate_copies"] = lm["rotate_copies"]
         result["parity"] = lm["parity"]

@@ -14,6 +14,7 @@ import sys
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
+INCLUDE = os.path.join(os.path.dirname(HERE), "include")
 LIB = os.path.join(HERE, "libnvfp4_gemv.so")
 ARCH = "gfx950"
 
@@ -31,7 +32,7 @@ def sources():
 
 def build(verbose: bool = False) -> str:
     hipcc = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
-    cmd = [hipcc, *FLAGS, "-o", LIB + ".tmp", *sources()]
+    cmd = [hipcc, *FLAGS, f"-I{INCLUDE}", "-o", LIB + ".tmp", *sources()]
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)

@@ -4,7 +4,7 @@
 #include <stdio.h>
 #include <string.h>
 
-#include "../../include/nvfp4_gemv.h"
+#include "nvfp4_gemv.h"
 #include "internal.h"
 
 static_assert(NVFP4_MAX_M == NVFP4_MAX_M_INTERNAL, "M limit mismatch");

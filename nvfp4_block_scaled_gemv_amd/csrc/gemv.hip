@@ -1,4 +1,6 @@
-// gemv.hip -- dense NVFP4 g16 W4A16 GEMV for 1 <= M <= 8 on gfx950:
+// gemv.hip -- dense NVFP4 g16 W4A16 GEMV on gfx950, vector-ALU path for
+// M <= 2 activation rows (M >= 3 goes to the matrix-core kernel in
+// gemv_mfma.hip):
 //   y[m, n] = g * sum_k e2m1(c[n,k]) * s[n, k/16] * x[m, k]
 // (graph.json node "l0.kda.q": act bf16, weight nvfp4/g16 -> bf16,
 // accumulate f32, scale f32). Bandwidth-bound: every weight byte is read
@@ -18,7 +20,9 @@ __global__ __launch_bounds__(256) void k_gemv(const uint8_t* __restrict__ codes,
                                               const uint16_t* __restrict__ x, int64_t N,
                                               int64_t K, float* __restrict__ y) {
   const int lane = threadIdx.x & 63;
-  const int64_t wave = (int64_t)blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6);
+  // wavefront index, made provably uniform so loop control stays scalar
+  const int64_t wave =
+      (int64_t)blockIdx.x * kWavesPerBlock + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int64_t nwaves = (int64_t)gridDim.x * kWavesPerBlock;
   const float g = *gscale;
   const uint16_t* xs[M];
@@ -72,13 +76,9 @@ hipError_t launch_gemv(const uint8_t* codes, const uint8_t* scales, const float*
   switch (M) {
     case 1: launch_m<1, 4>(codes, scales, gscale, x, N, K, y, stream); break;
     case 2: launch_m<2, 4>(codes, scales, gscale, x, N, K, y, stream); break;
-    case 3: launch_m<3, 4>(codes, scales, gscale, x, N, K, y, stream); break;
-    case 4: launch_m<4, 4>(codes, scales, gscale, x, N, K, y, stream); break;
-    case 5: launch_m<5, 4>(codes, scales, gscale, x, N, K, y, stream); break;
-    case 6: launch_m<6, 4>(codes, scales, gscale, x, N, K, y, stream); break;
-    case 7: launch_m<7, 4>(codes, scales, gscale, x, N, K, y, stream); break;
-    case 8: launch_m<8, 4>(codes, scales, gscale, x, N, K, y, stream); break;
-    default: return hipErrorInvalidValue;
+    default:
+      if (M < 1 || M > NVFP4_MAX_M_INTERNAL) return hipErrorInvalidValue;
+      return launch_gemv_mfma(codes, scales, gscale, x, M, N, K, y, stream);
   }
   return hipGetLastError();
 }

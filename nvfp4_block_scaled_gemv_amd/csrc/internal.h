@@ -22,6 +22,10 @@ hipError_t launch_gemv(const uint8_t* codes, const uint8_t* scales, const float*
                        const uint16_t* x, int M, int64_t N, int64_t K, float* y,
                        hipStream_t stream);
 
+hipError_t launch_gemv_mfma(const uint8_t* codes, const uint8_t* scales, const float* gscale,
+                            const uint16_t* x, int M, int64_t N, int64_t K, float* y,
+                            hipStream_t stream);
+
 hipError_t launch_fill_zero(float* y, size_t n, hipStream_t stream);
 
 // MoE workspace layout (byte offsets from the workspace base, 256-aligned).

@@ -96,7 +96,8 @@ __global__ __launch_bounds__(256) void k_moe_gate_up(
   const uint8_t* codes = w13_codes + (int64_t)e * (2 * I) * (H / 2);
   const uint8_t* scales = w13_scales + (int64_t)e * (2 * I) * (H / 16);
   const float g = w13_gscale[e];
-  const int64_t wave = (int64_t)blockIdx.y * kMoeWaves + (threadIdx.x >> 6);
+  const int64_t wave =
+      (int64_t)blockIdx.y * kMoeWaves + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int64_t nwaves = (int64_t)gridDim.y * kMoeWaves;
 
   int start = 0;
@@ -137,7 +138,8 @@ __global__ __launch_bounds__(256) void k_moe_down(
   const uint8_t* codes = w2_codes + (int64_t)e * H * (I / 2);
   const uint8_t* scales = w2_scales + (int64_t)e * H * (I / 16);
   const float g = w2_gscale[e];
-  const int64_t wave = (int64_t)blockIdx.y * kMoeWaves + (threadIdx.x >> 6);
+  const int64_t wave =
+      (int64_t)blockIdx.y * kMoeWaves + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int64_t nwaves = (int64_t)gridDim.y * kMoeWaves;
 
   int start = 0;
