@@ -229,6 +229,131 @@ def leg_moe(torch, nv, workloads, traffic, steps, warmup, M):
             "tokens_per_s": M / (ms * 1e-3), "rotating_batches": nb}
 
 
+def leg_copy(torch, steps, warmup):
+    """Calibration for the HBM byte counters: a plain fp32 copy kernel
+    (dst = src * 1) of known size, 512 MiB read and 512 MiB written per
+    launch, two buffer pairs alternating so the MALL cannot serve repeats."""
+    n = (512 << 20) // 4
+    bufs = [(torch.ones(n, device="cuda"), torch.empty(n, device="cuda")) for _ in range(2)]
+
+    def step(i):
+        src, dst = bufs[i % 2]
+        torch.mul(src, 1.0, out=dst)
+
+    ms, kms = timed_steps(torch, step, steps, warmup)
+    return {"bytes_read": n * 4, "bytes_written": n * 4, "us_events": kms * 1e3,
+            "gbs": 2 * n * 4 / (kms * 1e-3) / 1e9}
+
+
+# ------------------------------------------------------- profile summaries
+
+LM_KERNEL = "nvfp4::k_gemv<1, 4>"
+COPY_KERNEL = "MulFunctor<float>"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_k_gemv_lm_head_m1_151936x4096.txt")
+KERNEL_SOURCES = ["gemv.hip", "gemv_core.h", "device.h"]
+
+
+def kernel_source_hash():
+    import hashlib
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "nvfp4_block_scaled_gemv_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def _pmc_means(csv_path, counter):
+    """Mean per-dispatch value of `counter` for each kernel name."""
+    import csv
+    acc = {}
+    with open(csv_path, newline="") as f:
+        for row in csv.DictReader(f):
+            if row["Counter_Name"] != counter:
+                continue
+            acc.setdefault(row["Kernel_Name"], []).append(float(row["Counter_Value"]))
+    return {k: (sum(v) / len(v), len(v)) for k, v in acc.items()}
+
+
+def _pick(means, key):
+    hits = [(k, v) for k, v in means.items() if key in k]
+    if len(hits) != 1:
+        raise SystemExit(f"expected one kernel matching {key!r}, found {[k for k, _ in hits]}")
+    return hits[0][1]
+
+
+def summarize_pmc(fetch_csv, write_csv, cmd, out):
+    """HBM traffic of the LM-head kernel per launch from two rocprofv3 --pmc
+    passes (FETCH_SIZE, WRITE_SIZE; KiB per dispatch), each scaled by what
+    the same counter reads for the copy kernel of known size."""
+    from nvfp4_block_scaled_gemv_amd import traffic
+    f_k, nf = _pick(_pmc_means(fetch_csv, "FETCH_SIZE"), LM_KERNEL)
+    f_c, nfc = _pick(_pmc_means(fetch_csv, "FETCH_SIZE"), COPY_KERNEL)
+    w_k, nw = _pick(_pmc_means(write_csv, "WRITE_SIZE"), LM_KERNEL)
+    w_c, nwc = _pick(_pmc_means(write_csv, "WRITE_SIZE"), COPY_KERNEL)
+    copy_bytes = 512 << 20
+    fr, fw = copy_bytes / f_c, copy_bytes / w_c        # bytes per counter unit
+    read_b, write_b = f_k * fr, w_k * fw
+    alg = traffic.gemv_bytes(1, 151936, 4096)
+    lines = [
+        "# HBM traffic of nvfp4::k_gemv<1, 4>, LM head M=1 N=151936 K=4096",
+        "# commands (run from /tmp with TMPDIR=/tmp):",
+        *[f"#   {c}" for c in cmd],
+        f"kernel_source_sha256_16: {kernel_source_hash()}",
+        f"fetch_kib_per_dispatch: {f_k:.1f}  (mean of {nf} dispatches)",
+        f"write_kib_per_dispatch: {w_k:.1f}  (mean of {nw} dispatches)",
+        f"copy_fetch_kib_per_dispatch: {f_c:.1f}  (mean of {nfc}; 512 MiB read)",
+        f"copy_write_kib_per_dispatch: {w_c:.1f}  (mean of {nwc}; 512 MiB written)",
+        f"calibration_bytes_per_unit: fetch {fr:.2f}, write {fw:.2f}",
+        f"read_bytes_per_launch: {read_b:.0f}",
+        f"write_bytes_per_launch: {write_b:.0f}",
+        f"traffic_bytes_per_launch: {read_b + write_b:.0f}",
+        f"algorithmic_bytes_per_launch: {alg}",
+        f"traffic_over_algorithmic: {(read_b + write_b) / alg:.4f}",
+    ]
+    with open(out, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
+def read_traffic():
+    """traffic bytes per launch from the committed counter summary, or None
+    when it is missing or was taken on different kernel sources."""
+    try:
+        kv = {}
+        with open(TRAFFIC_FILE) as f:
+            for line in f:
+                if ":" in line and not line.startswith("#"):
+                    k, v = line.split(":", 1)
+                    kv[k.strip()] = v.strip().split()[0]
+        if kv.get("kernel_source_sha256_16") != kernel_source_hash():
+            return None
+        return float(kv["traffic_bytes_per_launch"])
+    except (OSError, KeyError, ValueError):
+        return None
+
+
+def summarize_stats(stats_csv, cmd, out, top=14):
+    """Short text table from a rocprofv3 --stats kernel summary."""
+    import csv
+    rows = []
+    with open(stats_csv, newline="") as f:
+        for r in csv.DictReader(f):
+            rows.append(r)
+    rows.sort(key=lambda r: -float(r["TotalDurationNs"]))
+    lines = ["# rocprofv3 --kernel-trace --stats kernel summary",
+             "# commands (run from /tmp with TMPDIR=/tmp):", *[f"#   {c}" for c in cmd],
+             f"{'calls':>7} {'avg_us':>10} {'min_us':>10} {'max_us':>10} {'pct':>6}  kernel"]
+    for r in rows[:top]:
+        name = r["Name"]
+        short = name.split("(")[0] if name.startswith(("nvfp4", "void nvfp4")) else name[:90]
+        lines.append(f"{int(r['Calls']):7d} {float(r['AverageNs']) / 1e3:10.2f} "
+                     f"{float(r['MinNs']) / 1e3:10.2f} {float(r['MaxNs']) / 1e3:10.2f} "
+                     f"{float(r['Percentage']):6.2f}  {short}")
+    with open(out, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
 # ------------------------------------------------------------------- main
 
 def main():
@@ -237,9 +362,22 @@ def main():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--legs", default="lm_head,m8,moe",
-                    help="comma list of lm_head, m8, moe (lm_head is the headline)")
+                    help="comma list of lm_head, m8, moe, copy (lm_head is the headline; "
+                         "copy is the byte-counter calibration kernel)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--summarize-pmc", nargs=3, metavar=("FETCH_CSV", "WRITE_CSV", "OUT"),
+                    help="write the traffic summary from two rocprofv3 --pmc passes")
+    ap.add_argument("--summarize-stats", nargs=2, metavar=("STATS_CSV", "OUT"),
+                    help="write a short table from a rocprofv3 --stats kernel summary")
+    ap.add_argument("--cmd", action="append", default=[],
+                    help="command line(s) that produced the profile, for the summary header")
     args = ap.parse_args()
+    if args.summarize_pmc:
+        summarize_pmc(*args.summarize_pmc[:2], args.cmd, args.summarize_pmc[2])
+        return
+    if args.summarize_stats:
+        summarize_stats(args.summarize_stats[0], args.cmd, args.summarize_stats[1])
+        return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print(f"bench.py measures one GPU only: --gpus {args.gpus} (WORLD_SIZE {world}) is not "
@@ -275,8 +413,9 @@ def main():
         result["frac_of_peak_wall"] = lm["gbs_wall"] / HBM_PEAK_GBS
         result["roofline"] = {"bound": "hbm", "achieved": lm["gbs_kernel"],
                               "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                              "frac": lm["gbs_kernel"] / HBM_PEAK_GBS, "traffic": None,
-                              "kernel": "nvfp4::k_gemv<1, 4>",
+                              "frac": lm["gbs_kernel"] / HBM_PEAK_GBS,
+                              "traffic": read_traffic(),
+                              "kernel": LM_KERNEL,
                               "kernel_avg_us": lm["kernel_us_events"],
                               "bytes_per_launch": lm["bytes_per_step"]}
         result["config"]["rotate_copies"] = lm["rotate_copies"]
@@ -285,6 +424,8 @@ def main():
             result["cpu_baseline"] = lm["cpu_baseline"]
     if "m8" in legs:
         result["m8"] = leg_m8(torch, nv, workloads, traffic, args.steps, args.warmup)
+    if "copy" in legs:
+        result["copy_calibration"] = leg_copy(torch, args.steps, args.warmup)
     if "moe" in legs:
         result["moe"] = {f"m{M}": leg_moe(torch, nv, workloads, traffic, args.steps,
                                           args.warmup, M) for M in (1, 8)}

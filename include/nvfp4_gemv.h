@@ -61,6 +61,8 @@ extern "C" {
 #define NVFP4_MAX_M 8
 /* Largest number of expert slots per token in the MoE call. */
 #define NVFP4_MAX_TOPK 16
+/* Largest MoE intermediate size I (down-projection row length) per call. */
+#define NVFP4_MOE_MAX_I (1 << 24)
 
 typedef enum nvfp4_status {
   NVFP4_OK = 0,
@@ -145,8 +147,9 @@ nvfp4_status nvfp4_gemv(const uint8_t* codes, const uint8_t* scales,
 
 /*
  * nvfp4_moe_workspace_bytes -- device workspace that nvfp4_moe_gemv needs for
- * the given sizes (the row-union tables, the bf16 SwiGLU activations
- * h[M*topk, I] and the per-slot fp32 outputs [M*topk, H]).
+ * the given sizes: the bf16 SwiGLU activations h[M*topk, I] (slot-major, at
+ * offset 0), rounded up to 256 bytes. Slots whose id is invalid leave their
+ * row of h untouched.
  */
 size_t nvfp4_moe_workspace_bytes(int64_t M, int64_t H, int64_t I, int64_t topk);
 
@@ -160,9 +163,11 @@ size_t nvfp4_moe_workspace_bytes(int64_t M, int64_t H, int64_t I, int64_t topk);
  *   h  = bf16( silu(a[0:I]) * a[I:2I] ),  silu(v) = v / (1 + exp(-v))
  *   y[m] += gate_w[m, j] * ( g2[e] * W2[e] . h )
  *
- * Each distinct expert of the batch is streamed once (the union of ids over
- * the M rows is built on the device, no host sync). The combine sums the
- * slots of a token in slot order (deterministic).
+ * Each distinct expert's gate|up rows are streamed once for all slots routed
+ * to it (the union of ids over the M rows is found on the device, no host
+ * sync). The down projection and the combine are one pass: y[m] is a single
+ * dot product over the token's valid slots, reduced in a fixed order
+ * (deterministic, no atomics).
  *
  *   w13_codes  uint8[E, 2I, H/2] (rows 0..I-1 gate, I..2I-1 up), 16-byte
  *              aligned; w13_scales uint8[E, 2I, H/16], 2-byte aligned;
@@ -172,6 +177,7 @@ size_t nvfp4_moe_workspace_bytes(int64_t M, int64_t H, int64_t I, int64_t topk);
  *   x          bf16[M, H] (uint16 bits), 16-byte aligned;
  *   expert_ids int32[M, topk];  gate_w float[M, topk];
  *   M          0 <= M <= NVFP4_MAX_M; 1 <= topk <= NVFP4_MAX_TOPK; E >= 1;
+ *              I <= NVFP4_MOE_MAX_I;
  *              H % 32 == 0, I % 32 == 0, H > 0, I > 0;
  *   y          float[M, H] out, 16-byte aligned;
  *   workspace  device buffer of at least nvfp4_moe_workspace_bytes(M, H, I,

@@ -207,9 +207,5 @@ def moe_gemv(w13_codes, w13_scales, w13_gscale, w2_codes, w2_scales, w2_gscale, 
 def moe_workspace_layout(M: int, H: int, I: int, topk: int) -> dict:
     """Byte offsets inside the MoE workspace (for inspecting the bf16 SwiGLU
     activations h[M*topk, I] after a call)."""
-    def a256(v):
-        return (v + 255) & ~255
     S = M * topk
-    h_off = a256((S + 1) * 4)
-    o_off = a256(h_off + S * I * 2)
-    return {"union": 0, "h": h_off, "o": o_off, "total": a256(o_off + S * H * 4)}
+    return {"h": 0, "total": (S * I * 2 + 255) & ~255}

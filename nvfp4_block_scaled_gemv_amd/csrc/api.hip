@@ -146,9 +146,11 @@ nvfp4_status nvfp4_moe_gemv(const uint8_t* w13_codes, const uint8_t* w13_scales,
                 "nvfp4_moe_gemv: need M >= 0, E >= 1, topk >= 1, H, I > 0 and multiples of 32 "
                 "(M=%lld E=%lld H=%lld I=%lld topk=%lld)",
                 (long long)M, (long long)E, (long long)H, (long long)I, (long long)topk);
-  if (M > NVFP4_MAX_M || topk > NVFP4_MAX_TOPK)
-    return fail(NVFP4_ERR_UNSUPPORTED, "nvfp4_moe_gemv: M=%lld (max %d), topk=%lld (max %d)",
-                (long long)M, NVFP4_MAX_M, (long long)topk, NVFP4_MAX_TOPK);
+  if (M > NVFP4_MAX_M || topk > NVFP4_MAX_TOPK || I > NVFP4_MOE_MAX_I)
+    return fail(NVFP4_ERR_UNSUPPORTED,
+                "nvfp4_moe_gemv: M=%lld (max %d), topk=%lld (max %d), I=%lld (max %d)",
+                (long long)M, NVFP4_MAX_M, (long long)topk, NVFP4_MAX_TOPK, (long long)I,
+                NVFP4_MOE_MAX_I);
   if (M == 0) return NVFP4_OK;
   if (!w13_codes || !w13_scales || !w13_gscale || !w2_codes || !w2_scales || !w2_gscale || !x ||
       !expert_ids || !gate_w || !y)

@@ -82,7 +82,8 @@ __device__ __forceinline__ void wave_row_dots(const uint8_t* __restrict__ codes,
 #pragma unroll
   for (int r = 0; r < R; ++r)
 #pragma unroll
-    for (int m = 0; m < MS; ++m) out[r][m] = wave_sum(out[r][m]);
+    for (int m = 0; m < MS; ++m)
+      if (m < ns) out[r][m] = wave_sum(out[r][m]);
 }
 
 }  // namespace nvfp4

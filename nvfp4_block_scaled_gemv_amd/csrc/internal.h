@@ -28,12 +28,10 @@ hipError_t launch_gemv_mfma(const uint8_t* codes, const uint8_t* scales, const f
 
 hipError_t launch_fill_zero(float* y, size_t n, hipStream_t stream);
 
-// MoE workspace layout (byte offsets from the workspace base, 256-aligned).
+// MoE workspace layout (byte offsets from the workspace base).
 struct MoeLayout {
-  size_t union_off;   // int32: [0] = number of distinct experts, [1..S] ids
-  size_t h_off;       // uint16 bf16 h[S, I]
-  size_t o_off;       // float per-slot outputs [S, H]
-  size_t total;
+  size_t h_off;       // uint16 bf16 SwiGLU activations h[M * topk, I]
+  size_t total;       // rounded up to 256 bytes
 };
 MoeLayout moe_layout(int64_t M, int64_t H, int64_t I, int64_t topk);
 

@@ -3,77 +3,39 @@
 // The pages' MoE decode path (graph.json nodes "l3.moe.experts_gate_up",
 // "l3.moe.experts_act", "l3.moe.experts_down", "l3.moe.blend"; card.json
 // performance[31] row union, performance[33] W4A16 slot GEMV, performance[64]
-// union sweep) becomes four launches, all on the caller's stream and with no
-// host synchronisation:
-//   1. k_moe_union:   distinct valid expert ids of the batch (the "row union").
-//   2. k_moe_gate_up: per distinct expert, stream its gate|up rows once, dot
-//                     them with x of every slot routed to it, and write
-//                     h = bf16(silu(gate) * up) per slot (SwiGLU fused).
-//   3. k_moe_down:    per distinct expert, stream its down rows once and write
-//                     the fp32 output of every slot routed to it.
-//   4. k_moe_combine: y[m] = sum_j gate_w[m, j] * o[m, j] in slot order.
-// Steps 2 and 3 launch one grid row per possible distinct expert (M * topk);
-// rows past the device-side count exit at once.
+// union sweep) runs as two launches on the caller's stream, with no host
+// synchronisation and no atomics:
+//   1. k_moe_gate_up: grid (slot j, row block). The workgroup of the first
+//      slot that names an expert streams that expert's gate|up rows once and
+//      dots them with x of every slot routed to it (the row union, found with
+//      wavefront ballots over the ids); it writes h = bf16(silu(gate) * up)
+//      per slot. Workgroups of later slots with the same id, and of invalid
+//      ids, exit at once.
+//   2. k_moe_down: the down projection and the gate-weighted combine in one
+//      pass. For output row n and token m,
+//        y[m, n] = sum_j gate_w[m, j] * g2[e_j] * W2[e_j][n, :] . h_j
+//      is one dot product over the token's valid slots laid end to end (a
+//      K axis of (valid slots) x I), so a wavefront owns R output rows and
+//      walks (slot, 32-element chunk) pairs with all 64 lanes busy whatever
+//      I is. The slot sum is a fixed-order register reduction: deterministic,
+//      no per-slot output buffer, no separate combine launch.
 #include "gemv_core.h"
 #include "internal.h"
 
 namespace nvfp4 {
 
-constexpr int kMaxSlots = NVFP4_MAX_M_INTERNAL * NVFP4_MAX_TOPK_INTERNAL;  // 128
-constexpr int kSlotPass = 8;   // slots of one expert handled per pass
-constexpr int kMoeWaves = 4;
+constexpr int kMoeWaves = 4;     // wavefronts per workgroup
+constexpr int kDownRows = 2;     // output rows per wavefront in the down pass
+constexpr int kDownUnroll = 2;   // (slot, chunk) pairs in flight per lane
 
 static inline size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 
 MoeLayout moe_layout(int64_t M, int64_t H, int64_t I, int64_t topk) {
+  (void)H;
   MoeLayout L;
-  const size_t S = (size_t)(M * topk);
-  L.union_off = 0;
-  L.h_off = align256(L.union_off + (S + 1) * sizeof(int32_t));
-  L.o_off = align256(L.h_off + S * (size_t)I * sizeof(uint16_t));
-  L.total = align256(L.o_off + S * (size_t)H * sizeof(float));
+  L.h_off = 0;
+  L.total = align256((size_t)(M * topk) * (size_t)I * sizeof(uint16_t));
   return L;
-}
-
-// One workgroup of kMaxSlots threads. uni[0] = number of distinct valid ids,
-// uni[1 + u] = the u-th distinct id in order of first appearance.
-__global__ __launch_bounds__(kMaxSlots) void k_moe_union(const int32_t* __restrict__ ids,
-                                                         int S, int64_t E,
-                                                         int32_t* __restrict__ uni) {
-  __shared__ int32_t sid[kMaxSlots];
-  __shared__ int32_t first[kMaxSlots];
-  const int i = threadIdx.x;
-  const int32_t id = (i < S) ? ids[i] : -1;
-  sid[i] = id;
-  __syncthreads();
-  bool f = (i < S) && id >= 0 && (int64_t)id < E;
-  for (int j = 0; j < i && f; ++j)
-    if (sid[j] == id) f = false;
-  first[i] = f ? 1 : 0;
-  __syncthreads();
-  if (f) {
-    int rank = 0;
-    for (int j = 0; j < i; ++j) rank += first[j];
-    uni[1 + rank] = id;
-  }
-  if (i == 0) {
-    int cnt = 0;
-    for (int j = 0; j < S; ++j) cnt += first[j];
-    uni[0] = cnt;
-  }
-}
-
-// Slots (in increasing order) whose id equals e, from position `start` on;
-// returns how many were written to slot[] (at most kSlotPass) and the next
-// start position. Uniform across the wavefront.
-__device__ __forceinline__ int next_slots(const int32_t* __restrict__ ids, int S, int32_t e,
-                                          int& start, int (&slot)[kSlotPass]) {
-  int n = 0;
-  while (start < S && n < kSlotPass) {
-    if (ids[start] == e) slot[n++] = start;
-    ++start;
-  }
-  return n;
 }
 
 __device__ __forceinline__ uint16_t bf16_rne(float v) {
@@ -82,105 +44,187 @@ __device__ __forceinline__ uint16_t bf16_rne(float v) {
   return (uint16_t)((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
 }
 
-// gate|up sweep: grid (M*topk, Y). A wavefront takes 2 consecutive outputs
-// r, r+1 and streams the 4 weight rows r, r+1 (gate) and I+r, I+r+1 (up).
+// One wavefront: gate rows r0, r0+1 and up rows I+r0, I+r0+1 of one expert
+// against x of up to MS slots; writes h[slot, r0 .. r0+1].
+template <int MS>
+__device__ __forceinline__ void gate_up_rows(const uint8_t* __restrict__ codes,
+                                             const uint8_t* __restrict__ scales, float g,
+                                             const uint16_t* __restrict__ x, int64_t H,
+                                             int64_t I, int64_t r0, int topk,
+                                             const int (&slot)[MS], int ns,
+                                             uint16_t* __restrict__ h) {
+  const int lane = threadIdx.x & 63;
+  const int64_t r1 = (r0 + 1 < I) ? r0 + 1 : r0;
+  const int64_t rows[4] = {r0, r1, I + r0, I + r1};
+  const uint16_t* xs[MS];
+#pragma unroll
+  for (int m = 0; m < MS; ++m) xs[m] = x + (int64_t)(slot[m] / topk) * H;
+  float acc[4][MS];
+  wave_row_dots<MS, 4>(codes, scales, H, rows, xs, ns, acc);
+#pragma unroll
+  for (int p = 0; p < 2; ++p)
+#pragma unroll
+    for (int m = 0; m < MS; ++m)
+      if (lane == p * MS + m && m < ns && r0 + p < I) {
+        const float G = g * acc[p][m], U = g * acc[2 + p][m];
+        const float act = G / (1.0f + expf(-G)) * U;
+        h[(int64_t)slot[m] * I + r0 + p] = bf16_rne(act);
+      }
+}
+
+// grid (S, ceil(ceil(I/2) / kMoeWaves)); a wavefront owns one gate/up row pair.
 __global__ __launch_bounds__(256) void k_moe_gate_up(
     const uint8_t* __restrict__ w13_codes, const uint8_t* __restrict__ w13_scales,
     const float* __restrict__ w13_gscale, const uint16_t* __restrict__ x,
-    const int32_t* __restrict__ ids, const int32_t* __restrict__ uni, int S, int topk,
-    int64_t H, int64_t I, uint16_t* __restrict__ h) {
-  const int u = blockIdx.x;
-  if (u >= uni[0]) return;
-  const int32_t e = uni[1 + u];
+    const int32_t* __restrict__ ids, int S, int topk, int64_t E, int64_t H, int64_t I,
+    uint16_t* __restrict__ h) {
+  const int j = blockIdx.x;
   const int lane = threadIdx.x & 63;
+  const int64_t pair =
+      (int64_t)blockIdx.y * kMoeWaves + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int64_t r0 = pair * 2;
+  if (r0 >= I) return;
+  const int32_t e = ids[j];
+  if (e < 0 || (int64_t)e >= E) return;
+  // lane l looks at slots l and l + 64 (S <= 128)
+  const int32_t a = lane < S ? ids[lane] : -1;
+  const int32_t b = lane + 64 < S ? ids[lane + 64] : -1;
+  const uint64_t earlier = __ballot(a == e && lane < j) | __ballot(b == e && lane + 64 < j);
+  if (earlier) return;   // the workgroup of an earlier slot streams this expert
+  uint64_t m0 = __ballot(a == e), m1 = __ballot(b == e);   // all >= j, j included
+
   const uint8_t* codes = w13_codes + (int64_t)e * (2 * I) * (H / 2);
   const uint8_t* scales = w13_scales + (int64_t)e * (2 * I) * (H / 16);
   const float g = w13_gscale[e];
-  const int64_t wave =
-      (int64_t)blockIdx.y * kMoeWaves + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int64_t nwaves = (int64_t)gridDim.y * kMoeWaves;
-
-  int start = 0;
-  int slot[kSlotPass];
-  int ns;
-  while ((ns = next_slots(ids, S, e, start, slot)) > 0) {
-    const uint16_t* xs[kSlotPass];
+  if (__popcll(m0) + __popcll(m1) == 1) {
+    const int slot[1] = {j};
+    gate_up_rows<1>(codes, scales, g, x, H, I, r0, topk, slot, 1, h);
+    return;
+  }
+  while (m0 | m1) {
+    int slot[4];
+    int ns = 0;
 #pragma unroll
-    for (int m = 0; m < kSlotPass; ++m) xs[m] = x + (int64_t)(slot[m < ns ? m : 0] / topk) * H;
-    for (int64_t r0 = wave * 2; r0 < I; r0 += nwaves * 2) {
-      const int64_t r1 = (r0 + 1 < I) ? r0 + 1 : r0;
-      const int64_t rows[4] = {r0, r1, I + r0, I + r1};
-      float acc[4][kSlotPass];
-      wave_row_dots<kSlotPass, 4>(codes, scales, H, rows, xs, ns, acc);
-#pragma unroll
-      for (int p = 0; p < 2; ++p)
-#pragma unroll
-        for (int m = 0; m < kSlotPass; ++m)
-          if (lane == p * kSlotPass + m && m < ns && r0 + p < I) {
-            const float G = g * acc[p][m], U = g * acc[2 + p][m];
-            const float act = G / (1.0f + expf(-G)) * U;
-            h[(int64_t)slot[m] * I + r0 + p] = bf16_rne(act);
-          }
+    for (int q = 0; q < 4; ++q) {
+      if (m0) {
+        slot[q] = __builtin_ctzll(m0);
+        m0 &= m0 - 1;
+        ++ns;
+      } else if (m1) {
+        slot[q] = 64 + __builtin_ctzll(m1);
+        m1 &= m1 - 1;
+        ++ns;
+      } else {
+        slot[q] = j;   // unused column (q >= ns)
+      }
     }
+    gate_up_rows<4>(codes, scales, g, x, H, I, r0, topk, slot, ns, h);
   }
 }
 
-// down sweep: grid (M*topk, Y). A wavefront takes 4 consecutive output rows.
+// grid ceil(H / (R * kMoeWaves)); a wavefront owns output rows n0 .. n0+R-1
+// for every token.
+template <int R, int U>
 __global__ __launch_bounds__(256) void k_moe_down(
     const uint8_t* __restrict__ w2_codes, const uint8_t* __restrict__ w2_scales,
     const float* __restrict__ w2_gscale, const uint16_t* __restrict__ h,
-    const int32_t* __restrict__ ids, const int32_t* __restrict__ uni, int S, int64_t H,
-    int64_t I, float* __restrict__ o) {
-  const int u = blockIdx.x;
-  if (u >= uni[0]) return;
-  const int32_t e = uni[1 + u];
+    const int32_t* __restrict__ ids, const float* __restrict__ gate_w, int M, int topk,
+    int64_t E, int64_t H, int64_t I, float* __restrict__ y) {
   const int lane = threadIdx.x & 63;
-  const uint8_t* codes = w2_codes + (int64_t)e * H * (I / 2);
-  const uint8_t* scales = w2_scales + (int64_t)e * H * (I / 16);
-  const float g = w2_gscale[e];
-  const int64_t wave =
-      (int64_t)blockIdx.y * kMoeWaves + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int64_t nwaves = (int64_t)gridDim.y * kMoeWaves;
+  const int64_t n0 =
+      ((int64_t)blockIdx.x * kMoeWaves + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6)) * R;
+  if (n0 >= H) return;
+  const int C = (int)(I >> 5);        // 32-element chunks per expert row
+  const int64_t cb = I >> 1, sb = I >> 4;
+  const int64_t ecb = H * cb, esb = H * sb;
+  const float invC = 1.0f / (float)C;
+  int64_t rows[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) rows[r] = (n0 + r < H) ? n0 + r : H - 1;
 
-  int start = 0;
-  int slot[kSlotPass];
-  int ns;
-  while ((ns = next_slots(ids, S, e, start, slot)) > 0) {
-    const uint16_t* xs[kSlotPass];
+  for (int m = 0; m < M; ++m) {
+    // compact the token's valid slots into lanes 0 .. nv-1, in slot order
+    const int jl = m * topk + lane;
+    const int32_t ev = lane < topk ? ids[jl] : -1;
+    const bool valid = lane < topk && ev >= 0 && (int64_t)ev < E;
+    const uint64_t vm = __ballot(valid);
+    const int nv = __popcll(vm);
+    float coef = 0.0f;
+    if (valid) coef = gate_w[jl] * w2_gscale[ev];
+    const int q = __builtin_amdgcn_mbcnt_hi((uint32_t)(vm >> 32),
+                                            __builtin_amdgcn_mbcnt_lo((uint32_t)vm, 0u));
+    const int dst = (valid ? q : 63) * 4;    // lane 63 is never read (nv <= 16)
+    const int e_c = __builtin_amdgcn_ds_permute(dst, ev);
+    const int j_c = __builtin_amdgcn_ds_permute(dst, jl);
+    const int f_c = __builtin_amdgcn_ds_permute(dst, __float_as_int(coef));
+
+    float acc[R];
 #pragma unroll
-    for (int m = 0; m < kSlotPass; ++m) xs[m] = h + (int64_t)slot[m < ns ? m : 0] * I;
-    for (int64_t n0 = wave * 4; n0 < H; n0 += nwaves * 4) {
-      int64_t rows[4];
+    for (int r = 0; r < R; ++r) acc[r] = 0.0f;
+    const int P = nv * C;   // (slot, chunk) pairs of this token
+    for (int p0 = 0; p0 < P; p0 += 64 * U) {
+      u32x4_t qv[U][R];
+      uint32_t sw[U][R];
+      u32x4_t hv[U][4];
+      float cf[U];
+      bool live[U];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) rows[r] = (n0 + r < H) ? n0 + r : H - 1;
-      float acc[4][kSlotPass];
-      wave_row_dots<kSlotPass, 4>(codes, scales, I, rows, xs, ns, acc);
+      for (int u = 0; u < U; ++u) {
+        const int p = p0 + lane + 64 * u;
+        live[u] = p < P;
+        const int pc = live[u] ? p : P - 1;
+        int qi = (int)(((float)pc + 0.5f) * invC);
+        if (qi * C > pc) --qi;
+        if ((qi + 1) * C <= pc) ++qi;
+        const int c = pc - qi * C;
+        const int ee = __shfl(e_c, qi, 64);
+        const int jj = __shfl(j_c, qi, 64);
+        cf[u] = __int_as_float(__shfl(f_c, qi, 64));
+        const uint8_t* cbase = w2_codes + (int64_t)ee * ecb + (int64_t)c * 16;
+        const uint8_t* sbase = w2_scales + (int64_t)ee * esb + (int64_t)c * 2;
 #pragma unroll
-      for (int r = 0; r < 4; ++r)
+        for (int r = 0; r < R; ++r) {
+          qv[u][r] = load_stream(cbase + rows[r] * cb);
+          sw[u][r] = *reinterpret_cast<const uint16_t*>(sbase + rows[r] * sb);
+        }
+        const u32x4_t* hp = reinterpret_cast<const u32x4_t*>(h + (int64_t)jj * I + c * 32);
 #pragma unroll
-        for (int m = 0; m < kSlotPass; ++m)
-          if (lane == r * kSlotPass + m && m < ns && n0 + r < H)
-            o[(int64_t)slot[m] * H + n0 + r] = g * acc[r][m];
+        for (int t = 0; t < 4; ++t) hv[u][t] = hp[t];
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+#pragma unroll
+        for (int b2 = 0; b2 < 2; ++b2) {
+          const u32x4_t xa = hv[u][2 * b2], xb = hv[u][2 * b2 + 1];
+          const bf16x2_t xv[8] = {as_bf16x2(xa.x), as_bf16x2(xa.y), as_bf16x2(xa.z),
+                                  as_bf16x2(xa.w), as_bf16x2(xb.x), as_bf16x2(xb.y),
+                                  as_bf16x2(xb.z), as_bf16x2(xb.w)};
+#pragma unroll
+          for (int r = 0; r < R; ++r) {
+            const uint32_t w0 = b2 ? qv[u][r].z : qv[u][r].x;
+            const uint32_t w1 = b2 ? qv[u][r].w : qv[u][r].y;
+            float p = 0.0f;
+            p = dot2(e2m1x2_to_bf16<0>(w0), xv[0], p);
+            p = dot2(e2m1x2_to_bf16<1>(w0), xv[1], p);
+            p = dot2(e2m1x2_to_bf16<2>(w0), xv[2], p);
+            p = dot2(e2m1x2_to_bf16<3>(w0), xv[3], p);
+            p = dot2(e2m1x2_to_bf16<0>(w1), xv[4], p);
+            p = dot2(e2m1x2_to_bf16<1>(w1), xv[5], p);
+            p = dot2(e2m1x2_to_bf16<2>(w1), xv[6], p);
+            p = dot2(e2m1x2_to_bf16<3>(w1), xv[7], p);
+            const float s = (b2 ? e4m3_to_f32<1>(sw[u][r]) : e4m3_to_f32<0>(sw[u][r])) * cf[u];
+            const float na = __builtin_fmaf(p, s, acc[r]);
+            acc[r] = live[u] ? na : acc[r];
+          }
+        }
+      }
+    }
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const float t = wave_sum(acc[r]);
+      if (lane == r && n0 + r < H) y[(int64_t)m * H + n0 + r] = t;
     }
   }
-}
-
-// y[m, n] = sum_j gate_w[m, j] * o[m*topk + j, n] over valid slots, j in order.
-__global__ __launch_bounds__(256) void k_moe_combine(const float* __restrict__ o,
-                                                     const int32_t* __restrict__ ids,
-                                                     const float* __restrict__ gate_w,
-                                                     int M, int topk, int64_t E, int64_t H,
-                                                     float* __restrict__ y) {
-  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (i >= (int64_t)M * H) return;
-  const int64_t m = i / H, n = i - m * H;
-  float acc = 0.0f;
-  for (int j = 0; j < topk; ++j) {
-    const int32_t e = ids[m * topk + j];
-    if (e >= 0 && (int64_t)e < E)
-      acc = __builtin_fmaf(gate_w[m * topk + j], o[(m * topk + j) * H + n], acc);
-  }
-  y[i] = acc;
 }
 
 hipError_t launch_moe(const uint8_t* w13_codes, const uint8_t* w13_scales,
@@ -189,31 +233,19 @@ hipError_t launch_moe(const uint8_t* w13_codes, const uint8_t* w13_scales,
                       const int32_t* ids, const float* gate_w, int M, int64_t E, int64_t H,
                       int64_t I, int topk, float* y, void* workspace, hipStream_t stream) {
   const MoeLayout L = moe_layout(M, H, I, topk);
-  char* ws = static_cast<char*>(workspace);
-  int32_t* uni = reinterpret_cast<int32_t*>(ws + L.union_off);
-  uint16_t* h = reinterpret_cast<uint16_t*>(ws + L.h_off);
-  float* o = reinterpret_cast<float*>(ws + L.o_off);
+  uint16_t* h = reinterpret_cast<uint16_t*>(static_cast<char*>(workspace) + L.h_off);
   const int S = M * topk;
-  hipLaunchKernelGGL(k_moe_union, dim3(1), dim3(kMaxSlots), 0, stream, ids, S, E, uni);
-  // gate|up: one wavefront per 2 outputs, up to 64 workgroups per expert
   {
-    const int64_t groups = (I + 1) / 2;
-    int64_t yb = (groups + kMoeWaves - 1) / kMoeWaves;
-    if (yb > 64) yb = 64;
+    const int64_t pairs = (I + 1) / 2;
+    const int64_t yb = (pairs + kMoeWaves - 1) / kMoeWaves;
     hipLaunchKernelGGL(k_moe_gate_up, dim3(S, (unsigned)yb), dim3(256), 0, stream, w13_codes,
-                       w13_scales, w13_gscale, x, ids, uni, S, topk, H, I, h);
+                       w13_scales, w13_gscale, x, ids, S, topk, E, H, I, h);
   }
   {
-    const int64_t groups = (H + 3) / 4;
-    int64_t yb = (groups + kMoeWaves - 1) / kMoeWaves;
-    if (yb > 64) yb = 64;
-    hipLaunchKernelGGL(k_moe_down, dim3(S, (unsigned)yb), dim3(256), 0, stream, w2_codes,
-                       w2_scales, w2_gscale, h, ids, uni, S, H, I, o);
-  }
-  {
-    const int64_t n = (int64_t)M * H;
-    hipLaunchKernelGGL(k_moe_combine, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream,
-                       o, ids, gate_w, M, topk, E, H, y);
+    const int64_t wgs = (H + kDownRows * kMoeWaves - 1) / (kDownRows * kMoeWaves);
+    hipLaunchKernelGGL((k_moe_down<kDownRows, kDownUnroll>), dim3((unsigned)wgs), dim3(256), 0,
+                       stream, w2_codes, w2_scales, w2_gscale, h, ids, gate_w, M, topk, E, H, I,
+                       y);
   }
   return hipGetLastError();
 }

@@ -22,12 +22,10 @@ def weight_bytes(N: int, K: int) -> int:
 def moe_bytes(M: int, H: int, I: int, topk: int, distinct: int) -> int:
     """One MoE call: every distinct expert's gate|up [2I, H] and down [H, I]
     weights plus its two tensor scales, x, ids and gate weights, the bf16
-    SwiGLU activations (written and read) and the per-slot fp32 outputs
-    (written and read) and y."""
+    SwiGLU activations h[M*topk, I] (written once, read once) and y."""
     S = M * topk
     per_expert = weight_bytes(2 * I, H) + weight_bytes(H, I) + 8
-    return (distinct * per_expert + M * H * 2 + S * 8 + 2 * S * I * 2
-            + 2 * S * H * 4 + M * H * 4)
+    return distinct * per_expert + M * H * 2 + S * 8 + 2 * S * I * 2 + M * H * 4
 
 
 def pages_floor_us(M: float, N: int, K: int, experts: float, bits: float,

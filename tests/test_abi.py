@@ -86,13 +86,16 @@ def test_pack_and_dequant_checks(L):
 def test_moe_checks(L):
     ws = nv.moe_workspace_bytes(8, 4096, 1536, 8)
     assert ws == nv.moe_workspace_layout(8, 4096, 1536, 8)["total"]
-    assert ws >= 64 * 1536 * 2 + 64 * 4096 * 4
+    assert ws == 64 * 1536 * 2   # bf16 h[M*topk, I], already a multiple of 256
+    assert nv.moe_workspace_bytes(1, 64, 32, 3) == 256
     args = [A + i * 0x10000000 for i in range(9)]
     f = L.nvfp4_moe_gemv
     assert f(*args, 1, 4, 64, 48, 2, B, B + 0x1000000, ws, None) == ERR_SHAPE   # I % 32
     assert f(*args, 9, 4, 64, 64, 2, B, B + 0x1000000, ws, None) == ERR_UNSUPPORTED
     assert f(*args, 1, 4, 64, 64, 17, B, B + 0x1000000, ws, None) == ERR_UNSUPPORTED
     assert f(*args, 1, 0, 64, 64, 2, B, B + 0x1000000, ws, None) == ERR_SHAPE
+    big_i = (1 << 24) + 32
+    assert f(*args, 1, 4, 64, big_i, 2, B, B + 0x1000000, 1 << 40, None) == ERR_UNSUPPORTED
     need = nv.moe_workspace_bytes(1, 64, 64, 2)
     assert f(*args, 1, 4, 64, 64, 2, B, B + 0x1000000, need - 1, None) == ERR_WORKSPACE
     assert f(*args, 1, 4, 64, 64, 2, B, None, need, None) == ERR_WORKSPACE
