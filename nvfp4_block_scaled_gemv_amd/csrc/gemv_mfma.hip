@@ -1,5 +1,6 @@
 // gemv_mfma.hip -- NVFP4 g16 W4A16 GEMV on the CDNA4 matrix cores, for
-// 3 <= M <= 8 activation rows (the instruction has room for 16).
+// 3 <= M <= 8 activation rows (the instruction has room for 16) and K not a
+// multiple of 512 (those go to gemv_mfma3.hip).
 //
 // Why MFMA here: at M rows the plain VALU path spends about 0.5 + M/2
 // instructions per weight (one bf16 pair dot per two weights per row), which
@@ -370,6 +371,7 @@ hipError_t launch_gemv_mfma_shape(const uint8_t* codes, const uint8_t* scales,
 hipError_t launch_gemv_mfma(const uint8_t* codes, const uint8_t* scales, const float* gscale,
                             const uint16_t* x, int M, int64_t N, int64_t K, float* y,
                             hipStream_t stream) {
+  if (mfma3_applicable(M, N, K)) return launch_gemv_mfma3(codes, scales, gscale, x, M, N, K, y, stream);
   int T, W;
   mfma_shape(N, K, &T, &W);
   return launch_gemv_mfma_shape(codes, scales, gscale, x, M, N, K, y, T, W, stream);

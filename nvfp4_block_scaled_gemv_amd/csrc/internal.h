@@ -26,6 +26,18 @@ hipError_t launch_gemv_mfma(const uint8_t* codes, const uint8_t* scales, const f
                             const uint16_t* x, int M, int64_t N, int64_t K, float* y,
                             hipStream_t stream);
 
+// K % 512 == 0 matrix-core path (block scale applied to the MFMA output).
+bool mfma3_applicable(int M, int64_t N, int64_t K);
+void mfma3_shape(int M, int64_t N, int64_t K, int* W_out, int* S_out, int* T_out,
+                 int* J_out);
+hipError_t launch_gemv_mfma3(const uint8_t* codes, const uint8_t* scales, const float* gscale,
+                             const uint16_t* x, int M, int64_t N, int64_t K, float* y,
+                             hipStream_t stream);
+hipError_t launch_gemv_mfma3_shape(const uint8_t* codes, const uint8_t* scales,
+                                   const float* gscale, const uint16_t* x, int M, int64_t N,
+                                   int64_t K, float* y, int W, int S, int T, int J,
+                                   hipStream_t stream);
+
 hipError_t launch_fill_zero(float* y, size_t n, hipStream_t stream);
 
 // MoE workspace layout (byte offsets from the workspace base).

@@ -28,8 +28,16 @@ __global__ __launch_bounds__(256) void k_amax(const float4* __restrict__ W, size
     const uint32_t c = __float_as_uint(fabsf(v.z)), d = __float_as_uint(fabsf(v.w));
     m = max(m, max(max(a, b), max(c, d)));
   }
+  // one atomic per workgroup: atomics on a single address serialise in L2,
+  // so their count, not the read, bounds this kernel when it is large
+  __shared__ uint32_t wmax[4];
   m = wave_max_u32(m);
-  if ((threadIdx.x & 63) == 0 && m != 0u) atomicMax(amax_bits, m);
+  if ((threadIdx.x & 63) == 0) wmax[threadIdx.x >> 6] = m;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const uint32_t t = max(max(wmax[0], wmax[1]), max(wmax[2], wmax[3]));
+    if (t != 0u) atomicMax(amax_bits, t);
+  }
 }
 
 // One thread: turn the amax bits in *gscale into g (or copy the override).
@@ -113,7 +121,7 @@ hipError_t launch_pack(const float* W, int64_t N, int64_t K, uint8_t* codes,
     if (numel) {
       const size_t n4 = numel / 4;
       const size_t want = (n4 + 255) / 256;
-      const unsigned grid = (unsigned)(want < 4096 ? (want ? want : 1) : 4096);
+      const unsigned grid = (unsigned)(want < 512 ? (want ? want : 1) : 512);
       hipLaunchKernelGGL(k_amax, dim3(grid), dim3(256), 0, stream,
                          reinterpret_cast<const float4*>(W), n4, amax);
     }

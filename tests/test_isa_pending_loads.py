@@ -1,0 +1,46 @@
+"""The matrix-core GEMV for K % 512 == 0 issues its weight loads through inline
+asm; its compiled gfx950 code must never touch a load's destination registers
+before a vmcnt wait has retired that load (a tail that issued loads nobody
+consumed once let the epilogue reuse those registers while the data was still
+in flight). Compiles the kernel with hipcc (no GPU needed) and walks the
+assembly."""
+import os
+import shutil
+import subprocess
+
+import pytest
+
+from isa_pending import check_asm, violations
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+SRC = os.path.join(ROOT, "nvfp4_block_scaled_gemv_amd", "csrc", "gemv_mfma3.hip")
+HIPCC = "/opt/rocm/bin/hipcc"
+
+
+def test_walker_flags_a_touch_before_the_wait():
+    body = ["global_load_dwordx4 v[4:7], v[0:1], off nt",
+            "v_add_u32_e32 v5, v5, v2",            # touches a pending dest
+            "s_waitcnt vmcnt(0)",
+            "v_add_u32_e32 v6, v6, v2"]
+    found = violations(body)
+    assert [f[0] for f in found] == [1]
+    ok = ["global_load_dwordx4 v[4:7], v[0:1], off nt",
+          "global_load_lds_dwordx4 v[0:1], off",
+          "s_waitcnt vmcnt(1)",
+          "v_add_u32_e32 v5, v5, v2"]
+    assert violations(ok) == []
+
+
+@pytest.mark.skipif(not os.path.exists(HIPCC), reason="hipcc not installed")
+def test_mfma3_kernels_leave_pending_loads_alone(tmp_path):
+    out = tmp_path / "mfma3.s"
+    cmd = [HIPCC, "--offload-arch=gfx950", "-O3", "-std=c++17", "-ffp-contract=off",
+           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+           "-I", os.path.join(ROOT, "include"), "--cuda-device-only", "-S",
+           "-o", str(out), SRC]
+    subprocess.run(cmd, check=True, capture_output=True, timeout=600)
+    res = check_asm(out.read_text(), r"_Z\S*k_gemv_mfma3\S*")
+    # M = 3..8 x (S=3,T=1), (S=3,T=2), (S=4,T=1), chunks of 2 steps
+    assert len(res) == 18, sorted(res)
+    bad = {k: v[:3] for k, v in res.items() if v}
+    assert not bad, bad
