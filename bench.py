@@ -5,9 +5,14 @@ W4A16 GEMV on one MI355X.
 Headline leg (``value``): the LM-head-sized GEMV, M=1, N=151936, K=4096 (the
 llama.cpp trace page's output.weight at one token). A step is one GEMV call.
 Secondary legs, measured the same way and reported in the same JSON line:
-  m8   - the stress GEMV pair at M=8 (12288x4096 and 4096x12288, Student-t
-         weights with 1% zero blocks), one step = both calls;
-  moe  - the 288-expert MoE expert-slot pass at M=8 (and M=1), top-8.
+  m8    - the stress GEMV pair at M=8 (12288x4096 and 4096x12288, Student-t
+          weights with 1% zero blocks), one step = both calls;
+  layer - the dense decode layer at M=5 (q, k, v, o, gate, up, down), one
+          step = the seven calls;
+  moe   - the 288-expert MoE expert-slot pass at M=8 (and M=1), top-8;
+  copy  - a plain fp32 copy kernel of 2 x 512 MiB per launch: the measured
+          bandwidth that the other legs are also reported against, and the
+          calibration of the HBM byte counters.
 Throughput counts algorithmic bytes (codes + scales + tensor scale + x + y;
 for the MoE every distinct expert's weights once) per second, inputs already
 resident in HBM. Weight copies are rotated so that each call reads memory
@@ -149,9 +154,22 @@ def cpu_baseline(c0, s0, g0, x_bits, B, M):
         oracle.gemv(c0, s0, g0, x_bits)
         times.append(time.perf_counter() - t)
     tm = float(np.median(times))
-    return {"value": B / tm / 1e9, "unit": "GB/s", "cores": threads, "kind": "oracle",
-            "sample": f"full 151936x4096 M=1 GEMV, {len(times)} runs, median {tm:.3f} s",
-            "tokens_per_s": M / tm, "cpu": cpu_model(), "host_cpus": os.cpu_count()}
+    out = {"value": B / tm / 1e9, "unit": "GB/s", "cores": threads, "kind": "oracle",
+           "sample": f"full 151936x4096 M=1 GEMV, {len(times)} runs, median {tm:.3f} s",
+           "tokens_per_s": M / tm, "cpu": cpu_model(), "host_cpus": os.cpu_count()}
+    # the same oracle on one thread (one run of the full matrix)
+    try:
+        import ctypes
+        gomp = ctypes.CDLL("libgomp.so.1")
+        gomp.omp_set_num_threads(1)
+        t = time.perf_counter()
+        oracle.gemv(c0, s0, g0, x_bits)
+        t1 = time.perf_counter() - t
+        gomp.omp_set_num_threads(threads)
+        out["one_thread"] = {"value": B / t1 / 1e9, "unit": "GB/s", "seconds": t1}
+    except OSError:
+        pass
+    return out
 
 
 def leg_m8(torch, nv, workloads, traffic, steps, warmup):
@@ -182,6 +200,73 @@ def leg_m8(torch, nv, workloads, traffic, steps, warmup):
             "gbs_wall": B / (ms * 1e-3) / 1e9, "gbs_kernel": B / (kt * 1e-3) / 1e9,
             "frac_of_peak": B / (kt * 1e-3) / 1e9 / HBM_PEAK_GBS,
             "tokens_per_s": M / (ms * 1e-3), "rotate_copies": R}
+
+
+def leg_layer(torch, nv, workloads, traffic, steps, warmup):
+    """The dense decode layer at M=5: q, k, v, o, gate, up, down, each matrix
+    from its own weight stream. Timed twice: seven separate calls (each with its
+    own x), and fused into four launches (q|k|v and gate|up as one
+    multi-projection call each, sharing the group's x)."""
+    M = 5
+    names = [n for n, _, _ in workloads.DECODE_LAYER]
+    packed, B, wb = {}, 0, 0
+    for si, (name, N, K) in enumerate(workloads.DECODE_LAYER):
+        log(f"[bench] layer: generating {name} {N}x{K}")
+        W = workloads.dense_weights(2, 0, si, N, K)
+        c, s, g = nv.pack(torch.from_numpy(W).cuda())
+        del W
+        x = torch.from_numpy(workloads.x_bf16(2, 0, si, M, K).view(np.int16)).cuda().view(
+            torch.bfloat16)
+        y = torch.empty((M, N), dtype=torch.float32, device="cuda")
+        packed[name] = (c, s, g, x, y)
+        B += traffic.gemv_bytes(M, N, K)
+        wb += traffic.weight_bytes(N, K)
+    R = max(2, -(-MIN_ROTATION_BYTES // wb))
+    copies = [packed] + [{k: (c.clone(), s.clone(), g.clone(), x, y)
+                          for k, (c, s, g, x, y) in packed.items()} for _ in range(R - 1)]
+    groups = [("q", "k", "v"), ("o",), ("gate", "up"), ("down",)]
+    # fused: x read once per launch
+    Bf = B - sum((len(gr) - 1) * M * 4096 * 2 for gr in groups)
+
+    def step(i):
+        cp = copies[i % R]
+        for n in names:
+            c, s, g, x, y = cp[n]
+            nv.gemv_into(c, s, g, x, y)
+
+    def step_fused(i):
+        cp = copies[i % R]
+        for gr in groups:
+            mats = [cp[n][:3] for n in gr]
+            nv.gemv_segments_into(mats, cp[gr[0]][3], [cp[n][4] for n in gr])
+
+    ms, kt = timed_steps(torch, step, steps, warmup)
+    msf, ktf = timed_steps(torch, step_fused, steps, warmup)
+    return {"workload": "decode_layer_m5 (q,k,v,o 4096/1024 x 4096; gate, up 12288x4096; "
+                        "down 4096x12288)", "M": M, "launches_per_step": len(names),
+            "bytes_per_step": B, "ms_per_step": ms, "step_us_events": kt * 1e3,
+            "gbs_wall": B / (ms * 1e-3) / 1e9, "gbs_kernel": B / (kt * 1e-3) / 1e9,
+            "frac_of_peak": B / (kt * 1e-3) / 1e9 / HBM_PEAK_GBS,
+            "tokens_per_s": M / (ms * 1e-3), "rotate_copies": R,
+            "fused": {"launches_per_step": len(groups), "bytes_per_step": Bf,
+                      "ms_per_step": msf, "step_us_events": ktf * 1e3,
+                      "gbs_kernel": Bf / (ktf * 1e-3) / 1e9,
+                      "frac_of_peak": Bf / (ktf * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                      "tokens_per_s": M / (msf * 1e-3)}}
+
+
+def gpu_clock_state():
+    """Best-effort read of the DPM clock tables (read-only sysfs)."""
+    import glob
+    out = {}
+    for f in sorted(glob.glob("/sys/class/drm/card*/device/pp_dpm_*clk"))[:8]:
+        try:
+            with open(f) as fh:
+                cur = [l.strip() for l in fh if "*" in l]
+            out[f.split("/")[-1] + "@" + f.split("/")[-3]] = cur[0] if cur else None
+        except OSError:
+            pass
+    return out or None
 
 
 def leg_moe(torch, nv, workloads, traffic, steps, warmup, M):
@@ -332,23 +417,35 @@ def read_traffic():
         return None
 
 
-def summarize_stats(stats_csv, cmd, out, top=14):
-    """Short text table from a rocprofv3 --stats kernel summary."""
+def summarize_stats(stats_csv, cmd, out, top=16):
+    """Short text table from a rocprofv3 --stats kernel summary, with the
+    per-dispatch median, p10 and p90 from the kernel trace next to it."""
     import csv
     rows = []
     with open(stats_csv, newline="") as f:
         for r in csv.DictReader(f):
             rows.append(r)
     rows.sort(key=lambda r: -float(r["TotalDurationNs"]))
-    lines = ["# rocprofv3 --kernel-trace --stats kernel summary",
+    durs = {}
+    trace_csv = stats_csv.replace("kernel_stats", "kernel_trace")
+    if os.path.exists(trace_csv):
+        with open(trace_csv, newline="") as f:
+            for r in csv.DictReader(f):
+                durs.setdefault(r["Kernel_Name"], []).append(
+                    (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+    lines = ["# rocprofv3 --kernel-trace --stats kernel summary (durations in us;",
+             "# median/p10/p90 over the dispatches in the kernel trace)",
              "# commands (run from /tmp with TMPDIR=/tmp):", *[f"#   {c}" for c in cmd],
-             f"{'calls':>7} {'avg_us':>10} {'min_us':>10} {'max_us':>10} {'pct':>6}  kernel"]
+             f"{'calls':>7} {'avg':>9} {'median':>9} {'p10':>9} {'p90':>9} {'min':>9} "
+             f"{'max':>9} {'pct':>6}  kernel"]
     for r in rows[:top]:
         name = r["Name"]
         short = name.split("(")[0] if name.startswith(("nvfp4", "void nvfp4")) else name[:90]
-        lines.append(f"{int(r['Calls']):7d} {float(r['AverageNs']) / 1e3:10.2f} "
-                     f"{float(r['MinNs']) / 1e3:10.2f} {float(r['MaxNs']) / 1e3:10.2f} "
-                     f"{float(r['Percentage']):6.2f}  {short}")
+        d = np.sort(np.array(durs.get(name, [float("nan")])))
+        med, p10, p90 = (float(np.percentile(d, q)) for q in (50, 10, 90))
+        lines.append(f"{int(r['Calls']):7d} {float(r['AverageNs']) / 1e3:9.2f} {med:9.2f} "
+                     f"{p10:9.2f} {p90:9.2f} {float(r['MinNs']) / 1e3:9.2f} "
+                     f"{float(r['MaxNs']) / 1e3:9.2f} {float(r['Percentage']):6.2f}  {short}")
     with open(out, "w") as f:
         f.write("\n".join(lines) + "\n")
     print("\n".join(lines))
@@ -361,9 +458,10 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--legs", default="lm_head,m8,moe",
-                    help="comma list of lm_head, m8, moe, copy (lm_head is the headline; "
-                         "copy is the byte-counter calibration kernel)")
+    ap.add_argument("--legs", default="lm_head,m8,layer,moe,copy",
+                    help="comma list of lm_head, m8, layer, moe, copy (lm_head is the "
+                         "headline; copy is a plain copy kernel: the byte-counter "
+                         "calibration and the measured-bandwidth reference)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--summarize-pmc", nargs=3, metavar=("FETCH_CSV", "WRITE_CSV", "OUT"),
                     help="write the traffic summary from two rocprofv3 --pmc passes")
@@ -424,12 +522,22 @@ def main():
             result["cpu_baseline"] = lm["cpu_baseline"]
     if "m8" in legs:
         result["m8"] = leg_m8(torch, nv, workloads, traffic, args.steps, args.warmup)
+    if "layer" in legs:
+        result["layer_m5"] = leg_layer(torch, nv, workloads, traffic, args.steps, args.warmup)
     if "copy" in legs:
-        result["copy_calibration"] = leg_copy(torch, args.steps, args.warmup)
+        cp = leg_copy(torch, min(args.steps, 50), min(args.warmup, 5))
+        result["copy_calibration"] = cp
+        # fractions of the measured copy bandwidth (read + write bytes per second)
+        if result.get("roofline"):
+            result["roofline"]["frac_of_measured_copy"] = result["roofline"]["achieved"] / cp["gbs"]
+        for k in ("m8", "layer_m5"):
+            if k in result:
+                result[k]["frac_of_measured_copy"] = result[k]["gbs_kernel"] / cp["gbs"]
     if "moe" in legs:
         result["moe"] = {f"m{M}": leg_moe(torch, nv, workloads, traffic, args.steps,
                                           args.warmup, M) for M in (1, 8)}
     result["env"] = {"gpu": props.name, "cus": props.multi_processor_count,
+                     "dpm_clocks": gpu_clock_state(),
                      "hip": torch.version.hip, "torch": torch.__version__, "git": git_sha(),
                      "argv": sys.argv[1:]}
     print(json.dumps(result), flush=True)

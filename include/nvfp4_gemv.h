@@ -55,7 +55,7 @@
 extern "C" {
 #endif
 
-#define NVFP4_ABI_VERSION 1
+#define NVFP4_ABI_VERSION 2
 
 /* Largest number of activation rows (tokens) one GEMV / MoE call takes. */
 #define NVFP4_MAX_M 8
@@ -144,6 +144,42 @@ nvfp4_status nvfp4_dequant(const uint8_t* codes, const uint8_t* scales,
 nvfp4_status nvfp4_gemv(const uint8_t* codes, const uint8_t* scales,
                         const float* gscale, const uint16_t* x, int64_t M,
                         int64_t N, int64_t K, float* y, hipStream_t stream);
+
+/* Largest number of matrices one nvfp4_gemv_segments call takes. */
+#define NVFP4_MAX_SEGMENTS 8
+
+/* One matrix of a fused multi-projection GEMV (device pointers). */
+typedef struct nvfp4_gemv_segment {
+  const uint8_t* codes;    /* uint8[N, K/2], 16-byte aligned */
+  const uint8_t* scales;   /* uint8[N, K/16], 2-byte aligned */
+  const float* gscale;     /* float[1], 4-byte aligned */
+  float* y;                /* float[M, N] out, 4-byte aligned */
+  int64_t N;               /* rows of this matrix, >= 0 (0: skipped) */
+} nvfp4_gemv_segment;
+
+/*
+ * nvfp4_gemv_segments -- several NVFP4 matrices that read the same
+ * activations (q|k|v, gate|up), in one launch: for every segment s,
+ *
+ *   y_s[m, n] = g_s * sum_k decode(W_s)[n, k] * x[m, k]
+ *
+ * exactly as n_segments separate nvfp4_gemv calls would compute it, but the
+ * work units of all matrices share one grid, so small matrices no longer leave
+ * most of the GPU idle (blueprint card.json performance[6], the segmented
+ * W4A16 GEMV, N = 8726 in one launch; plan flag glm_w4a16_gemv_seg).
+ *
+ *   segs        host array of n_segments descriptors (read during the call
+ *               only); the pointers inside are device pointers;
+ *   n_segments  0 .. NVFP4_MAX_SEGMENTS;
+ *   x           bf16[M, K] shared by every segment, 16-byte aligned;
+ *   M, K        as for nvfp4_gemv (M <= NVFP4_MAX_M, K % 32 == 0).
+ * No output may overlap any input or another output.
+ * Errors: NULL, SHAPE, ALIGN, UNSUPPORTED (n_segments or M too large), ALIAS,
+ * HIP.
+ */
+nvfp4_status nvfp4_gemv_segments(const nvfp4_gemv_segment* segs, int64_t n_segments,
+                                 const uint16_t* x, int64_t M, int64_t K,
+                                 hipStream_t stream);
 
 /*
  * nvfp4_moe_workspace_bytes -- device workspace that nvfp4_moe_gemv needs for

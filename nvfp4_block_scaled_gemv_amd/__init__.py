@@ -10,6 +10,7 @@ Functions (same names as the C entry points, without the prefix):
   pack(W[, gscale_override])             -> codes, scales, gscale
   dequant(codes, scales, gscale)         -> W_hat (fp32)
   gemv(codes, scales, gscale, x)         -> y (fp32 [M, N])
+  gemv_segments([(codes, scales, gscale), ...], x) -> [y_s] (one launch)
   moe_workspace_bytes(M, H, I, topk)     -> int
   moe_gemv(w13..., w2..., x, ids, gate_w[, workspace]) -> y (fp32 [M, H])
 The ``*_into`` variants write into caller-provided outputs.
@@ -41,6 +42,15 @@ class Nvfp4Error(RuntimeError):
         self.status = status
 
 
+class GemvSegment(ctypes.Structure):
+    """nvfp4_gemv_segment: one matrix of a fused multi-projection GEMV."""
+    _fields_ = [("codes", ctypes.c_void_p), ("scales", ctypes.c_void_p),
+                ("gscale", ctypes.c_void_p), ("y", ctypes.c_void_p), ("N", ctypes.c_int64)]
+
+
+MAX_SEGMENTS = 8
+
+
 def lib() -> ctypes.CDLL:
     """The loaded C library (raises if it has not been built)."""
     global _lib
@@ -62,6 +72,9 @@ def lib() -> ctypes.CDLL:
         L.nvfp4_dequant.argtypes = [_VP, _VP, _VP, _I64, _I64, _VP, _VP]
         L.nvfp4_gemv.restype = ctypes.c_int
         L.nvfp4_gemv.argtypes = [_VP, _VP, _VP, _VP, _I64, _I64, _I64, _VP, _VP]
+        L.nvfp4_gemv_segments.restype = ctypes.c_int
+        L.nvfp4_gemv_segments.argtypes = [ctypes.POINTER(GemvSegment), _I64, _VP, _I64, _I64,
+                                          _VP]
         L.nvfp4_moe_workspace_bytes.restype = ctypes.c_size_t
         L.nvfp4_moe_workspace_bytes.argtypes = [_I64, _I64, _I64, _I64]
         L.nvfp4_moe_gemv.restype = ctypes.c_int
@@ -163,6 +176,36 @@ def gemv(codes, scales, gscale, x) -> torch.Tensor:
     y = torch.empty((x.shape[0], codes.shape[0]), dtype=torch.float32, device=codes.device)
     gemv_into(codes, scales, gscale, x, y)
     return y
+
+
+def gemv_segments_into(mats, x, ys) -> None:
+    """One launch for several matrices reading the same x[M, K]:
+    ys[s] = g_s * decode(W_s) . x^T, mats[s] = (codes, scales, gscale)."""
+    if len(mats) != len(ys):
+        raise ValueError("one output per matrix")
+    if len(mats) > MAX_SEGMENTS:
+        raise ValueError(f"at most {MAX_SEGMENTS} matrices per launch")
+    _dev(x, *ys, *[t for m in mats for t in m])
+    _dtype(x, torch.bfloat16, torch.int16, torch.uint16, name="x")
+    M, K = x.shape
+    segs = (GemvSegment * max(1, len(mats)))()
+    for i, ((c, sc, g), y) in enumerate(zip(mats, ys)):
+        _dtype(y, torch.float32, name="y")
+        N = c.shape[0]
+        if c.shape[1] * 2 != K or tuple(y.shape) != (M, N):
+            raise ValueError(f"segment {i}: codes {tuple(c.shape)}, x {tuple(x.shape)}, "
+                             f"y {tuple(y.shape)}")
+        segs[i] = GemvSegment(_p(c), _p(sc), _p(g), _p(y), N)
+    _check("nvfp4_gemv_segments",
+           lib().nvfp4_gemv_segments(segs, len(mats), _p(x), M, K, _stream(x)))
+
+
+def gemv_segments(mats, x):
+    """[y_s] for mats = [(codes, scales, gscale), ...] sharing x (one launch)."""
+    ys = [torch.empty((x.shape[0], c.shape[0]), dtype=torch.float32, device=x.device)
+          for c, _, _ in mats]
+    gemv_segments_into(mats, x, ys)
+    return ys
 
 
 # ------------------------------------------------------------------- moe

@@ -41,6 +41,8 @@ nvfp4_status hip_result(hipError_t e, const char* what) {
 
 }  // namespace
 
+static_assert(NVFP4_MAX_SEGMENTS == nvfp4::kMaxSegments, "segment limit mismatch");
+
 extern "C" {
 
 int nvfp4_abi_version(void) { return NVFP4_ABI_VERSION; }
@@ -127,6 +129,73 @@ nvfp4_status nvfp4_gemv(const uint8_t* codes, const uint8_t* scales, const float
     return fail(NVFP4_ERR_ALIAS, "nvfp4_gemv: y overlaps an input");
   return hip_result(nvfp4::launch_gemv(codes, scales, gscale, x, (int)M, N, K, y, stream),
                     "nvfp4_gemv launch");
+}
+
+nvfp4_status nvfp4_gemv_segments(const nvfp4_gemv_segment* segs, int64_t n_segments,
+                                 const uint16_t* x, int64_t M, int64_t K, hipStream_t stream) {
+  clear_error();
+  if (n_segments < 0 || M < 0 || K < 0 || (K % 32) != 0)
+    return fail(NVFP4_ERR_SHAPE,
+                "nvfp4_gemv_segments: need n_segments, M, K >= 0 and K %% 32 == 0 "
+                "(n=%lld M=%lld K=%lld)",
+                (long long)n_segments, (long long)M, (long long)K);
+  if (n_segments > NVFP4_MAX_SEGMENTS || M > NVFP4_MAX_M)
+    return fail(NVFP4_ERR_UNSUPPORTED,
+                "nvfp4_gemv_segments: n_segments=%lld (max %d), M=%lld (max %d)",
+                (long long)n_segments, NVFP4_MAX_SEGMENTS, (long long)M, NVFP4_MAX_M);
+  if (n_segments == 0 || M == 0) return NVFP4_OK;
+  if (!segs) return fail(NVFP4_ERR_NULL, "nvfp4_gemv_segments: segs is NULL");
+  nvfp4::SegDesc d[NVFP4_MAX_SEGMENTS];
+  int n = 0;
+  for (int64_t s = 0; s < n_segments; ++s) {
+    const nvfp4_gemv_segment& g = segs[s];
+    if (g.N < 0)
+      return fail(NVFP4_ERR_SHAPE, "nvfp4_gemv_segments: segment %lld has N=%lld < 0",
+                  (long long)s, (long long)g.N);
+    if (g.N == 0) continue;
+    if (!g.y) return fail(NVFP4_ERR_NULL, "nvfp4_gemv_segments: segment %lld y is NULL", (long long)s);
+    if (!aligned(g.y, 4))
+      return fail(NVFP4_ERR_ALIGN, "nvfp4_gemv_segments: segment %lld y must be 4-byte aligned",
+                  (long long)s);
+    if (K > 0) {
+      if (!g.codes || !g.scales || !g.gscale || !x)
+        return fail(NVFP4_ERR_NULL, "nvfp4_gemv_segments: segment %lld has a NULL input",
+                    (long long)s);
+      if (!aligned(g.codes, 16) || !aligned(g.scales, 2) || !aligned(g.gscale, 4) ||
+          !aligned(x, 16))
+        return fail(NVFP4_ERR_ALIGN,
+                    "nvfp4_gemv_segments: segment %lld: codes and x must be 16-byte, scales "
+                    "2-byte, gscale 4-byte aligned", (long long)s);
+    }
+    d[n++] = {g.codes, g.scales, g.gscale, g.y, g.N};
+  }
+  if (n == 0) return NVFP4_OK;
+  // no output may overlap any input or another output
+  for (int a = 0; a < n; ++a) {
+    const size_t ya = (size_t)M * (size_t)d[a].N * 4;
+    if (K > 0 && overlap(d[a].y, ya, x, (size_t)M * (size_t)K * 2))
+      return fail(NVFP4_ERR_ALIAS, "nvfp4_gemv_segments: an output overlaps x");
+    for (int b = 0; b < n; ++b) {
+      const size_t nk = (size_t)d[b].N * (size_t)K;
+      if (K > 0 && (overlap(d[a].y, ya, d[b].codes, nk / 2) ||
+                    overlap(d[a].y, ya, d[b].scales, nk / 16) ||
+                    overlap(d[a].y, ya, d[b].gscale, 4)))
+        return fail(NVFP4_ERR_ALIAS, "nvfp4_gemv_segments: an output overlaps an input");
+      if (b != a && overlap(d[a].y, ya, d[b].y, (size_t)M * (size_t)d[b].N * 4))
+        return fail(NVFP4_ERR_ALIAS, "nvfp4_gemv_segments: two outputs overlap");
+    }
+  }
+  if (K == 0) {
+    for (int a = 0; a < n; ++a) {
+      const nvfp4_status st =
+          hip_result(nvfp4::launch_fill_zero(d[a].y, (size_t)M * (size_t)d[a].N, stream),
+                     "nvfp4_gemv_segments zero fill");
+      if (st != NVFP4_OK) return st;
+    }
+    return NVFP4_OK;
+  }
+  return hip_result(nvfp4::launch_gemv_segments(d, n, x, (int)M, K, stream),
+                    "nvfp4_gemv_segments launch");
 }
 
 size_t nvfp4_moe_workspace_bytes(int64_t M, int64_t H, int64_t I, int64_t topk) {

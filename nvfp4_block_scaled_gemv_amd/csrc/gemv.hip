@@ -12,35 +12,39 @@ namespace nvfp4 {
 
 constexpr int kWavesPerBlock = 4;
 
-// Each wavefront takes groups of R consecutive rows, striding over the grid.
-template <int M, int R>
-__global__ __launch_bounds__(256) void k_gemv(const uint8_t* __restrict__ codes,
-                                              const uint8_t* __restrict__ scales,
-                                              const float* __restrict__ gscale,
-                                              const uint16_t* __restrict__ x, int64_t N,
-                                              int64_t K, float* __restrict__ y) {
+// Each wavefront takes groups of R consecutive rows of one segment, striding
+// over the groups of all segments.
+template <int M, int R, bool SEG>
+__global__ __launch_bounds__(256) void k_gemv(const SegTable tab, const uint16_t* __restrict__ x,
+                                              int64_t K) {
   const int lane = threadIdx.x & 63;
   // wavefront index, made provably uniform so loop control stays scalar
   const int64_t wave =
       (int64_t)blockIdx.x * kWavesPerBlock + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int64_t nwaves = (int64_t)gridDim.x * kWavesPerBlock;
-  const float g = *gscale;
+  const int64_t units = tab.start[kMaxSegments];
   const uint16_t* xs[M];
 #pragma unroll
   for (int m = 0; m < M; ++m) xs[m] = x + (int64_t)m * K;
 
-  for (int64_t n0 = wave * R; n0 < N; n0 += nwaves * R) {
+  for (int64_t u = wave; u < units; u += nwaves) {
+    // a single matrix skips the lookup (it costs registers in this loop)
+    const Seg sg = SEG ? find_seg(tab, u)
+                       : Seg{tab.codes[0], tab.scales[0], tab.gscale[0], tab.y[0], tab.N[0], u};
+    const int64_t N = sg.N;
+    const int64_t n0 = sg.unit * R;
     int64_t rows[R];
 #pragma unroll
     for (int r = 0; r < R; ++r) rows[r] = (n0 + r < N) ? (n0 + r) : (N - 1);
     float acc[R][M];
-    wave_row_dots<M, R>(codes, scales, K, rows, xs, M, acc);
+    wave_row_dots<M, R>(sg.codes, sg.scales, K, rows, xs, M, acc);
+    const float g = *sg.gscale;
     // lane (r * M + m) stores one result
 #pragma unroll
     for (int r = 0; r < R; ++r)
 #pragma unroll
       for (int m = 0; m < M; ++m)
-        if (lane == r * M + m && n0 + r < N) y[(int64_t)m * N + n0 + r] = acc[r][m] * g;
+        if (lane == r * M + m && n0 + r < N) sg.y[(int64_t)m * N + n0 + r] = acc[r][m] * g;
   }
 }
 
@@ -62,41 +66,52 @@ hipError_t launch_fill_zero(float* y, size_t n, hipStream_t stream) {
 // One wavefront per row group, no grid-stride reuse unless the matrix is huge:
 // a launch-shape sweep on the 151936 x 4096 LM head measured 53.1 us with
 // one group per wavefront against 56.1 us with the grid capped at 8
-// workgroups per CU. Rows per wavefront grow with N so that small matrices
-// still spread over every CU (1024 rows: R = 1 -> 3.5 us, R = 4 -> 4.6 us).
+// workgroups per CU. Rows per wavefront grow with the row count so that small
+// matrices still spread over every CU (1024 rows: R = 1 -> 3.5 us, R = 4 ->
+// 4.6 us).
 template <int M, int R>
-static void launch_m(const uint8_t* codes, const uint8_t* scales, const float* gscale,
-                     const uint16_t* x, int64_t N, int64_t K, float* y, hipStream_t stream) {
-  const int64_t groups = (N + R - 1) / R;
-  const int64_t want = (groups + kWavesPerBlock - 1) / kWavesPerBlock;
+static void launch_m(const SegDesc* d, int n, const uint16_t* x, int64_t K,
+                     hipStream_t stream) {
+  const SegTable tab = make_seg_table(d, n, R);
+  const int64_t units = tab.start[kMaxSegments];
+  const int64_t want = (units + kWavesPerBlock - 1) / kWavesPerBlock;
   const int64_t cap = (int64_t)1 << 20;
   const unsigned grid = (unsigned)(want < cap ? want : cap);
-  hipLaunchKernelGGL((k_gemv<M, R>), dim3(grid), dim3(256), 0, stream, codes, scales, gscale,
-                     x, N, K, y);
+  if (n == 1)
+    hipLaunchKernelGGL((k_gemv<M, R, false>), dim3(grid), dim3(256), 0, stream, tab, x, K);
+  else
+    hipLaunchKernelGGL((k_gemv<M, R, true>), dim3(grid), dim3(256), 0, stream, tab, x, K);
 }
 
 template <int M>
-static void launch_valu(const uint8_t* codes, const uint8_t* scales, const float* gscale,
-                        const uint16_t* x, int64_t N, int64_t K, float* y, hipStream_t stream) {
-  if (N >= 32768)
-    launch_m<M, 4>(codes, scales, gscale, x, N, K, y, stream);
-  else if (N >= 4096)
-    launch_m<M, 2>(codes, scales, gscale, x, N, K, y, stream);
+static void launch_valu(const SegDesc* d, int n, int64_t rows, const uint16_t* x, int64_t K,
+                        hipStream_t stream) {
+  if (rows >= 32768)
+    launch_m<M, 4>(d, n, x, K, stream);
+  else if (rows >= 4096)
+    launch_m<M, 2>(d, n, x, K, stream);
   else
-    launch_m<M, 1>(codes, scales, gscale, x, N, K, y, stream);
+    launch_m<M, 1>(d, n, x, K, stream);
+}
+
+hipError_t launch_gemv_segments(const SegDesc* d, int n, const uint16_t* x, int M, int64_t K,
+                                hipStream_t stream) {
+  if (n < 1 || n > kMaxSegments || M < 1 || M > NVFP4_MAX_M_INTERNAL) return hipErrorInvalidValue;
+  int64_t rows = 0;
+  for (int s = 0; s < n; ++s) rows += d[s].N;
+  switch (M) {
+    case 1: launch_valu<1>(d, n, rows, x, K, stream); break;
+    case 2: launch_valu<2>(d, n, rows, x, K, stream); break;
+    default: return launch_gemv_mfma(d, n, x, M, K, stream);
+  }
+  return hipGetLastError();
 }
 
 hipError_t launch_gemv(const uint8_t* codes, const uint8_t* scales, const float* gscale,
                        const uint16_t* x, int M, int64_t N, int64_t K, float* y,
                        hipStream_t stream) {
-  switch (M) {
-    case 1: launch_valu<1>(codes, scales, gscale, x, N, K, y, stream); break;
-    case 2: launch_valu<2>(codes, scales, gscale, x, N, K, y, stream); break;
-    default:
-      if (M < 1 || M > NVFP4_MAX_M_INTERNAL) return hipErrorInvalidValue;
-      return launch_gemv_mfma(codes, scales, gscale, x, M, N, K, y, stream);
-  }
-  return hipGetLastError();
+  const SegDesc d = {codes, scales, gscale, y, N};
+  return launch_gemv_segments(&d, 1, x, M, K, stream);
 }
 
 }  // namespace nvfp4

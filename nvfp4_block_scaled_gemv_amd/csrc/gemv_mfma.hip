@@ -223,9 +223,14 @@ __device__ __forceinline__ void mfma_step(const Chunk<T>& cur, Chunk<T>& ld, uin
 
 template <int T, bool FULL>
 __global__ __launch_bounds__(64 * kMfmaMaxWaves) void k_gemv_mfma(
-    const uint8_t* __restrict__ codes, const uint8_t* __restrict__ scales,
-    const float* __restrict__ gscale, const uint16_t* __restrict__ x, int M, int64_t N,
-    int64_t K, float* __restrict__ y) {
+    const SegTable tab, const uint16_t* __restrict__ x, int M, int64_t K) {
+  // workgroup = one unit of 16T rows of one segment
+  const Seg sg = find_seg(tab, blockIdx.x);
+  const uint8_t* __restrict__ codes = sg.codes;
+  const uint8_t* __restrict__ scales = sg.scales;
+  const float* __restrict__ gscale = sg.gscale;
+  float* __restrict__ y = sg.y;
+  const int64_t N = sg.N;
   // dynamic LDS: per wavefront two x chunk buffers of M rows, then the
   // cross-wavefront reduction area (W * T * 32 lanes * 4 floats)
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
@@ -234,7 +239,7 @@ __global__ __launch_bounds__(64 * kMfmaMaxWaves) void k_gemv_mfma(
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int W = blockDim.x >> 6;
   const int i = lane & 15, g = lane >> 4;
-  const int64_t n0 = (int64_t)blockIdx.x * (16 * T);
+  const int64_t n0 = sg.unit * (16 * T);
   const int64_t cb = K >> 1, sb = K >> 4;
   const int64_t IT = (K + 127) >> 7;
   // this wavefront's chunks of kChunkIters iterations (the last may be short)
@@ -340,8 +345,7 @@ __global__ __launch_bounds__(64 * kMfmaMaxWaves) void k_gemv_mfma(
 }
 
 // Launch shape: T row tiles per workgroup and W wavefronts splitting K.
-void mfma_shape(int64_t N, int64_t K, int* T_out, int* W_out) {
-  const int64_t tiles = (N + 15) / 16;
+void mfma_shape(int64_t tiles, int64_t K, int* T_out, int* W_out) {
   const int64_t chunks = ((K + 127) / 128 + kChunkIters - 1) / kChunkIters;
   const int T = 1;  // two tiles per workgroup spill registers with the 3-stage ring
   const int64_t wgs = (tiles + T - 1) / T;
@@ -353,28 +357,29 @@ void mfma_shape(int64_t N, int64_t K, int* T_out, int* W_out) {
   *W_out = W;
 }
 
-hipError_t launch_gemv_mfma_shape(const uint8_t* codes, const uint8_t* scales,
-                                  const float* gscale, const uint16_t* x, int M, int64_t N,
-                                  int64_t K, float* y, int T, int W, hipStream_t stream) {
-  const int64_t wgs = ((N + 15) / 16 + T - 1) / T;
-  const size_t lds = (size_t)2 * W * M * kXRowStride + (size_t)W * T * 32 * 4 * sizeof(float);
+hipError_t launch_gemv_mfma_shape(const SegDesc* d, int n, const uint16_t* x, int M,
+                                  int64_t K, int T, int W, hipStream_t stream) {
+  (void)T;   // one tile per workgroup
+  const SegTable tab = make_seg_table(d, n, 16);
+  const int64_t wgs = tab.start[kMaxSegments];
+  const size_t lds = (size_t)2 * W * M * kXRowStride + (size_t)W * 32 * 4 * sizeof(float);
   const bool full = (K % (128 * kChunkIters)) == 0;
 #define NVFP4_LAUNCH_MFMA(TT, FF)                                                        \
   hipLaunchKernelGGL((k_gemv_mfma<TT, FF>), dim3((unsigned)wgs), dim3(64 * W), lds, stream, \
-                     codes, scales, gscale, x, M, N, K, y)
-  (void)T;
+                     tab, x, M, K)
   if (full) NVFP4_LAUNCH_MFMA(1, true); else NVFP4_LAUNCH_MFMA(1, false);
 #undef NVFP4_LAUNCH_MFMA
   return hipGetLastError();
 }
 
-hipError_t launch_gemv_mfma(const uint8_t* codes, const uint8_t* scales, const float* gscale,
-                            const uint16_t* x, int M, int64_t N, int64_t K, float* y,
+hipError_t launch_gemv_mfma(const SegDesc* d, int n, const uint16_t* x, int M, int64_t K,
                             hipStream_t stream) {
-  if (mfma3_applicable(M, N, K)) return launch_gemv_mfma3(codes, scales, gscale, x, M, N, K, y, stream);
+  if (mfma3_applicable(M, K)) return launch_gemv_mfma3(d, n, x, M, K, stream);
+  int64_t tiles = 0;
+  for (int s = 0; s < n; ++s) tiles += (d[s].N + 15) / 16;
   int T, W;
-  mfma_shape(N, K, &T, &W);
-  return launch_gemv_mfma_shape(codes, scales, gscale, x, M, N, K, y, T, W, stream);
+  mfma_shape(tiles, K, &T, &W);
+  return launch_gemv_mfma_shape(d, n, x, M, K, T, W, stream);
 }
 
 }  // namespace nvfp4

@@ -222,20 +222,26 @@ __device__ __forceinline__ void mfma3_step(const Mfma3<M, S, T, J>& eng, const R
 }
 
 // codes, scales and x are deliberately not __restrict__: read-only noalias
-// arguments would let the compiler treat their memory as invariant and sink
-// the prefetch loads past the ring's ordering points.
+// pointers would let the compiler treat their memory as invariant and sink the
+// prefetch loads past the ring's ordering points.
 template <int M, int S, int T, int J>
-__global__ __launch_bounds__(64 * kMaxWaves3) void k_gemv_mfma3(
-    const uint8_t* codes, const uint8_t* scales, const float* __restrict__ gscale,
-    const uint16_t* x, int64_t N, int64_t K, float* __restrict__ y) {
+__global__ __launch_bounds__(64 * kMaxWaves3) void k_gemv_mfma3(const SegTable tab,
+                                                                const uint16_t* x, int64_t K) {
   using G = Mfma3<M, S, T, J>;
   constexpr int CK = Chunk<J>::kK;
+  // workgroup = one unit of 16T rows of one segment
+  const Seg sg = find_seg(tab, blockIdx.x);
+  const uint8_t* codes = sg.codes;
+  const uint8_t* scales = sg.scales;
+  const float* __restrict__ gscale = sg.gscale;
+  float* __restrict__ y = sg.y;
+  const int64_t N = sg.N;
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int W = blockDim.x >> 6;
   const int i = lane & 15, g = lane >> 4;
-  const int64_t n0 = (int64_t)blockIdx.x * (16 * T);
+  const int64_t n0 = sg.unit * (16 * T);
   const int64_t nch_all = K / CK;
   const int64_t cbeg = nch_all * w / W;
   const int nch = (int)(nch_all * (w + 1) / W - cbeg);
@@ -348,22 +354,23 @@ static size_t mfma3_lds(int M, int W, int S, int T, int J) {
   return (size_t)kZero + (size_t)W * ((size_t)S * M * xrow + (size_t)T * kRed);
 }
 
-bool mfma3_applicable(int M, int64_t N, int64_t K) {
-  return M >= 3 && M <= 8 && N > 0 && K > 0 && (K % kChunkAlign) == 0;
+bool mfma3_applicable(int M, int64_t K) {
+  return M >= 3 && M <= 8 && K > 0 && (K % kChunkAlign) == 0;
 }
 
 // Launch shape (from a sweep of J, T, S and W on the decode-layer and stress
 // shapes): 256-k chunks (a smaller x ring in LDS lets more wavefronts in
 // flight), one tile per wavefront with a ring of 4 (two tiles with a ring of 3
-// once N >= 16384), and W wavefronts per tile so that about 768 run (three
-// per CU), within the chunk count and the LDS budget.
-void mfma3_shape(int M, int64_t N, int64_t K, int* W_out, int* S_out, int* T_out,
+// once there are at least 1024 tiles of 16 rows), and W wavefronts per unit so
+// that about 768 run (three per CU), within the chunk count and the LDS
+// budget. `units16` is the number of 16-row tiles over all segments.
+void mfma3_shape(int M, int64_t units16, int64_t K, int* W_out, int* S_out, int* T_out,
                  int* J_out) {
   const int J = 2;
   const int64_t chunks = K / (128 * J);
-  const int T = N >= 16384 ? 2 : 1;
+  const int T = units16 >= 1024 ? 2 : 1;
   const int S = T == 2 ? 3 : 4;
-  const int64_t units = (N + 16 * T - 1) / (16 * T);
+  const int64_t units = (units16 + T - 1) / T;
   int64_t want = (768 + units - 1) / units;
   if (want > kMaxWaves3) want = kMaxWaves3;
   if (want > chunks) want = chunks;
@@ -375,20 +382,19 @@ void mfma3_shape(int M, int64_t N, int64_t K, int* W_out, int* S_out, int* T_out
   *J_out = J;
 }
 
-hipError_t launch_gemv_mfma3_shape(const uint8_t* codes, const uint8_t* scales,
-                                   const float* gscale, const uint16_t* x, int M, int64_t N,
-                                   int64_t K, float* y, int W, int S, int T, int J,
-                                   hipStream_t stream) {
+hipError_t launch_gemv_mfma3_shape(const SegDesc* d, int n, const uint16_t* x, int M,
+                                   int64_t K, int W, int S, int T, int J, hipStream_t stream) {
   // (S = 4 with T = 2 would not fit the register file)
-  if (!mfma3_applicable(M, N, K) || W < 1 || W > kMaxWaves3 || S < 3 || S > 4 || T < 1 ||
-      T > 2 || (S == 4 && T == 2) || J != 2 ||
+  if (!mfma3_applicable(M, K) || n < 1 || n > kMaxSegments || W < 1 || W > kMaxWaves3 ||
+      S < 3 || S > 4 || T < 1 || T > 2 || (S == 4 && T == 2) || J != 2 ||
       mfma3_lds(M, W, S, T, J) > (size_t)kLdsMax)
     return hipErrorInvalidValue;
   const size_t lds = mfma3_lds(M, W, S, T, J);
-  const unsigned grid = (unsigned)((N + 16 * T - 1) / (16 * T));
+  const SegTable tab = make_seg_table(d, n, 16 * T);
+  const unsigned grid = (unsigned)tab.start[kMaxSegments];
 #define NVFP4_L3(MM, SS, TT, JJ)                                                             \
   hipLaunchKernelGGL((k_gemv_mfma3<MM, SS, TT, JJ>), dim3(grid), dim3(64 * W), lds, stream, \
-                     codes, scales, gscale, x, N, K, y)
+                     tab, x, K)
 #define NVFP4_L3J(MM, SS, TT) NVFP4_L3(MM, SS, TT, 2)
 #define NVFP4_L3M(MM)                              \
   if (S == 4) {                                    \
@@ -412,12 +418,13 @@ hipError_t launch_gemv_mfma3_shape(const uint8_t* codes, const uint8_t* scales,
   return hipGetLastError();
 }
 
-hipError_t launch_gemv_mfma3(const uint8_t* codes, const uint8_t* scales, const float* gscale,
-                             const uint16_t* x, int M, int64_t N, int64_t K, float* y,
+hipError_t launch_gemv_mfma3(const SegDesc* d, int n, const uint16_t* x, int M, int64_t K,
                              hipStream_t stream) {
+  int64_t units16 = 0;
+  for (int s = 0; s < n; ++s) units16 += (d[s].N + 15) / 16;
   int W, S, T, J;
-  mfma3_shape(M, N, K, &W, &S, &T, &J);
-  return launch_gemv_mfma3_shape(codes, scales, gscale, x, M, N, K, y, W, S, T, J, stream);
+  mfma3_shape(M, units16, K, &W, &S, &T, &J);
+  return launch_gemv_mfma3_shape(d, n, x, M, K, W, S, T, J, stream);
 }
 
 }  // namespace nvfp4

@@ -5,6 +5,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include "segments.h"
+
 // Limits of one call (the public header exports the same values).
 #define NVFP4_MAX_M_INTERNAL 8
 #define NVFP4_MAX_TOPK_INTERNAL 16
@@ -22,21 +24,21 @@ hipError_t launch_gemv(const uint8_t* codes, const uint8_t* scales, const float*
                        const uint16_t* x, int M, int64_t N, int64_t K, float* y,
                        hipStream_t stream);
 
-hipError_t launch_gemv_mfma(const uint8_t* codes, const uint8_t* scales, const float* gscale,
-                            const uint16_t* x, int M, int64_t N, int64_t K, float* y,
-                            hipStream_t stream);
+// One launch over n <= kMaxSegments matrices sharing x[M, K] (all N > 0).
+hipError_t launch_gemv_segments(const SegDesc* d, int n, const uint16_t* x, int M, int64_t K,
+                                hipStream_t stream);
 
-// K % 512 == 0 matrix-core path (block scale applied to the MFMA output).
-bool mfma3_applicable(int M, int64_t N, int64_t K);
-void mfma3_shape(int M, int64_t N, int64_t K, int* W_out, int* S_out, int* T_out,
+// Matrix-core paths, 3 <= M <= 8 (gemv_mfma.hip routes K % 512 == 0 to
+// gemv_mfma3.hip).
+hipError_t launch_gemv_mfma(const SegDesc* d, int n, const uint16_t* x, int M, int64_t K,
+                            hipStream_t stream);
+bool mfma3_applicable(int M, int64_t K);
+void mfma3_shape(int M, int64_t units16, int64_t K, int* W_out, int* S_out, int* T_out,
                  int* J_out);
-hipError_t launch_gemv_mfma3(const uint8_t* codes, const uint8_t* scales, const float* gscale,
-                             const uint16_t* x, int M, int64_t N, int64_t K, float* y,
+hipError_t launch_gemv_mfma3(const SegDesc* d, int n, const uint16_t* x, int M, int64_t K,
                              hipStream_t stream);
-hipError_t launch_gemv_mfma3_shape(const uint8_t* codes, const uint8_t* scales,
-                                   const float* gscale, const uint16_t* x, int M, int64_t N,
-                                   int64_t K, float* y, int W, int S, int T, int J,
-                                   hipStream_t stream);
+hipError_t launch_gemv_mfma3_shape(const SegDesc* d, int n, const uint16_t* x, int M,
+                                   int64_t K, int W, int S, int T, int J, hipStream_t stream);
 
 hipError_t launch_fill_zero(float* y, size_t n, hipStream_t stream);
 

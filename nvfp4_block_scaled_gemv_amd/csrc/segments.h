@@ -1,0 +1,83 @@
+// segments.h -- the segment table of a multi-matrix GEMV launch.
+//
+// One launch can cover up to kMaxSegments weight matrices that share the same
+// activations x[M, K] (q|k|v, gate|up): each segment has its own codes,
+// scales, tensor scale, row count and output. The kernels number their work
+// units (a group of rows: R rows of the vector-ALU kernel, a 16-row tile of
+// the matrix-core kernels) across the segments in order; start[s] is the
+// first unit of segment s. The table is passed by value as a kernel argument.
+#pragma once
+
+#include <stdint.h>
+
+namespace nvfp4 {
+
+constexpr int kMaxSegments = 8;
+
+struct SegTable {
+  const uint8_t* codes[kMaxSegments];
+  const uint8_t* scales[kMaxSegments];
+  const float* gscale[kMaxSegments];
+  float* y[kMaxSegments];
+  int64_t N[kMaxSegments];
+  int64_t start[kMaxSegments + 1];   // start[n] = total units
+  int n;
+};
+
+// Host-side description of one segment.
+struct SegDesc {
+  const uint8_t* codes;
+  const uint8_t* scales;
+  const float* gscale;
+  float* y;
+  int64_t N;
+};
+
+// The table for n segments with `rows` rows per work unit.
+inline SegTable make_seg_table(const SegDesc* d, int n, int64_t rows) {
+  SegTable t = {};
+  t.n = n;
+  int64_t u = 0;
+  for (int s = 0; s < n; ++s) {
+    t.codes[s] = d[s].codes;
+    t.scales[s] = d[s].scales;
+    t.gscale[s] = d[s].gscale;
+    t.y[s] = d[s].y;
+    t.N[s] = d[s].N;
+    t.start[s] = u;
+    u += (d[s].N + rows - 1) / rows;
+  }
+  for (int s = n; s <= kMaxSegments; ++s) t.start[s] = u;
+  return t;
+}
+
+#if defined(__HIPCC__) || defined(__HIP__)
+// The segment of work unit u (wavefront-uniform) with its pointers; a scan with
+// constant indices so that the table stays in kernel-argument (scalar) memory.
+struct Seg {
+  const uint8_t* codes;
+  const uint8_t* scales;
+  const float* gscale;
+  float* y;
+  int64_t N;
+  int64_t unit;   // unit index inside the segment
+};
+
+__device__ __forceinline__ Seg find_seg(const SegTable& t, int64_t u) {
+  Seg s = {t.codes[0], t.scales[0], t.gscale[0], t.y[0], t.N[0], u};
+#pragma unroll
+  for (int k = 1; k < kMaxSegments; ++k) {
+    if (k < t.n && u >= t.start[k]) {
+      s.codes = t.codes[k];
+      s.scales = t.scales[k];
+      s.gscale = t.gscale[k];
+      s.y = t.y[k];
+      s.N = t.N[k];
+      s.unit = u - t.start[k];
+    }
+  }
+  return s;
+}
+#endif
+
+}  // namespace nvfp4

@@ -29,7 +29,7 @@ def declared_functions():
 
 def test_exports_every_declared_symbol(L):
     names = declared_functions()
-    assert {"nvfp4_pack", "nvfp4_dequant", "nvfp4_gemv", "nvfp4_moe_gemv",
+    assert {"nvfp4_pack", "nvfp4_dequant", "nvfp4_gemv", "nvfp4_gemv_segments", "nvfp4_moe_gemv",
             "nvfp4_moe_workspace_bytes", "nvfp4_abi_version", "nvfp4_status_string",
             "nvfp4_last_error"} <= set(names)
     for n in names:
@@ -37,7 +37,7 @@ def test_exports_every_declared_symbol(L):
 
 
 def test_version_and_status_strings(L):
-    assert L.nvfp4_abi_version() == 1
+    assert L.nvfp4_abi_version() == 2
     for s in range(8):
         assert L.nvfp4_status_string(s)
     assert L.nvfp4_status_string(99) == b"unknown status"
@@ -109,3 +109,40 @@ def test_binding_raises_without_device_tensors():
     with pytest.raises(ValueError):
         nv.gemv(torch.zeros(4, 16, dtype=torch.uint8), torch.zeros(4, 2, dtype=torch.uint8),
                 torch.ones(1), torch.zeros(1, 32, dtype=torch.bfloat16))
+
+
+def test_gemv_segments_checks(L):
+    """Host-side validation of the fused multi-projection call (no launch)."""
+    Seg = nv.GemvSegment
+    arr = (Seg * 9)()
+    for i in range(9):
+        arr[i] = Seg(A + i * 0x100000, A + 0x10000000 + i * 0x10000, A + 0x20000000 + 16 * i,
+                     B + i * 0x100000, 64)
+    f = L.nvfp4_gemv_segments
+    X = A + 0x30000000
+    assert f(arr, 9, X, 1, 64, None) == ERR_UNSUPPORTED          # > 8 segments
+    assert f(arr, 2, X, 9, 64, None) == ERR_UNSUPPORTED          # M > 8
+    assert f(arr, 2, X, 1, 48, None) == ERR_SHAPE                # K % 32
+    assert f(arr, -1, X, 1, 64, None) == ERR_SHAPE
+    assert f(None, 2, X, 1, 64, None) == ERR_NULL
+    assert f(arr, 0, X, 1, 64, None) == OK                       # nothing to do
+    assert f(arr, 2, X, 0, 64, None) == OK                       # M == 0
+    bad = (Seg * 2)(arr[0], arr[1])
+    bad[1].N = -1
+    assert f(bad, 2, X, 1, 64, None) == ERR_SHAPE
+    bad = (Seg * 2)(arr[0], arr[1])
+    bad[1].y = None
+    assert f(bad, 2, X, 1, 64, None) == ERR_NULL
+    bad = (Seg * 2)(arr[0], arr[1])
+    bad[1].codes = A + 8
+    assert f(bad, 2, X, 1, 64, None) == ERR_ALIGN
+    bad = (Seg * 2)(arr[0], arr[1])
+    bad[1].y = bad[0].y + 16                                    # outputs overlap
+    assert f(bad, 2, X, 1, 64, None) == ERR_ALIAS
+    bad = (Seg * 2)(arr[0], arr[1])
+    bad[1].y = bad[0].codes                                     # output on an input
+    assert f(bad, 2, X, 1, 64, None) == ERR_ALIAS
+    bad = (Seg * 2)(arr[0], arr[1])
+    bad[0].y = X                                                # output on x
+    assert f(bad, 2, X, 1, 64, None) == ERR_ALIAS
+    assert "segment" in L.nvfp4_last_error().decode()
