@@ -27,10 +27,14 @@ __global__ __launch_bounds__(256) void k_gemv(const SegTable tab, const uint16_t
 #pragma unroll
   for (int m = 0; m < M; ++m) xs[m] = x + (int64_t)m * K;
 
+  // A single matrix reads its tensor scale once, before the loop (a load
+  // after the dot products would add its latency to every wavefront's tail),
+  // and skips the segment lookup (it costs registers in this loop).
+  const float g0 = SEG ? 0.0f : *tab.gscale[0];
   for (int64_t u = wave; u < units; u += nwaves) {
-    // a single matrix skips the lookup (it costs registers in this loop)
     const Seg sg = SEG ? find_seg(tab, u)
                        : Seg{tab.codes[0], tab.scales[0], tab.gscale[0], tab.y[0], tab.N[0], u};
+    const float g = SEG ? *sg.gscale : g0;
     const int64_t N = sg.N;
     const int64_t n0 = sg.unit * R;
     int64_t rows[R];
@@ -38,7 +42,6 @@ __global__ __launch_bounds__(256) void k_gemv(const SegTable tab, const uint16_t
     for (int r = 0; r < R; ++r) rows[r] = (n0 + r < N) ? (n0 + r) : (N - 1);
     float acc[R][M];
     wave_row_dots<M, R>(sg.codes, sg.scales, K, rows, xs, M, acc);
-    const float g = *sg.gscale;
     // lane (r * M + m) stores one result
 #pragma unroll
     for (int r = 0; r < R; ++r)
