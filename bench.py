@@ -332,7 +332,7 @@ def leg_copy(torch, steps, warmup):
 
 # ------------------------------------------------------- profile summaries
 
-LM_KERNEL = "nvfp4::k_gemv<1, 4>"
+LM_KERNEL = "nvfp4::k_gemv<1, 4, false>"
 COPY_KERNEL = "MulFunctor<float>"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_k_gemv_lm_head_m1_151936x4096.txt")
 KERNEL_SOURCES = ["gemv.hip", "gemv_core.h", "device.h"]
@@ -380,7 +380,7 @@ def summarize_pmc(fetch_csv, write_csv, cmd, out):
     read_b, write_b = f_k * fr, w_k * fw
     alg = traffic.gemv_bytes(1, 151936, 4096)
     lines = [
-        "# HBM traffic of nvfp4::k_gemv<1, 4>, LM head M=1 N=151936 K=4096",
+        "# HBM traffic of the LM-head GEMV kernel, LM head M=1 N=151936 K=4096",
         "# commands (run from /tmp with TMPDIR=/tmp):",
         *[f"#   {c}" for c in cmd],
         f"kernel_source_sha256_16: {kernel_source_hash()}",
