@@ -33,7 +33,7 @@ __global__ __launch_bounds__(256) void k_gemv(const SegTable tab, const uint16_t
   const float g0 = SEG ? 0.0f : *tab.gscale[0];
   for (int64_t u = wave; u < units; u += nwaves) {
     const Seg sg = SEG ? find_seg(tab, u)
-                       : Seg{tab.codes[0], tab.scales[0], tab.gscale[0], tab.y[0], tab.N[0], u};
+                       : Seg{tab.codes[0], tab.scales[0], tab.gscale[0], tab.y[0], tab.N[0], u, 0};
     const float g = SEG ? *sg.gscale : g0;
     const int64_t N = sg.N;
     const int64_t n0 = sg.unit * R;

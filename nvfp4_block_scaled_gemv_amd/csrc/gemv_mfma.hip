@@ -1,6 +1,6 @@
 // gemv_mfma.hip -- NVFP4 g16 W4A16 GEMV on the CDNA4 matrix cores, for
 // 3 <= M <= 8 activation rows (the instruction has room for 16) and K not a
-// multiple of 512 (those go to gemv_mfma3.hip).
+// multiple of 256 (those go to gemv_splitk.hip).
 //
 // Why MFMA here: at M rows the plain VALU path spends about 0.5 + M/2
 // instructions per weight (one bf16 pair dot per two weights per row), which
@@ -374,7 +374,7 @@ hipError_t launch_gemv_mfma_shape(const SegDesc* d, int n, const uint16_t* x, in
 
 hipError_t launch_gemv_mfma(const SegDesc* d, int n, const uint16_t* x, int M, int64_t K,
                             hipStream_t stream) {
-  if (mfma3_applicable(M, K)) return launch_gemv_mfma3(d, n, x, M, K, stream);
+  if (splitk_applicable(M, K)) return launch_gemv_splitk(d, n, x, M, K, stream);
   int64_t tiles = 0;
   for (int s = 0; s < n; ++s) tiles += (d[s].N + 15) / 16;
   int T, W;

@@ -28,17 +28,16 @@ hipError_t launch_gemv(const uint8_t* codes, const uint8_t* scales, const float*
 hipError_t launch_gemv_segments(const SegDesc* d, int n, const uint16_t* x, int M, int64_t K,
                                 hipStream_t stream);
 
-// Matrix-core paths, 3 <= M <= 8 (gemv_mfma.hip routes K % 512 == 0 to
-// gemv_mfma3.hip).
+// Matrix-core paths, 3 <= M <= 8 (gemv_mfma.hip routes K % 256 == 0 to
+// gemv_splitk.hip).
 hipError_t launch_gemv_mfma(const SegDesc* d, int n, const uint16_t* x, int M, int64_t K,
                             hipStream_t stream);
-bool mfma3_applicable(int M, int64_t K);
-void mfma3_shape(int M, int64_t units16, int64_t K, int* W_out, int* S_out, int* T_out,
-                 int* J_out);
-hipError_t launch_gemv_mfma3(const SegDesc* d, int n, const uint16_t* x, int M, int64_t K,
-                             hipStream_t stream);
-hipError_t launch_gemv_mfma3_shape(const SegDesc* d, int n, const uint16_t* x, int M,
-                                   int64_t K, int W, int S, int T, int J, hipStream_t stream);
+bool splitk_applicable(int M, int64_t K);
+int splitk_default_ks(int64_t K);
+hipError_t launch_gemv_splitk(const SegDesc* d, int n, const uint16_t* x, int M, int64_t K,
+                              hipStream_t stream);
+hipError_t launch_gemv_splitk_shape(const SegDesc* d, int n, const uint16_t* x, int M,
+                                    int64_t K, int KS, int D, int64_t grid, hipStream_t stream);
 
 hipError_t launch_fill_zero(float* y, size_t n, hipStream_t stream);
 

@@ -10,6 +10,12 @@
 
 #include <stdint.h>
 
+#if defined(__HIPCC__) || defined(__HIP__)
+#define NVFP4_HD __host__ __device__
+#else
+#define NVFP4_HD
+#endif
+
 namespace nvfp4 {
 
 constexpr int kMaxSegments = 8;
@@ -51,6 +57,37 @@ inline SegTable make_seg_table(const SegDesc* d, int n, int64_t rows) {
   return t;
 }
 
+// The segment of a unit index that only moves forward (a kernel's running
+// tile): k is the segment and [first, end) its units. The cursor never moves
+// past the last segment, so a unit at or past the total (one past a
+// workgroup's last tile) leaves it on the last segment instead of reading
+// beyond the table. Empty segments are stepped over. Host and device code.
+struct SegCursor {
+  int k;
+  int64_t first, end;
+
+  NVFP4_HD void begin(const SegTable& t, int64_t u) {
+    k = 0;
+    first = 0;
+    end = t.start[1];
+    advance(t, u);
+  }
+  // true when the segment changed
+  NVFP4_HD bool seek(const SegTable& t, int64_t u) {
+    return u < end ? false : advance(t, u);
+  }
+  NVFP4_HD bool advance(const SegTable& t, int64_t u) {
+    bool moved = false;
+    while (u >= end && k + 1 < t.n) {
+      ++k;
+      first = end;
+      end = t.start[k + 1];
+      moved = true;
+    }
+    return moved;
+  }
+};
+
 #if defined(__HIPCC__) || defined(__HIP__)
 // The segment of work unit u (wavefront-uniform) with its pointers; a scan with
 // constant indices so that the table stays in kernel-argument (scalar) memory.
@@ -61,10 +98,11 @@ struct Seg {
   float* y;
   int64_t N;
   int64_t unit;   // unit index inside the segment
+  int index;      // segment number
 };
 
 __device__ __forceinline__ Seg find_seg(const SegTable& t, int64_t u) {
-  Seg s = {t.codes[0], t.scales[0], t.gscale[0], t.y[0], t.N[0], u};
+  Seg s = {t.codes[0], t.scales[0], t.gscale[0], t.y[0], t.N[0], u, 0};
 #pragma unroll
   for (int k = 1; k < kMaxSegments; ++k) {
     if (k < t.n && u >= t.start[k]) {
@@ -74,6 +112,7 @@ __device__ __forceinline__ Seg find_seg(const SegTable& t, int64_t u) {
       s.y = t.y[k];
       s.N = t.N[k];
       s.unit = u - t.start[k];
+      s.index = k;
     }
   }
   return s;

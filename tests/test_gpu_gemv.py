@@ -50,6 +50,26 @@ def test_random_storage_shapes(M, N, K):
     check_tol(y, y_ref, ad, f"M={M} N={N} K={K}")
 
 
+@pytest.mark.parametrize("M", [3, 6, 8])
+@pytest.mark.parametrize("N,K", [(33, 256), (100, 768), (50, 4352), (4800, 8192)])
+def test_split_k_shapes(M, N, K):
+    """The matrix-core kernel's K splits: one wavefront (K = 256), three, one
+    wavefront over 17 slices (a prime slice count) and eight wavefronts of four
+    slices with several tiles per workgroup (4800 rows); the largest compares
+    a sample of rows, first and last included."""
+    say(f"[gemv] split-K M={M} N={N} K={K}")
+    codes, scales = workloads.random_nvfp4(9, M, N * 3 + K, N, K)
+    x = workloads.x_bf16(9, M, N * 3 + K, M, K)
+    g = np.float32(0.031)
+    y = run_gpu(codes, scales, g, x)
+    rows = None
+    if N > 1000:
+        rows = np.unique(np.concatenate([[0, 15, 16, N - 1],
+                                         np.random.default_rng(N).choice(N, 600, replace=False)]))
+    y_ref, ad = oracle.gemv(codes, scales, g, x, rows=rows)
+    check_tol(y if rows is None else y[:, rows], y_ref, ad, f"M={M} N={N} K={K}")
+
+
 @pytest.mark.parametrize("M", [1, 2, 5, 8])
 def test_subnormal_and_max_scales(M):
     N, K = 200, 1024

@@ -1,8 +1,8 @@
-"""The matrix-core GEMV for K % 512 == 0 issues its weight loads through inline
-asm; its compiled gfx950 code must never touch a load's destination registers
+"""The matrix-core GEMV kernels issue their weight loads through inline asm;
+their compiled gfx950 code must never touch a load's destination registers
 before a vmcnt wait has retired that load (a tail that issued loads nobody
 consumed once let the epilogue reuse those registers while the data was still
-in flight). Compiles the kernel with hipcc (no GPU needed) and walks the
+in flight). Compiles the kernels with hipcc (no GPU needed) and walks the
 assembly."""
 import os
 import shutil
@@ -13,7 +13,7 @@ import pytest
 from isa_pending import check_asm, violations
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-SRC = os.path.join(ROOT, "nvfp4_block_scaled_gemv_amd", "csrc", "gemv_mfma3.hip")
+CSRC = os.path.join(ROOT, "nvfp4_block_scaled_gemv_amd", "csrc")
 HIPCC = "/opt/rocm/bin/hipcc"
 
 
@@ -32,15 +32,21 @@ def test_walker_flags_a_touch_before_the_wait():
 
 
 @pytest.mark.skipif(not os.path.exists(HIPCC), reason="hipcc not installed")
-def test_mfma3_kernels_leave_pending_loads_alone(tmp_path):
-    out = tmp_path / "mfma3.s"
+def test_splitk_kernels_leave_pending_loads_alone(tmp_path):
+    out = tmp_path / "splitk.s"
     cmd = [HIPCC, "--offload-arch=gfx950", "-O3", "-std=c++17", "-ffp-contract=off",
            "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
            "-I", os.path.join(ROOT, "include"), "--cuda-device-only", "-S",
-           "-o", str(out), SRC]
+           "-o", str(out), os.path.join(CSRC, "gemv_splitk.hip")]
     subprocess.run(cmd, check=True, capture_output=True, timeout=600)
-    res = check_asm(out.read_text(), r"_Z\S*k_gemv_mfma3\S*")
-    # M = 3..8 x (S=3,T=1), (S=3,T=2), (S=4,T=1), chunks of 2 steps
+    text = out.read_text()
+    res = check_asm(text, r"_Z\S*k_gemv_splitk\S*")
+    # M = 3..8 x (x held with a ring of 3, x streamed with rings of 3 and 4)
     assert len(res) == 18, sorted(res)
     bad = {k: v[:3] for k, v in res.items() if v}
     assert not bad, bad
+    # the loads are really there and waited for by count, not drained
+    assert text.count("global_load_dwordx4") >= 18 * 11
+    assert "vmcnt(3)" in text and "vmcnt(11)" in text
+    # no spills: a spilled ring register would be stored while its load is pending
+    assert "scratch_" not in text
