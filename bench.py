@@ -451,6 +451,49 @@ def summarize_stats(stats_csv, cmd, out, top=16):
     print("\n".join(lines))
 
 
+def summarize_counters(csvs, cmd, out, match="nvfp4::"):
+    """Per-kernel means of every counter in rocprofv3 --pmc CSVs (one per
+    pass), for kernels whose name contains `match`. FETCH_SIZE is also given
+    in bytes, scaled by what it reads for the copy kernel of known size when
+    that kernel is in the same CSV, and divided by TCP_TCC_READ_REQ_sum where
+    both were collected (HBM bytes per L1-to-L2 read request)."""
+    import csv
+    fetch_scale = None
+    for path in csvs:
+        means = _pmc_means(path, "FETCH_SIZE")
+        if any(COPY_KERNEL in k for k in means):
+            fetch_scale = (512 << 20) / _pick(means, COPY_KERNEL)[0]
+    vals = {}
+    for path in csvs:
+        with open(path, newline="") as f:
+            for r in csv.DictReader(f):
+                name = r["Kernel_Name"]
+                if match not in name:
+                    continue
+                short = name.split("(")[0].replace("void ", "")
+                vals.setdefault(short, {}).setdefault(r["Counter_Name"], []).append(
+                    float(r["Counter_Value"]))
+    lines = ["# rocprofv3 --pmc counter means per dispatch (one pass per command)",
+             "# commands (run from /tmp with TMPDIR=/tmp):", *[f"#   {c}" for c in cmd],
+             f"# FETCH_SIZE calibration: {fetch_scale:.2f} bytes per unit (copy kernel)"
+             if fetch_scale else "# FETCH_SIZE calibration: no copy kernel in the CSVs"]
+    for kern in sorted(vals):
+        c = {k: float(np.mean(v)) for k, v in vals[kern].items()}
+        n = min(len(v) for v in vals[kern].values())
+        lines.append(f"kernel {kern}  ({n}+ dispatches)")
+        for k in sorted(c):
+            lines.append(f"  {k:40s} {c[k]:14.6g}")
+        if "FETCH_SIZE" in c and fetch_scale:
+            fb = c["FETCH_SIZE"] * fetch_scale
+            lines.append(f"  {'HBM bytes read (calibrated FETCH_SIZE)':40s} {fb:14.6g}")
+            if c.get("TCP_TCC_READ_REQ_sum"):
+                lines.append(f"  {'HBM bytes per L1->L2 read request':40s} "
+                             f"{fb / c['TCP_TCC_READ_REQ_sum']:14.1f}")
+    with open(out, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
 # ------------------------------------------------------------------- main
 
 def main():
@@ -467,6 +510,9 @@ def main():
                     help="write the traffic summary from two rocprofv3 --pmc passes")
     ap.add_argument("--summarize-stats", nargs=2, metavar=("STATS_CSV", "OUT"),
                     help="write a short table from a rocprofv3 --stats kernel summary")
+    ap.add_argument("--summarize-counters", nargs="+", metavar="CSV_THEN_OUT",
+                    help="write per-kernel counter means from rocprofv3 --pmc CSVs "
+                         "(last argument: the output file)")
     ap.add_argument("--cmd", action="append", default=[],
                     help="command line(s) that produced the profile, for the summary header")
     args = ap.parse_args()
@@ -475,6 +521,11 @@ def main():
         return
     if args.summarize_stats:
         summarize_stats(args.summarize_stats[0], args.cmd, args.summarize_stats[1])
+        return
+    if args.summarize_counters:
+        if len(args.summarize_counters) < 2:
+            ap.error("--summarize-counters needs at least one CSV and the output file")
+        summarize_counters(args.summarize_counters[:-1], args.cmd, args.summarize_counters[-1])
         return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:

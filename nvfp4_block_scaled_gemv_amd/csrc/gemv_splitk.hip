@@ -70,8 +70,9 @@ typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 
 constexpr int kSliceK = 256;
-constexpr int kSkWavesStationary = 16;   // KS = 1: x held for the whole kernel
-constexpr int kSkWavesStreamed = 8;      // KS > 1: x loaded with every slice
+// wavefronts per workgroup at most: x held in registers for one slice (128
+// registers per lane), for two slices, or streamed with every slice
+constexpr int sk_max_waves(int XS) { return XS == 1 ? 16 : 8; }
 constexpr int kSkCUs = 256;
 
 // s_waitcnt immediate (gfx9 encoding: vmcnt bits 3..0 and 15..14, expcnt
@@ -110,14 +111,15 @@ __device__ __forceinline__ f32x4_t sk_add_upper_half(f32x4_t v) {
   return r;
 }
 
-// One ring stage: the codes of the two row-major loads of a slice, the
-// lane's two scale dwords of the slice and, when x is streamed, the slice's A
-// operands.
-template <bool WX>
+// One ring stage (an item): per slice the codes of the two row-major loads
+// and the lane's two scale dwords; when x is streamed (XS = 0, one slice per
+// item), also the slice's A operands.
+template <int XS>
 struct SkStage {
-  u32x4_t q[2];
-  u32x2_t s;
-  u32x4_t a[WX ? 8 : 1];
+  static constexpr int kSl = XS == 0 ? 1 : XS;   // slices per item
+  u32x4_t q[kSl][2];
+  u32x2_t s[kSl];
+  u32x4_t a[XS == 0 ? 8 : 1];
 };
 
 // Codes of one slice (two loads, rows 8t + l / 8 at byte 16 (l % 8) of the
@@ -214,7 +216,7 @@ struct SkCursor {
 };
 
 // Per-wavefront state of the weight stream.
-template <bool WX>
+template <int XS>
 struct SkEngine {
   int64_t K;
   int64_t kw;                 // wavefront's first k
@@ -222,19 +224,23 @@ struct SkEngine {
   int64_t xstride;            // bytes per slice (0 for all-zero lanes)
   int i, g, lane;
 
+  // item (tile, slice sl) when x is streamed; (tile, all XS slices) else
   __device__ __forceinline__ void issue(const SkCursor& cs, int64_t tile, int sl,
-                                        SkStage<WX>& st) const {
+                                        SkStage<XS>& st) const {
     const int64_t r0 = (tile - cs.first()) * 16;
     const int64_t n = r0 + i;              // scale row of lane (i, g)
     const int64_t a = r0 + (lane >> 3);    // code rows of the two loads
     const int64_t row = n < cs.N ? n : cs.N - 1;
     const int64_t row0 = a < cs.N ? a : cs.N - 1;
     const int64_t row1 = a + 8 < cs.N ? a + 8 : cs.N - 1;
-    const int64_t k0 = kw + (int64_t)sl * kSliceK;
-    const uint8_t* cb = cs.codes + (k0 >> 1) + 16 * (lane & 7);
-    sk_load_weights(cb + row0 * (K >> 1), cb + row1 * (K >> 1),
-                    cs.scales + row * (K >> 4) + (k0 >> 4) + 8 * (g >> 1), st.q, st.s);
-    if constexpr (WX) sk_load_x(xl + sl * xstride, st.a);
+#pragma unroll
+    for (int u = 0; u < SkStage<XS>::kSl; ++u) {
+      const int64_t k0 = kw + (int64_t)(sl + u) * kSliceK;
+      const uint8_t* cb = cs.codes + (k0 >> 1) + 16 * (lane & 7);
+      sk_load_weights(cb + row0 * (K >> 1), cb + row1 * (K >> 1),
+                      cs.scales + row * (K >> 4) + (k0 >> 4) + 8 * (g >> 1), st.q[u], st.s[u]);
+    }
+    if constexpr (XS == 0) sk_load_x(xl + sl * xstride, st.a);
   }
 };
 
@@ -332,11 +338,13 @@ __device__ __forceinline__ void sk_finish(const SkCursor& cs, int64_t tile, int 
 // codes, scales and x are deliberately not __restrict__: read-only noalias
 // pointers would let the compiler treat their memory as invariant and move
 // the ring's loads across its ordering points.
-template <int M, bool WX, int D>
-__global__ __launch_bounds__(64 * (WX ? kSkWavesStreamed : kSkWavesStationary)) void
+template <int M, int XS, int D>
+__global__ __launch_bounds__(64 * sk_max_waves(XS)) void
 k_gemv_splitk(const SegTable tab, const uint16_t* x, int64_t K, int KS) {
-  constexpr int kIssue = 3 + (WX ? 8 : 0);   // vector-memory instructions per item
-  static_assert(D >= 3 && (D - 2) * kIssue <= 63, "vmcnt is a 6-bit counter");
+  constexpr bool WX = XS == 0;
+  constexpr int kSl = SkStage<XS>::kSl;
+  constexpr int kIssue = 3 * kSl + (WX ? 8 : 0);   // vector-memory instructions per item
+  static_assert(D >= 3 && D <= 5 && (D - 2) * kIssue <= 63, "vmcnt is a 6-bit counter");
   extern __shared__ __attribute__((aligned(16))) f32x4_t lds[];
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -346,8 +354,9 @@ k_gemv_splitk(const SegTable tab, const uint16_t* x, int64_t K, int KS) {
   const int64_t t0 = tiles * blockIdx.x / gridDim.x;
   const int nt = (int)(tiles * (blockIdx.x + 1) / gridDim.x - t0);
   if (nt <= 0) return;   // the same for the whole workgroup
-  const int ks = WX ? KS : 1;
-  const int n = nt * ks;   // items (tile, slice) of every wavefront
+  const int ks = WX ? KS : XS;   // slices per wavefront
+  const int ipt = WX ? KS : 1;   // items per tile
+  const int n = nt * ipt;        // items of every wavefront
 
   SkShared sh;
   sh.part = lds;
@@ -357,7 +366,7 @@ k_gemv_splitk(const SegTable tab, const uint16_t* x, int64_t K, int KS) {
   if (threadIdx.x < 2 * kSlots) sh.cnt[threadIdx.x] = 0u;
   __syncthreads();   // before any load of the ring is in flight
 
-  SkEngine<WX> eng;
+  SkEngine<XS> eng;
   eng.K = K;
   eng.kw = (int64_t)w * ks * kSliceK;
   eng.i = i;
@@ -381,19 +390,22 @@ k_gemv_splitk(const SegTable tab, const uint16_t* x, int64_t K, int KS) {
       reinterpret_cast<const u32x4_t*>(stage + kStagePitch * i + 16 * (g & 1) + 64 * (g >> 1));
 
   // stationary x operands (issued first: the first step's wait covers them)
-  u32x4_t xa[WX ? 1 : 8];
-  if constexpr (!WX) sk_load_x(eng.xl, xa);
+  u32x4_t xa[WX ? 1 : XS][8];
+  if constexpr (!WX) {
+#pragma unroll
+    for (int u = 0; u < XS; ++u) sk_load_x(eng.xl + u * eng.xstride, xa[u]);
+  }
 
-  SkStage<WX> R0, R1, R2, R3;
+  SkStage<XS> R0, R1, R2, R3, R4;
   SkCursor ci, cf;   // segments of the next tile to issue and to finish
   ci.begin(tab, t0);
   cf = ci;
   cf.load_gs();
   int64_t itile = t0;   // next item to issue: (itile, isl)
   int isl = 0;
-  auto issue_next = [&](SkStage<WX>& st) {
+  auto issue_next = [&](SkStage<XS>& st) {
     eng.issue(ci, itile, isl, st);
-    if (++isl == ks) {
+    if (++isl == ipt) {
       isl = 0;
       if (++itile < t0 + nt) ci.seek(tab, itile);
     }
@@ -401,7 +413,8 @@ k_gemv_splitk(const SegTable tab, const uint16_t* x, int64_t K, int KS) {
   // prologue: items 0 .. min(D - 1, n) - 1
   issue_next(R0);
   if (1 < n) issue_next(R1);
-  if (D == 4 && 2 < n) issue_next(R2);
+  if (D >= 4 && 2 < n) issue_next(R2);
+  if (D >= 5 && 3 < n) issue_next(R3);
   asm volatile("" ::: "memory");
 
   f32x4_t acc = f32x4_t{0.f, 0.f, 0.f, 0.f};
@@ -410,8 +423,8 @@ k_gemv_splitk(const SegTable tab, const uint16_t* x, int64_t K, int KS) {
   // One ring step for item c held in `cur`: wait until it has landed (items
   // c + 1 .. c + D - 2 may stay in flight), issue item c + D - 1 into `nxt`
   // (the stage item c - 1 used), multiply item c, and finish the tile after
-  // its last slice.
-  auto step = [&](const SkStage<WX>& cur, SkStage<WX>& nxt, int c) {
+  // its last item.
+  auto step = [&](const SkStage<XS>& cur, SkStage<XS>& nxt, int c) {
     if (c + D - 2 < n)
       __builtin_amdgcn_s_waitcnt(sk_vmcnt((D - 2) * kIssue));
     else
@@ -420,26 +433,29 @@ k_gemv_splitk(const SegTable tab, const uint16_t* x, int64_t K, int KS) {
     if (c + D - 1 < n) issue_next(nxt);
     asm volatile("" ::: "memory");
     __builtin_amdgcn_sched_barrier(0);
-    // a tile's last slice: read its slot's release count now, so that the
+    // a tile's last item: read its slot's release count now, so that the
     // check after the math finds it in a register
-    const bool last = csl + 1 == ks;
+    const bool last = csl + 1 == ipt;
     uint32_t done_seen = 0xFFFFFFFFu;
     if (last)
       done_seen = __hip_atomic_load(&sh.done[(int)(ctile - t0) % kSlots], __ATOMIC_RELAXED,
                                     __HIP_MEMORY_SCOPE_WORKGROUP);
-    // the transpose: the buffer's previous reads were waited for by the
-    // compiler before their results were used, and LDS keeps one wavefront's
-    // accesses in order
-    *st_w0 = cur.q[0];
-    *st_w1 = cur.q[1];
-    const u32x4_t qt[2] = {st_r[0], st_r[2]};
-    if constexpr (WX)
-      sk_compute(qt, cur.s, cur.a, acc);
-    else
-      sk_compute(qt, cur.s, xa, acc);
-    if (++csl == ks) {
-      sk_finish<M, WX ? kSkWavesStreamed : kSkWavesStationary>(cf, ctile, (int)(ctile - t0), acc,
-                                                               done_seen, sh, w, W, lane);
+#pragma unroll
+    for (int u = 0; u < kSl; ++u) {
+      // the transpose: the buffer's previous reads were waited for by the
+      // compiler before their results were used, and LDS keeps one
+      // wavefront's accesses in order
+      *st_w0 = cur.q[u][0];
+      *st_w1 = cur.q[u][1];
+      const u32x4_t qt[2] = {st_r[0], st_r[2]};
+      if constexpr (WX)
+        sk_compute(qt, cur.s[u], cur.a, acc);
+      else
+        sk_compute(qt, cur.s[u], xa[u], acc);
+    }
+    if (++csl == ipt) {
+      sk_finish<M, sk_max_waves(XS)>(cf, ctile, (int)(ctile - t0), acc, done_seen, sh, w, W,
+                                     lane);
       csl = 0;
       if (++ctile < t0 + nt && cf.seek(tab, ctile)) cf.load_gs();
     }
@@ -453,7 +469,7 @@ k_gemv_splitk(const SegTable tab, const uint16_t* x, int64_t K, int KS) {
       step(R2, R1, c);
       if (++c >= n) break;
     }
-  } else {
+  } else if constexpr (D == 4) {
     for (int c = 0;;) {
       step(R0, R3, c);
       if (++c >= n) break;
@@ -464,6 +480,19 @@ k_gemv_splitk(const SegTable tab, const uint16_t* x, int64_t K, int KS) {
       step(R3, R2, c);
       if (++c >= n) break;
     }
+  } else {
+    for (int c = 0;;) {
+      step(R0, R4, c);
+      if (++c >= n) break;
+      step(R1, R0, c);
+      if (++c >= n) break;
+      step(R2, R1, c);
+      if (++c >= n) break;
+      step(R3, R2, c);
+      if (++c >= n) break;
+      step(R4, R3, c);
+      if (++c >= n) break;
+    }
   }
 }
 
@@ -471,45 +500,59 @@ bool splitk_applicable(int M, int64_t K) {
   return M >= 3 && M <= 8 && K > 0 && (K % kSliceK) == 0;
 }
 
-// KS slices of 256 k per wavefront: one (x held in registers) while K fits
-// 16 wavefronts, else the smallest divisor of the slice count that fits 8.
-int splitk_default_ks(int64_t K) {
+// Default launch shape (from sweeps of the decode-layer, stress and LM-head
+// shapes): two x slices held per wavefront with a ring of 4 while the slice
+// count is even and fits 8 wavefronts (K = 512 .. 4096), one held slice with a
+// ring of 3 while it fits 16, else x streamed with KS slices per wavefront, KS
+// the smallest divisor of the slice count that fits 8 wavefronts.
+void splitk_default_shape(int64_t K, int* KS, int* XS, int* D) {
   const int64_t S = K / kSliceK;
-  if (S <= kSkWavesStationary) return 1;
-  for (int64_t ks = (S + kSkWavesStreamed - 1) / kSkWavesStreamed; ks < S; ++ks)
-    if (S % ks == 0) return (int)ks;
-  return (int)S;
+  if (S % 2 == 0 && S / 2 <= sk_max_waves(2)) {
+    *KS = 2, *XS = 2, *D = 4;
+  } else if (S <= sk_max_waves(1)) {
+    *KS = 1, *XS = 1, *D = 3;
+  } else {
+    int64_t ks = (S + sk_max_waves(0) - 1) / sk_max_waves(0);
+    while (S % ks) ++ks;
+    *KS = (int)ks, *XS = 0, *D = 3;
+  }
 }
 
-// Launch with KS slices per wavefront, D ring stages and `grid` workgroups
-// (0: as many as fill the chip once).
+// Launch with KS slices per wavefront (x held in registers for XS = KS = 1
+// or 2 slices; XS = 0 streams x), D ring stages and `grid` workgroups (0: as
+// many as fill the chip once).
 hipError_t launch_gemv_splitk_shape(const SegDesc* d, int n, const uint16_t* x, int M,
-                                    int64_t K, int KS, int D, int64_t grid, hipStream_t stream) {
-  // (a ring of 4 with x held in registers does not fit the 128 registers of a
-  // 16-wavefront workgroup)
-  if (!splitk_applicable(M, K) || n < 1 || n > kMaxSegments || KS < 1 || (D != 3 && D != 4) ||
-      (KS == 1 && D != 3))
+                                    int64_t K, int KS, int XS, int D, int64_t grid,
+                                    hipStream_t stream) {
+  // shapes that are built: one held slice with a ring of 3 (a ring of 4 does
+  // not fit the 128 registers of a 16-wavefront workgroup), two held slices
+  // with a ring of 4 (5 spills), streamed x with rings of 3 and 4
+  const bool built = (XS == 1 && D == 3) || (XS == 2 && D == 4) ||
+                     (XS == 0 && (D == 3 || D == 4));
+  if (!splitk_applicable(M, K) || n < 1 || n > kMaxSegments || KS < 1 || !built ||
+      (XS != 0 && KS != XS))
     return hipErrorInvalidValue;
   const int64_t S = K / kSliceK;
   if (S % KS) return hipErrorInvalidValue;
   const int W = (int)(S / KS);
-  const bool wx = KS > 1;
-  if (W > (wx ? kSkWavesStreamed : kSkWavesStationary)) return hipErrorInvalidValue;
+  if (W > sk_max_waves(XS)) return hipErrorInvalidValue;
   const SegTable tab = make_seg_table(d, n, 16);
   const int64_t tiles = tab.start[kMaxSegments];
-  if (grid <= 0) grid = (int64_t)kSkCUs * ((wx ? kSkWavesStreamed : kSkWavesStationary) / W);
+  if (grid <= 0) grid = (int64_t)kSkCUs * (sk_max_waves(XS) == 16 ? 16 / W : 8 / W);
   if (grid > tiles) grid = tiles;
   if (grid > (1 << 20)) return hipErrorInvalidValue;
   const size_t lds = splitk_lds(W);
-#define NVFP4_SK(MM, WXX, DD)                                                              \
-  hipLaunchKernelGGL((k_gemv_splitk<MM, WXX, DD>), dim3((unsigned)grid), dim3(64 * W), lds, \
+#define NVFP4_SK(MM, XX, DD)                                                              \
+  hipLaunchKernelGGL((k_gemv_splitk<MM, XX, DD>), dim3((unsigned)grid), dim3(64 * W), lds, \
                      stream, tab, x, K, KS)
-#define NVFP4_SKM(MM)                  \
-  if (wx) {                            \
-    if (D == 3) NVFP4_SK(MM, true, 3); \
-    else NVFP4_SK(MM, true, 4);        \
-  } else {                             \
-    NVFP4_SK(MM, false, 3);            \
+#define NVFP4_SKM(MM)                    \
+  if (XS == 1) {                         \
+    NVFP4_SK(MM, 1, 3);                  \
+  } else if (XS == 2) {                  \
+    NVFP4_SK(MM, 2, 4);                  \
+  } else {                               \
+    if (D == 3) NVFP4_SK(MM, 0, 3);      \
+    else NVFP4_SK(MM, 0, 4);             \
   }
   switch (M) {
     case 3: NVFP4_SKM(3); break;
@@ -526,8 +569,9 @@ hipError_t launch_gemv_splitk_shape(const SegDesc* d, int n, const uint16_t* x, 
 
 hipError_t launch_gemv_splitk(const SegDesc* d, int n, const uint16_t* x, int M, int64_t K,
                               hipStream_t stream) {
-  const int KS = splitk_default_ks(K);
-  return launch_gemv_splitk_shape(d, n, x, M, K, KS, 3, 0, stream);
+  int KS, XS, D;
+  splitk_default_shape(K, &KS, &XS, &D);
+  return launch_gemv_splitk_shape(d, n, x, M, K, KS, XS, D, 0, stream);
 }
 
 }  // namespace nvfp4

@@ -33,11 +33,12 @@ hipError_t launch_gemv_segments(const SegDesc* d, int n, const uint16_t* x, int 
 hipError_t launch_gemv_mfma(const SegDesc* d, int n, const uint16_t* x, int M, int64_t K,
                             hipStream_t stream);
 bool splitk_applicable(int M, int64_t K);
-int splitk_default_ks(int64_t K);
+void splitk_default_shape(int64_t K, int* KS, int* XS, int* D);
 hipError_t launch_gemv_splitk(const SegDesc* d, int n, const uint16_t* x, int M, int64_t K,
                               hipStream_t stream);
 hipError_t launch_gemv_splitk_shape(const SegDesc* d, int n, const uint16_t* x, int M,
-                                    int64_t K, int KS, int D, int64_t grid, hipStream_t stream);
+                                    int64_t K, int KS, int XS, int D, int64_t grid,
+                                    hipStream_t stream);
 
 hipError_t launch_fill_zero(float* y, size_t n, hipStream_t stream);
 
