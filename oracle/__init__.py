@@ -55,6 +55,11 @@ def lib():
         L.oracle_moe.argtypes = [_u8p, _u8p, _f32p, _u8p, _u8p, _f32p, _u16p,
                                  _i32p, _f32p, _i64, _i64, _i64, _i64, _i64,
                                  _f64p, _f64p, _u16p]
+        L.oracle_moe_shared.restype = ctypes.c_int
+        L.oracle_moe_shared.argtypes = [_u8p, _u8p, _f32p, _u8p, _u8p, _f32p, _u16p,
+                                        _i32p, _f32p, _i64, _i64, _i64, _i64, _i64,
+                                        _u8p, _u8p, _f32p, _u8p, _u8p, _f32p, _i64,
+                                        _f64p, _f64p, _u16p, _u16p]
         _lib = L
     return _lib
 
@@ -185,3 +190,51 @@ def moe(w13_codes, w13_scales, w13_g, w2_codes, w2_scales, w2_g, x_bits,
                           _ptr(h, _u16p) if h is not None else None)
     _check(rc, "moe")
     return (y, bound, h) if want_h else (y, bound)
+
+
+def moe_shared(w13_codes, w13_scales, w13_g, w2_codes, w2_scales, w2_g, x_bits,
+               ids, gate_w, shared, want_h=False):
+    """MoE with a shared expert: y, bound (fp64 [M, H]) and optionally the h
+    bits (uint16 [M*topk, I]) and hs bits (uint16 [M, Is]). `shared` is
+    (codes13 [2Is, H/2], scales13 [2Is, H/16], g13, codes2 [H, Is/2],
+    scales2 [H, Is/16], g2) with g13, g2 scalars."""
+    w13_codes = _c(w13_codes, np.uint8)
+    w13_scales = _c(w13_scales, np.uint8)
+    w2_codes = _c(w2_codes, np.uint8)
+    w2_scales = _c(w2_scales, np.uint8)
+    w13_g = _c(w13_g, np.float32)
+    w2_g = _c(w2_g, np.float32)
+    x_bits = _c(x_bits, np.uint16)
+    ids = _c(ids, np.int32)
+    gate_w = _c(gate_w, np.float32)
+    sc13, ss13, sg13, sc2, ss2, sg2 = shared
+    sc13 = _c(sc13, np.uint8)
+    ss13 = _c(ss13, np.uint8)
+    sc2 = _c(sc2, np.uint8)
+    ss2 = _c(ss2, np.uint8)
+    sg13 = _c(np.asarray(sg13, np.float32).reshape(1), np.float32)
+    sg2 = _c(np.asarray(sg2, np.float32).reshape(1), np.float32)
+    E, twoI, Hh = w13_codes.shape
+    H = Hh * 2
+    I = twoI // 2
+    M, topk = ids.shape
+    Is = sc13.shape[0] // 2
+    if (w2_codes.shape != (E, H, I // 2) or x_bits.shape != (M, H)
+            or sc13.shape != (2 * Is, H // 2) or sc2.shape != (H, Is // 2)):
+        raise ValueError("inconsistent MoE shapes")
+    y = np.empty((M, H), np.float64)
+    bound = np.empty((M, H), np.float64)
+    h = np.empty((M * topk, I), np.uint16) if want_h else None
+    hs = np.empty((M, Is), np.uint16) if want_h else None
+    rc = lib().oracle_moe_shared(_ptr(w13_codes, _u8p), _ptr(w13_scales, _u8p),
+                                 _ptr(w13_g, _f32p), _ptr(w2_codes, _u8p),
+                                 _ptr(w2_scales, _u8p), _ptr(w2_g, _f32p),
+                                 _ptr(x_bits, _u16p), _ptr(ids, _i32p),
+                                 _ptr(gate_w, _f32p), M, E, H, I, topk,
+                                 _ptr(sc13, _u8p), _ptr(ss13, _u8p), _ptr(sg13, _f32p),
+                                 _ptr(sc2, _u8p), _ptr(ss2, _u8p), _ptr(sg2, _f32p), Is,
+                                 _ptr(y, _f64p), _ptr(bound, _f64p),
+                                 _ptr(h, _u16p) if h is not None else None,
+                                 _ptr(hs, _u16p) if hs is not None else None)
+    _check(rc, "moe_shared")
+    return (y, bound, h, hs) if want_h else (y, bound)

@@ -20,6 +20,10 @@
  *    "l3.moe.experts_act" (silu_mul, bf16 out), "l3.moe.experts_down",
  *    "l3.moe.blend" (combine by gate weight, f32); llama.cpp SWIGLU op
  *    (ggml trace page, ffn_swiglu rows) = silu(gate) * up.
+ *  - Shared expert: graph.json nodes "l3.moe.shared_gate_up",
+ *    "l3.moe.shared_act", "l3.moe.shared_down"; card.json performance[4]
+ *    and [9] (gate|up N = 768 + 768, down K = 768); "l3.moe.blend" adds it to
+ *    the routed slots ("routed slots + shared in").
  *
  * Build: gcc -O2 -ffp-contract=off (no -ffast-math), optionally -fopenmp.
  * fp32 expressions below are evaluated in fp32 (SSE, FLT_EVAL_METHOD 0).
@@ -316,6 +320,63 @@ int oracle_moe(const uint8_t* w13_codes, const uint8_t* w13_scales, const float*
     free(xv);
     free(a);
     free(h);
+  }
+  return ORACLE_OK;
+}
+
+/* One dense SwiGLU FFN (gate|up rows, bf16 activations, down) for one token,
+   added to y and bound: the shared expert of oracle_moe_shared. */
+static void shared_ffn_add(const uint8_t* c13, const uint8_t* s13, double g13,
+                           const uint8_t* c2, const uint8_t* s2, double g2,
+                           const double* xv, int64_t H, int64_t Is,
+                           double* y, double* bound, uint16_t* hs_out) {
+  double* a = (double*)malloc((size_t)(2 * Is) * sizeof(double));
+  double* h = (double*)malloc((size_t)Is * sizeof(double));
+  int64_t r, n;
+#pragma omp parallel for schedule(static)
+  for (r = 0; r < 2 * Is; ++r) {
+    double d;
+    row_dot(c13, s13, H, r, xv, &d, NULL);
+    a[r] = g13 * d;
+  }
+  for (r = 0; r < Is; ++r) {
+    double G = a[r], U = a[Is + r];
+    uint16_t hb = oracle_bf16_from_double(G / (1.0 + exp(-G)) * U);
+    h[r] = bf16_value(hb);
+    if (hs_out) hs_out[r] = hb;
+  }
+#pragma omp parallel for schedule(static)
+  for (n = 0; n < H; ++n) {
+    double d, ad;
+    row_dot(c2, s2, Is, n, h, &d, &ad);
+    y[n] += 1.0 * (g2 * d);
+    if (bound) bound[n] += fabs(g2) * ad;
+  }
+  free(a);
+  free(h);
+}
+
+int oracle_moe_shared(const uint8_t* w13_codes, const uint8_t* w13_scales, const float* w13_g,
+                      const uint8_t* w2_codes, const uint8_t* w2_scales, const float* w2_g,
+                      const uint16_t* x, const int32_t* ids, const float* gate_w,
+                      int64_t M, int64_t E, int64_t H, int64_t I, int64_t topk,
+                      const uint8_t* ws13_codes, const uint8_t* ws13_scales, const float* ws13_g,
+                      const uint8_t* ws2_codes, const uint8_t* ws2_scales, const float* ws2_g,
+                      int64_t Is, double* y, double* bound, uint16_t* h_out, uint16_t* hs_out) {
+  int64_t m, k;
+  int rc;
+  if (Is < 0 || (Is % 16) != 0) return ORACLE_ERR_SHAPE;
+  /* the routed slots first (blend order: routed, then shared) */
+  rc = oracle_moe(w13_codes, w13_scales, w13_g, w2_codes, w2_scales, w2_g, x, ids, gate_w,
+                  M, E, H, I, topk, y, bound, h_out);
+  if (rc != ORACLE_OK) return rc;
+  for (m = 0; m < M; ++m) {
+    double* xv = (double*)malloc((size_t)H * sizeof(double));
+    for (k = 0; k < H; ++k) xv[k] = bf16_value(x[m * H + k]);
+    shared_ffn_add(ws13_codes, ws13_scales, (double)ws13_g[0], ws2_codes, ws2_scales,
+                   (double)ws2_g[0], xv, H, Is, y + m * H, bound ? bound + m * H : NULL,
+                   hs_out ? hs_out + m * Is : NULL);
+    free(xv);
   }
   return ORACLE_OK;
 }

@@ -88,6 +88,25 @@ int oracle_moe(const uint8_t* w13_codes, const uint8_t* w13_scales, const float*
                int64_t M, int64_t E, int64_t H, int64_t I, int64_t topk,
                double* y, double* bound, uint16_t* h_out);
 
+/* MoE with a shared expert (graph.json nodes "l3.moe.shared_gate_up",
+   "l3.moe.shared_act", "l3.moe.shared_down" and "l3.moe.blend", which takes
+   the routed slots and the shared output): y is oracle_moe's y plus, for every
+   token m,
+     a   = gs13 * WS13 . x[m]                     (2 Is values)
+     hs  = bf16( silu(a[0:Is]) * a[Is:2Is] )
+     y[m] += gs2 * WS2 . hs
+   added after the routed slots, with weight 1; bound grows by
+   |gs2| * sum |WS2 * hs|. hs_out (may be NULL): [M, Is] bf16 bits of hs.
+   Shared weights: codes [2 Is, H/2], scales [2 Is, H/16], gs13 [1];
+                   codes [H, Is/2],  scales [H, Is/16],  gs2 [1]. */
+int oracle_moe_shared(const uint8_t* w13_codes, const uint8_t* w13_scales, const float* w13_g,
+                      const uint8_t* w2_codes, const uint8_t* w2_scales, const float* w2_g,
+                      const uint16_t* x, const int32_t* ids, const float* gate_w,
+                      int64_t M, int64_t E, int64_t H, int64_t I, int64_t topk,
+                      const uint8_t* ws13_codes, const uint8_t* ws13_scales, const float* ws13_g,
+                      const uint8_t* ws2_codes, const uint8_t* ws2_scales, const float* ws2_g,
+                      int64_t Is, double* y, double* bound, uint16_t* h_out, uint16_t* hs_out);
+
 /* Round a double to the nearest bf16 (ties to even), returning its bits. */
 uint16_t oracle_bf16_from_double(double v);
 

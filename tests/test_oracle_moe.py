@@ -1,5 +1,7 @@
 """Pins for the oracle's MoE expert-slot path (CPU only): reduction to the
-GEMV oracle plus SwiGLU, brute force against numpy, and invariants."""
+GEMV oracle plus SwiGLU, brute force against numpy, and invariants; the
+shared expert pinned to the routed path (a shared expert equal to expert e is
+an extra slot naming e with gate weight 1) and to plain numpy."""
 import numpy as np
 import pytest
 
@@ -116,3 +118,68 @@ def test_moe_out_of_range_ids_contribute_nothing(oracle, small_experts):
     y2, _, h = oracle.moe(c13, s13, g13, c2, s2, g2, x, ids_bad, gw_bad, want_h=True)
     assert np.array_equal(y, y2)
     assert np.all(h[1] == 0) and np.all(h[3] == 0) and np.all(h[4] == 0)
+
+
+def _shared_from_expert(small_experts, e):
+    c13, s13, g13, c2, s2, g2 = small_experts
+    return (c13[e], s13[e], g13[e], c2[e], s2[e], g2[e])
+
+
+def test_moe_shared_equals_extra_slot_with_unit_gate(oracle, small_experts):
+    """The blend adds the shared expert after the routed slots with weight 1:
+    bit-identical to routing every token to the same expert once more, as its
+    last slot, with gate weight 1."""
+    E, H, I, M, topk = 6, 64, 32, 3, 2
+    x = workloads.x_bf16(4, 2, 0, M, H)
+    ids, gw = workloads.moe_routing(4, 2, M, E, topk)
+    for e in (0, 5):
+        y, bound, h, hs = oracle.moe_shared(*small_experts, x, ids, gw,
+                                            _shared_from_expert(small_experts, e),
+                                            want_h=True)
+        ids2 = np.concatenate([ids, np.full((M, 1), e, np.int32)], axis=1)
+        gw2 = np.concatenate([gw, np.ones((M, 1), np.float32)], axis=1)
+        y2, bound2, h2 = oracle.moe(*small_experts, x, ids2, gw2, want_h=True)
+        assert np.array_equal(y, y2) and np.array_equal(bound, bound2)
+        h2 = h2.reshape(M, topk + 1, I)
+        assert np.array_equal(h.reshape(M, topk, I), h2[:, :topk])
+        assert np.array_equal(hs, h2[:, topk])
+
+
+def test_moe_shared_zero_expert_adds_nothing(oracle, small_experts):
+    E, H, I, Is, M, topk = 6, 64, 32, 48, 2, 3
+    x = workloads.x_bf16(4, 3, 0, M, H)
+    ids, gw = workloads.moe_routing(4, 3, M, E, topk)
+    zero = (np.zeros((2 * Is, H // 2), np.uint8), np.zeros((2 * Is, H // 16), np.uint8),
+            np.float32(1.0), np.zeros((H, Is // 2), np.uint8),
+            np.zeros((H, Is // 16), np.uint8), np.float32(1.0))
+    y, bound = oracle.moe_shared(*small_experts, x, ids, gw, zero)
+    y0, bound0 = oracle.moe(*small_experts, x, ids, gw)
+    assert np.array_equal(y, y0) and np.array_equal(bound, bound0)
+
+
+def test_moe_shared_brute_force_numpy(oracle, small_experts):
+    """A shared expert of another width (Is = 48) against numpy: decode, fp64
+    gate|up, SwiGLU rounded once to bf16, fp64 down."""
+    import oracle as o
+    E, H, I, Is, M, topk = 6, 64, 32, 48, 2, 3
+    x = workloads.x_bf16(4, 4, 0, M, H)
+    ids, gw = workloads.moe_routing(4, 4, M, E, topk)
+    w13, w2 = workloads.moe_shared_weights(4, 4, H, Is)
+    sc13, ss13, sg13 = o.pack(w13)
+    sc2, ss2, sg2 = o.pack(w2)
+    y, bound, _, hs = oracle.moe_shared(*small_experts, x, ids, gw,
+                                        (sc13, ss13, sg13, sc2, ss2, sg2), want_h=True)
+    y0, bound0 = oracle.moe(*small_experts, x, ids, gw)
+    W13 = decode(sc13, ss13) * np.float64(sg13)
+    W2 = decode(sc2, ss2)
+    xv = bf16_value(x)
+    for m in range(M):
+        a = W13 @ xv[m]
+        G, U = a[:Is], a[Is:]
+        hb = _bf16_round(G / (1 + np.exp(-G)) * U)
+        assert np.array_equal(hs[m], hb)
+        t = W2 * bf16_value(hb)[None, :]
+        sh = np.float64(sg2) * t.sum(axis=1)
+        np.testing.assert_allclose(y[m], y0[m] + sh, rtol=1e-12, atol=1e-12)
+        np.testing.assert_allclose(bound[m], bound0[m] + abs(np.float64(sg2)) * np.abs(t).sum(axis=1),
+                                   rtol=1e-12)

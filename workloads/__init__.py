@@ -178,6 +178,15 @@ def moe_expert_weights(workload: int, rep: int, e: int, H: int, I: int,
     return w13, w2
 
 
+def moe_shared_weights(workload: int, rep: int, H: int, Is: int,
+                       threads: int | None = None):
+    """fp32 (WS13[2 Is, H], WS2[H, Is]) of the shared expert, N(0, 0.02), each
+    from its own stream (apart from every routed expert's)."""
+    w13 = normal_weights(workload, rep, 1 << 22, 2 * Is, H, threads=threads)
+    w2 = normal_weights(workload, rep, (1 << 22) + 1, H, Is, threads=threads)
+    return w13, w2
+
+
 def random_nvfp4(workload: int, rep: int, stream: int, N: int, K: int,
                  scale_lo: int = 0x00, scale_hi: int = 0x7E):
     """Arbitrary NVFP4 storage (not produced by a pack): uniform code bytes
