@@ -9,7 +9,8 @@ Secondary legs, measured the same way and reported in the same JSON line:
           weights with 1% zero blocks), one step = both calls;
   layer - the dense decode layer at M=5 (q, k, v, o, gate, up, down), one
           step = the seven calls;
-  moe   - the 288-expert MoE expert-slot pass at M=8 (and M=1), top-8;
+  moe   - the 288-expert MoE expert-slot pass at M=8 (and M=1), top-8, and
+          the same pass with the pages' shared expert (768 wide) fused in;
   copy  - a plain fp32 copy kernel of 2 x 512 MiB per launch: the measured
           bandwidth that the other legs are also reported against, and the
           calibration of the HBM byte counters.
@@ -294,24 +295,48 @@ def leg_moe(torch, nv, workloads, traffic, steps, warmup, M):
             torch.bfloat16)
         batches.append((torch.from_numpy(ids).cuda(), torch.from_numpy(gw).cuda(), x,
                         len(set(ids.ravel().tolist()))))
-    ws = torch.empty(nv.moe_workspace_bytes(M, H, I, topk), dtype=torch.uint8, device="cuda")
     y = torch.empty((M, H), dtype=torch.float32, device="cuda")
+    D = float(np.mean([batches[(warmup + i) % nb][3] for i in range(steps)]))
+
+    def run(step, nbytes, workload):
+        ms, kms = timed_steps(torch, step, steps, warmup)
+        # bytes of the steps actually timed (each step's own distinct-expert count)
+        B = float(np.mean([nbytes(batches[(warmup + i) % nb][3]) for i in range(steps)]))
+        return {"workload": workload, "M": M,
+                "distinct_experts_mean": D, "bytes_per_step": B, "ms_per_step": ms,
+                "pass_us": kms * 1e3, "gbs_wall": B / (ms * 1e-3) / 1e9,
+                "gbs_pass": B / (kms * 1e-3) / 1e9,
+                "frac_of_peak": B / (kms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                "tokens_per_s": M / (ms * 1e-3), "rotating_batches": nb}
+
+    ws = torch.empty(nv.moe_workspace_bytes(M, H, I, topk), dtype=torch.uint8, device="cuda")
 
     def step(i):
         ids, gw, x, _ = batches[i % nb]
         nv.moe_gemv_into(c13, s13, g13, c2, s2, g2, x, ids, gw, y, ws)
 
-    ms, kms = timed_steps(torch, step, steps, warmup)
-    # bytes of the steps actually timed (each step's own distinct-expert count)
-    Bs = [traffic.moe_bytes(M, H, I, topk, batches[(warmup + i) % nb][3]) for i in range(steps)]
-    B = float(np.mean(Bs))
-    D = float(np.mean([batches[(warmup + i) % nb][3] for i in range(steps)]))
-    return {"workload": f"moe_288x(3072x4096,4096x1536)_top8_m{M}", "M": M,
-            "distinct_experts_mean": D, "bytes_per_step": B, "ms_per_step": ms,
-            "pass_us": kms * 1e3, "gbs_wall": B / (ms * 1e-3) / 1e9,
-            "gbs_pass": B / (kms * 1e-3) / 1e9,
-            "frac_of_peak": B / (kms * 1e-3) / 1e9 / HBM_PEAK_GBS,
-            "tokens_per_s": M / (ms * 1e-3), "rotating_batches": nb}
+    routed = run(step, lambda d: traffic.moe_bytes(M, H, I, topk, d),
+                 f"moe_288x(3072x4096,4096x1536)_top8_m{M}")
+
+    # the same call with the shared expert of the pages (gate|up 768+768 x
+    # 4096, down 4096 x 768) in the same two launches
+    Is = 768
+    w = torch.randn((2 * Is, H), generator=gen, device="cuda") * 0.02
+    sh13 = nv.pack(w)
+    w = torch.randn((H, Is), generator=gen, device="cuda") * 0.02
+    sh2 = nv.pack(w)
+    del w
+    shared = (*sh13, *sh2)
+    wss = torch.empty(nv.moe_shared_workspace_bytes(M, H, I, topk, Is), dtype=torch.uint8,
+                      device="cuda")
+
+    def step_shared(i):
+        ids, gw, x, _ = batches[i % nb]
+        nv.moe_shared_gemv_into(c13, s13, g13, c2, s2, g2, x, ids, gw, shared, y, wss)
+
+    with_shared = run(step_shared, lambda d: traffic.moe_shared_bytes(M, H, I, topk, d, Is),
+                      f"moe_288x(3072x4096,4096x1536)_top8_shared768_m{M}")
+    return routed, with_shared
 
 
 def leg_copy(torch, steps, warmup):
@@ -585,8 +610,12 @@ def main():
             if k in result:
                 result[k]["frac_of_measured_copy"] = result[k]["gbs_kernel"] / cp["gbs"]
     if "moe" in legs:
-        result["moe"] = {f"m{M}": leg_moe(torch, nv, workloads, traffic, args.steps,
-                                          args.warmup, M) for M in (1, 8)}
+        result["moe"], result["moe_shared"] = {}, {}
+        for M in (1, 8):
+            routed, with_shared = leg_moe(torch, nv, workloads, traffic, args.steps,
+                                          args.warmup, M)
+            result["moe"][f"m{M}"] = routed
+            result["moe_shared"][f"m{M}"] = with_shared
     result["env"] = {"gpu": props.name, "cus": props.multi_processor_count,
                      "dpm_clocks": gpu_clock_state(),
                      "hip": torch.version.hip, "torch": torch.__version__, "git": git_sha(),

@@ -55,7 +55,7 @@
 extern "C" {
 #endif
 
-#define NVFP4_ABI_VERSION 2
+#define NVFP4_ABI_VERSION 3
 
 /* Largest number of activation rows (tokens) one GEMV / MoE call takes. */
 #define NVFP4_MAX_M 8
@@ -228,6 +228,70 @@ nvfp4_status nvfp4_moe_gemv(const uint8_t* w13_codes, const uint8_t* w13_scales,
                             const float* gate_w, int64_t M, int64_t E, int64_t H,
                             int64_t I, int64_t topk, float* y, void* workspace,
                             size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * nvfp4_moe_shared -- the shared expert of a MoE layer: a dense SwiGLU FFN
+ * of width Is that every token passes through (graph.json nodes
+ * "l3.moe.shared_gate_up", "l3.moe.shared_act", "l3.moe.shared_down"; card.json
+ * performance[4] and [9] give gate|up N = 768 + 768, K = 4096 and down
+ * N = 4096, K = 768).
+ *
+ *   w13_codes  uint8[2Is, H/2] (rows 0..Is-1 gate, Is..2Is-1 up), 16-byte
+ *              aligned; w13_scales uint8[2Is, H/16], 2-byte aligned;
+ *              w13_gscale float[1];
+ *   w2_codes   uint8[H, Is/2], 16-byte aligned; w2_scales uint8[H, Is/16],
+ *              2-byte aligned; w2_gscale float[1];
+ *   I          Is, > 0, a multiple of 32, <= NVFP4_MOE_MAX_I.
+ * The structure is read on the host during the call; the arrays are device
+ * memory read by the kernels.
+ */
+typedef struct nvfp4_moe_shared {
+  const uint8_t* w13_codes;
+  const uint8_t* w13_scales;
+  const float* w13_gscale;
+  const uint8_t* w2_codes;
+  const uint8_t* w2_scales;
+  const float* w2_gscale;
+  int64_t I;
+} nvfp4_moe_shared;
+
+/*
+ * nvfp4_moe_shared_workspace_bytes -- device workspace that
+ * nvfp4_moe_shared_gemv needs: the routed h[M * topk, I] and the shared
+ * hs[M, I_shared] bf16 activations, each 256-byte aligned. 0 for negative
+ * sizes.
+ */
+size_t nvfp4_moe_shared_workspace_bytes(int64_t M, int64_t H, int64_t I, int64_t topk,
+                                        int64_t I_shared);
+
+/*
+ * nvfp4_moe_shared_gemv -- nvfp4_moe_gemv plus a shared expert, blended as
+ * "routed slots + shared" (graph.json node "l3.moe.blend"): for token m,
+ *
+ *   y[m] = (nvfp4_moe_gemv's y[m])
+ *        + gs2 * WS2 . bf16( silu(a[0:Is]) * a[Is:2Is] ),  a = gs13 * WS13 . x[m]
+ *
+ * with the shared term added after the routed slots (weight 1). The shared
+ * expert runs inside the same two launches as the routed slots: its gate|up
+ * rows are streamed once for all M tokens, and its down rows join each
+ * token's down-and-combine dot product. Deterministic, no atomics.
+ *
+ * Arguments as nvfp4_moe_gemv, plus
+ *   shared     the shared expert (must not be NULL);
+ *   workspace  at least nvfp4_moe_shared_workspace_bytes(M, H, I, topk,
+ *              shared->I) bytes, 256-byte aligned; overwritten; must not be
+ *              shared by calls that may run concurrently.
+ * y and the workspace must not overlap any input, the shared arrays included.
+ * Errors: NULL, SHAPE, ALIGN, UNSUPPORTED, WORKSPACE, ALIAS, HIP.
+ */
+nvfp4_status nvfp4_moe_shared_gemv(const uint8_t* w13_codes, const uint8_t* w13_scales,
+                                   const float* w13_gscale, const uint8_t* w2_codes,
+                                   const uint8_t* w2_scales, const float* w2_gscale,
+                                   const uint16_t* x, const int32_t* expert_ids,
+                                   const float* gate_w, int64_t M, int64_t E, int64_t H,
+                                   int64_t I, int64_t topk, const nvfp4_moe_shared* shared,
+                                   float* y, void* workspace, size_t workspace_bytes,
+                                   hipStream_t stream);
 
 #ifdef __cplusplus
 }

@@ -13,6 +13,8 @@ Functions (same names as the C entry points, without the prefix):
   gemv_segments([(codes, scales, gscale), ...], x) -> [y_s] (one launch)
   moe_workspace_bytes(M, H, I, topk)     -> int
   moe_gemv(w13..., w2..., x, ids, gate_w[, workspace]) -> y (fp32 [M, H])
+  moe_shared_workspace_bytes(M, H, I, topk, I_shared) -> int
+  moe_shared_gemv(w13..., w2..., x, ids, gate_w, shared[, workspace]) -> y
 The ``*_into`` variants write into caller-provided outputs.
 """
 from __future__ import annotations
@@ -51,6 +53,14 @@ class GemvSegment(ctypes.Structure):
 MAX_SEGMENTS = 8
 
 
+class MoeShared(ctypes.Structure):
+    """nvfp4_moe_shared: the shared expert of a MoE call."""
+    _fields_ = [("w13_codes", ctypes.c_void_p), ("w13_scales", ctypes.c_void_p),
+                ("w13_gscale", ctypes.c_void_p), ("w2_codes", ctypes.c_void_p),
+                ("w2_scales", ctypes.c_void_p), ("w2_gscale", ctypes.c_void_p),
+                ("I", ctypes.c_int64)]
+
+
 def lib() -> ctypes.CDLL:
     """The loaded C library (raises if it has not been built)."""
     global _lib
@@ -79,6 +89,12 @@ def lib() -> ctypes.CDLL:
         L.nvfp4_moe_workspace_bytes.argtypes = [_I64, _I64, _I64, _I64]
         L.nvfp4_moe_gemv.restype = ctypes.c_int
         L.nvfp4_moe_gemv.argtypes = [_VP] * 9 + [_I64] * 5 + [_VP, _VP, ctypes.c_size_t, _VP]
+        L.nvfp4_moe_shared_workspace_bytes.restype = ctypes.c_size_t
+        L.nvfp4_moe_shared_workspace_bytes.argtypes = [_I64] * 5
+        L.nvfp4_moe_shared_gemv.restype = ctypes.c_int
+        L.nvfp4_moe_shared_gemv.argtypes = ([_VP] * 9 + [_I64] * 5 +
+                                            [ctypes.POINTER(MoeShared), _VP, _VP,
+                                             ctypes.c_size_t, _VP])
         _lib = L
     return _lib
 
@@ -252,3 +268,55 @@ def moe_workspace_layout(M: int, H: int, I: int, topk: int) -> dict:
     activations h[M*topk, I] after a call)."""
     S = M * topk
     return {"h": 0, "total": (S * I * 2 + 255) & ~255}
+
+
+def moe_shared_workspace_bytes(M: int, H: int, I: int, topk: int, I_shared: int) -> int:
+    return int(lib().nvfp4_moe_shared_workspace_bytes(M, H, I, topk, I_shared))
+
+
+def moe_shared_gemv_into(w13_codes, w13_scales, w13_gscale, w2_codes, w2_scales, w2_gscale,
+                         x, expert_ids, gate_w, shared, y, workspace) -> None:
+    """`shared` = (codes13 [2Is, H/2], scales13 [2Is, H/16], gscale13 [1],
+    codes2 [H, Is/2], scales2 [H, Is/16], gscale2 [1]) device tensors."""
+    sc13, ss13, sg13, sc2, ss2, sg2 = shared
+    _dev(w13_codes, w13_scales, w13_gscale, w2_codes, w2_scales, w2_gscale, x,
+         expert_ids, gate_w, y, workspace, sc13, ss13, sg13, sc2, ss2, sg2)
+    _dtype(x, torch.bfloat16, torch.int16, torch.uint16, name="x")
+    _dtype(expert_ids, torch.int32, name="expert_ids")
+    _dtype(gate_w, torch.float32, name="gate_w")
+    E, twoI, Hh = w13_codes.shape
+    H, I = Hh * 2, twoI // 2
+    M, topk = expert_ids.shape
+    Is = sc13.shape[0] // 2
+    if tuple(w2_codes.shape) != (E, H, I // 2) or tuple(x.shape) != (M, H) \
+            or tuple(gate_w.shape) != (M, topk) or tuple(y.shape) != (M, H) \
+            or tuple(sc13.shape) != (2 * Is, H // 2) or tuple(sc2.shape) != (H, Is // 2):
+        raise ValueError("inconsistent MoE shapes")
+    sh = MoeShared(_p(sc13), _p(ss13), _p(sg13), _p(sc2), _p(ss2), _p(sg2), Is)
+    _check("nvfp4_moe_shared_gemv", lib().nvfp4_moe_shared_gemv(
+        _p(w13_codes), _p(w13_scales), _p(w13_gscale), _p(w2_codes), _p(w2_scales),
+        _p(w2_gscale), _p(x), _p(expert_ids), _p(gate_w), M, E, H, I, topk, ctypes.byref(sh),
+        _p(y), _p(workspace), workspace.numel() * workspace.element_size(), _stream(x)))
+
+
+def moe_shared_gemv(w13_codes, w13_scales, w13_gscale, w2_codes, w2_scales, w2_gscale, x,
+                    expert_ids, gate_w, shared,
+                    workspace: torch.Tensor | None = None) -> torch.Tensor:
+    E, twoI, Hh = w13_codes.shape
+    H, I = Hh * 2, twoI // 2
+    M, topk = expert_ids.shape
+    Is = shared[0].shape[0] // 2
+    if workspace is None:
+        workspace = torch.empty(max(moe_shared_workspace_bytes(M, H, I, topk, Is), 256),
+                                dtype=torch.uint8, device=x.device)
+    y = torch.empty((M, H), dtype=torch.float32, device=x.device)
+    moe_shared_gemv_into(w13_codes, w13_scales, w13_gscale, w2_codes, w2_scales, w2_gscale, x,
+                         expert_ids, gate_w, shared, y, workspace)
+    return y
+
+
+def moe_shared_workspace_layout(M: int, H: int, I: int, topk: int, I_shared: int) -> dict:
+    """Byte offsets inside the workspace of nvfp4_moe_shared_gemv: the routed
+    h[M*topk, I] and the shared hs[M, I_shared] bf16 activations."""
+    hs = (M * topk * I * 2 + 255) & ~255
+    return {"h": 0, "hs": hs, "total": (hs + M * I_shared * 2 + 255) & ~255}

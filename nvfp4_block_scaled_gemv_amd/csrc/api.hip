@@ -200,8 +200,99 @@ nvfp4_status nvfp4_gemv_segments(const nvfp4_gemv_segment* segs, int64_t n_segme
 
 size_t nvfp4_moe_workspace_bytes(int64_t M, int64_t H, int64_t I, int64_t topk) {
   if (M < 0 || H < 0 || I < 0 || topk < 0) return 0;
-  return nvfp4::moe_layout(M, H, I, topk).total;
+  return nvfp4::moe_layout(M, H, I, topk, 0).total;
 }
+
+size_t nvfp4_moe_shared_workspace_bytes(int64_t M, int64_t H, int64_t I, int64_t topk,
+                                        int64_t I_shared) {
+  if (M < 0 || H < 0 || I < 0 || topk < 0 || I_shared < 0) return 0;
+  return nvfp4::moe_layout(M, H, I, topk, I_shared).total;
+}
+
+}  // extern "C"
+
+namespace {
+
+// Checks and launch shared by nvfp4_moe_gemv and nvfp4_moe_shared_gemv
+// (shared == NULL: no shared expert).
+nvfp4_status moe_checked(const char* fn, const uint8_t* w13_codes, const uint8_t* w13_scales,
+                         const float* w13_gscale, const uint8_t* w2_codes,
+                         const uint8_t* w2_scales, const float* w2_gscale, const uint16_t* x,
+                         const int32_t* expert_ids, const float* gate_w, int64_t M, int64_t E,
+                         int64_t H, int64_t I, int64_t topk, const nvfp4_moe_shared* shared,
+                         float* y, void* workspace, size_t workspace_bytes,
+                         hipStream_t stream) {
+  clear_error();
+  if (M < 0 || E < 1 || H <= 0 || I <= 0 || topk < 1 || (H % 32) != 0 || (I % 32) != 0)
+    return fail(NVFP4_ERR_SHAPE,
+                "%s: need M >= 0, E >= 1, topk >= 1, H, I > 0 and multiples of 32 "
+                "(M=%lld E=%lld H=%lld I=%lld topk=%lld)",
+                fn, (long long)M, (long long)E, (long long)H, (long long)I, (long long)topk);
+  const int64_t Is = shared ? shared->I : 0;
+  if (shared && (Is <= 0 || (Is % 32) != 0))
+    return fail(NVFP4_ERR_SHAPE, "%s: shared expert width I=%lld must be > 0 and a multiple of 32",
+                fn, (long long)Is);
+  if (M > NVFP4_MAX_M || topk > NVFP4_MAX_TOPK || I > NVFP4_MOE_MAX_I || Is > NVFP4_MOE_MAX_I)
+    return fail(NVFP4_ERR_UNSUPPORTED,
+                "%s: M=%lld (max %d), topk=%lld (max %d), I=%lld, shared I=%lld (max %d)", fn,
+                (long long)M, NVFP4_MAX_M, (long long)topk, NVFP4_MAX_TOPK, (long long)I,
+                (long long)Is, NVFP4_MOE_MAX_I);
+  if (M == 0) return NVFP4_OK;
+  if (!w13_codes || !w13_scales || !w13_gscale || !w2_codes || !w2_scales || !w2_gscale || !x ||
+      !expert_ids || !gate_w || !y)
+    return fail(NVFP4_ERR_NULL, "%s: NULL pointer", fn);
+  if (shared && (!shared->w13_codes || !shared->w13_scales || !shared->w13_gscale ||
+                 !shared->w2_codes || !shared->w2_scales || !shared->w2_gscale))
+    return fail(NVFP4_ERR_NULL, "%s: NULL pointer in the shared expert", fn);
+  const size_t need = nvfp4::moe_layout(M, H, I, topk, Is).total;
+  if (!workspace || workspace_bytes < need)
+    return fail(NVFP4_ERR_WORKSPACE, "%s: workspace of %zu bytes needed, %zu given", fn, need,
+                workspace ? workspace_bytes : (size_t)0);
+  if (!aligned(w13_codes, 16) || !aligned(w2_codes, 16) || !aligned(w13_scales, 2) ||
+      !aligned(w2_scales, 2) || !aligned(x, 16) || !aligned(y, 16) || !aligned(workspace, 256) ||
+      !aligned(expert_ids, 4) || !aligned(gate_w, 4) || !aligned(w13_gscale, 4) ||
+      !aligned(w2_gscale, 4))
+    return fail(NVFP4_ERR_ALIGN, "%s: alignment rule broken (see nvfp4_gemv.h)", fn);
+  if (shared && (!aligned(shared->w13_codes, 16) || !aligned(shared->w2_codes, 16) ||
+                 !aligned(shared->w13_scales, 2) || !aligned(shared->w2_scales, 2) ||
+                 !aligned(shared->w13_gscale, 4) || !aligned(shared->w2_gscale, 4)))
+    return fail(NVFP4_ERR_ALIGN, "%s: alignment rule broken in the shared expert", fn);
+  const size_t e13 = (size_t)E * 2 * (size_t)I * (size_t)H, e2 = (size_t)E * (size_t)H * (size_t)I;
+  const size_t s13 = 2 * (size_t)Is * (size_t)H, s2 = (size_t)H * (size_t)Is;
+  const size_t yb = (size_t)M * (size_t)H * 4, S = (size_t)(M * topk);
+  const void* ins[] = {w13_codes, w13_scales, w13_gscale, w2_codes, w2_scales, w2_gscale, x,
+                       expert_ids, gate_w,
+                       shared ? shared->w13_codes : nullptr, shared ? shared->w13_scales : nullptr,
+                       shared ? shared->w13_gscale : nullptr, shared ? shared->w2_codes : nullptr,
+                       shared ? shared->w2_scales : nullptr, shared ? shared->w2_gscale : nullptr};
+  const size_t insz[] = {e13 / 2, e13 / 16, (size_t)E * 4, e2 / 2, e2 / 16, (size_t)E * 4,
+                         (size_t)M * (size_t)H * 2, S * 4, S * 4,
+                         s13 / 2, s13 / 16, 4, s2 / 2, s2 / 16, 4};
+  for (int i = 0; i < 15; ++i) {
+    if (overlap(y, yb, ins[i], insz[i]) || overlap(workspace, need, ins[i], insz[i]))
+      return fail(NVFP4_ERR_ALIAS, "%s: y or workspace overlaps input %d", fn, i);
+  }
+  if (overlap(y, yb, workspace, need))
+    return fail(NVFP4_ERR_ALIAS, "%s: y overlaps the workspace", fn);
+  nvfp4::MoeShared sh = {};
+  if (shared) {
+    sh.c13 = shared->w13_codes;
+    sh.s13 = shared->w13_scales;
+    sh.g13 = shared->w13_gscale;
+    sh.c2 = shared->w2_codes;
+    sh.s2 = shared->w2_scales;
+    sh.g2 = shared->w2_gscale;
+    sh.I = Is;
+  }
+  return hip_result(nvfp4::launch_moe(w13_codes, w13_scales, w13_gscale, w2_codes, w2_scales,
+                                      w2_gscale, x, expert_ids, gate_w, (int)M, E, H, I,
+                                      (int)topk, shared ? &sh : nullptr, y, workspace, stream),
+                    fn);
+}
+
+}  // namespace
+
+extern "C" {
 
 nvfp4_status nvfp4_moe_gemv(const uint8_t* w13_codes, const uint8_t* w13_scales,
                             const float* w13_gscale, const uint8_t* w2_codes,
@@ -209,46 +300,26 @@ nvfp4_status nvfp4_moe_gemv(const uint8_t* w13_codes, const uint8_t* w13_scales,
                             const int32_t* expert_ids, const float* gate_w, int64_t M, int64_t E,
                             int64_t H, int64_t I, int64_t topk, float* y, void* workspace,
                             size_t workspace_bytes, hipStream_t stream) {
-  clear_error();
-  if (M < 0 || E < 1 || H <= 0 || I <= 0 || topk < 1 || (H % 32) != 0 || (I % 32) != 0)
-    return fail(NVFP4_ERR_SHAPE,
-                "nvfp4_moe_gemv: need M >= 0, E >= 1, topk >= 1, H, I > 0 and multiples of 32 "
-                "(M=%lld E=%lld H=%lld I=%lld topk=%lld)",
-                (long long)M, (long long)E, (long long)H, (long long)I, (long long)topk);
-  if (M > NVFP4_MAX_M || topk > NVFP4_MAX_TOPK || I > NVFP4_MOE_MAX_I)
-    return fail(NVFP4_ERR_UNSUPPORTED,
-                "nvfp4_moe_gemv: M=%lld (max %d), topk=%lld (max %d), I=%lld (max %d)",
-                (long long)M, NVFP4_MAX_M, (long long)topk, NVFP4_MAX_TOPK, (long long)I,
-                NVFP4_MOE_MAX_I);
-  if (M == 0) return NVFP4_OK;
-  if (!w13_codes || !w13_scales || !w13_gscale || !w2_codes || !w2_scales || !w2_gscale || !x ||
-      !expert_ids || !gate_w || !y)
-    return fail(NVFP4_ERR_NULL, "nvfp4_moe_gemv: NULL pointer");
-  const size_t need = nvfp4::moe_layout(M, H, I, topk).total;
-  if (!workspace || workspace_bytes < need)
-    return fail(NVFP4_ERR_WORKSPACE, "nvfp4_moe_gemv: workspace of %zu bytes needed, %zu given",
-                need, workspace ? workspace_bytes : (size_t)0);
-  if (!aligned(w13_codes, 16) || !aligned(w2_codes, 16) || !aligned(w13_scales, 2) ||
-      !aligned(w2_scales, 2) || !aligned(x, 16) || !aligned(y, 16) || !aligned(workspace, 256) ||
-      !aligned(expert_ids, 4) || !aligned(gate_w, 4) || !aligned(w13_gscale, 4) ||
-      !aligned(w2_gscale, 4))
-    return fail(NVFP4_ERR_ALIGN, "nvfp4_moe_gemv: alignment rule broken (see nvfp4_gemv.h)");
-  const size_t e13 = (size_t)E * 2 * (size_t)I * (size_t)H, e2 = (size_t)E * (size_t)H * (size_t)I;
-  const size_t yb = (size_t)M * (size_t)H * 4, S = (size_t)(M * topk);
-  const void* ins[] = {w13_codes, w13_scales, w13_gscale, w2_codes, w2_scales,
-                       w2_gscale, x,          expert_ids, gate_w};
-  const size_t insz[] = {e13 / 2, e13 / 16, (size_t)E * 4, e2 / 2, e2 / 16,
-                         (size_t)E * 4, (size_t)M * (size_t)H * 2, S * 4, S * 4};
-  for (int i = 0; i < 9; ++i) {
-    if (overlap(y, yb, ins[i], insz[i]) || overlap(workspace, need, ins[i], insz[i]))
-      return fail(NVFP4_ERR_ALIAS, "nvfp4_moe_gemv: y or workspace overlaps input %d", i);
+  return moe_checked("nvfp4_moe_gemv", w13_codes, w13_scales, w13_gscale, w2_codes, w2_scales,
+                     w2_gscale, x, expert_ids, gate_w, M, E, H, I, topk, nullptr, y, workspace,
+                     workspace_bytes, stream);
+}
+
+nvfp4_status nvfp4_moe_shared_gemv(const uint8_t* w13_codes, const uint8_t* w13_scales,
+                                   const float* w13_gscale, const uint8_t* w2_codes,
+                                   const uint8_t* w2_scales, const float* w2_gscale,
+                                   const uint16_t* x, const int32_t* expert_ids,
+                                   const float* gate_w, int64_t M, int64_t E, int64_t H,
+                                   int64_t I, int64_t topk, const nvfp4_moe_shared* shared,
+                                   float* y, void* workspace, size_t workspace_bytes,
+                                   hipStream_t stream) {
+  if (!shared) {
+    clear_error();
+    return fail(NVFP4_ERR_NULL, "nvfp4_moe_shared_gemv: NULL shared expert");
   }
-  if (overlap(y, yb, workspace, need))
-    return fail(NVFP4_ERR_ALIAS, "nvfp4_moe_gemv: y overlaps the workspace");
-  return hip_result(nvfp4::launch_moe(w13_codes, w13_scales, w13_gscale, w2_codes, w2_scales,
-                                      w2_gscale, x, expert_ids, gate_w, (int)M, E, H, I,
-                                      (int)topk, y, workspace, stream),
-                    "nvfp4_moe_gemv launch");
+  return moe_checked("nvfp4_moe_shared_gemv", w13_codes, w13_scales, w13_gscale, w2_codes,
+                     w2_scales, w2_gscale, x, expert_ids, gate_w, M, E, H, I, topk, shared, y,
+                     workspace, workspace_bytes, stream);
 }
 
 }  // extern "C"

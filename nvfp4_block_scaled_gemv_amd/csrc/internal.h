@@ -45,14 +45,28 @@ hipError_t launch_fill_zero(float* y, size_t n, hipStream_t stream);
 // MoE workspace layout (byte offsets from the workspace base).
 struct MoeLayout {
   size_t h_off;       // uint16 bf16 SwiGLU activations h[M * topk, I]
+  size_t hs_off;      // the shared expert's hs[M, Is] (empty when Is = 0)
   size_t total;       // rounded up to 256 bytes
 };
-MoeLayout moe_layout(int64_t M, int64_t H, int64_t I, int64_t topk);
+MoeLayout moe_layout(int64_t M, int64_t H, int64_t I, int64_t topk, int64_t Is);
+
+// The shared expert of a MoE call (I = 0: none). h is set by the launcher.
+struct MoeShared {
+  const uint8_t* c13;   // codes [2 Is, H/2]
+  const uint8_t* s13;   // scales [2 Is, H/16]
+  const float* g13;     // [1]
+  const uint8_t* c2;    // codes [H, Is/2]
+  const uint8_t* s2;    // scales [H, Is/16]
+  const float* g2;      // [1]
+  int64_t I;            // Is
+  uint16_t* h;          // hs [M, Is] in the workspace
+};
 
 hipError_t launch_moe(const uint8_t* w13_codes, const uint8_t* w13_scales,
                       const float* w13_gscale, const uint8_t* w2_codes,
                       const uint8_t* w2_scales, const float* w2_gscale, const uint16_t* x,
                       const int32_t* ids, const float* gate_w, int M, int64_t E, int64_t H,
-                      int64_t I, int topk, float* y, void* workspace, hipStream_t stream);
+                      int64_t I, int topk, const MoeShared* shared, float* y, void* workspace,
+                      hipStream_t stream);
 
 }  // namespace nvfp4

@@ -19,6 +19,12 @@
 //      walks (slot, 32-element chunk) pairs with all 64 lanes busy whatever
 //      I is. The slot sum is a fixed-order register reduction: deterministic,
 //      no per-slot output buffer, no separate combine launch.
+// An optional shared expert (graph.json nodes "l3.moe.shared_gate_up",
+// "l3.moe.shared_act", "l3.moe.shared_down"; "l3.moe.blend" takes the routed
+// slots and the shared output) rides in the same two launches: one more
+// gate|up workgroup column streams its rows once for all M tokens, and each
+// token's down dot product runs on over the shared expert's chunks after its
+// routed slots, with coefficient g2s (gate weight 1).
 #include "gemv_core.h"
 #include "internal.h"
 
@@ -30,11 +36,12 @@ constexpr int kDownUnroll = 2;   // (slot, chunk) pairs in flight per lane
 
 static inline size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 
-MoeLayout moe_layout(int64_t M, int64_t H, int64_t I, int64_t topk) {
+MoeLayout moe_layout(int64_t M, int64_t H, int64_t I, int64_t topk, int64_t Is) {
   (void)H;
   MoeLayout L;
   L.h_off = 0;
-  L.total = align256((size_t)(M * topk) * (size_t)I * sizeof(uint16_t));
+  L.hs_off = align256((size_t)(M * topk) * (size_t)I * sizeof(uint16_t));
+  L.total = align256(L.hs_off + (size_t)M * (size_t)Is * sizeof(uint16_t));
   return L;
 }
 
@@ -46,11 +53,13 @@ __device__ __forceinline__ uint16_t bf16_rne(float v) {
 
 // One wavefront: gate rows r0, r0+1 and up rows I+r0, I+r0+1 of one expert
 // against x of up to MS slots; writes h[slot, r0 .. r0+1].
+// The token of slot s is s / xdiv (topk for routed slots, 1 for the shared
+// expert, whose slots are the tokens).
 template <int MS>
 __device__ __forceinline__ void gate_up_rows(const uint8_t* __restrict__ codes,
                                              const uint8_t* __restrict__ scales, float g,
                                              const uint16_t* __restrict__ x, int64_t H,
-                                             int64_t I, int64_t r0, int topk,
+                                             int64_t I, int64_t r0, int xdiv,
                                              const int (&slot)[MS], int ns,
                                              uint16_t* __restrict__ h) {
   const int lane = threadIdx.x & 63;
@@ -58,7 +67,7 @@ __device__ __forceinline__ void gate_up_rows(const uint8_t* __restrict__ codes,
   const int64_t rows[4] = {r0, r1, I + r0, I + r1};
   const uint16_t* xs[MS];
 #pragma unroll
-  for (int m = 0; m < MS; ++m) xs[m] = x + (int64_t)(slot[m] / topk) * H;
+  for (int m = 0; m < MS; ++m) xs[m] = x + (int64_t)(slot[m] / xdiv) * H;
   float acc[4][MS];
   wave_row_dots<MS, 4>(codes, scales, H, rows, xs, ns, acc);
 #pragma unroll
@@ -72,17 +81,31 @@ __device__ __forceinline__ void gate_up_rows(const uint8_t* __restrict__ codes,
       }
 }
 
-// grid (S, ceil(ceil(I/2) / kMoeWaves)); a wavefront owns one gate/up row pair.
+// grid (S [+ 1 for the shared expert], ceil(ceil(max(I, Is)/2) / kMoeWaves));
+// a wavefront owns one gate/up row pair.
 __global__ __launch_bounds__(256) void k_moe_gate_up(
     const uint8_t* __restrict__ w13_codes, const uint8_t* __restrict__ w13_scales,
     const float* __restrict__ w13_gscale, const uint16_t* __restrict__ x,
     const int32_t* __restrict__ ids, int S, int topk, int64_t E, int64_t H, int64_t I,
-    uint16_t* __restrict__ h) {
+    uint16_t* __restrict__ h, const MoeShared sh, int M) {
   const int j = blockIdx.x;
   const int lane = threadIdx.x & 63;
   const int64_t pair =
       (int64_t)blockIdx.y * kMoeWaves + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int64_t r0 = pair * 2;
+  if (j == S) {
+    // the shared expert: its rows once, for all M tokens (its slots)
+    if (r0 >= sh.I) return;
+    const float gs = *sh.g13;
+    for (int b = 0; b < M; b += 4) {
+      int slot[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) slot[q] = b + q < M ? b + q : b;
+      gate_up_rows<4>(sh.c13, sh.s13, gs, x, H, sh.I, r0, 1, slot, M - b < 4 ? M - b : 4,
+                      sh.h);
+    }
+    return;
+  }
   if (r0 >= I) return;
   const int32_t e = ids[j];
   if (e < 0 || (int64_t)e >= E) return;
@@ -129,7 +152,7 @@ __global__ __launch_bounds__(256) void k_moe_down(
     const uint8_t* __restrict__ w2_codes, const uint8_t* __restrict__ w2_scales,
     const float* __restrict__ w2_gscale, const uint16_t* __restrict__ h,
     const int32_t* __restrict__ ids, const float* __restrict__ gate_w, int M, int topk,
-    int64_t E, int64_t H, int64_t I, float* __restrict__ y) {
+    int64_t E, int64_t H, int64_t I, float* __restrict__ y, const MoeShared sh) {
   const int lane = threadIdx.x & 63;
   const int64_t n0 =
       ((int64_t)blockIdx.x * kMoeWaves + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6)) * R;
@@ -138,6 +161,10 @@ __global__ __launch_bounds__(256) void k_moe_down(
   const int64_t cb = I >> 1, sb = I >> 4;
   const int64_t ecb = H * cb, esb = H * sb;
   const float invC = 1.0f / (float)C;
+  // the shared expert's chunks follow each token's routed slots
+  const int Cs = (int)(sh.I >> 5);
+  const int64_t cbs = sh.I >> 1, sbs = sh.I >> 4;
+  const float gs2 = Cs > 0 ? *sh.g2 : 0.0f;
   int64_t rows[R];
 #pragma unroll
   for (int r = 0; r < R; ++r) rows[r] = (n0 + r < H) ? n0 + r : H - 1;
@@ -161,7 +188,8 @@ __global__ __launch_bounds__(256) void k_moe_down(
     float acc[R];
 #pragma unroll
     for (int r = 0; r < R; ++r) acc[r] = 0.0f;
-    const int P = nv * C;   // (slot, chunk) pairs of this token
+    const int PR = nv * C;   // (slot, chunk) pairs of this token's routed slots
+    const int P = PR + Cs;   // then the shared expert's chunks
     for (int p0 = 0; p0 < P; p0 += 64 * U) {
       u32x4_t qv[U][R];
       uint32_t sw[U][R];
@@ -173,21 +201,28 @@ __global__ __launch_bounds__(256) void k_moe_down(
         const int p = p0 + lane + 64 * u;
         live[u] = p < P;
         const int pc = live[u] ? p : P - 1;
-        int qi = (int)(((float)pc + 0.5f) * invC);
-        if (qi * C > pc) --qi;
-        if ((qi + 1) * C <= pc) ++qi;
-        const int c = pc - qi * C;
+        const bool shp = pc >= PR;   // a shared-expert chunk
+        const int pr = shp ? 0 : pc;
+        int qi = (int)(((float)pr + 0.5f) * invC);
+        if (qi * C > pr) --qi;
+        if ((qi + 1) * C <= pr) ++qi;
+        const int c = shp ? pc - PR : pr - qi * C;
         const int ee = __shfl(e_c, qi, 64);
         const int jj = __shfl(j_c, qi, 64);
-        cf[u] = __int_as_float(__shfl(f_c, qi, 64));
-        const uint8_t* cbase = w2_codes + (int64_t)ee * ecb + (int64_t)c * 16;
-        const uint8_t* sbase = w2_scales + (int64_t)ee * esb + (int64_t)c * 2;
+        const float fr = __int_as_float(__shfl(f_c, qi, 64));
+        cf[u] = shp ? gs2 : fr;
+        const uint8_t* cbase = shp ? sh.c2 + (int64_t)c * 16
+                                   : w2_codes + (int64_t)ee * ecb + (int64_t)c * 16;
+        const uint8_t* sbase = shp ? sh.s2 + (int64_t)c * 2
+                                   : w2_scales + (int64_t)ee * esb + (int64_t)c * 2;
+        const int64_t rcb = shp ? cbs : cb, rsb = shp ? sbs : sb;
 #pragma unroll
         for (int r = 0; r < R; ++r) {
-          qv[u][r] = load_stream(cbase + rows[r] * cb);
-          sw[u][r] = *reinterpret_cast<const uint16_t*>(sbase + rows[r] * sb);
+          qv[u][r] = load_stream(cbase + rows[r] * rcb);
+          sw[u][r] = *reinterpret_cast<const uint16_t*>(sbase + rows[r] * rsb);
         }
-        const u32x4_t* hp = reinterpret_cast<const u32x4_t*>(h + (int64_t)jj * I + c * 32);
+        const uint16_t* hrow = shp ? sh.h + (int64_t)m * sh.I : h + (int64_t)jj * I;
+        const u32x4_t* hp = reinterpret_cast<const u32x4_t*>(hrow + c * 32);
 #pragma unroll
         for (int t = 0; t < 4; ++t) hv[u][t] = hp[t];
       }
@@ -231,21 +266,26 @@ hipError_t launch_moe(const uint8_t* w13_codes, const uint8_t* w13_scales,
                       const float* w13_gscale, const uint8_t* w2_codes,
                       const uint8_t* w2_scales, const float* w2_gscale, const uint16_t* x,
                       const int32_t* ids, const float* gate_w, int M, int64_t E, int64_t H,
-                      int64_t I, int topk, float* y, void* workspace, hipStream_t stream) {
-  const MoeLayout L = moe_layout(M, H, I, topk);
+                      int64_t I, int topk, const MoeShared* shared, float* y, void* workspace,
+                      hipStream_t stream) {
+  MoeShared sh = {};
+  if (shared) sh = *shared;
+  const MoeLayout L = moe_layout(M, H, I, topk, sh.I);
   uint16_t* h = reinterpret_cast<uint16_t*>(static_cast<char*>(workspace) + L.h_off);
+  sh.h = reinterpret_cast<uint16_t*>(static_cast<char*>(workspace) + L.hs_off);
   const int S = M * topk;
   {
-    const int64_t pairs = (I + 1) / 2;
+    const int64_t pairs = ((sh.I > I ? sh.I : I) + 1) / 2;
     const int64_t yb = (pairs + kMoeWaves - 1) / kMoeWaves;
-    hipLaunchKernelGGL(k_moe_gate_up, dim3(S, (unsigned)yb), dim3(256), 0, stream, w13_codes,
-                       w13_scales, w13_gscale, x, ids, S, topk, E, H, I, h);
+    hipLaunchKernelGGL(k_moe_gate_up, dim3(S + (sh.I > 0 ? 1 : 0), (unsigned)yb), dim3(256), 0,
+                       stream, w13_codes, w13_scales, w13_gscale, x, ids, S, topk, E, H, I, h,
+                       sh, M);
   }
   {
     const int64_t wgs = (H + kDownRows * kMoeWaves - 1) / (kDownRows * kMoeWaves);
     hipLaunchKernelGGL((k_moe_down<kDownRows, kDownUnroll>), dim3((unsigned)wgs), dim3(256), 0,
                        stream, w2_codes, w2_scales, w2_gscale, h, ids, gate_w, M, topk, E, H, I,
-                       y);
+                       y, sh);
   }
   return hipGetLastError();
 }

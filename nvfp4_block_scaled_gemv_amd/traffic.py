@@ -28,6 +28,14 @@ def moe_bytes(M: int, H: int, I: int, topk: int, distinct: int) -> int:
     return distinct * per_expert + M * H * 2 + S * 8 + 2 * S * I * 2 + M * H * 4
 
 
+def moe_shared_bytes(M: int, H: int, I: int, topk: int, distinct: int, Is: int) -> int:
+    """moe_bytes plus the shared expert: its gate|up [2Is, H] and down [H, Is]
+    weights and two tensor scales, and its bf16 activations hs[M, Is]
+    (written once, read once)."""
+    shared = weight_bytes(2 * Is, H) + weight_bytes(H, Is) + 8 + 2 * M * Is * 2
+    return moe_bytes(M, H, I, topk, distinct) + shared
+
+
 def pages_floor_us(M: float, N: int, K: int, experts: float, bits: float,
                    act_bytes_per_elem: float, out_elems: int,
                    bw_bytes_per_s: float = 249e9) -> float:

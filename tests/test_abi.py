@@ -30,14 +30,15 @@ def declared_functions():
 def test_exports_every_declared_symbol(L):
     names = declared_functions()
     assert {"nvfp4_pack", "nvfp4_dequant", "nvfp4_gemv", "nvfp4_gemv_segments", "nvfp4_moe_gemv",
-            "nvfp4_moe_workspace_bytes", "nvfp4_abi_version", "nvfp4_status_string",
+            "nvfp4_moe_workspace_bytes", "nvfp4_moe_shared_gemv",
+            "nvfp4_moe_shared_workspace_bytes", "nvfp4_abi_version", "nvfp4_status_string",
             "nvfp4_last_error"} <= set(names)
     for n in names:
         assert hasattr(L, n), n
 
 
 def test_version_and_status_strings(L):
-    assert L.nvfp4_abi_version() == 2
+    assert L.nvfp4_abi_version() == 3
     for s in range(8):
         assert L.nvfp4_status_string(s)
     assert L.nvfp4_status_string(99) == b"unknown status"
@@ -102,6 +103,44 @@ def test_moe_checks(L):
     assert f(*args, 1, 4, 64, 64, 2, B, B + 0x1000000 + 64, need, None) == ERR_ALIGN
     assert f(*args, 1, 4, 64, 64, 2, args[6], B + 0x1000000, need, None) == ERR_ALIAS
     assert f(*args, 0, 4, 64, 64, 2, B, B + 0x1000000, need, None) == OK
+
+
+def test_moe_shared_checks(L):
+    """Host-side validation of the MoE call with a shared expert (no launch)."""
+    Sh = nv.MoeShared
+    ws = nv.moe_shared_workspace_bytes(8, 4096, 1536, 8, 768)
+    assert ws == nv.moe_shared_workspace_layout(8, 4096, 1536, 8, 768)["total"]
+    assert ws == 64 * 1536 * 2 + 8 * 768 * 2
+    assert nv.moe_shared_workspace_bytes(1, 64, 32, 3, 32) == 512
+    assert nv.moe_shared_workspace_bytes(1, 64, 32, 3, -32) == 0
+    args = [A + i * 0x10000000 for i in range(9)]
+    sh_base = [A + 0x90000000 + i * 0x1000000 for i in range(6)]
+    f = L.nvfp4_moe_shared_gemv
+    Y, WS = B, B + 0x1000000
+    need = nv.moe_shared_workspace_bytes(1, 64, 64, 2, 96)
+    good = Sh(*sh_base, 96)
+    assert f(*args, 1, 4, 64, 64, 2, None, Y, WS, need, None) == ERR_NULL
+    assert f(*args, 1, 4, 64, 64, 2, ctypes.byref(Sh(*sh_base, 80)), Y, WS, need,
+             None) == ERR_SHAPE                                              # Is % 32
+    assert f(*args, 1, 4, 64, 64, 2, ctypes.byref(Sh(*sh_base, 0)), Y, WS, need,
+             None) == ERR_SHAPE
+    assert f(*args, 1, 4, 64, 64, 2, ctypes.byref(Sh(*sh_base, (1 << 24) + 32)), Y, WS,
+             1 << 40, None) == ERR_UNSUPPORTED
+    nul = Sh(*sh_base, 96)
+    nul.w2_scales = None
+    assert f(*args, 1, 4, 64, 64, 2, ctypes.byref(nul), Y, WS, need, None) == ERR_NULL
+    assert f(*args, 1, 4, 64, 64, 2, ctypes.byref(good), Y, WS, need - 1, None) == ERR_WORKSPACE
+    # the routed-only size is too small once a shared expert needs hs
+    assert f(*args, 1, 4, 64, 64, 2, ctypes.byref(good), Y, WS,
+             nv.moe_workspace_bytes(1, 64, 64, 2), None) == ERR_WORKSPACE
+    mis = Sh(*sh_base, 96)
+    mis.w2_codes = sh_base[3] + 8
+    assert f(*args, 1, 4, 64, 64, 2, ctypes.byref(mis), Y, WS, need, None) == ERR_ALIGN
+    assert f(*args, 1, 4, 64, 64, 2, ctypes.byref(good), sh_base[0], WS, need,
+             None) == ERR_ALIAS                                              # y on WS13
+    assert f(*args, 1, 4, 64, 64, 2, ctypes.byref(good), Y, sh_base[4], need,
+             None) == ERR_ALIAS                                              # workspace on WS2 scales
+    assert f(*args, 0, 4, 64, 64, 2, ctypes.byref(good), Y, WS, need, None) == OK
 
 
 def test_binding_raises_without_device_tensors():

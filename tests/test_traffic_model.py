@@ -33,3 +33,12 @@ def test_moe_bytes_counts_distinct_experts():
     one = traffic.moe_bytes(1, 4096, 1536, 8, 8)
     assert one > 8 * (traffic.weight_bytes(3072, 4096) + traffic.weight_bytes(4096, 1536))
     assert traffic.moe_bytes(8, 4096, 1536, 8, 58) < traffic.moe_bytes(8, 4096, 1536, 8, 64)
+
+
+def test_moe_shared_bytes_add_the_shared_expert_once():
+    # the pages' shared expert: gate|up 768 + 768 by 4096, down 4096 by 768
+    routed = traffic.moe_bytes(8, 4096, 1536, 8, 58)
+    shared = traffic.moe_shared_bytes(8, 4096, 1536, 8, 58, 768)
+    w = 1536 * 4096 * 9 // 16 + 4096 * 768 * 9 // 16   # 4.5 bits per weight
+    assert shared - routed == w + 8 + 2 * 8 * 768 * 2
+    assert traffic.moe_shared_bytes(1, 64, 32, 2, 1, 0) == traffic.moe_bytes(1, 64, 32, 2, 1) + 8
