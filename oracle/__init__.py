@@ -60,6 +60,11 @@ def lib():
                                         _i32p, _f32p, _i64, _i64, _i64, _i64, _i64,
                                         _u8p, _u8p, _f32p, _u8p, _u8p, _f32p, _i64,
                                         _f64p, _f64p, _u16p, _u16p]
+        L.oracle_quantize_act.restype = ctypes.c_int
+        L.oracle_quantize_act.argtypes = [_u16p, _i64, _i64, ctypes.c_float, _u8p, _u8p]
+        L.oracle_gemv_w4a4.restype = ctypes.c_int
+        L.oracle_gemv_w4a4.argtypes = [_u8p, _u8p, ctypes.c_float, _u8p, _u8p, ctypes.c_float,
+                                       _i64, _i64, _i64, _i64p, _i64, _f64p, _f64p]
         _lib = L
     return _lib
 
@@ -238,3 +243,43 @@ def moe_shared(w13_codes, w13_scales, w13_g, w2_codes, w2_scales, w2_g, x_bits,
                                  _ptr(hs, _u16p) if hs is not None else None)
     _check(rc, "moe_shared")
     return (y, bound, h, hs) if want_h else (y, bound)
+
+
+# ------------------------------------------------------------------- w4a4
+
+def quantize_act(x_bits, g_x):
+    """bf16 x [M, K] (uint16 bits) -> (codes u8[M, K/2], scales u8[M, K/16])
+    with the static input scale g_x."""
+    x_bits = _c(x_bits, np.uint16)
+    M, K = x_bits.shape
+    codes = np.empty((M, K // 2), np.uint8)
+    scales = np.empty((M, K // 16), np.uint8)
+    rc = lib().oracle_quantize_act(_ptr(x_bits, _u16p), M, K, float(g_x),
+                                   _ptr(codes, _u8p), _ptr(scales, _u8p))
+    _check(rc, "quantize_act")
+    return codes, scales
+
+
+def gemv_w4a4(codes_w, scales_w, g_w, codes_x, scales_x, g_x, rows=None):
+    """y, absdot (fp64, [M, N] or [M, len(rows)]) of the W4A4 product."""
+    codes_w = _c(codes_w, np.uint8)
+    scales_w = _c(scales_w, np.uint8)
+    codes_x = _c(codes_x, np.uint8)
+    scales_x = _c(scales_x, np.uint8)
+    N, K = codes_w.shape[0], codes_w.shape[1] * 2
+    M = codes_x.shape[0]
+    if codes_x.shape[1] * 2 != K:
+        raise ValueError("x has the wrong K")
+    if rows is not None:
+        rows = _c(np.asarray(rows, np.int64), np.int64)
+        cnt = rows.shape[0]
+    else:
+        cnt = N
+    y = np.empty((M, cnt), np.float64)
+    ad = np.empty((M, cnt), np.float64)
+    rc = lib().oracle_gemv_w4a4(_ptr(codes_w, _u8p), _ptr(scales_w, _u8p), float(g_w),
+                                _ptr(codes_x, _u8p), _ptr(scales_x, _u8p), float(g_x),
+                                M, N, K, _ptr(rows, _i64p) if rows is not None else None,
+                                cnt, _ptr(y, _f64p), _ptr(ad, _f64p))
+    _check(rc, "gemv_w4a4")
+    return y, ad

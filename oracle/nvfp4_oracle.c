@@ -104,6 +104,36 @@ unsigned oracle_e2m1_encode(float t) {
 
 /* ------------------------------------------------------------------ pack */
 
+/* Steps 2-4 of the recipe for one block of 16 fp32 values w with tensor
+   scale g: the scale byte and the 8 code bytes. */
+static void quantize_block(const float* w, float g, uint8_t* c, uint8_t* scale) {
+  const float d6 = 6.0f * g;
+  float ab = 0.0f, r, s;
+  unsigned sc;
+  int j;
+  /* Step 2: block amax relative to 6 * g. */
+  for (j = 0; j < 16; ++j) {
+    float a = fabsf(w[j]);
+    if (a > ab) ab = a;
+  }
+  r = ab / d6;
+  /* Step 3: the block scale byte and its value. */
+  sc = oracle_e4m3_encode(r);
+  *scale = (uint8_t)sc;
+  s = (float)oracle_e4m3_value(sc);
+  /* Step 4: element codes relative to s * g. */
+  if (s == 0.0f) {
+    memset(c, 0, 8);
+  } else {
+    const float dn = s * g;
+    for (j = 0; j < 8; ++j) {
+      unsigned lo = oracle_e2m1_encode(w[2 * j] / dn);
+      unsigned hi = oracle_e2m1_encode(w[2 * j + 1] / dn);
+      c[j] = (uint8_t)(lo | (hi << 4));
+    }
+  }
+}
+
 int oracle_pack(const float* W, int64_t N, int64_t K, uint8_t* codes,
                 uint8_t* scales, float* gscale_out, const float* gscale_override) {
   int64_t i, n;
@@ -128,36 +158,9 @@ int oracle_pack(const float* W, int64_t N, int64_t K, uint8_t* codes,
 #pragma omp parallel for schedule(static)
   for (n = 0; n < N; ++n) {
     const int64_t nb = K / 16;
-    const float d6 = 6.0f * g;
     int64_t b;
-    for (b = 0; b < nb; ++b) {
-      const float* w = W + n * K + b * 16;
-      uint8_t* c = codes + n * (K / 2) + b * 8;
-      float ab = 0.0f, r, s;
-      unsigned sc;
-      int j;
-      /* Step 2: block amax relative to 6 * g. */
-      for (j = 0; j < 16; ++j) {
-        float a = fabsf(w[j]);
-        if (a > ab) ab = a;
-      }
-      r = ab / d6;
-      /* Step 3: the block scale byte and its value. */
-      sc = oracle_e4m3_encode(r);
-      scales[n * nb + b] = (uint8_t)sc;
-      s = (float)oracle_e4m3_value(sc);
-      /* Step 4: element codes relative to s * g. */
-      if (s == 0.0f) {
-        memset(c, 0, 8);
-      } else {
-        const float dn = s * g;
-        for (j = 0; j < 8; ++j) {
-          unsigned lo = oracle_e2m1_encode(w[2 * j] / dn);
-          unsigned hi = oracle_e2m1_encode(w[2 * j + 1] / dn);
-          c[j] = (uint8_t)(lo | (hi << 4));
-        }
-      }
-    }
+    for (b = 0; b < nb; ++b)
+      quantize_block(W + n * K + b * 16, g, codes + n * (K / 2) + b * 8, scales + n * nb + b);
   }
   return ORACLE_OK;
 }
@@ -377,6 +380,60 @@ int oracle_moe_shared(const uint8_t* w13_codes, const uint8_t* w13_scales, const
                    (double)ws2_g[0], xv, H, Is, y + m * H, bound ? bound + m * H : NULL,
                    hs_out ? hs_out + m * Is : NULL);
     free(xv);
+  }
+  return ORACLE_OK;
+}
+
+/* ------------------------------------------------------------------ w4a4 */
+
+int oracle_quantize_act(const uint16_t* x, int64_t M, int64_t K, float g_x, uint8_t* codes,
+                        uint8_t* scales) {
+  int64_t m;
+  if (M < 0 || K < 0 || (K % 16) != 0) return ORACLE_ERR_SHAPE;
+  if (!(g_x > 0.0f) || !isfinite(g_x)) return ORACLE_ERR_GSCALE;
+  for (m = 0; m < M * K; ++m)
+    if (!isfinite(bf16_value(x[m]))) return ORACLE_ERR_NONFINITE;
+  for (m = 0; m < M; ++m) {
+    int64_t b;
+    for (b = 0; b < K / 16; ++b) {
+      float w[16];
+      int j;
+      for (j = 0; j < 16; ++j) w[j] = (float)bf16_value(x[m * K + b * 16 + j]);  /* exact */
+      quantize_block(w, g_x, codes + m * (K / 2) + b * 8, scales + m * (K / 16) + b);
+    }
+  }
+  return ORACLE_OK;
+}
+
+int oracle_gemv_w4a4(const uint8_t* codes_w, const uint8_t* scales_w, float g_w,
+                     const uint8_t* codes_x, const uint8_t* scales_x, float g_x,
+                     int64_t M, int64_t N, int64_t K, const int64_t* rows, int64_t n_rows,
+                     double* y, double* absdot) {
+  const int64_t cnt = rows ? n_rows : N;
+  int64_t i;
+  if (M < 0 || N < 0 || K < 0 || (K % 16) != 0) return ORACLE_ERR_SHAPE;
+  if (rows) {
+    for (i = 0; i < n_rows; ++i)
+      if (rows[i] < 0 || rows[i] >= N) return ORACLE_ERR_SHAPE;
+  }
+#pragma omp parallel for schedule(dynamic, 16)
+  for (i = 0; i < cnt; ++i) {
+    const int64_t n = rows ? rows[i] : i;
+    int64_t m, k;
+    for (m = 0; m < M; ++m) {
+      double sum = 0.0, asum = 0.0;
+      for (k = 0; k < K; ++k) {
+        double w = oracle_e2m1_value(code_at(codes_w, K, n, k)) *
+                   oracle_e4m3_value(scales_w[n * (K / 16) + k / 16]);
+        double v = oracle_e2m1_value(code_at(codes_x, K, m, k)) *
+                   oracle_e4m3_value(scales_x[m * (K / 16) + k / 16]);
+        double t = w * v;   /* exact in fp64 */
+        sum += t;
+        asum += fabs(t);
+      }
+      y[m * cnt + i] = (double)g_w * (double)g_x * sum;
+      if (absdot) absdot[m * cnt + i] = fabs((double)g_w * (double)g_x) * asum;
+    }
   }
   return ORACLE_OK;
 }

@@ -107,6 +107,22 @@ int oracle_moe_shared(const uint8_t* w13_codes, const uint8_t* w13_scales, const
                       const uint8_t* ws2_codes, const uint8_t* ws2_scales, const float* ws2_g,
                       int64_t Is, double* y, double* bound, uint16_t* h_out, uint16_t* hs_out);
 
+/* W4A4 (card.json "W4A4 NVFP4 x NVFP4 (static input scale)"; graph.json node
+   "l0.mlp.xn_quant", op act_quant, bf16 -> nvfp4/g16, step "compute f32").
+   oracle_quantize_act: each row of bf16 x[M, K] is quantized to NVFP4 g16
+   like a weight row, with the given static tensor scale g_x in place of
+   max|x| / 2688 (steps 2-4 of oracle_pack on the exact fp32 values of x).
+   Codes [M, K/2], scales [M, K/16].
+   oracle_gemv_w4a4: y[m, n] = g_w * g_x * sum_k (e2m1_w * s_w) * (e2m1_x * s_x)
+   in fp64 (every product exact); absdot the same with |.|; rows as in
+   oracle_gemv. */
+int oracle_quantize_act(const uint16_t* x, int64_t M, int64_t K, float g_x, uint8_t* codes,
+                        uint8_t* scales);
+int oracle_gemv_w4a4(const uint8_t* codes_w, const uint8_t* scales_w, float g_w,
+                     const uint8_t* codes_x, const uint8_t* scales_x, float g_x,
+                     int64_t M, int64_t N, int64_t K, const int64_t* rows, int64_t n_rows,
+                     double* y, double* absdot);
+
 /* Round a double to the nearest bf16 (ties to even), returning its bits. */
 uint16_t oracle_bf16_from_double(double v);
 

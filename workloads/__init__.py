@@ -159,6 +159,11 @@ WORKLOADS = {
             topk=8, Ms=(1, 8), dist="normal"),
     5: dict(name="stress_m8_t3", M=8, mats=[("a", 12288, 4096), ("b", 4096, 12288)],
             dist="student_t"),
+    # the pages' W4A4 dense FFN (card.json performance[20], [24]: "dense FFN
+    # gate/up/down M=2 N=4096 K=4096", NVFP4 x NVFP4 with a static input scale)
+    6: dict(name="w4a4_ffn_m2", M=2,
+            mats=[("gate", 4096, 4096), ("up", 4096, 4096), ("down", 4096, 4096)],
+            dist="normal"),
 }
 
 
