@@ -9,6 +9,8 @@ Secondary legs, measured the same way and reported in the same JSON line:
           weights with 1% zero blocks), one step = both calls;
   layer - the dense decode layer at M=5 (q, k, v, o, gate, up, down), one
           step = the seven calls;
+  w4a4  - the pages' W4A4 dense FFN at M=2 (gate, up, down 4096x4096): one
+          step = quantizing x with a static input scale and the three calls;
   moe   - the 288-expert MoE expert-slot pass at M=8 (and M=1), top-8, and
           the same pass with the pages' shared expert (768 wide) fused in;
   copy  - a plain fp32 copy kernel of 2 x 512 MiB per launch: the measured
@@ -254,6 +256,48 @@ def leg_layer(torch, nv, workloads, traffic, steps, warmup):
                       "gbs_kernel": Bf / (ktf * 1e-3) / 1e9,
                       "frac_of_peak": Bf / (ktf * 1e-3) / 1e9 / HBM_PEAK_GBS,
                       "tokens_per_s": M / (msf * 1e-3)}}
+
+
+def leg_w4a4(torch, nv, workloads, traffic, steps, warmup):
+    """The pages' W4A4 dense FFN (gate, up, down 4096x4096 at M=2): one step =
+    quantizing the activations with a static input scale and the three W4A4
+    GEMVs on them."""
+    wl = workloads.WORKLOADS[6]
+    M = wl["M"]
+    mats = []
+    for i, (name, N, K) in enumerate(wl["mats"]):
+        log(f"[bench] w4a4: packing {name} {N}x{K}")
+        W = torch.from_numpy(workloads.dense_weights(6, 0, i, N, K)).cuda()
+        mats.append((nv.pack(W), N, K))
+        del W
+    K = wl["mats"][0][2]
+    wb = sum(traffic.weight_bytes(N, K) for _, N, K in mats)
+    reps = max(2, (1 << 30) // wb + 1)
+    copies = [mats] + [[(tuple(t.clone() for t in p), N, K) for p, N, K in mats]
+                       for _ in range(reps - 1)]
+    x = torch.from_numpy(workloads.x_bf16(6, 0, 0, M, K).view(np.int16)).cuda().view(
+        torch.bfloat16)
+    calib = workloads.x_bf16(6, 1, 0, M, K)
+    gx = torch.tensor([np.abs(((calib.astype(np.uint32) << 16).view(np.float32))).max()
+                       / 2688.0], dtype=torch.float32, device="cuda")
+    cx, sx = nv.quantize_act(x, gx)
+    ws = torch.empty(nv.gemv_w4a4_workspace_bytes(M, K), dtype=torch.uint8, device="cuda")
+    ys = [torch.empty((M, N), dtype=torch.float32, device="cuda") for _, N, _ in mats]
+
+    def step(i):
+        nv.quantize_act_into(x, gx, cx, sx)
+        for ((c, s, g), N, K), y in zip(copies[i % reps], ys):
+            nv.gemv_w4a4_into(c, s, g, cx, sx, gx, y, ws)
+
+    ms, kms = timed_steps(torch, step, steps, warmup)
+    B = traffic.quantize_act_bytes(M, K) + sum(traffic.gemv_w4a4_bytes(M, N, K)
+                                               for _, N, K in mats)
+    return {"workload": "w4a4_ffn_m2 (gate, up, down 4096x4096; static input scale)", "M": M,
+            "launches_per_step": 1 + 2 * len(mats), "bytes_per_step": B, "ms_per_step": ms,
+            "step_us_events": kms * 1e3, "gbs_wall": B / (ms * 1e-3) / 1e9,
+            "gbs_kernel": B / (kms * 1e-3) / 1e9,
+            "frac_of_peak": B / (kms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+            "tokens_per_s": M / (ms * 1e-3), "rotate_copies": reps}
 
 
 def gpu_clock_state():
@@ -526,8 +570,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--legs", default="lm_head,m8,layer,moe,copy",
-                    help="comma list of lm_head, m8, layer, moe, copy (lm_head is the "
+    ap.add_argument("--legs", default="lm_head,m8,layer,w4a4,moe,copy",
+                    help="comma list of lm_head, m8, layer, w4a4, moe, copy (lm_head is the "
                          "headline; copy is a plain copy kernel: the byte-counter "
                          "calibration and the measured-bandwidth reference)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -600,13 +644,15 @@ def main():
         result["m8"] = leg_m8(torch, nv, workloads, traffic, args.steps, args.warmup)
     if "layer" in legs:
         result["layer_m5"] = leg_layer(torch, nv, workloads, traffic, args.steps, args.warmup)
+    if "w4a4" in legs:
+        result["w4a4_ffn_m2"] = leg_w4a4(torch, nv, workloads, traffic, args.steps, args.warmup)
     if "copy" in legs:
         cp = leg_copy(torch, min(args.steps, 50), min(args.warmup, 5))
         result["copy_calibration"] = cp
         # fractions of the measured copy bandwidth (read + write bytes per second)
         if result.get("roofline"):
             result["roofline"]["frac_of_measured_copy"] = result["roofline"]["achieved"] / cp["gbs"]
-        for k in ("m8", "layer_m5"):
+        for k in ("m8", "layer_m5", "w4a4_ffn_m2"):
             if k in result:
                 result[k]["frac_of_measured_copy"] = result[k]["gbs_kernel"] / cp["gbs"]
     if "moe" in legs:

@@ -55,7 +55,7 @@
 extern "C" {
 #endif
 
-#define NVFP4_ABI_VERSION 3
+#define NVFP4_ABI_VERSION 4
 
 /* Largest number of activation rows (tokens) one GEMV / MoE call takes. */
 #define NVFP4_MAX_M 8
@@ -228,6 +228,52 @@ nvfp4_status nvfp4_moe_gemv(const uint8_t* w13_codes, const uint8_t* w13_scales,
                             const float* gate_w, int64_t M, int64_t E, int64_t H,
                             int64_t I, int64_t topk, float* y, void* workspace,
                             size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * nvfp4_quantize_act -- NVFP4 activations with a static input scale (card.json
+ * "W4A4 NVFP4 x NVFP4 (static input scale)"; graph.json node
+ * "l0.mlp.xn_quant", op act_quant, bf16 -> nvfp4/g16). Each row of x is
+ * quantized like a weight row by nvfp4_pack, with *gscale_x in place of
+ * max|x| / 2688:
+ *   s = E4M3(amax_block / (6 g_x)),  code = E2M1(x / (s g_x))   (IEEE fp32)
+ *
+ *   x         bf16[M, K] (uint16 bits), 16-byte aligned, finite;
+ *   gscale_x  float[1], > 0 (the static input scale), 4-byte aligned;
+ *   codes_x   uint8[M, K/2] out, 8-byte aligned; scales_x uint8[M, K/16] out;
+ *   K % 32 == 0.
+ * Errors: NULL, SHAPE, ALIGN, ALIAS, HIP.
+ */
+nvfp4_status nvfp4_quantize_act(const uint16_t* x, int64_t M, int64_t K, const float* gscale_x,
+                                uint8_t* codes_x, uint8_t* scales_x, hipStream_t stream);
+
+/*
+ * nvfp4_gemv_w4a4_workspace_bytes -- device workspace of nvfp4_gemv_w4a4: the
+ * decoded activations (bf16[M, K]) and one float, 256-byte aligned.
+ */
+size_t nvfp4_gemv_w4a4_workspace_bytes(int64_t M, int64_t K);
+
+/*
+ * nvfp4_gemv_w4a4 -- y[M, N] (fp32) = g_w * g_x * decode(W) . decode(x)^T, both
+ * operands NVFP4 g16 (card.json performance[20], [24]: the W4A4 dense FFN).
+ * The activation values e2m1_x * s_x are exact in bf16; they are decoded once
+ * into the workspace and multiplied by the weight stream as in nvfp4_gemv,
+ * with g_w * g_x (rounded once to fp32) applied to the fp32 sum.
+ *
+ *   codes_w, scales_w, gscale_w  the weight, as in nvfp4_gemv;
+ *   codes_x   uint8[M, K/2], 16-byte aligned; scales_x uint8[M, K/16], 2-byte
+ *             aligned; gscale_x float[1] (from nvfp4_quantize_act);
+ *   M         0 <= M <= NVFP4_MAX_M; K % 32 == 0;
+ *   y         float[M, N] out;
+ *   workspace at least nvfp4_gemv_w4a4_workspace_bytes(M, K) bytes,
+ *             256-byte aligned; overwritten; must not be shared by calls that
+ *             may run concurrently.
+ * Errors: NULL, SHAPE, ALIGN, UNSUPPORTED, WORKSPACE, ALIAS, HIP.
+ */
+nvfp4_status nvfp4_gemv_w4a4(const uint8_t* codes_w, const uint8_t* scales_w,
+                             const float* gscale_w, const uint8_t* codes_x,
+                             const uint8_t* scales_x, const float* gscale_x, int64_t M,
+                             int64_t N, int64_t K, float* y, void* workspace,
+                             size_t workspace_bytes, hipStream_t stream);
 
 /*
  * nvfp4_moe_shared -- the shared expert of a MoE layer: a dense SwiGLU FFN

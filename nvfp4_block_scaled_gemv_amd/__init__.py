@@ -11,6 +11,8 @@ Functions (same names as the C entry points, without the prefix):
   dequant(codes, scales, gscale)         -> W_hat (fp32)
   gemv(codes, scales, gscale, x)         -> y (fp32 [M, N])
   gemv_segments([(codes, scales, gscale), ...], x) -> [y_s] (one launch)
+  quantize_act(x, gscale_x)              -> codes_x, scales_x (static input scale)
+  gemv_w4a4(codes, scales, gscale, codes_x, scales_x, gscale_x) -> y (fp32)
   moe_workspace_bytes(M, H, I, topk)     -> int
   moe_gemv(w13..., w2..., x, ids, gate_w[, workspace]) -> y (fp32 [M, H])
   moe_shared_workspace_bytes(M, H, I, topk, I_shared) -> int
@@ -85,6 +87,12 @@ def lib() -> ctypes.CDLL:
         L.nvfp4_gemv_segments.restype = ctypes.c_int
         L.nvfp4_gemv_segments.argtypes = [ctypes.POINTER(GemvSegment), _I64, _VP, _I64, _I64,
                                           _VP]
+        L.nvfp4_quantize_act.restype = ctypes.c_int
+        L.nvfp4_quantize_act.argtypes = [_VP, _I64, _I64, _VP, _VP, _VP, _VP]
+        L.nvfp4_gemv_w4a4_workspace_bytes.restype = ctypes.c_size_t
+        L.nvfp4_gemv_w4a4_workspace_bytes.argtypes = [_I64, _I64]
+        L.nvfp4_gemv_w4a4.restype = ctypes.c_int
+        L.nvfp4_gemv_w4a4.argtypes = [_VP] * 6 + [_I64] * 3 + [_VP, _VP, ctypes.c_size_t, _VP]
         L.nvfp4_moe_workspace_bytes.restype = ctypes.c_size_t
         L.nvfp4_moe_workspace_bytes.argtypes = [_I64, _I64, _I64, _I64]
         L.nvfp4_moe_gemv.restype = ctypes.c_int
@@ -222,6 +230,58 @@ def gemv_segments(mats, x):
           for c, _, _ in mats]
     gemv_segments_into(mats, x, ys)
     return ys
+
+
+# ------------------------------------------------------------------ w4a4
+
+def quantize_act_into(x, gscale_x, codes_x, scales_x) -> None:
+    """bf16 x[M, K] -> NVFP4 codes_x u8[M, K/2], scales_x u8[M, K/16] with the
+    static input scale gscale_x (fp32 [1])."""
+    _dev(x, gscale_x, codes_x, scales_x)
+    _dtype(x, torch.bfloat16, torch.int16, torch.uint16, name="x")
+    M, K = x.shape
+    if tuple(codes_x.shape) != (M, K // 2) or tuple(scales_x.shape) != (M, K // 16):
+        raise ValueError("codes_x / scales_x have the wrong shape")
+    _check("nvfp4_quantize_act", lib().nvfp4_quantize_act(
+        _p(x), M, K, _p(gscale_x), _p(codes_x), _p(scales_x), _stream(x)))
+
+
+def quantize_act(x, gscale_x):
+    M, K = x.shape
+    codes_x = torch.empty((M, K // 2), dtype=torch.uint8, device=x.device)
+    scales_x = torch.empty((M, K // 16), dtype=torch.uint8, device=x.device)
+    quantize_act_into(x, gscale_x, codes_x, scales_x)
+    return codes_x, scales_x
+
+
+def gemv_w4a4_workspace_bytes(M: int, K: int) -> int:
+    return int(lib().nvfp4_gemv_w4a4_workspace_bytes(M, K))
+
+
+def gemv_w4a4_into(codes, scales, gscale, codes_x, scales_x, gscale_x, y, workspace) -> None:
+    """y[M, N] (fp32) = g_w g_x decode(W) . decode(x)^T, both NVFP4 g16."""
+    _dev(codes, scales, gscale, codes_x, scales_x, gscale_x, y, workspace)
+    _dtype(y, torch.float32, name="y")
+    N, K = codes.shape[0], codes.shape[1] * 2
+    M = codes_x.shape[0]
+    if codes_x.shape[1] * 2 != K or tuple(scales_x.shape) != (M, K // 16) \
+            or tuple(y.shape) != (M, N):
+        raise ValueError(f"shape mismatch: codes {tuple(codes.shape)}, codes_x "
+                         f"{tuple(codes_x.shape)}, y {tuple(y.shape)}")
+    _check("nvfp4_gemv_w4a4", lib().nvfp4_gemv_w4a4(
+        _p(codes), _p(scales), _p(gscale), _p(codes_x), _p(scales_x), _p(gscale_x), M, N, K,
+        _p(y), _p(workspace), workspace.numel() * workspace.element_size(), _stream(codes)))
+
+
+def gemv_w4a4(codes, scales, gscale, codes_x, scales_x, gscale_x,
+              workspace: torch.Tensor | None = None) -> torch.Tensor:
+    M, K = codes_x.shape[0], codes_x.shape[1] * 2
+    if workspace is None:
+        workspace = torch.empty(max(gemv_w4a4_workspace_bytes(M, K), 256), dtype=torch.uint8,
+                                device=codes.device)
+    y = torch.empty((M, codes.shape[0]), dtype=torch.float32, device=codes.device)
+    gemv_w4a4_into(codes, scales, gscale, codes_x, scales_x, gscale_x, y, workspace)
+    return y
 
 
 # ------------------------------------------------------------------- moe

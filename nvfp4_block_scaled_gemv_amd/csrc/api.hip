@@ -198,6 +198,78 @@ nvfp4_status nvfp4_gemv_segments(const nvfp4_gemv_segment* segs, int64_t n_segme
                     "nvfp4_gemv_segments launch");
 }
 
+nvfp4_status nvfp4_quantize_act(const uint16_t* x, int64_t M, int64_t K, const float* gscale_x,
+                                uint8_t* codes_x, uint8_t* scales_x, hipStream_t stream) {
+  clear_error();
+  if (M < 0 || K < 0 || (K % 32) != 0)
+    return fail(NVFP4_ERR_SHAPE,
+                "nvfp4_quantize_act: need M, K >= 0 and K %% 32 == 0 (M=%lld K=%lld)",
+                (long long)M, (long long)K);
+  const size_t numel = (size_t)M * (size_t)K;
+  if (numel == 0) return NVFP4_OK;
+  if (!x || !gscale_x || !codes_x || !scales_x)
+    return fail(NVFP4_ERR_NULL, "nvfp4_quantize_act: NULL pointer");
+  if (!aligned(x, 16) || !aligned(codes_x, 8) || !aligned(gscale_x, 4))
+    return fail(NVFP4_ERR_ALIGN,
+                "nvfp4_quantize_act: x must be 16-byte, codes 8-byte, gscale_x 4-byte aligned");
+  const size_t xb = numel * 2, cb = numel / 2, sb = numel / 16;
+  if (overlap(codes_x, cb, x, xb) || overlap(scales_x, sb, x, xb) ||
+      overlap(codes_x, cb, gscale_x, 4) || overlap(scales_x, sb, gscale_x, 4) ||
+      overlap(codes_x, cb, scales_x, sb))
+    return fail(NVFP4_ERR_ALIAS, "nvfp4_quantize_act: outputs overlap each other or an input");
+  return hip_result(nvfp4::launch_quantize_act(x, M, K, gscale_x, codes_x, scales_x, stream),
+                    "nvfp4_quantize_act launch");
+}
+
+size_t nvfp4_gemv_w4a4_workspace_bytes(int64_t M, int64_t K) {
+  if (M < 0 || K < 0) return 0;
+  return nvfp4::w4a4_layout(M, K).total;
+}
+
+nvfp4_status nvfp4_gemv_w4a4(const uint8_t* codes_w, const uint8_t* scales_w,
+                             const float* gscale_w, const uint8_t* codes_x,
+                             const uint8_t* scales_x, const float* gscale_x, int64_t M,
+                             int64_t N, int64_t K, float* y, void* workspace,
+                             size_t workspace_bytes, hipStream_t stream) {
+  clear_error();
+  if (M < 0 || N < 0 || K < 0 || (K % 32) != 0)
+    return fail(NVFP4_ERR_SHAPE,
+                "nvfp4_gemv_w4a4: need M, N, K >= 0 and K %% 32 == 0 (M=%lld N=%lld K=%lld)",
+                (long long)M, (long long)N, (long long)K);
+  if (M > NVFP4_MAX_M)
+    return fail(NVFP4_ERR_UNSUPPORTED, "nvfp4_gemv_w4a4: M=%lld exceeds %d", (long long)M,
+                NVFP4_MAX_M);
+  if (M == 0 || N == 0) return NVFP4_OK;
+  if (!y) return fail(NVFP4_ERR_NULL, "nvfp4_gemv_w4a4: y is NULL");
+  if (!aligned(y, 4)) return fail(NVFP4_ERR_ALIGN, "nvfp4_gemv_w4a4: y must be 4-byte aligned");
+  const size_t yb = (size_t)M * (size_t)N * 4;
+  if (K == 0) return hip_result(nvfp4::launch_fill_zero(y, (size_t)M * (size_t)N, stream),
+                                "nvfp4_gemv_w4a4 zero fill");
+  if (!codes_w || !scales_w || !gscale_w || !codes_x || !scales_x || !gscale_x)
+    return fail(NVFP4_ERR_NULL, "nvfp4_gemv_w4a4: NULL input");
+  const size_t need = nvfp4::w4a4_layout(M, K).total;
+  if (!workspace || workspace_bytes < need)
+    return fail(NVFP4_ERR_WORKSPACE, "nvfp4_gemv_w4a4: workspace of %zu bytes needed, %zu given",
+                need, workspace ? workspace_bytes : (size_t)0);
+  if (!aligned(codes_w, 16) || !aligned(scales_w, 2) || !aligned(gscale_w, 4) ||
+      !aligned(codes_x, 16) || !aligned(scales_x, 2) || !aligned(gscale_x, 4) ||
+      !aligned(workspace, 256))
+    return fail(NVFP4_ERR_ALIGN,
+                "nvfp4_gemv_w4a4: codes 16-byte, scales 2-byte, scales of the tensors 4-byte, "
+                "workspace 256-byte aligned");
+  const size_t nk = (size_t)N * (size_t)K, mk = (size_t)M * (size_t)K;
+  const void* ins[] = {codes_w, scales_w, gscale_w, codes_x, scales_x, gscale_x};
+  const size_t insz[] = {nk / 2, nk / 16, 4, mk / 2, mk / 16, 4};
+  for (int i = 0; i < 6; ++i)
+    if (overlap(y, yb, ins[i], insz[i]) || overlap(workspace, need, ins[i], insz[i]))
+      return fail(NVFP4_ERR_ALIAS, "nvfp4_gemv_w4a4: y or workspace overlaps input %d", i);
+  if (overlap(y, yb, workspace, need))
+    return fail(NVFP4_ERR_ALIAS, "nvfp4_gemv_w4a4: y overlaps the workspace");
+  return hip_result(nvfp4::launch_gemv_w4a4(codes_w, scales_w, gscale_w, codes_x, scales_x,
+                                            gscale_x, (int)M, N, K, y, workspace, stream),
+                    "nvfp4_gemv_w4a4 launch");
+}
+
 size_t nvfp4_moe_workspace_bytes(int64_t M, int64_t H, int64_t I, int64_t topk) {
   if (M < 0 || H < 0 || I < 0 || topk < 0) return 0;
   return nvfp4::moe_layout(M, H, I, topk, 0).total;

@@ -97,6 +97,30 @@ __device__ __forceinline__ uint32_t e2m1_encode(float t) {
   return (t < 0.0f && mag != 0u) ? (mag | 8u) : mag;
 }
 
+// One 16-element block with tensor scale g: s = E4M3(amax / (6 g)), then
+// codes E2M1(w / (s g)) (all-zero codes when s is 0). Returns the scale byte;
+// lo holds elements 0..7 and hi elements 8..15, element i in nibble i % 8.
+__device__ __forceinline__ uint32_t encode_block16(const float (&w)[16], float g,
+                                                   uint32_t& lo, uint32_t& hi) {
+  float ab = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) ab = fmaxf(ab, fabsf(w[i]));
+  const float d6 = 6.0f * g;
+  const float r = ab / d6;
+  const uint32_t sc = e4m3_encode(r);
+  const float s = e4m3_to_f32<0>(sc);
+  lo = 0u;
+  hi = 0u;
+  if (s != 0.0f) {
+    const float dn = s * g;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) lo |= e2m1_encode(w[i] / dn) << (4 * i);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) hi |= e2m1_encode(w[8 + i] / dn) << (4 * i);
+  }
+  return sc;
+}
+
 // --------------------------------------------------------------- reductions
 
 // Sum over the 64 lanes of a wavefront; every lane receives the total.

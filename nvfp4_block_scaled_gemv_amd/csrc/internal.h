@@ -40,6 +40,22 @@ hipError_t launch_gemv_splitk_shape(const SegDesc* d, int n, const uint16_t* x, 
                                     int64_t K, int KS, int XS, int D, int64_t grid,
                                     hipStream_t stream);
 
+// W4A4: activation quantization with a static input scale, and the GEMV on
+// quantized activations (workspace: the exact bf16 activations, then the
+// product of the two tensor scales).
+struct W4a4Layout {
+  size_t x_off;   // uint16 bf16 x~[M, K]
+  size_t g_off;   // float g_w * g_x
+  size_t total;   // rounded up to 256 bytes
+};
+W4a4Layout w4a4_layout(int64_t M, int64_t K);
+hipError_t launch_quantize_act(const uint16_t* x, int64_t M, int64_t K, const float* gscale_x,
+                               uint8_t* codes, uint8_t* scales, hipStream_t stream);
+hipError_t launch_gemv_w4a4(const uint8_t* codes_w, const uint8_t* scales_w,
+                            const float* gscale_w, const uint8_t* codes_x,
+                            const uint8_t* scales_x, const float* gscale_x, int M, int64_t N,
+                            int64_t K, float* y, void* workspace, hipStream_t stream);
+
 hipError_t launch_fill_zero(float* y, size_t n, hipStream_t stream);
 
 // MoE workspace layout (byte offsets from the workspace base).

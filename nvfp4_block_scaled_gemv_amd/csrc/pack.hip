@@ -65,22 +65,8 @@ __global__ __launch_bounds__(256) void k_quantize(const float* __restrict__ W,
     const float4 v = wp[i];
     w[4 * i] = v.x; w[4 * i + 1] = v.y; w[4 * i + 2] = v.z; w[4 * i + 3] = v.w;
   }
-  const float g = *gscale;
-  float ab = 0.0f;
-#pragma unroll
-  for (int i = 0; i < 16; ++i) ab = fmaxf(ab, fabsf(w[i]));
-  const float d6 = 6.0f * g;
-  const float r = ab / d6;
-  const uint32_t sc = e4m3_encode(r);
-  const float s = e4m3_to_f32<0>(sc);
-  uint32_t lo = 0u, hi = 0u;
-  if (s != 0.0f) {
-    const float dn = s * g;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) lo |= e2m1_encode(w[i] / dn) << (4 * i);
-#pragma unroll
-    for (int i = 0; i < 8; ++i) hi |= e2m1_encode(w[8 + i] / dn) << (4 * i);
-  }
+  uint32_t lo, hi;
+  const uint32_t sc = encode_block16(w, *gscale, lo, hi);
   *reinterpret_cast<uint2*>(codes + b * 8) = make_uint2(lo, hi);
   scales[b] = (uint8_t)sc;
 }

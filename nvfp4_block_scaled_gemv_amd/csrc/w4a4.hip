@@ -1,0 +1,111 @@
+// w4a4.hip -- NVFP4 activations (W4A4) on gfx950.
+//
+// The pages' W4A4 path (card.json "W4A4 NVFP4 x NVFP4 (static input scale)",
+// performance[20] and [24]; graph.json node "l0.mlp.xn_quant", op act_quant,
+// bf16 -> nvfp4/g16):
+//   k_quantize_act: each row of bf16 x[M, K] is quantized like a weight row,
+//     with the caller's static tensor scale g_x: s = E4M3(amax / (6 g_x)),
+//     code = E2M1(x / (s g_x)), in IEEE fp32 (the same block encoder as pack).
+//   nvfp4_gemv_w4a4: y = g_w g_x sum_k (e2m1_w s_w)(e2m1_x s_x). The
+//     activation values e2m1_x s_x have at most 6 significant bits and lie in
+//     [2^-10, 2688], so they are exact in bf16: k_w4a4_prep writes them to the
+//     workspace as bf16 together with the product scale g_w g_x (one fp32
+//     rounding), and the W4A16 GEMV kernels do the rest (M <= 2 on the vector
+//     ALUs, M >= 3 on the matrix cores). x is at most 8 x K values, so the
+//     extra pass moves kilobytes next to the weight stream.
+#include "device.h"
+#include "internal.h"
+
+namespace nvfp4 {
+
+static inline size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
+
+W4a4Layout w4a4_layout(int64_t M, int64_t K) {
+  W4a4Layout L;
+  L.x_off = 0;
+  L.g_off = align256((size_t)M * (size_t)K * sizeof(uint16_t));
+  L.total = align256(L.g_off + sizeof(float));
+  return L;
+}
+
+// One thread per 16-element block of x.
+__global__ __launch_bounds__(256) void k_quantize_act(const uint16_t* __restrict__ x,
+                                                      size_t nblocks,
+                                                      const float* __restrict__ gscale_x,
+                                                      uint8_t* __restrict__ codes,
+                                                      uint8_t* __restrict__ scales) {
+  const size_t b = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (b >= nblocks) return;
+  const uint4* xp = reinterpret_cast<const uint4*>(x + b * 16);
+  const uint4 v0 = xp[0], v1 = xp[1];
+  const uint32_t u[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+  float w[16];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {   // bf16 -> fp32 is exact
+    w[2 * i] = __uint_as_float(u[i] << 16);
+    w[2 * i + 1] = __uint_as_float(u[i] & 0xFFFF0000u);
+  }
+  uint32_t lo, hi;
+  const uint32_t sc = encode_block16(w, *gscale_x, lo, hi);
+  *reinterpret_cast<uint2*>(codes + b * 8) = make_uint2(lo, hi);
+  scales[b] = (uint8_t)sc;
+}
+
+// One thread per 32 activation elements (16 code bytes, two blocks): the
+// exact bf16 values e2m1 * s; thread 0 also writes g_w * g_x.
+__global__ __launch_bounds__(256) void k_w4a4_prep(const uint8_t* __restrict__ codes_x,
+                                                   const uint8_t* __restrict__ scales_x,
+                                                   size_t nchunks, const float* __restrict__ g_w,
+                                                   const float* __restrict__ g_x,
+                                                   uint16_t* __restrict__ xt,
+                                                   float* __restrict__ g_prod) {
+  const size_t c = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (c == 0) *g_prod = *g_w * *g_x;
+  if (c >= nchunks) return;
+  const uint4 q = *reinterpret_cast<const uint4*>(codes_x + c * 16);
+  const uint32_t sw = (uint32_t)scales_x[2 * c] | ((uint32_t)scales_x[2 * c + 1] << 8);
+  const float s0 = e4m3_to_f32<0>(sw), s1 = e4m3_to_f32<1>(sw);
+  const uint32_t words[4] = {q.x, q.y, q.z, q.w};
+  uint4* o = reinterpret_cast<uint4*>(xt + c * 32);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float s = (i < 2) ? s0 : s1;
+    uint32_t out[4];
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      const float2_t v = p == 0 ? e2m1x2_to_f32<0>(words[i]) : p == 1 ? e2m1x2_to_f32<1>(words[i])
+                       : p == 2 ? e2m1x2_to_f32<2>(words[i]) : e2m1x2_to_f32<3>(words[i]);
+      // e2m1 * s is exact in fp32 and has at most 6 significant bits: its
+      // upper 16 bits are the exact bf16
+      out[p] = (__float_as_uint(v.x * s) >> 16) | (__float_as_uint(v.y * s) & 0xFFFF0000u);
+    }
+    o[i] = make_uint4(out[0], out[1], out[2], out[3]);
+  }
+}
+
+hipError_t launch_quantize_act(const uint16_t* x, int64_t M, int64_t K, const float* gscale_x,
+                               uint8_t* codes, uint8_t* scales, hipStream_t stream) {
+  const size_t nblocks = (size_t)M * (size_t)K / 16;
+  if (nblocks)
+    hipLaunchKernelGGL(k_quantize_act, dim3((unsigned)((nblocks + 255) / 256)), dim3(256), 0,
+                       stream, x, nblocks, gscale_x, codes, scales);
+  return hipGetLastError();
+}
+
+hipError_t launch_gemv_w4a4(const uint8_t* codes_w, const uint8_t* scales_w,
+                            const float* gscale_w, const uint8_t* codes_x,
+                            const uint8_t* scales_x, const float* gscale_x, int M, int64_t N,
+                            int64_t K, float* y, void* workspace, hipStream_t stream) {
+  const W4a4Layout L = w4a4_layout(M, K);
+  uint16_t* xt = reinterpret_cast<uint16_t*>(static_cast<char*>(workspace) + L.x_off);
+  float* gp = reinterpret_cast<float*>(static_cast<char*>(workspace) + L.g_off);
+  const size_t nchunks = (size_t)M * (size_t)K / 32;
+  hipLaunchKernelGGL(k_w4a4_prep, dim3((unsigned)((nchunks + 255) / 256 + (nchunks ? 0 : 1))),
+                     dim3(256), 0, stream, codes_x, scales_x, nchunks, gscale_w, gscale_x, xt,
+                     gp);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  return launch_gemv(codes_w, scales_w, gp, xt, M, N, K, y, stream);
+}
+
+}  // namespace nvfp4

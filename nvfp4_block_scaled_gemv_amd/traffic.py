@@ -19,6 +19,18 @@ def weight_bytes(N: int, K: int) -> int:
     return N * K // 2 + N * K // 16
 
 
+def quantize_act_bytes(M: int, K: int) -> int:
+    """Activation quantization: read bf16 x, write its codes and scales (the
+    static scale is 4 bytes)."""
+    return M * K * 2 + 4 + M * K // 2 + M * K // 16
+
+
+def gemv_w4a4_bytes(M: int, N: int, K: int) -> int:
+    """One W4A4 GEMV: the weight (codes, scales, g) and the NVFP4 activation
+    (codes, scales, g) read once, fp32 y written."""
+    return weight_bytes(N, K) + 4 + M * K // 2 + M * K // 16 + 4 + M * N * 4
+
+
 def moe_bytes(M: int, H: int, I: int, topk: int, distinct: int) -> int:
     """One MoE call: every distinct expert's gate|up [2I, H] and down [H, I]
     weights plus its two tensor scales, x, ids and gate weights, the bf16

@@ -31,14 +31,15 @@ def test_exports_every_declared_symbol(L):
     names = declared_functions()
     assert {"nvfp4_pack", "nvfp4_dequant", "nvfp4_gemv", "nvfp4_gemv_segments", "nvfp4_moe_gemv",
             "nvfp4_moe_workspace_bytes", "nvfp4_moe_shared_gemv",
-            "nvfp4_moe_shared_workspace_bytes", "nvfp4_abi_version", "nvfp4_status_string",
+            "nvfp4_moe_shared_workspace_bytes", "nvfp4_quantize_act", "nvfp4_gemv_w4a4",
+            "nvfp4_gemv_w4a4_workspace_bytes", "nvfp4_abi_version", "nvfp4_status_string",
             "nvfp4_last_error"} <= set(names)
     for n in names:
         assert hasattr(L, n), n
 
 
 def test_version_and_status_strings(L):
-    assert L.nvfp4_abi_version() == 3
+    assert L.nvfp4_abi_version() == 4
     for s in range(8):
         assert L.nvfp4_status_string(s)
     assert L.nvfp4_status_string(99) == b"unknown status"
@@ -141,6 +142,34 @@ def test_moe_shared_checks(L):
     assert f(*args, 1, 4, 64, 64, 2, ctypes.byref(good), Y, sh_base[4], need,
              None) == ERR_ALIAS                                              # workspace on WS2 scales
     assert f(*args, 0, 4, 64, 64, 2, ctypes.byref(good), Y, WS, need, None) == OK
+
+
+def test_w4a4_checks(L):
+    """Host-side validation of the W4A4 calls (no launch)."""
+    q = L.nvfp4_quantize_act
+    X, G, C, S = A, A + 0x1000000, A + 0x2000000, A + 0x3000000
+    assert q(X, 2, 48, G, C, S, None) == ERR_SHAPE                # K % 32
+    assert q(X, -1, 64, G, C, S, None) == ERR_SHAPE
+    assert q(X, 0, 64, G, C, S, None) == OK
+    assert q(X, 2, 64, None, C, S, None) == ERR_NULL
+    assert q(X + 8, 2, 64, G, C, S, None) == ERR_ALIGN
+    assert q(X, 2, 64, G, X, S, None) == ERR_ALIAS                # codes over x
+    assert q(X, 2, 64, G, C, C + 16, None) == ERR_ALIAS           # scales over codes
+    f = L.nvfp4_gemv_w4a4
+    assert nv.gemv_w4a4_workspace_bytes(8, 4096) == 8 * 4096 * 2 + 256
+    assert nv.gemv_w4a4_workspace_bytes(1, 32) == 256 + 256
+    w = [A + i * 0x1000000 for i in range(6)]
+    Y, WS = B, B + 0x1000000
+    need = nv.gemv_w4a4_workspace_bytes(2, 64)
+    assert f(*w, 2, 16, 48, Y, WS, need, None) == ERR_SHAPE
+    assert f(*w, 9, 16, 64, Y, WS, need, None) == ERR_UNSUPPORTED
+    assert f(*w, 0, 16, 64, Y, WS, need, None) == OK
+    assert f(*w, 2, 16, 64, Y, WS, need - 1, None) == ERR_WORKSPACE
+    assert f(*w, 2, 16, 64, Y, None, need, None) == ERR_WORKSPACE
+    assert f(*w[:5], None, 2, 16, 64, Y, WS, need, None) == ERR_NULL
+    assert f(*w, 2, 16, 64, Y, WS + 64, need, None) == ERR_ALIGN
+    assert f(*w, 2, 16, 64, w[3], WS, need, None) == ERR_ALIAS    # y over codes_x
+    assert f(*w, 2, 16, 64, Y, w[0], need, None) == ERR_ALIAS     # workspace over codes_w
 
 
 def test_binding_raises_without_device_tensors():

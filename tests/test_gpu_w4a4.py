@@ -1,0 +1,84 @@
+"""GPU W4A4 against the oracle: activation quantization with a static input
+scale bit for bit (calibrated and saturating scales), and the W4A4 GEMV within
+|y - y_ref| <= 1e-3 sum|w x| + 1e-6 on the pages' W4A4 dense FFN (gate, up,
+down 4096x4096 at M=2) and on shapes that take every GEMV kernel (vector ALU
+for M <= 2, the matrix-core kernels for K % 256 == 0 and otherwise)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+import nvfp4_block_scaled_gemv_amd as nv
+from gpu_util import check_tol, dev, dev_x, host, say
+from refdecode import bf16_value
+
+pytestmark = pytest.mark.gpu
+
+
+def static_scale(wl, M, K):
+    """A static input scale calibrated on another batch of the same
+    distribution (rep 1), as an fp32."""
+    calib = bf16_value(workloads.x_bf16(wl, 1, 0, M, K))
+    return np.float32(np.abs(calib).max() / 2688.0)
+
+
+@pytest.mark.parametrize("M,K", [(1, 32), (2, 4096), (8, 4096), (3, 12288)])
+@pytest.mark.parametrize("under", [1.0, 50.0])
+def test_quantize_act_bit_exact(M, K, under):
+    """`under` > 1 makes the static scale too small: blocks saturate."""
+    x = workloads.x_bf16(6, 0, M * 7 + K, M, K)
+    gx = np.float32(static_scale(6, M, K) / under)
+    say(f"[w4a4] quantize M={M} K={K} g_x={gx:.3e}")
+    cx, sx = nv.quantize_act(dev_x(x), dev(np.array([gx], np.float32)))
+    rc, rs = oracle.quantize_act(x, gx)
+    assert np.array_equal(host(sx), rs)
+    assert np.array_equal(host(cx), rc)
+    if under > 1:
+        assert np.any(rs == 0x7E)
+
+
+def run_w4a4(cw, sw, gw, x, gx):
+    """GPU: quantize x, then the W4A4 GEMV; the oracle: the same two steps."""
+    gxd = dev(np.array([gx], np.float32))
+    cx, sx = nv.quantize_act(dev_x(x), gxd)
+    y = host(nv.gemv_w4a4(dev(cw), dev(sw), dev(np.array([gw], np.float32)), cx, sx, gxd))
+    rcx, rsx = oracle.quantize_act(x, gx)
+    assert np.array_equal(host(cx), rcx) and np.array_equal(host(sx), rsx)
+    return y, oracle.gemv_w4a4(cw, sw, gw, rcx, rsx, gx)
+
+
+@pytest.mark.parametrize("i", range(3))
+def test_workload_6_w4a4_ffn(i):
+    name, N, K = workloads.WORKLOADS[6]["mats"][i]
+    M = workloads.WORKLOADS[6]["M"]
+    say(f"[w4a4] workload 6 {name} {N}x{K} M={M}")
+    W = workloads.dense_weights(6, 0, i, N, K)
+    cw, sw, gw = oracle.pack(W)
+    c1, s1, g1 = nv.pack(dev(W))
+    assert np.array_equal(host(c1), cw) and np.array_equal(host(s1), sw)
+    x = workloads.x_bf16(6, 0, 10 + i, M, K)
+    y, (y_ref, ad) = run_w4a4(cw, sw, gw, x, static_scale(6, M, K))
+    r = check_tol(y, y_ref, ad, f"w4a4 {name}")
+    say(f"  max err / tol = {r:.3e}")
+
+
+@pytest.mark.parametrize("M", [1, 2, 3, 5, 8])
+@pytest.mark.parametrize("N,K", [(37, 96), (257, 2048), (130, 4096), (64, 12288)])
+def test_w4a4_shapes(M, N, K):
+    say(f"[w4a4] M={M} N={N} K={K}")
+    cw, sw = workloads.random_nvfp4(6, M, N * 5 + K, N, K, 0x20, 0x50)
+    gw = np.float32(0.0173)
+    x = workloads.x_bf16(6, M, N * 5 + K, M, K)
+    y, (y_ref, ad) = run_w4a4(cw, sw, gw, x, static_scale(6, M, K))
+    check_tol(y, y_ref, ad, f"w4a4 M={M} N={N} K={K}")
+
+
+def test_w4a4_zero_k_and_empty():
+    c = torch.zeros((4, 16), dtype=torch.uint8, device="cuda")
+    s = torch.zeros((4, 2), dtype=torch.uint8, device="cuda")
+    one = torch.ones(1, device="cuda")
+    cx = torch.zeros((0, 16), dtype=torch.uint8, device="cuda")
+    sx = torch.zeros((0, 2), dtype=torch.uint8, device="cuda")
+    y = nv.gemv_w4a4(c, s, one, cx, sx, one)
+    assert y.shape == (0, 4)

@@ -42,3 +42,10 @@ def test_moe_shared_bytes_add_the_shared_expert_once():
     w = 1536 * 4096 * 9 // 16 + 4096 * 768 * 9 // 16   # 4.5 bits per weight
     assert shared - routed == w + 8 + 2 * 8 * 768 * 2
     assert traffic.moe_shared_bytes(1, 64, 32, 2, 1, 0) == traffic.moe_bytes(1, 64, 32, 2, 1) + 8
+
+
+def test_w4a4_bytes():
+    # the pages' W4A4 dense FFN matrix: 4096 x 4096 at M=2
+    assert traffic.gemv_w4a4_bytes(2, 4096, 4096) == (4096 * 4096 * 9 // 16 + 4
+                                                      + 2 * 4096 * 9 // 16 + 4 + 2 * 4096 * 4)
+    assert traffic.quantize_act_bytes(2, 4096) == 2 * 4096 * 2 + 4 + 2 * 4096 * 9 // 16
