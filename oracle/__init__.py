@@ -65,6 +65,12 @@ def lib():
         L.oracle_gemv_w4a4.restype = ctypes.c_int
         L.oracle_gemv_w4a4.argtypes = [_u8p, _u8p, ctypes.c_float, _u8p, _u8p, ctypes.c_float,
                                        _i64, _i64, _i64, _i64p, _i64, _f64p, _f64p]
+        L.oracle_moe_w4a4.restype = ctypes.c_int
+        L.oracle_moe_w4a4.argtypes = [_u8p, _u8p, _f32p, _u8p, _u8p, _f32p, _u16p,
+                                      _i32p, _f32p, _i64, _i64, _i64, _i64, _i64,
+                                      ctypes.c_float, ctypes.c_float,
+                                      _u8p, _u8p, _f32p, _u8p, _u8p, _f32p, _i64,
+                                      _u16p, _f64p, _f64p, _u16p, _u8p, _u8p]
         _lib = L
     return _lib
 
@@ -283,3 +289,61 @@ def gemv_w4a4(codes_w, scales_w, g_w, codes_x, scales_x, g_x, rows=None):
                                 cnt, _ptr(y, _f64p), _ptr(ad, _f64p))
     _check(rc, "gemv_w4a4")
     return y, ad
+
+
+def moe_w4a4(w13_codes, w13_scales, w13_g, w2_codes, w2_scales, w2_g, x_bits,
+             ids, gate_w, g_a13, g_a2, shared=None, h_in=None):
+    """W4A4 routed experts with static input scales g_a13 (x) and g_a2 (h),
+    and an optional W4A16 shared expert (the tuple of moe_shared).
+    Returns y, bound (fp64 [M, H]), h bits (uint16 [M*topk, I], computed
+    here), and the quantized h: codes (uint8 [M*topk, I/2]) and scales
+    (uint8 [M*topk, I/16]) of h_in if given, else of h."""
+    w13_codes = _c(w13_codes, np.uint8)
+    w13_scales = _c(w13_scales, np.uint8)
+    w2_codes = _c(w2_codes, np.uint8)
+    w2_scales = _c(w2_scales, np.uint8)
+    w13_g = _c(w13_g, np.float32)
+    w2_g = _c(w2_g, np.float32)
+    x_bits = _c(x_bits, np.uint16)
+    ids = _c(ids, np.int32)
+    gate_w = _c(gate_w, np.float32)
+    E, twoI, Hh = w13_codes.shape
+    H = Hh * 2
+    I = twoI // 2
+    M, topk = ids.shape
+    if w2_codes.shape != (E, H, I // 2) or x_bits.shape != (M, H):
+        raise ValueError("inconsistent MoE shapes")
+    sp = [None] * 6
+    Is = 0
+    if shared is not None:
+        sc13, ss13, sg13, sc2, ss2, sg2 = shared
+        sp = [_c(sc13, np.uint8), _c(ss13, np.uint8),
+              _c(np.asarray(sg13, np.float32).reshape(1), np.float32),
+              _c(sc2, np.uint8), _c(ss2, np.uint8),
+              _c(np.asarray(sg2, np.float32).reshape(1), np.float32)]
+        Is = sp[0].shape[0] // 2
+        if sp[0].shape != (2 * Is, H // 2) or sp[3].shape != (H, Is // 2):
+            raise ValueError("inconsistent shared expert shapes")
+    if h_in is not None:
+        h_in = _c(h_in, np.uint16)
+        if h_in.shape != (M * topk, I):
+            raise ValueError("h_in must be [M*topk, I]")
+    y = np.empty((M, H), np.float64)
+    bound = np.empty((M, H), np.float64)
+    h = np.empty((M * topk, I), np.uint16)
+    hc = np.empty((M * topk, I // 2), np.uint8)
+    hs = np.empty((M * topk, I // 16), np.uint8)
+    types = [_u8p, _u8p, _f32p, _u8p, _u8p, _f32p]
+    rc = lib().oracle_moe_w4a4(_ptr(w13_codes, _u8p), _ptr(w13_scales, _u8p),
+                               _ptr(w13_g, _f32p), _ptr(w2_codes, _u8p),
+                               _ptr(w2_scales, _u8p), _ptr(w2_g, _f32p),
+                               _ptr(x_bits, _u16p), _ptr(ids, _i32p),
+                               _ptr(gate_w, _f32p), M, E, H, I, topk,
+                               float(g_a13), float(g_a2),
+                               *[_ptr(a, t) if a is not None else None
+                                 for a, t in zip(sp, types)], Is,
+                               _ptr(h_in, _u16p) if h_in is not None else None,
+                               _ptr(y, _f64p), _ptr(bound, _f64p), _ptr(h, _u16p),
+                               _ptr(hc, _u8p), _ptr(hs, _u8p))
+    _check(rc, "moe_w4a4")
+    return y, bound, h, hc, hs

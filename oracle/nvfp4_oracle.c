@@ -24,6 +24,9 @@
  *    "l3.moe.shared_act", "l3.moe.shared_down"; card.json performance[4]
  *    and [9] (gate|up N = 768 + 768, down K = 768); "l3.moe.blend" adds it to
  *    the routed slots ("routed slots + shared in").
+ *  - W4A4: card.json "W4A4 NVFP4 x NVFP4 (static input scale)",
+ *    performance[20] and [24] (dense), [64] and [65] (MoE union sweeps);
+ *    graph.json node "l0.mlp.xn_quant" (act_quant bf16 -> nvfp4/g16).
  *
  * Build: gcc -O2 -ffp-contract=off (no -ffast-math), optionally -fopenmp.
  * fp32 expressions below are evaluated in fp32 (SSE, FLT_EVAL_METHOD 0).
@@ -434,6 +437,121 @@ int oracle_gemv_w4a4(const uint8_t* codes_w, const uint8_t* scales_w, float g_w,
       y[m * cnt + i] = (double)g_w * (double)g_x * sum;
       if (absdot) absdot[m * cnt + i] = fabs((double)g_w * (double)g_x) * asum;
     }
+  }
+  return ORACLE_OK;
+}
+
+/* One row of bf16 activations quantized with a static scale (as in
+   oracle_quantize_act) and decoded to the exact values e2m1 * s (fp64,
+   without the tensor scale). */
+static void quantize_decode_row(const uint16_t* x, int64_t K, float g, uint8_t* codes,
+                                uint8_t* scales, double* v) {
+  int64_t b;
+  for (b = 0; b < K / 16; ++b) {
+    float w[16];
+    int j;
+    for (j = 0; j < 16; ++j) w[j] = (float)bf16_value(x[b * 16 + j]);
+    quantize_block(w, g, codes + b * 8, scales + b);
+  }
+  for (b = 0; b < K; ++b) {
+    unsigned c = (codes[b / 2] >> (4 * (b % 2))) & 15u;
+    v[b] = oracle_e2m1_value(c) * oracle_e4m3_value(scales[b / 16]);
+  }
+}
+
+int oracle_moe_w4a4(const uint8_t* w13_codes, const uint8_t* w13_scales, const float* w13_g,
+                    const uint8_t* w2_codes, const uint8_t* w2_scales, const float* w2_g,
+                    const uint16_t* x, const int32_t* ids, const float* gate_w,
+                    int64_t M, int64_t E, int64_t H, int64_t I, int64_t topk,
+                    float g_a13, float g_a2,
+                    const uint8_t* ws13_codes, const uint8_t* ws13_scales, const float* ws13_g,
+                    const uint8_t* ws2_codes, const uint8_t* ws2_scales, const float* ws2_g,
+                    int64_t Is, const uint16_t* h_in, double* y, double* bound,
+                    uint16_t* h_out, uint8_t* hq_codes, uint8_t* hq_scales) {
+  int64_t m, i;
+  if (M < 0 || E < 0 || H < 0 || I < 0 || topk < 0 || Is < 0) return ORACLE_ERR_SHAPE;
+  if ((H % 16) != 0 || (I % 16) != 0 || (Is % 16) != 0) return ORACLE_ERR_SHAPE;
+  if (!(g_a13 > 0.0f) || !isfinite(g_a13) || !(g_a2 > 0.0f) || !isfinite(g_a2))
+    return ORACLE_ERR_GSCALE;
+  for (i = 0; i < M * H; ++i)
+    if (!isfinite(bf16_value(x[i]))) return ORACLE_ERR_NONFINITE;
+  for (i = 0; i < M * H; ++i) {
+    y[i] = 0.0;
+    if (bound) bound[i] = 0.0;
+  }
+  if (h_out) memset(h_out, 0, (size_t)(M * topk * I) * sizeof(uint16_t));
+  if (hq_codes) memset(hq_codes, 0, (size_t)(M * topk * (I / 2)));
+  if (hq_scales) memset(hq_scales, 0, (size_t)(M * topk * (I / 16)));
+
+  for (m = 0; m < M; ++m) {
+    uint8_t* xc = (uint8_t*)malloc((size_t)(H / 2) + 1);
+    uint8_t* xs = (uint8_t*)malloc((size_t)(H / 16) + 1);
+    double* xq = (double*)malloc((size_t)H * sizeof(double) + 8);
+    double* a = (double*)malloc((size_t)(2 * I) * sizeof(double) + 8);
+    uint16_t* hb = (uint16_t*)malloc((size_t)I * sizeof(uint16_t) + 2);
+    uint8_t* hc = (uint8_t*)malloc((size_t)(I / 2) + 1);
+    uint8_t* hs = (uint8_t*)malloc((size_t)(I / 16) + 1);
+    double* hq = (double*)malloc((size_t)I * sizeof(double) + 8);
+    int64_t j, k;
+    /* the token's activations on the NVFP4 grid of the static scale g_a13 */
+    quantize_decode_row(x + m * H, H, g_a13, xc, xs, xq);
+    for (j = 0; j < topk; ++j) {
+      const int64_t slot = m * topk + j;
+      const int32_t e = ids[slot];
+      const double gw = (double)gate_w[slot];
+      const uint8_t *c13, *s13, *c2, *s2;
+      double g13, g2;
+      int64_t r, n;
+      if (e < 0 || (int64_t)e >= E) continue;  /* out-of-range slot: nothing */
+      c13 = w13_codes + (int64_t)e * (2 * I) * (H / 2);
+      s13 = w13_scales + (int64_t)e * (2 * I) * (H / 16);
+      c2 = w2_codes + (int64_t)e * H * (I / 2);
+      s2 = w2_scales + (int64_t)e * H * (I / 16);
+      g13 = (double)w13_g[e] * (double)g_a13;   /* exact: two fp32 factors */
+      g2 = (double)w2_g[e] * (double)g_a2;
+      /* gate_up of the quantized token: a = g13 * g_a13 * W13 . xq */
+#pragma omp parallel for schedule(static)
+      for (r = 0; r < 2 * I; ++r) {
+        double d;
+        row_dot(c13, s13, H, r, xq, &d, NULL);
+        a[r] = g13 * d;
+      }
+      /* SwiGLU, one rounding to bf16 */
+      for (r = 0; r < I; ++r) {
+        double G = a[r], U = a[I + r];
+        hb[r] = oracle_bf16_from_double(G / (1.0 + exp(-G)) * U);
+        if (h_out) h_out[slot * I + r] = hb[r];
+      }
+      /* h on the NVFP4 grid of the static scale g_a2 (from h_in if given) */
+      quantize_decode_row(h_in ? h_in + slot * I : hb, I, g_a2, hc, hs, hq);
+      if (hq_codes) memcpy(hq_codes + slot * (I / 2), hc, (size_t)(I / 2));
+      if (hq_scales) memcpy(hq_scales + slot * (I / 16), hs, (size_t)(I / 16));
+      /* down, then combine by gate weight */
+#pragma omp parallel for schedule(static)
+      for (n = 0; n < H; ++n) {
+        double d, ad;
+        row_dot(c2, s2, I, n, hq, &d, &ad);
+        y[m * H + n] += gw * (g2 * d);
+        if (bound) bound[m * H + n] += fabs(gw) * fabs(g2) * ad;
+      }
+    }
+    /* the shared expert: W4A16 on the token's unquantized activations */
+    if (Is > 0) {
+      double* xv = (double*)malloc((size_t)H * sizeof(double) + 8);
+      for (k = 0; k < H; ++k) xv[k] = bf16_value(x[m * H + k]);
+      shared_ffn_add(ws13_codes, ws13_scales, (double)ws13_g[0], ws2_codes, ws2_scales,
+                     (double)ws2_g[0], xv, H, Is, y + m * H, bound ? bound + m * H : NULL,
+                     NULL);
+      free(xv);
+    }
+    free(xc);
+    free(xs);
+    free(xq);
+    free(a);
+    free(hb);
+    free(hc);
+    free(hs);
+    free(hq);
   }
   return ORACLE_OK;
 }

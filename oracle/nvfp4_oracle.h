@@ -123,6 +123,34 @@ int oracle_gemv_w4a4(const uint8_t* codes_w, const uint8_t* scales_w, float g_w,
                      int64_t M, int64_t N, int64_t K, const int64_t* rows, int64_t n_rows,
                      double* y, double* absdot);
 
+/* W4A4 MoE (card.json performance[64] and [65]: the routed gate|up and down
+   union sweeps of W4A4 experts; performance[24] and graph.json node
+   "l0.mlp.xn_quant": activations quantized with a static input scale; the
+   shared expert stays W4A16, card.json performance[4] and [9]). Per token m:
+     xq = e2m1 * s of oracle_quantize_act(x[m], g_a13)      (exact values)
+   and per valid slot j with expert e:
+     a  = g13[e] * g_a13 * W13[e] . xq                       (2I values, fp64)
+     h  = bf16( silu(a[0:I]) * a[I:2I] )                     (one rounding)
+     hq = e2m1 * s of oracle_quantize_act(h, g_a2)            (exact values)
+     y[m] += gate_w[m, j] * (g2[e] * g_a2 * W2[e] . hq)       (fp64)
+   then the shared expert as in oracle_moe_shared, on the unquantized x
+   (skipped when Is == 0; its pointers may then be NULL).
+   h_in (may be NULL): [M*topk, I] bf16 bits used in place of h for the
+   quantization and the down projection of every valid slot, so that a
+   caller can take the rounding decisions on an h computed elsewhere; h_out
+   still receives the h computed here. hq_codes [M*topk, I/2] and hq_scales
+   [M*topk, I/16] (may be NULL) receive the quantized h (zeros for skipped
+   slots). bound as in oracle_moe, with |g2[e] * g_a2| and |hq|. */
+int oracle_moe_w4a4(const uint8_t* w13_codes, const uint8_t* w13_scales, const float* w13_g,
+                    const uint8_t* w2_codes, const uint8_t* w2_scales, const float* w2_g,
+                    const uint16_t* x, const int32_t* ids, const float* gate_w,
+                    int64_t M, int64_t E, int64_t H, int64_t I, int64_t topk,
+                    float g_a13, float g_a2,
+                    const uint8_t* ws13_codes, const uint8_t* ws13_scales, const float* ws13_g,
+                    const uint8_t* ws2_codes, const uint8_t* ws2_scales, const float* ws2_g,
+                    int64_t Is, const uint16_t* h_in, double* y, double* bound,
+                    uint16_t* h_out, uint8_t* hq_codes, uint8_t* hq_scales);
+
 /* Round a double to the nearest bf16 (ties to even), returning its bits. */
 uint16_t oracle_bf16_from_double(double v);
 
