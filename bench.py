@@ -380,7 +380,28 @@ def leg_moe(torch, nv, workloads, traffic, steps, warmup, M):
 
     with_shared = run(step_shared, lambda d: traffic.moe_shared_bytes(M, H, I, topk, d, Is),
                       f"moe_288x(3072x4096,4096x1536)_top8_shared768_m{M}")
-    return routed, with_shared
+
+    # W4A4 routed experts (static input scales for x and h, calibrated on
+    # another batch of the same distributions) with the W4A16 shared expert
+    xc = torch.from_numpy(workloads.x_bf16(4, nb, 0, M, H).view(np.int16)).cuda().view(
+        torch.bfloat16)
+    gx = (xc.float().abs().max() / 2688.0).reshape(1)
+    idc, gwc = (torch.from_numpy(a).cuda() for a in workloads.moe_routing(4, nb, M, E, topk))
+    nv.moe_shared_gemv_into(c13, s13, g13, c2, s2, g2, xc, idc, gwc, shared, y, wss)
+    hc = wss[:M * topk * I * 2].view(torch.bfloat16).float()
+    gh = (hc.abs().max() / 2688.0).reshape(1)
+    wsq = torch.empty(nv.moe_w4a4_workspace_bytes(M, H, I, topk, Is), dtype=torch.uint8,
+                      device="cuda")
+
+    def step_w4a4(i):
+        ids, gw, x, _ = batches[i % nb]
+        nv.moe_w4a4_gemv_into(c13, s13, g13, c2, s2, g2, x, gx, gh, ids, gw, y, wsq,
+                              shared=shared)
+
+    w4a4 = run(step_w4a4, lambda d: traffic.moe_w4a4_bytes(M, H, I, topk, d, Is),
+               f"moe_w4a4_288x(3072x4096,4096x1536)_top8_shared768_m{M}")
+    w4a4["launches_per_step"] = 4
+    return routed, with_shared, w4a4
 
 
 def leg_copy(torch, steps, warmup):
@@ -656,12 +677,13 @@ def main():
             if k in result:
                 result[k]["frac_of_measured_copy"] = result[k]["gbs_kernel"] / cp["gbs"]
     if "moe" in legs:
-        result["moe"], result["moe_shared"] = {}, {}
+        result["moe"], result["moe_shared"], result["moe_w4a4"] = {}, {}, {}
         for M in (1, 8):
-            routed, with_shared = leg_moe(torch, nv, workloads, traffic, args.steps,
-                                          args.warmup, M)
+            routed, with_shared, w4a4 = leg_moe(torch, nv, workloads, traffic, args.steps,
+                                                args.warmup, M)
             result["moe"][f"m{M}"] = routed
             result["moe_shared"][f"m{M}"] = with_shared
+            result["moe_w4a4"][f"m{M}"] = w4a4
     result["env"] = {"gpu": props.name, "cus": props.multi_processor_count,
                      "dpm_clocks": gpu_clock_state(),
                      "hip": torch.version.hip, "torch": torch.__version__, "git": git_sha(),

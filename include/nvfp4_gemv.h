@@ -55,7 +55,7 @@
 extern "C" {
 #endif
 
-#define NVFP4_ABI_VERSION 4
+#define NVFP4_ABI_VERSION 5
 
 /* Largest number of activation rows (tokens) one GEMV / MoE call takes. */
 #define NVFP4_MAX_M 8
@@ -338,6 +338,55 @@ nvfp4_status nvfp4_moe_shared_gemv(const uint8_t* w13_codes, const uint8_t* w13_
                                    int64_t I, int64_t topk, const nvfp4_moe_shared* shared,
                                    float* y, void* workspace, size_t workspace_bytes,
                                    hipStream_t stream);
+
+/*
+ * nvfp4_moe_w4a4_workspace_bytes -- device workspace that nvfp4_moe_w4a4_gemv
+ * needs: h[M * topk, I] (bf16, offset 0), the shared hs[M, I_shared], then
+ * h and x on the NVFP4 grid (bf16 e2m1 * s, [M * topk, I] and [M, H]), each
+ * 256-byte aligned. 0 for negative sizes.
+ */
+size_t nvfp4_moe_w4a4_workspace_bytes(int64_t M, int64_t H, int64_t I, int64_t topk,
+                                      int64_t I_shared);
+
+/*
+ * nvfp4_moe_w4a4_gemv -- MoE expert slots with W4A4 routed experts (card.json
+ * performance[64] and [65]: the gate|up and down union sweeps of NVFP4
+ * experts on NVFP4 activations; performance[24]: activations quantized with
+ * a static input scale) and an optional W4A16 shared expert (performance[4]
+ * and [9]). For token m:
+ *
+ *   xq = Q(x[m], g_x)                            (NVFP4 g16, static scale g_x)
+ *   per valid slot j, e = expert_ids[m, j]:
+ *     a  = g13[e] * g_x * W13[e] . xq
+ *     h  = bf16( silu(a[0:I]) * a[I:2I] )
+ *     y[m] += gate_w[m, j] * ( g2[e] * g_h * W2[e] . Q(h, g_h) )
+ *   y[m] += the shared expert's term of nvfp4_moe_shared_gemv on x[m]
+ *
+ * where Q(v, g) is the quantization of nvfp4_quantize_act (each 16-block:
+ * s = E4M3(amax / (6 g)), code = E2M1(v / (s g))) taken back to the values
+ * e2m1 * s, which are exact in bf16. Four launches on the stream: quantize
+ * x, gate|up (shared expert included), quantize h, down and combine.
+ *
+ * Arguments as nvfp4_moe_gemv, plus
+ *   gscale_x   float[1], > 0 and finite: the static input scale of x,
+ *              4-byte aligned (device memory);
+ *   gscale_h   float[1], > 0 and finite: the static input scale of h;
+ *   shared     the shared expert, or NULL for none;
+ *   workspace  at least nvfp4_moe_w4a4_workspace_bytes(M, H, I, topk,
+ *              shared ? shared->I : 0) bytes, 256-byte aligned; overwritten;
+ *              must not be shared by calls that may run concurrently.
+ * The static scales are device data and are not checked; other values give
+ * unspecified (but memory-safe) results.
+ * Errors: NULL, SHAPE, ALIGN, UNSUPPORTED, WORKSPACE, ALIAS, HIP.
+ */
+nvfp4_status nvfp4_moe_w4a4_gemv(const uint8_t* w13_codes, const uint8_t* w13_scales,
+                                 const float* w13_gscale, const uint8_t* w2_codes,
+                                 const uint8_t* w2_scales, const float* w2_gscale,
+                                 const uint16_t* x, const float* gscale_x, const float* gscale_h,
+                                 const int32_t* expert_ids, const float* gate_w, int64_t M,
+                                 int64_t E, int64_t H, int64_t I, int64_t topk,
+                                 const nvfp4_moe_shared* shared, float* y, void* workspace,
+                                 size_t workspace_bytes, hipStream_t stream);
 
 #ifdef __cplusplus
 }

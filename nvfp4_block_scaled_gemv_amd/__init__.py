@@ -103,6 +103,12 @@ def lib() -> ctypes.CDLL:
         L.nvfp4_moe_shared_gemv.argtypes = ([_VP] * 9 + [_I64] * 5 +
                                             [ctypes.POINTER(MoeShared), _VP, _VP,
                                              ctypes.c_size_t, _VP])
+        L.nvfp4_moe_w4a4_workspace_bytes.restype = ctypes.c_size_t
+        L.nvfp4_moe_w4a4_workspace_bytes.argtypes = [_I64] * 5
+        L.nvfp4_moe_w4a4_gemv.restype = ctypes.c_int
+        L.nvfp4_moe_w4a4_gemv.argtypes = ([_VP] * 11 + [_I64] * 5 +
+                                          [ctypes.POINTER(MoeShared), _VP, _VP,
+                                           ctypes.c_size_t, _VP])
         _lib = L
     return _lib
 
@@ -380,3 +386,69 @@ def moe_shared_workspace_layout(M: int, H: int, I: int, topk: int, I_shared: int
     h[M*topk, I] and the shared hs[M, I_shared] bf16 activations."""
     hs = (M * topk * I * 2 + 255) & ~255
     return {"h": 0, "hs": hs, "total": (hs + M * I_shared * 2 + 255) & ~255}
+
+
+def moe_w4a4_workspace_bytes(M: int, H: int, I: int, topk: int, I_shared: int = 0) -> int:
+    return int(lib().nvfp4_moe_w4a4_workspace_bytes(M, H, I, topk, I_shared))
+
+
+def moe_w4a4_gemv_into(w13_codes, w13_scales, w13_gscale, w2_codes, w2_scales, w2_gscale,
+                       x, gscale_x, gscale_h, expert_ids, gate_w, y, workspace,
+                       shared=None) -> None:
+    """W4A4 routed experts (static input scales gscale_x for x and gscale_h
+    for h, fp32 [1] device tensors) and an optional W4A16 shared expert
+    (the tuple of moe_shared_gemv_into)."""
+    extra = list(shared) if shared is not None else []
+    _dev(w13_codes, w13_scales, w13_gscale, w2_codes, w2_scales, w2_gscale, x, gscale_x,
+         gscale_h, expert_ids, gate_w, y, workspace, *extra)
+    _dtype(x, torch.bfloat16, torch.int16, torch.uint16, name="x")
+    _dtype(expert_ids, torch.int32, name="expert_ids")
+    _dtype(gate_w, torch.float32, name="gate_w")
+    _dtype(gscale_x, torch.float32, name="gscale_x")
+    _dtype(gscale_h, torch.float32, name="gscale_h")
+    E, twoI, Hh = w13_codes.shape
+    H, I = Hh * 2, twoI // 2
+    M, topk = expert_ids.shape
+    if tuple(w2_codes.shape) != (E, H, I // 2) or tuple(x.shape) != (M, H) \
+            or tuple(gate_w.shape) != (M, topk) or tuple(y.shape) != (M, H):
+        raise ValueError("inconsistent MoE shapes")
+    sh = None
+    if shared is not None:
+        sc13, ss13, sg13, sc2, ss2, sg2 = shared
+        Is = sc13.shape[0] // 2
+        if tuple(sc13.shape) != (2 * Is, H // 2) or tuple(sc2.shape) != (H, Is // 2):
+            raise ValueError("inconsistent shared expert shapes")
+        sh = MoeShared(_p(sc13), _p(ss13), _p(sg13), _p(sc2), _p(ss2), _p(sg2), Is)
+    _check("nvfp4_moe_w4a4_gemv", lib().nvfp4_moe_w4a4_gemv(
+        _p(w13_codes), _p(w13_scales), _p(w13_gscale), _p(w2_codes), _p(w2_scales),
+        _p(w2_gscale), _p(x), _p(gscale_x), _p(gscale_h), _p(expert_ids), _p(gate_w),
+        M, E, H, I, topk, ctypes.byref(sh) if sh is not None else None,
+        _p(y), _p(workspace), workspace.numel() * workspace.element_size(), _stream(x)))
+
+
+def moe_w4a4_gemv(w13_codes, w13_scales, w13_gscale, w2_codes, w2_scales, w2_gscale, x,
+                  gscale_x, gscale_h, expert_ids, gate_w, shared=None,
+                  workspace: torch.Tensor | None = None) -> torch.Tensor:
+    E, twoI, Hh = w13_codes.shape
+    H, I = Hh * 2, twoI // 2
+    M, topk = expert_ids.shape
+    Is = shared[0].shape[0] // 2 if shared is not None else 0
+    if workspace is None:
+        workspace = torch.empty(max(moe_w4a4_workspace_bytes(M, H, I, topk, Is), 256),
+                                dtype=torch.uint8, device=x.device)
+    y = torch.empty((M, H), dtype=torch.float32, device=x.device)
+    moe_w4a4_gemv_into(w13_codes, w13_scales, w13_gscale, w2_codes, w2_scales, w2_gscale, x,
+                       gscale_x, gscale_h, expert_ids, gate_w, y, workspace, shared=shared)
+    return y
+
+
+def moe_w4a4_workspace_layout(M: int, H: int, I: int, topk: int, I_shared: int = 0) -> dict:
+    """Byte offsets inside the workspace of nvfp4_moe_w4a4_gemv: h[M*topk, I]
+    (bf16 SwiGLU output), hs[M, I_shared], and h and x on the NVFP4 grid
+    (bf16 e2m1 * s): hq[M*topk, I], xq[M, H]."""
+    def a(v):
+        return (v + 255) & ~255
+    hs = a(M * topk * I * 2)
+    hq = a(hs + M * I_shared * 2)
+    xq = a(hq + M * topk * I * 2)
+    return {"h": 0, "hs": hs, "hq": hq, "xq": xq, "total": a(xq + M * H * 2)}

@@ -272,28 +272,35 @@ nvfp4_status nvfp4_gemv_w4a4(const uint8_t* codes_w, const uint8_t* scales_w,
 
 size_t nvfp4_moe_workspace_bytes(int64_t M, int64_t H, int64_t I, int64_t topk) {
   if (M < 0 || H < 0 || I < 0 || topk < 0) return 0;
-  return nvfp4::moe_layout(M, H, I, topk, 0).total;
+  return nvfp4::moe_layout(M, H, I, topk, 0, false).total;
 }
 
 size_t nvfp4_moe_shared_workspace_bytes(int64_t M, int64_t H, int64_t I, int64_t topk,
                                         int64_t I_shared) {
   if (M < 0 || H < 0 || I < 0 || topk < 0 || I_shared < 0) return 0;
-  return nvfp4::moe_layout(M, H, I, topk, I_shared).total;
+  return nvfp4::moe_layout(M, H, I, topk, I_shared, false).total;
+}
+
+size_t nvfp4_moe_w4a4_workspace_bytes(int64_t M, int64_t H, int64_t I, int64_t topk,
+                                      int64_t I_shared) {
+  if (M < 0 || H < 0 || I < 0 || topk < 0 || I_shared < 0) return 0;
+  return nvfp4::moe_layout(M, H, I, topk, I_shared, true).total;
 }
 
 }  // extern "C"
 
 namespace {
 
-// Checks and launch shared by nvfp4_moe_gemv and nvfp4_moe_shared_gemv
-// (shared == NULL: no shared expert).
+// Checks and launch shared by nvfp4_moe_gemv, nvfp4_moe_shared_gemv and
+// nvfp4_moe_w4a4_gemv (shared == NULL: no shared expert; w4a4: the routed
+// experts take NVFP4 activations with the static scales ga13 and ga2).
 nvfp4_status moe_checked(const char* fn, const uint8_t* w13_codes, const uint8_t* w13_scales,
                          const float* w13_gscale, const uint8_t* w2_codes,
                          const uint8_t* w2_scales, const float* w2_gscale, const uint16_t* x,
                          const int32_t* expert_ids, const float* gate_w, int64_t M, int64_t E,
                          int64_t H, int64_t I, int64_t topk, const nvfp4_moe_shared* shared,
-                         float* y, void* workspace, size_t workspace_bytes,
-                         hipStream_t stream) {
+                         bool w4a4, const float* ga13, const float* ga2, float* y,
+                         void* workspace, size_t workspace_bytes, hipStream_t stream) {
   clear_error();
   if (M < 0 || E < 1 || H <= 0 || I <= 0 || topk < 1 || (H % 32) != 0 || (I % 32) != 0)
     return fail(NVFP4_ERR_SHAPE,
@@ -316,7 +323,8 @@ nvfp4_status moe_checked(const char* fn, const uint8_t* w13_codes, const uint8_t
   if (shared && (!shared->w13_codes || !shared->w13_scales || !shared->w13_gscale ||
                  !shared->w2_codes || !shared->w2_scales || !shared->w2_gscale))
     return fail(NVFP4_ERR_NULL, "%s: NULL pointer in the shared expert", fn);
-  const size_t need = nvfp4::moe_layout(M, H, I, topk, Is).total;
+  if (w4a4 && (!ga13 || !ga2)) return fail(NVFP4_ERR_NULL, "%s: NULL static input scale", fn);
+  const size_t need = nvfp4::moe_layout(M, H, I, topk, Is, w4a4).total;
   if (!workspace || workspace_bytes < need)
     return fail(NVFP4_ERR_WORKSPACE, "%s: workspace of %zu bytes needed, %zu given", fn, need,
                 workspace ? workspace_bytes : (size_t)0);
@@ -329,6 +337,8 @@ nvfp4_status moe_checked(const char* fn, const uint8_t* w13_codes, const uint8_t
                  !aligned(shared->w13_scales, 2) || !aligned(shared->w2_scales, 2) ||
                  !aligned(shared->w13_gscale, 4) || !aligned(shared->w2_gscale, 4)))
     return fail(NVFP4_ERR_ALIGN, "%s: alignment rule broken in the shared expert", fn);
+  if (w4a4 && (!aligned(ga13, 4) || !aligned(ga2, 4)))
+    return fail(NVFP4_ERR_ALIGN, "%s: static input scales must be 4-byte aligned", fn);
   const size_t e13 = (size_t)E * 2 * (size_t)I * (size_t)H, e2 = (size_t)E * (size_t)H * (size_t)I;
   const size_t s13 = 2 * (size_t)Is * (size_t)H, s2 = (size_t)H * (size_t)Is;
   const size_t yb = (size_t)M * (size_t)H * 4, S = (size_t)(M * topk);
@@ -336,11 +346,12 @@ nvfp4_status moe_checked(const char* fn, const uint8_t* w13_codes, const uint8_t
                        expert_ids, gate_w,
                        shared ? shared->w13_codes : nullptr, shared ? shared->w13_scales : nullptr,
                        shared ? shared->w13_gscale : nullptr, shared ? shared->w2_codes : nullptr,
-                       shared ? shared->w2_scales : nullptr, shared ? shared->w2_gscale : nullptr};
+                       shared ? shared->w2_scales : nullptr, shared ? shared->w2_gscale : nullptr,
+                       w4a4 ? ga13 : nullptr, w4a4 ? ga2 : nullptr};
   const size_t insz[] = {e13 / 2, e13 / 16, (size_t)E * 4, e2 / 2, e2 / 16, (size_t)E * 4,
                          (size_t)M * (size_t)H * 2, S * 4, S * 4,
-                         s13 / 2, s13 / 16, 4, s2 / 2, s2 / 16, 4};
-  for (int i = 0; i < 15; ++i) {
+                         s13 / 2, s13 / 16, 4, s2 / 2, s2 / 16, 4, 4, 4};
+  for (int i = 0; i < 17; ++i) {
     if (overlap(y, yb, ins[i], insz[i]) || overlap(workspace, need, ins[i], insz[i]))
       return fail(NVFP4_ERR_ALIAS, "%s: y or workspace overlaps input %d", fn, i);
   }
@@ -356,9 +367,11 @@ nvfp4_status moe_checked(const char* fn, const uint8_t* w13_codes, const uint8_t
     sh.g2 = shared->w2_gscale;
     sh.I = Is;
   }
+  const nvfp4::MoeW4a4 q = {ga13, ga2};
   return hip_result(nvfp4::launch_moe(w13_codes, w13_scales, w13_gscale, w2_codes, w2_scales,
                                       w2_gscale, x, expert_ids, gate_w, (int)M, E, H, I,
-                                      (int)topk, shared ? &sh : nullptr, y, workspace, stream),
+                                      (int)topk, shared ? &sh : nullptr, w4a4 ? &q : nullptr, y,
+                                      workspace, stream),
                     fn);
 }
 
@@ -373,8 +386,8 @@ nvfp4_status nvfp4_moe_gemv(const uint8_t* w13_codes, const uint8_t* w13_scales,
                             int64_t H, int64_t I, int64_t topk, float* y, void* workspace,
                             size_t workspace_bytes, hipStream_t stream) {
   return moe_checked("nvfp4_moe_gemv", w13_codes, w13_scales, w13_gscale, w2_codes, w2_scales,
-                     w2_gscale, x, expert_ids, gate_w, M, E, H, I, topk, nullptr, y, workspace,
-                     workspace_bytes, stream);
+                     w2_gscale, x, expert_ids, gate_w, M, E, H, I, topk, nullptr, false, nullptr,
+                     nullptr, y, workspace, workspace_bytes, stream);
 }
 
 nvfp4_status nvfp4_moe_shared_gemv(const uint8_t* w13_codes, const uint8_t* w13_scales,
@@ -390,8 +403,21 @@ nvfp4_status nvfp4_moe_shared_gemv(const uint8_t* w13_codes, const uint8_t* w13_
     return fail(NVFP4_ERR_NULL, "nvfp4_moe_shared_gemv: NULL shared expert");
   }
   return moe_checked("nvfp4_moe_shared_gemv", w13_codes, w13_scales, w13_gscale, w2_codes,
-                     w2_scales, w2_gscale, x, expert_ids, gate_w, M, E, H, I, topk, shared, y,
-                     workspace, workspace_bytes, stream);
+                     w2_scales, w2_gscale, x, expert_ids, gate_w, M, E, H, I, topk, shared, false,
+                     nullptr, nullptr, y, workspace, workspace_bytes, stream);
+}
+
+nvfp4_status nvfp4_moe_w4a4_gemv(const uint8_t* w13_codes, const uint8_t* w13_scales,
+                                 const float* w13_gscale, const uint8_t* w2_codes,
+                                 const uint8_t* w2_scales, const float* w2_gscale,
+                                 const uint16_t* x, const float* gscale_x, const float* gscale_h,
+                                 const int32_t* expert_ids, const float* gate_w, int64_t M,
+                                 int64_t E, int64_t H, int64_t I, int64_t topk,
+                                 const nvfp4_moe_shared* shared, float* y, void* workspace,
+                                 size_t workspace_bytes, hipStream_t stream) {
+  return moe_checked("nvfp4_moe_w4a4_gemv", w13_codes, w13_scales, w13_gscale, w2_codes,
+                     w2_scales, w2_gscale, x, expert_ids, gate_w, M, E, H, I, topk, shared, true,
+                     gscale_x, gscale_h, y, workspace, workspace_bytes, stream);
 }
 
 }  // extern "C"

@@ -55,6 +55,12 @@ hipError_t launch_gemv_w4a4(const uint8_t* codes_w, const uint8_t* scales_w,
                             const float* gscale_w, const uint8_t* codes_x,
                             const uint8_t* scales_x, const float* gscale_x, int M, int64_t N,
                             int64_t K, float* y, void* workspace, hipStream_t stream);
+// bf16 rows [rows, K] quantized with the static scale *gscale and written
+// back as the exact bf16 values e2m1 * s (the tensor scale left out). With
+// ids, row r is skipped (not written) when ids[r] is outside [0, E).
+hipError_t launch_quantize_decode(const uint16_t* x, int64_t rows, int64_t K,
+                                  const float* gscale, const int32_t* ids, int64_t E,
+                                  uint16_t* out, hipStream_t stream);
 
 hipError_t launch_fill_zero(float* y, size_t n, hipStream_t stream);
 
@@ -62,9 +68,11 @@ hipError_t launch_fill_zero(float* y, size_t n, hipStream_t stream);
 struct MoeLayout {
   size_t h_off;       // uint16 bf16 SwiGLU activations h[M * topk, I]
   size_t hs_off;      // the shared expert's hs[M, Is] (empty when Is = 0)
+  size_t hq_off;      // W4A4: h on the NVFP4 grid, e2m1 * s as bf16 [M * topk, I]
+  size_t xq_off;      // W4A4: x on the NVFP4 grid, e2m1 * s as bf16 [M, H]
   size_t total;       // rounded up to 256 bytes
 };
-MoeLayout moe_layout(int64_t M, int64_t H, int64_t I, int64_t topk, int64_t Is);
+MoeLayout moe_layout(int64_t M, int64_t H, int64_t I, int64_t topk, int64_t Is, bool w4a4);
 
 // The shared expert of a MoE call (I = 0: none). h is set by the launcher.
 struct MoeShared {
@@ -78,11 +86,18 @@ struct MoeShared {
   uint16_t* h;          // hs [M, Is] in the workspace
 };
 
+// W4A4 routed experts: the static input scales of x (gate|up) and of h (down),
+// device fp32 [1] each. The shared expert stays W4A16.
+struct MoeW4a4 {
+  const float* ga13;
+  const float* ga2;
+};
+
 hipError_t launch_moe(const uint8_t* w13_codes, const uint8_t* w13_scales,
                       const float* w13_gscale, const uint8_t* w2_codes,
                       const uint8_t* w2_scales, const float* w2_gscale, const uint16_t* x,
                       const int32_t* ids, const float* gate_w, int M, int64_t E, int64_t H,
-                      int64_t I, int topk, const MoeShared* shared, float* y, void* workspace,
-                      hipStream_t stream);
+                      int64_t I, int topk, const MoeShared* shared, const MoeW4a4* w4a4,
+                      float* y, void* workspace, hipStream_t stream);
 
 }  // namespace nvfp4

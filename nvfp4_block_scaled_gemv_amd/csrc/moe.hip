@@ -36,12 +36,18 @@ constexpr int kDownUnroll = 2;   // (slot, chunk) pairs in flight per lane
 
 static inline size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 
-MoeLayout moe_layout(int64_t M, int64_t H, int64_t I, int64_t topk, int64_t Is) {
-  (void)H;
+MoeLayout moe_layout(int64_t M, int64_t H, int64_t I, int64_t topk, int64_t Is, bool w4a4) {
   MoeLayout L;
+  const size_t hbytes = (size_t)(M * topk) * (size_t)I * sizeof(uint16_t);
   L.h_off = 0;
-  L.hs_off = align256((size_t)(M * topk) * (size_t)I * sizeof(uint16_t));
-  L.total = align256(L.hs_off + (size_t)M * (size_t)Is * sizeof(uint16_t));
+  L.hs_off = align256(hbytes);
+  L.hq_off = align256(L.hs_off + (size_t)M * (size_t)Is * sizeof(uint16_t));
+  L.xq_off = L.hq_off;
+  L.total = L.hq_off;
+  if (w4a4) {
+    L.xq_off = align256(L.hq_off + hbytes);
+    L.total = align256(L.xq_off + (size_t)M * (size_t)H * sizeof(uint16_t));
+  }
   return L;
 }
 
@@ -83,9 +89,13 @@ __device__ __forceinline__ void gate_up_rows(const uint8_t* __restrict__ codes,
 
 // grid (S [+ 1 for the shared expert], ceil(ceil(max(I, Is)/2) / kMoeWaves));
 // a wavefront owns one gate/up row pair.
+// Routed slots read xr with weight scale w13_gscale[e] * *ga (xr = x and
+// ga = NULL for W4A16; the W4A4 activations on the NVFP4 grid and their
+// static scale otherwise); the shared expert always reads x.
 __global__ __launch_bounds__(256) void k_moe_gate_up(
     const uint8_t* __restrict__ w13_codes, const uint8_t* __restrict__ w13_scales,
     const float* __restrict__ w13_gscale, const uint16_t* __restrict__ x,
+    const uint16_t* __restrict__ xr, const float* __restrict__ ga,
     const int32_t* __restrict__ ids, int S, int topk, int64_t E, int64_t H, int64_t I,
     uint16_t* __restrict__ h, const MoeShared sh, int M) {
   const int j = blockIdx.x;
@@ -118,10 +128,10 @@ __global__ __launch_bounds__(256) void k_moe_gate_up(
 
   const uint8_t* codes = w13_codes + (int64_t)e * (2 * I) * (H / 2);
   const uint8_t* scales = w13_scales + (int64_t)e * (2 * I) * (H / 16);
-  const float g = w13_gscale[e];
+  const float g = ga ? w13_gscale[e] * *ga : w13_gscale[e];
   if (__popcll(m0) + __popcll(m1) == 1) {
     const int slot[1] = {j};
-    gate_up_rows<1>(codes, scales, g, x, H, I, r0, topk, slot, 1, h);
+    gate_up_rows<1>(codes, scales, g, xr, H, I, r0, topk, slot, 1, h);
     return;
   }
   while (m0 | m1) {
@@ -141,18 +151,21 @@ __global__ __launch_bounds__(256) void k_moe_gate_up(
         slot[q] = j;   // unused column (q >= ns)
       }
     }
-    gate_up_rows<4>(codes, scales, g, x, H, I, r0, topk, slot, ns, h);
+    gate_up_rows<4>(codes, scales, g, xr, H, I, r0, topk, slot, ns, h);
   }
 }
 
 // grid ceil(H / (R * kMoeWaves)); a wavefront owns output rows n0 .. n0+R-1
-// for every token.
+// for every token. Routed slots read h with coefficient gate_w * g2[e] * *ga
+// (ga = NULL for W4A16; for W4A4, h holds the activations on the NVFP4 grid
+// and ga their static scale).
 template <int R, int U>
 __global__ __launch_bounds__(256) void k_moe_down(
     const uint8_t* __restrict__ w2_codes, const uint8_t* __restrict__ w2_scales,
     const float* __restrict__ w2_gscale, const uint16_t* __restrict__ h,
-    const int32_t* __restrict__ ids, const float* __restrict__ gate_w, int M, int topk,
-    int64_t E, int64_t H, int64_t I, float* __restrict__ y, const MoeShared sh) {
+    const float* __restrict__ ga, const int32_t* __restrict__ ids,
+    const float* __restrict__ gate_w, int M, int topk, int64_t E, int64_t H, int64_t I,
+    float* __restrict__ y, const MoeShared sh) {
   const int lane = threadIdx.x & 63;
   const int64_t n0 =
       ((int64_t)blockIdx.x * kMoeWaves + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6)) * R;
@@ -165,6 +178,7 @@ __global__ __launch_bounds__(256) void k_moe_down(
   const int Cs = (int)(sh.I >> 5);
   const int64_t cbs = sh.I >> 1, sbs = sh.I >> 4;
   const float gs2 = Cs > 0 ? *sh.g2 : 0.0f;
+  const float gah = ga ? *ga : 1.0f;
   int64_t rows[R];
 #pragma unroll
   for (int r = 0; r < R; ++r) rows[r] = (n0 + r < H) ? n0 + r : H - 1;
@@ -177,7 +191,7 @@ __global__ __launch_bounds__(256) void k_moe_down(
     const uint64_t vm = __ballot(valid);
     const int nv = __popcll(vm);
     float coef = 0.0f;
-    if (valid) coef = gate_w[jl] * w2_gscale[ev];
+    if (valid) coef = ga ? gate_w[jl] * w2_gscale[ev] * gah : gate_w[jl] * w2_gscale[ev];
     const int q = __builtin_amdgcn_mbcnt_hi((uint32_t)(vm >> 32),
                                             __builtin_amdgcn_mbcnt_lo((uint32_t)vm, 0u));
     const int dst = (valid ? q : 63) * 4;    // lane 63 is never read (nv <= 16)
@@ -266,26 +280,48 @@ hipError_t launch_moe(const uint8_t* w13_codes, const uint8_t* w13_scales,
                       const float* w13_gscale, const uint8_t* w2_codes,
                       const uint8_t* w2_scales, const float* w2_gscale, const uint16_t* x,
                       const int32_t* ids, const float* gate_w, int M, int64_t E, int64_t H,
-                      int64_t I, int topk, const MoeShared* shared, float* y, void* workspace,
-                      hipStream_t stream) {
+                      int64_t I, int topk, const MoeShared* shared, const MoeW4a4* w4a4,
+                      float* y, void* workspace, hipStream_t stream) {
   MoeShared sh = {};
   if (shared) sh = *shared;
-  const MoeLayout L = moe_layout(M, H, I, topk, sh.I);
-  uint16_t* h = reinterpret_cast<uint16_t*>(static_cast<char*>(workspace) + L.h_off);
-  sh.h = reinterpret_cast<uint16_t*>(static_cast<char*>(workspace) + L.hs_off);
+  const MoeLayout L = moe_layout(M, H, I, topk, sh.I, w4a4 != nullptr);
+  char* ws = static_cast<char*>(workspace);
+  uint16_t* h = reinterpret_cast<uint16_t*>(ws + L.h_off);
+  sh.h = reinterpret_cast<uint16_t*>(ws + L.hs_off);
   const int S = M * topk;
+  const uint16_t* xr = x;        // routed gate|up input
+  const uint16_t* hr = h;        // routed down input
+  const float* ga13 = nullptr;
+  const float* ga2 = nullptr;
+  if (w4a4) {
+    // the token's activations onto the NVFP4 grid of their static scale
+    uint16_t* xq = reinterpret_cast<uint16_t*>(ws + L.xq_off);
+    hipError_t e = launch_quantize_decode(x, M, H, w4a4->ga13, nullptr, 0, xq, stream);
+    if (e != hipSuccess) return e;
+    xr = xq;
+    hr = reinterpret_cast<const uint16_t*>(ws + L.hq_off);
+    ga13 = w4a4->ga13;
+    ga2 = w4a4->ga2;
+  }
   {
     const int64_t pairs = ((sh.I > I ? sh.I : I) + 1) / 2;
     const int64_t yb = (pairs + kMoeWaves - 1) / kMoeWaves;
     hipLaunchKernelGGL(k_moe_gate_up, dim3(S + (sh.I > 0 ? 1 : 0), (unsigned)yb), dim3(256), 0,
-                       stream, w13_codes, w13_scales, w13_gscale, x, ids, S, topk, E, H, I, h,
-                       sh, M);
+                       stream, w13_codes, w13_scales, w13_gscale, x, xr, ga13, ids, S, topk, E,
+                       H, I, h, sh, M);
+  }
+  if (w4a4) {
+    // h of every valid slot onto the NVFP4 grid of its static scale
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    e = launch_quantize_decode(h, S, I, ga2, ids, E, const_cast<uint16_t*>(hr), stream);
+    if (e != hipSuccess) return e;
   }
   {
     const int64_t wgs = (H + kDownRows * kMoeWaves - 1) / (kDownRows * kMoeWaves);
     hipLaunchKernelGGL((k_moe_down<kDownRows, kDownUnroll>), dim3((unsigned)wgs), dim3(256), 0,
-                       stream, w2_codes, w2_scales, w2_gscale, h, ids, gate_w, M, topk, E, H, I,
-                       y, sh);
+                       stream, w2_codes, w2_scales, w2_gscale, hr, ga2, ids, gate_w, M, topk, E,
+                       H, I, y, sh);
   }
   return hipGetLastError();
 }

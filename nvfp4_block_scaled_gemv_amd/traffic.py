@@ -48,6 +48,17 @@ def moe_shared_bytes(M: int, H: int, I: int, topk: int, distinct: int, Is: int) 
     return moe_bytes(M, H, I, topk, distinct) + shared
 
 
+def moe_w4a4_bytes(M: int, H: int, I: int, topk: int, distinct: int, Is: int = 0) -> int:
+    """One W4A4 MoE call: moe_bytes (moe_shared_bytes with a shared expert)
+    plus the two quantization passes, each reading its bf16 input and writing
+    the values on the NVFP4 grid that the next pass reads: x[M, H] (read,
+    write, read) and h[M*topk, I] (read, write, read), and the two static
+    scales."""
+    base = (moe_shared_bytes(M, H, I, topk, distinct, Is) if Is
+            else moe_bytes(M, H, I, topk, distinct))
+    return base + 2 * M * H * 2 + 2 * M * topk * I * 2 + 8
+
+
 def pages_floor_us(M: float, N: int, K: int, experts: float, bits: float,
                    act_bytes_per_elem: float, out_elems: int,
                    bw_bytes_per_s: float = 249e9) -> float:

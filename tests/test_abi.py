@@ -32,14 +32,15 @@ def test_exports_every_declared_symbol(L):
     assert {"nvfp4_pack", "nvfp4_dequant", "nvfp4_gemv", "nvfp4_gemv_segments", "nvfp4_moe_gemv",
             "nvfp4_moe_workspace_bytes", "nvfp4_moe_shared_gemv",
             "nvfp4_moe_shared_workspace_bytes", "nvfp4_quantize_act", "nvfp4_gemv_w4a4",
-            "nvfp4_gemv_w4a4_workspace_bytes", "nvfp4_abi_version", "nvfp4_status_string",
+            "nvfp4_gemv_w4a4_workspace_bytes", "nvfp4_moe_w4a4_gemv",
+            "nvfp4_moe_w4a4_workspace_bytes", "nvfp4_abi_version", "nvfp4_status_string",
             "nvfp4_last_error"} <= set(names)
     for n in names:
         assert hasattr(L, n), n
 
 
 def test_version_and_status_strings(L):
-    assert L.nvfp4_abi_version() == 4
+    assert L.nvfp4_abi_version() == 5
     for s in range(8):
         assert L.nvfp4_status_string(s)
     assert L.nvfp4_status_string(99) == b"unknown status"
@@ -142,6 +143,50 @@ def test_moe_shared_checks(L):
     assert f(*args, 1, 4, 64, 64, 2, ctypes.byref(good), Y, sh_base[4], need,
              None) == ERR_ALIAS                                              # workspace on WS2 scales
     assert f(*args, 0, 4, 64, 64, 2, ctypes.byref(good), Y, WS, need, None) == OK
+
+
+def test_moe_w4a4_checks(L):
+    """Host-side validation of the W4A4 MoE call (no launch)."""
+    Sh = nv.MoeShared
+    lay = nv.moe_w4a4_workspace_layout(8, 4096, 1536, 8, 768)
+    assert nv.moe_w4a4_workspace_bytes(8, 4096, 1536, 8, 768) == lay["total"]
+    assert lay["hq"] == nv.moe_shared_workspace_bytes(8, 4096, 1536, 8, 768)
+    assert lay["total"] == lay["hq"] + 64 * 1536 * 2 + 8 * 4096 * 2
+    assert nv.moe_w4a4_workspace_bytes(1, 64, 32, 3, 0) == 256 + 256 + 256
+    assert nv.moe_w4a4_workspace_bytes(1, 64, 32, -3, 0) == 0
+    w = [A + i * 0x10000000 for i in range(7)]          # w13 x3, w2 x3, x
+    gx, gh = A + 0x70000000, A + 0x70000100
+    ids, gw = A + 0x80000000, A + 0x80001000
+    sh_base = [A + 0x90000000 + i * 0x1000000 for i in range(6)]
+    f = L.nvfp4_moe_w4a4_gemv
+    Y, WS = B, B + 0x1000000
+    need = nv.moe_w4a4_workspace_bytes(1, 64, 64, 2, 0)
+    assert f(*w, None, gh, ids, gw, 1, 4, 64, 64, 2, None, Y, WS, need, None) == ERR_NULL
+    assert f(*w, gx, None, ids, gw, 1, 4, 64, 64, 2, None, Y, WS, need, None) == ERR_NULL
+    assert f(*w, gx + 2, gh, ids, gw, 1, 4, 64, 64, 2, None, Y, WS, need, None) == ERR_ALIGN
+    assert f(*w, gx, gh, ids, gw, 1, 4, 64, 48, 2, None, Y, WS, need, None) == ERR_SHAPE
+    assert f(*w, gx, gh, ids, gw, 9, 4, 64, 64, 2, None, Y, WS, 1 << 40,
+             None) == ERR_UNSUPPORTED
+    # the W4A16 size lacks the quantized h and x
+    assert f(*w, gx, gh, ids, gw, 1, 4, 64, 64, 2, None, Y, WS,
+             nv.moe_workspace_bytes(1, 64, 64, 2), None) == ERR_WORKSPACE
+    assert f(*w, gx, gh, ids, gw, 1, 4, 64, 64, 2, None, Y, WS, need - 1,
+             None) == ERR_WORKSPACE
+    assert f(*w, gx, gh, ids, gw, 1, 4, 64, 64, 2, None, gx, WS, need,
+             None) == ERR_ALIAS                                              # y on g_x
+    assert f(*w, gx, gh, ids, gw, 1, 4, 64, 64, 2, None, Y, gh - 256, need,
+             None) == ERR_ALIAS                                              # workspace on g_h
+    good = Sh(*sh_base, 96)
+    need_s = nv.moe_w4a4_workspace_bytes(1, 64, 64, 2, 96)
+    assert need_s > need
+    assert f(*w, gx, gh, ids, gw, 1, 4, 64, 64, 2, ctypes.byref(good), Y, WS, need,
+             None) == ERR_WORKSPACE
+    nul = Sh(*sh_base, 96)
+    nul.w13_gscale = None
+    assert f(*w, gx, gh, ids, gw, 1, 4, 64, 64, 2, ctypes.byref(nul), Y, WS, need_s,
+             None) == ERR_NULL
+    assert f(*w, gx, gh, ids, gw, 0, 4, 64, 64, 2, ctypes.byref(good), Y, WS, need_s,
+             None) == OK
 
 
 def test_w4a4_checks(L):

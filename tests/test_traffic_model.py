@@ -49,3 +49,12 @@ def test_w4a4_bytes():
     assert traffic.gemv_w4a4_bytes(2, 4096, 4096) == (4096 * 4096 * 9 // 16 + 4
                                                       + 2 * 4096 * 9 // 16 + 4 + 2 * 4096 * 4)
     assert traffic.quantize_act_bytes(2, 4096) == 2 * 4096 * 2 + 4 + 2 * 4096 * 9 // 16
+
+
+def test_moe_w4a4_bytes_add_the_two_quantization_passes():
+    # the pages' W4A4 MoE sweeps: 288 experts of [3072, 4096] and [4096, 1536]
+    routed = traffic.moe_bytes(2, 4096, 1536, 8, 14)
+    q = traffic.moe_w4a4_bytes(2, 4096, 1536, 8, 14)
+    assert q - routed == 2 * 2 * 4096 * 2 + 2 * 16 * 1536 * 2 + 8
+    with_shared = traffic.moe_w4a4_bytes(2, 4096, 1536, 8, 14, 768)
+    assert with_shared - q == traffic.moe_shared_bytes(2, 4096, 1536, 8, 14, 768) - routed
