@@ -87,8 +87,11 @@ __device__ __forceinline__ void gate_up_rows(const uint8_t* __restrict__ codes,
       }
 }
 
-// grid (S [+ 1 for the shared expert], ceil(ceil(max(I, Is)/2) / kMoeWaves));
-// a wavefront owns one gate/up row pair.
+// grid (ceil(ceil(max(I, Is)/2) / kMoeWaves), S [+ 1 for the shared expert, row 0]);
+// a wavefront owns one gate/up row pair. Row blocks are the fast grid axis:
+// workgroups are dealt to the 8 XCDs round robin in linear order, so each
+// expert's rows spread over all XCDs (with the slot as the fast axis, every
+// row block of a slot's expert landed on the XCD of slot mod 8).
 // Routed slots read xr with weight scale w13_gscale[e] * *ga (xr = x and
 // ga = NULL for W4A16; the W4A4 activations on the NVFP4 grid and their
 // static scale otherwise); the shared expert always reads x.
@@ -98,10 +101,12 @@ __global__ __launch_bounds__(256) void k_moe_gate_up(
     const uint16_t* __restrict__ xr, const float* __restrict__ ga,
     const int32_t* __restrict__ ids, int S, int topk, int64_t E, int64_t H, int64_t I,
     uint16_t* __restrict__ h, const MoeShared sh, int M) {
-  const int j = blockIdx.x;
+  // the shared expert (when there is one) is grid row 0, so that its
+  // workgroups, which stream their rows once per 4 tokens, start first
+  const int j = sh.I > 0 ? (blockIdx.y == 0 ? S : (int)blockIdx.y - 1) : (int)blockIdx.y;
   const int lane = threadIdx.x & 63;
   const int64_t pair =
-      (int64_t)blockIdx.y * kMoeWaves + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+      (int64_t)blockIdx.x * kMoeWaves + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int64_t r0 = pair * 2;
   if (j == S) {
     // the shared expert: its rows once, for all M tokens (its slots)
@@ -306,7 +311,7 @@ hipError_t launch_moe(const uint8_t* w13_codes, const uint8_t* w13_scales,
   {
     const int64_t pairs = ((sh.I > I ? sh.I : I) + 1) / 2;
     const int64_t yb = (pairs + kMoeWaves - 1) / kMoeWaves;
-    hipLaunchKernelGGL(k_moe_gate_up, dim3(S + (sh.I > 0 ? 1 : 0), (unsigned)yb), dim3(256), 0,
+    hipLaunchKernelGGL(k_moe_gate_up, dim3((unsigned)yb, S + (sh.I > 0 ? 1 : 0)), dim3(256), 0,
                        stream, w13_codes, w13_scales, w13_gscale, x, xr, ga13, ids, S, topk, E,
                        H, I, h, sh, M);
   }

@@ -83,56 +83,44 @@ __global__ __launch_bounds__(256) void k_w4a4_prep(const uint8_t* __restrict__ c
   }
 }
 
-// One thread per 16-element block: quantize like k_quantize_act, then write
-// the decoded values e2m1 * s as bf16 (exact: at most 6 significant bits) in
-// place of the codes. Row r = block / bpr is skipped when ids names no expert
-// in [0, E) for it.
+// One lane per element, 16 lanes per block: quantize like k_quantize_act
+// (block amax by a 16-lane max, which is exact and order-free), then write
+// the decoded value e2m1 * s as bf16 (exact: at most 6 significant bits) in
+// place of the code. Row r = element / K is skipped when ids names no expert
+// in [0, E) for it. n and K are multiples of 16, so the lanes of a block
+// stay or leave together.
 __global__ __launch_bounds__(256) void k_quantize_decode(const uint16_t* __restrict__ x,
-                                                         size_t nblocks, int64_t bpr,
+                                                         size_t n, int64_t K,
                                                          const float* __restrict__ gscale,
                                                          const int32_t* __restrict__ ids,
                                                          int64_t E,
                                                          uint16_t* __restrict__ out) {
-  const size_t b = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (b >= nblocks) return;
+  const size_t t = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (t >= n) return;
   if (ids) {
-    const int32_t e = ids[b / (size_t)bpr];
+    const int32_t e = ids[t / (size_t)K];
     if (e < 0 || (int64_t)e >= E) return;
   }
-  const uint4* xp = reinterpret_cast<const uint4*>(x + b * 16);
-  const uint4 v0 = xp[0], v1 = xp[1];
-  const uint32_t u[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
-  float w[16];
+  const float g = *gscale;
+  const float w = __uint_as_float((uint32_t)x[t] << 16);   // bf16 -> fp32 is exact
+  float ab = fabsf(w);
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {   // bf16 -> fp32 is exact
-    w[2 * i] = __uint_as_float(u[i] << 16);
-    w[2 * i + 1] = __uint_as_float(u[i] & 0xFFFF0000u);
-  }
-  uint32_t lo, hi;
-  const uint32_t sc = encode_block16(w, *gscale, lo, hi);
-  const float s = e4m3_to_f32<0>(sc);
-  uint32_t o[8];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const float2_t a = i == 0 ? e2m1x2_to_f32<0>(lo) : i == 1 ? e2m1x2_to_f32<1>(lo)
-                     : i == 2 ? e2m1x2_to_f32<2>(lo) : e2m1x2_to_f32<3>(lo);
-    const float2_t c = i == 0 ? e2m1x2_to_f32<0>(hi) : i == 1 ? e2m1x2_to_f32<1>(hi)
-                     : i == 2 ? e2m1x2_to_f32<2>(hi) : e2m1x2_to_f32<3>(hi);
-    o[i] = (__float_as_uint(a.x * s) >> 16) | (__float_as_uint(a.y * s) & 0xFFFF0000u);
-    o[4 + i] = (__float_as_uint(c.x * s) >> 16) | (__float_as_uint(c.y * s) & 0xFFFF0000u);
-  }
-  uint4* op = reinterpret_cast<uint4*>(out + b * 16);
-  op[0] = make_uint4(o[0], o[1], o[2], o[3]);
-  op[1] = make_uint4(o[4], o[5], o[6], o[7]);
+  for (int off = 8; off >= 1; off >>= 1) ab = fmaxf(ab, __shfl_xor(ab, off, 16));
+  const float r = ab / (6.0f * g);
+  const float s = e4m3_to_f32<0>(e4m3_encode(r));
+  const uint32_t code = s != 0.0f ? e2m1_encode(w / (s * g)) : 0u;
+  const float v = e2m1x2_to_f32<0>(code).x * s;
+  out[t] = (uint16_t)(__float_as_uint(v) >> 16);
 }
 
 hipError_t launch_quantize_decode(const uint16_t* x, int64_t rows, int64_t K,
                                   const float* gscale, const int32_t* ids, int64_t E,
                                   uint16_t* out, hipStream_t stream) {
-  const size_t nblocks = (size_t)rows * (size_t)K / 16;
-  if (nblocks)
-    hipLaunchKernelGGL(k_quantize_decode, dim3((unsigned)((nblocks + 255) / 256)), dim3(256), 0,
-                       stream, x, nblocks, (int64_t)(K / 16), gscale, ids, E, out);
+  const size_t n = (size_t)rows * (size_t)K;
+  if (n > 0xFFFFFF00u) return hipErrorInvalidConfiguration;   // a grid counts < 2^32 lanes
+  if (n)
+    hipLaunchKernelGGL(k_quantize_decode, dim3((unsigned)((n + 255) / 256)), dim3(256), 0,
+                       stream, x, n, K, gscale, ids, E, out);
   return hipGetLastError();
 }
 
