@@ -123,11 +123,28 @@ __device__ __forceinline__ uint32_t encode_block16(const float (&w)[16], float g
 
 // --------------------------------------------------------------- reductions
 
-// Sum over the 64 lanes of a wavefront; every lane receives the total.
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float v) {
+  return __builtin_bit_cast(
+      float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), CTRL, 0xF, 0xF, true));
+}
+
+// Sum over the 64 lanes of a wavefront; every lane receives the total. All
+// 64 lanes must be active. Within each 16-lane row the partial sums travel
+// by DPP (quad permutations [1,0,3,2] and [2,3,0,1], then the half-row and
+// row mirrors), so each lane ends with its row's sum; the four row sums are
+// then read out with v_readlane and added in a fixed order. No LDS traffic,
+// and the same result on every lane.
 __device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
-  return v;
+  v += dpp_f32<0xB1>(v);    // quad_perm [1,0,3,2]
+  v += dpp_f32<0x4E>(v);    // quad_perm [2,3,0,1]
+  v += dpp_f32<0x141>(v);   // row_half_mirror
+  v += dpp_f32<0x140>(v);   // row_mirror
+  const float r0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 0));
+  const float r1 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 16));
+  const float r2 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 32));
+  const float r3 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 48));
+  return (r0 + r1) + (r2 + r3);
 }
 
 __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
