@@ -255,9 +255,13 @@ size_t nvfp4_gemv_w4a4_workspace_bytes(int64_t M, int64_t K);
 /*
  * nvfp4_gemv_w4a4 -- y[M, N] (fp32) = g_w * g_x * decode(W) . decode(x)^T, both
  * operands NVFP4 g16 (card.json performance[20], [24]: the W4A4 dense FFN).
- * The activation values e2m1_x * s_x are exact in bf16; they are decoded once
- * into the workspace and multiplied by the weight stream as in nvfp4_gemv,
- * with g_w * g_x (rounded once to fp32) applied to the fp32 sum.
+ * M <= 2: one launch; the activation codes are decoded in registers and each
+ * 16-block's sum of e2m1_w * e2m1_x, times s_w * s_x, is exact, so fp32
+ * accumulation is the only rounding. M >= 3: the activation values
+ * e2m1_x * s_x (exact in bf16) are decoded once into the workspace and
+ * multiplied by the weight stream as in nvfp4_gemv. Either way g_w * g_x
+ * (rounded once to fp32) scales the fp32 sum. The workspace is required for
+ * every M (unused when M <= 2).
  *
  *   codes_w, scales_w, gscale_w  the weight, as in nvfp4_gemv;
  *   codes_x   uint8[M, K/2], 16-byte aligned; scales_x uint8[M, K/16], 2-byte

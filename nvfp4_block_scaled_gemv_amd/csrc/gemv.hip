@@ -51,6 +51,44 @@ __global__ __launch_bounds__(256) void k_gemv(const SegTable tab, const uint16_t
   }
 }
 
+// W4A4 at M <= 2: k_gemv's loop with NVFP4 activations read and decoded in
+// place (wave_row_dots_q), and the tensor scale g_w * g_x (one fp32
+// rounding). One matrix.
+template <int M, int R>
+__global__ __launch_bounds__(256) void k_gemv_w4a4(const SegTable tab,
+                                                   const uint8_t* __restrict__ codes_x,
+                                                   const uint8_t* __restrict__ scales_x,
+                                                   const float* __restrict__ gscale_x,
+                                                   int64_t K) {
+  const int lane = threadIdx.x & 63;
+  const int64_t wave =
+      (int64_t)blockIdx.x * kWavesPerBlock + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int64_t nwaves = (int64_t)gridDim.x * kWavesPerBlock;
+  const int64_t units = tab.start[kMaxSegments];
+  const uint8_t* xc[M];
+  const uint8_t* xs[M];
+#pragma unroll
+  for (int m = 0; m < M; ++m) {
+    xc[m] = codes_x + (int64_t)m * (K / 2);
+    xs[m] = scales_x + (int64_t)m * (K / 16);
+  }
+  const float g = *tab.gscale[0] * *gscale_x;
+  const int64_t N = tab.N[0];
+  for (int64_t u = wave; u < units; u += nwaves) {
+    const int64_t n0 = u * R;
+    int64_t rows[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) rows[r] = (n0 + r < N) ? (n0 + r) : (N - 1);
+    float acc[R][M];
+    wave_row_dots_q<M, R>(tab.codes[0], tab.scales[0], K, rows, xc, xs, acc);
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+#pragma unroll
+      for (int m = 0; m < M; ++m)
+        if (lane == r * M + m && n0 + r < N) tab.y[0][(int64_t)m * N + n0 + r] = acc[r][m] * g;
+  }
+}
+
 __global__ void k_fill_zero(float* y, size_t n) {
   for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
        i += (size_t)gridDim.x * blockDim.x)
@@ -106,6 +144,42 @@ hipError_t launch_gemv_segments(const SegDesc* d, int n, const uint16_t* x, int 
     case 1: launch_valu<1>(d, n, rows, x, K, stream); break;
     case 2: launch_valu<2>(d, n, rows, x, K, stream); break;
     default: return launch_gemv_mfma(d, n, x, M, K, stream);
+  }
+  return hipGetLastError();
+}
+
+template <int M, int R>
+static void launch_w4a4_m(const SegDesc& d, const uint8_t* codes_x, const uint8_t* scales_x,
+                          const float* gscale_x, int64_t K, hipStream_t stream) {
+  const SegTable tab = make_seg_table(&d, 1, R);
+  const int64_t units = tab.start[kMaxSegments];
+  const int64_t want = (units + kWavesPerBlock - 1) / kWavesPerBlock;
+  const int64_t cap = (int64_t)1 << 20;
+  const unsigned grid = (unsigned)(want < cap ? want : cap);
+  hipLaunchKernelGGL((k_gemv_w4a4<M, R>), dim3(grid), dim3(256), 0, stream, tab, codes_x,
+                     scales_x, gscale_x, K);
+}
+
+template <int M>
+static void launch_w4a4_valu(const SegDesc& d, const uint8_t* codes_x, const uint8_t* scales_x,
+                             const float* gscale_x, int64_t K, hipStream_t stream) {
+  if (d.N >= 32768)
+    launch_w4a4_m<M, 4>(d, codes_x, scales_x, gscale_x, K, stream);
+  else if (d.N >= 4096)
+    launch_w4a4_m<M, 2>(d, codes_x, scales_x, gscale_x, K, stream);
+  else
+    launch_w4a4_m<M, 1>(d, codes_x, scales_x, gscale_x, K, stream);
+}
+
+hipError_t launch_gemv_w4a4_valu(const uint8_t* codes, const uint8_t* scales,
+                                 const float* gscale, const uint8_t* codes_x,
+                                 const uint8_t* scales_x, const float* gscale_x, int M,
+                                 int64_t N, int64_t K, float* y, hipStream_t stream) {
+  const SegDesc d = {codes, scales, gscale, y, N};
+  switch (M) {
+    case 1: launch_w4a4_valu<1>(d, codes_x, scales_x, gscale_x, K, stream); break;
+    case 2: launch_w4a4_valu<2>(d, codes_x, scales_x, gscale_x, K, stream); break;
+    default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
 }

@@ -86,4 +86,80 @@ __device__ __forceinline__ void wave_row_dots(const uint8_t* __restrict__ codes,
       if (m < ns) out[r][m] = wave_sum(out[r][m]);
 }
 
+// The same with NVFP4 activations (W4A4): activation row m is codes xc[m]
+// (two E2M1 per byte) and E4M3 scales xsc[m], one per 16 elements. Per
+// 16-element block, the 16 products e2m1_w * e2m1_x (exact in bf16 inputs)
+// are summed exactly (each is a multiple of 1/4 below 36), and the block sum
+// times s_w * s_x (a product of two E4M3 values, exact in fp32) is exact too:
+// accumulation is the only rounding.
+template <int MS, int R>
+__device__ __forceinline__ void wave_row_dots_q(const uint8_t* __restrict__ codes,
+                                                const uint8_t* __restrict__ scales,
+                                                int64_t K, const int64_t (&rows)[R],
+                                                const uint8_t* const (&xc)[MS],
+                                                const uint8_t* const (&xsc)[MS],
+                                                float (&out)[R][MS]) {
+  const int lane = threadIdx.x & 63;
+  const int64_t C = K >> 5, cb = K >> 1, sb = K >> 4;
+#pragma unroll
+  for (int r = 0; r < R; ++r)
+#pragma unroll
+    for (int m = 0; m < MS; ++m) out[r][m] = 0.0f;
+
+  for (int64_t c = lane; c < C; c += 64) {
+    u32x4_t q[R], qx[MS];
+    uint32_t sw[R], swx[MS];
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      q[r] = load_stream(codes + rows[r] * cb + c * 16);
+      sw[r] = *reinterpret_cast<const uint16_t*>(scales + rows[r] * sb + c * 2);
+    }
+#pragma unroll
+    for (int m = 0; m < MS; ++m) {
+      qx[m] = *reinterpret_cast<const u32x4_t*>(xc[m] + c * 16);
+      swx[m] = *reinterpret_cast<const uint16_t*>(xsc[m] + c * 2);
+    }
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+      bf16x2_t wd[R][8];
+      float s[R];
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        const uint32_t w0 = b ? q[r].z : q[r].x;
+        const uint32_t w1 = b ? q[r].w : q[r].y;
+        wd[r][0] = e2m1x2_to_bf16<0>(w0);
+        wd[r][1] = e2m1x2_to_bf16<1>(w0);
+        wd[r][2] = e2m1x2_to_bf16<2>(w0);
+        wd[r][3] = e2m1x2_to_bf16<3>(w0);
+        wd[r][4] = e2m1x2_to_bf16<0>(w1);
+        wd[r][5] = e2m1x2_to_bf16<1>(w1);
+        wd[r][6] = e2m1x2_to_bf16<2>(w1);
+        wd[r][7] = e2m1x2_to_bf16<3>(w1);
+        s[r] = b ? e4m3_to_f32<1>(sw[r]) : e4m3_to_f32<0>(sw[r]);
+      }
+#pragma unroll
+      for (int m = 0; m < MS; ++m) {
+        const uint32_t v0 = b ? qx[m].z : qx[m].x;
+        const uint32_t v1 = b ? qx[m].w : qx[m].y;
+        const bf16x2_t xv[8] = {e2m1x2_to_bf16<0>(v0), e2m1x2_to_bf16<1>(v0),
+                                e2m1x2_to_bf16<2>(v0), e2m1x2_to_bf16<3>(v0),
+                                e2m1x2_to_bf16<0>(v1), e2m1x2_to_bf16<1>(v1),
+                                e2m1x2_to_bf16<2>(v1), e2m1x2_to_bf16<3>(v1)};
+        const float sx = b ? e4m3_to_f32<1>(swx[m]) : e4m3_to_f32<0>(swx[m]);
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+          float p = 0.0f;
+#pragma unroll
+          for (int j = 0; j < 8; ++j) p = dot2(wd[r][j], xv[j], p);
+          out[r][m] = __builtin_fmaf(p, s[r] * sx, out[r][m]);
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int r = 0; r < R; ++r)
+#pragma unroll
+    for (int m = 0; m < MS; ++m) out[r][m] = wave_sum(out[r][m]);
+}
+
 }  // namespace nvfp4

@@ -55,6 +55,11 @@ hipError_t launch_gemv_w4a4(const uint8_t* codes_w, const uint8_t* scales_w,
                             const float* gscale_w, const uint8_t* codes_x,
                             const uint8_t* scales_x, const float* gscale_x, int M, int64_t N,
                             int64_t K, float* y, void* workspace, hipStream_t stream);
+// W4A4 GEMV at M <= 2 on the vector ALUs, activations read as NVFP4.
+hipError_t launch_gemv_w4a4_valu(const uint8_t* codes, const uint8_t* scales,
+                                 const float* gscale, const uint8_t* codes_x,
+                                 const uint8_t* scales_x, const float* gscale_x, int M,
+                                 int64_t N, int64_t K, float* y, hipStream_t stream);
 // bf16 rows [rows, K] quantized with the static scale *gscale and written
 // back as the exact bf16 values e2m1 * s (the tensor scale left out). With
 // ids, row r is skipped (not written) when ids[r] is outside [0, E).

@@ -28,27 +28,33 @@ W4a4Layout w4a4_layout(int64_t M, int64_t K) {
   return L;
 }
 
-// One thread per 16-element block of x.
-__global__ __launch_bounds__(256) void k_quantize_act(const uint16_t* __restrict__ x,
-                                                      size_t nblocks,
+// Eight lanes per 16-element block, two elements (one code byte) per lane:
+// the block amax by a max over the 8 lanes (DPP within quads and half-rows;
+// exact and order-free), then the same scale and element encoders as pack.
+// Lane 0 of each group writes the scale byte. n (code bytes) is a multiple
+// of 8, so the lanes of a block stay or leave together.
+__global__ __launch_bounds__(256) void k_quantize_act(const uint16_t* __restrict__ x, size_t n,
                                                       const float* __restrict__ gscale_x,
                                                       uint8_t* __restrict__ codes,
                                                       uint8_t* __restrict__ scales) {
-  const size_t b = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (b >= nblocks) return;
-  const uint4* xp = reinterpret_cast<const uint4*>(x + b * 16);
-  const uint4 v0 = xp[0], v1 = xp[1];
-  const uint32_t u[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
-  float w[16];
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {   // bf16 -> fp32 is exact
-    w[2 * i] = __uint_as_float(u[i] << 16);
-    w[2 * i + 1] = __uint_as_float(u[i] & 0xFFFF0000u);
+  const size_t t = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (t >= n) return;
+  const float g = *gscale_x;
+  const uint32_t u = reinterpret_cast<const uint32_t*>(x)[t];
+  const float w0 = __uint_as_float(u << 16), w1 = __uint_as_float(u & 0xFFFF0000u);
+  float ab = fmaxf(fabsf(w0), fabsf(w1));
+  ab = fmaxf(ab, dpp_f32<0xB1>(ab));    // quad_perm [1,0,3,2]
+  ab = fmaxf(ab, dpp_f32<0x4E>(ab));    // quad_perm [2,3,0,1]
+  ab = fmaxf(ab, dpp_f32<0x141>(ab));   // row_half_mirror: the other quad of the 8
+  const uint32_t sc = e4m3_encode(ab / (6.0f * g));
+  const float s = e4m3_to_f32<0>(sc);
+  uint32_t byte = 0u;
+  if (s != 0.0f) {
+    const float dn = s * g;
+    byte = e2m1_encode(w0 / dn) | (e2m1_encode(w1 / dn) << 4);
   }
-  uint32_t lo, hi;
-  const uint32_t sc = encode_block16(w, *gscale_x, lo, hi);
-  *reinterpret_cast<uint2*>(codes + b * 8) = make_uint2(lo, hi);
-  scales[b] = (uint8_t)sc;
+  codes[t] = (uint8_t)byte;
+  if ((t & 7) == 0) scales[t >> 3] = (uint8_t)sc;
 }
 
 // One thread per 32 activation elements (16 code bytes, two blocks): the
@@ -83,10 +89,10 @@ __global__ __launch_bounds__(256) void k_w4a4_prep(const uint8_t* __restrict__ c
   }
 }
 
-// One lane per element, 16 lanes per block: quantize like k_quantize_act
-// (block amax by a 16-lane max, which is exact and order-free), then write
-// the decoded value e2m1 * s as bf16 (exact: at most 6 significant bits) in
-// place of the code. Row r = element / K is skipped when ids names no expert
+// One lane per element, 16 lanes per block (a DPP row): quantize like
+// k_quantize_act (block amax by a max over the row, exact and order-free),
+// then write the decoded value e2m1 * s as bf16 (exact: at most 6
+// significant bits) in place of the code. Row r = element / K is skipped when ids names no expert
 // in [0, E) for it. n and K are multiples of 16, so the lanes of a block
 // stay or leave together.
 __global__ __launch_bounds__(256) void k_quantize_decode(const uint16_t* __restrict__ x,
@@ -104,8 +110,10 @@ __global__ __launch_bounds__(256) void k_quantize_decode(const uint16_t* __restr
   const float g = *gscale;
   const float w = __uint_as_float((uint32_t)x[t] << 16);   // bf16 -> fp32 is exact
   float ab = fabsf(w);
-#pragma unroll
-  for (int off = 8; off >= 1; off >>= 1) ab = fmaxf(ab, __shfl_xor(ab, off, 16));
+  ab = fmaxf(ab, dpp_f32<0xB1>(ab));    // quad_perm [1,0,3,2]
+  ab = fmaxf(ab, dpp_f32<0x4E>(ab));    // quad_perm [2,3,0,1]
+  ab = fmaxf(ab, dpp_f32<0x141>(ab));   // row_half_mirror
+  ab = fmaxf(ab, dpp_f32<0x140>(ab));   // row_mirror: the 16-lane row
   const float r = ab / (6.0f * g);
   const float s = e4m3_to_f32<0>(e4m3_encode(r));
   const uint32_t code = s != 0.0f ? e2m1_encode(w / (s * g)) : 0u;
@@ -126,10 +134,11 @@ hipError_t launch_quantize_decode(const uint16_t* x, int64_t rows, int64_t K,
 
 hipError_t launch_quantize_act(const uint16_t* x, int64_t M, int64_t K, const float* gscale_x,
                                uint8_t* codes, uint8_t* scales, hipStream_t stream) {
-  const size_t nblocks = (size_t)M * (size_t)K / 16;
-  if (nblocks)
-    hipLaunchKernelGGL(k_quantize_act, dim3((unsigned)((nblocks + 255) / 256)), dim3(256), 0,
-                       stream, x, nblocks, gscale_x, codes, scales);
+  const size_t n = (size_t)M * (size_t)K / 2;
+  if (n > 0xFFFFFF00u) return hipErrorInvalidConfiguration;   // a grid counts < 2^32 lanes
+  if (n)
+    hipLaunchKernelGGL(k_quantize_act, dim3((unsigned)((n + 255) / 256)), dim3(256), 0,
+                       stream, x, n, gscale_x, codes, scales);
   return hipGetLastError();
 }
 
@@ -137,6 +146,9 @@ hipError_t launch_gemv_w4a4(const uint8_t* codes_w, const uint8_t* scales_w,
                             const float* gscale_w, const uint8_t* codes_x,
                             const uint8_t* scales_x, const float* gscale_x, int M, int64_t N,
                             int64_t K, float* y, void* workspace, hipStream_t stream) {
+  if (M <= 2)   // the vector-ALU kernel reads the NVFP4 activations directly
+    return launch_gemv_w4a4_valu(codes_w, scales_w, gscale_w, codes_x, scales_x, gscale_x, M,
+                                 N, K, y, stream);
   const W4a4Layout L = w4a4_layout(M, K);
   uint16_t* xt = reinterpret_cast<uint16_t*>(static_cast<char*>(workspace) + L.x_off);
   float* gp = reinterpret_cast<float*>(static_cast<char*>(workspace) + L.g_off);

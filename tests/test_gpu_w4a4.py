@@ -74,6 +74,19 @@ def test_w4a4_shapes(M, N, K):
     check_tol(y, y_ref, ad, f"w4a4 M={M} N={N} K={K}")
 
 
+@pytest.mark.parametrize("M", [1, 2])
+def test_w4a4_four_rows_per_wavefront_with_ragged_tail(M):
+    """N >= 32768 takes four rows per wavefront at M <= 2; N = 40003 leaves
+    a tail of three rows."""
+    N, K = 40003, 64
+    say(f"[w4a4] M={M} N={N} K={K}")
+    cw, sw = workloads.random_nvfp4(6, M, 77, N, K, 0x20, 0x50)
+    gw = np.float32(0.0173)
+    x = workloads.x_bf16(6, M, 77, M, K)
+    y, (y_ref, ad) = run_w4a4(cw, sw, gw, x, static_scale(6, M, K))
+    check_tol(y, y_ref, ad, f"w4a4 M={M} N={N} K={K}")
+
+
 def test_w4a4_zero_k_and_empty():
     c = torch.zeros((4, 16), dtype=torch.uint8, device="cuda")
     s = torch.zeros((4, 2), dtype=torch.uint8, device="cuda")
