@@ -62,6 +62,19 @@ def git_sha():
         return None
 
 
+def library_source_hash():
+    """Hash of the library's sources and public header (identifies the build
+    where the tree carries no git metadata)."""
+    import glob
+    import hashlib
+    h = hashlib.sha256()
+    for path in sorted(glob.glob(os.path.join(ROOT, "nvfp4_block_scaled_gemv_amd", "csrc", "*"))
+                       + [os.path.join(ROOT, "include", "nvfp4_gemv.h")]):
+        with open(path, "rb") as f:
+            h.update(os.path.basename(path).encode() + b"\0" + f.read())
+    return h.hexdigest()[:16]
+
+
 def cpu_model():
     try:
         with open("/proc/cpuinfo") as f:
@@ -537,9 +550,49 @@ def summarize_stats(stats_csv, cmd, out, top=16):
         lines.append(f"{int(r['Calls']):7d} {float(r['AverageNs']) / 1e3:9.2f} {med:9.2f} "
                      f"{p10:9.2f} {p90:9.2f} {float(r['MinNs']) / 1e3:9.2f} "
                      f"{float(r['MaxNs']) / 1e3:9.2f} {float(r['Percentage']):6.2f}  {short}")
+    if os.path.exists(trace_csv):
+        lines += moe_pass_sums(trace_csv)
     with open(out, "w") as f:
         f.write("\n".join(lines) + "\n")
     print("\n".join(lines))
+
+
+def moe_pass_sums(trace_csv):
+    """MoE passes from a kernel trace, in dispatch order: each pass is
+    [k_quantize_decode] k_moe_gate_up [k_quantize_decode] k_moe_down, and
+    its time is the sum of its kernels' durations (gaps between launches
+    excluded). Grouped by the gate|up grid's y size (slots M*topk, plus one
+    row when a shared expert rides along) and by whether the activations
+    are quantized (W4A4)."""
+    import csv
+    with open(trace_csv, newline="") as f:
+        rows = [r for r in csv.DictReader(f)
+                if any(k in r["Kernel_Name"] for k in
+                       ("k_moe_gate_up", "k_moe_down", "k_quantize_decode"))]
+    rows.sort(key=lambda r: int(r["Start_Timestamp"]))
+    passes, cur = {}, None
+    for r in rows:
+        d = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
+        name = r["Kernel_Name"]
+        if cur is None:
+            cur = {"w4a4": "k_quantize_decode" in name, "gy": None, "us": 0.0, "n": 0}
+        cur["us"] += d
+        cur["n"] += 1
+        if "k_moe_gate_up" in name:
+            cur["gy"] = int(r.get("Grid_Size_Y", 0) or 0)
+        if "k_moe_down" in name:
+            key = (cur["gy"], cur["w4a4"], cur["n"])
+            passes.setdefault(key, []).append(cur["us"])
+            cur = None
+    out = ["", "# MoE passes: sum of the kernel durations of each pass (us), by gate|up",
+           "# grid.y (slots M*topk, +1 with a shared expert) and W4A4 or not",
+           f"{'passes':>7} {'median':>9} {'p10':>9} {'p90':>9}  pass"]
+    for (gy, w4, n), v in sorted(passes.items(), key=lambda kv: (kv[0][0] or 0, kv[0][1])):
+        a = np.array(v)
+        out.append(f"{len(v):7d} {np.median(a):9.2f} {np.percentile(a, 10):9.2f} "
+                   f"{np.percentile(a, 90):9.2f}  gate|up grid.y={gy}, "
+                   f"{'W4A4' if w4 else 'W4A16'}, {n} launches")
+    return out
 
 
 def summarize_counters(csvs, cmd, out, match="nvfp4::"):
@@ -688,6 +741,7 @@ def main():
     result["env"] = {"gpu": props.name, "cus": props.multi_processor_count,
                      "dpm_clocks": gpu_clock_state(),
                      "hip": torch.version.hip, "torch": torch.__version__, "git": git_sha(),
+                     "library_sources_sha256_16": library_source_hash(),
                      "argv": sys.argv[1:]}
     print(json.dumps(result), flush=True)
 
