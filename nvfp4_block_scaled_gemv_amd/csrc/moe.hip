@@ -1,30 +1,35 @@
-// moe.hip -- NVFP4 g16 W4A16 MoE expert slots on gfx950.
+// moe.hip -- NVFP4 g16 MoE expert slots on gfx950.
 //
 // The pages' MoE decode path (graph.json nodes "l3.moe.experts_gate_up",
 // "l3.moe.experts_act", "l3.moe.experts_down", "l3.moe.blend"; card.json
 // performance[31] row union, performance[33] W4A16 slot GEMV, performance[64]
 // union sweep) runs as two launches on the caller's stream, with no host
 // synchronisation and no atomics:
-//   1. k_moe_gate_up: grid (slot j, row block). The workgroup of the first
+//   1. k_moe_gate_up: grid (row block, slot j). The workgroup of the first
 //      slot that names an expert streams that expert's gate|up rows once and
 //      dots them with x of every slot routed to it (the row union, found with
 //      wavefront ballots over the ids); it writes h = bf16(silu(gate) * up)
 //      per slot. Workgroups of later slots with the same id, and of invalid
 //      ids, exit at once.
-//   2. k_moe_down: the down projection and the gate-weighted combine in one
-//      pass. For output row n and token m,
+//   2. The down projection and the gate-weighted combine in one pass. For
+//      output row n and token m,
 //        y[m, n] = sum_j gate_w[m, j] * g2[e_j] * W2[e_j][n, :] . h_j
 //      is one dot product over the token's valid slots laid end to end (a
-//      K axis of (valid slots) x I), so a wavefront owns R output rows and
-//      walks (slot, 32-element chunk) pairs with all 64 lanes busy whatever
-//      I is. The slot sum is a fixed-order register reduction: deterministic,
-//      no per-slot output buffer, no separate combine launch.
+//      K axis of (valid slots) x I), walked in (slot, 32-element chunk)
+//      pairs with all 64 lanes busy whatever I is. At M = 1 a wavefront owns
+//      R output rows (k_moe_down); at M >= 2 the pairs of all tokens are
+//      split over the wavefronts of a workgroup (k_moe_down_split). Sums run
+//      in a fixed order: deterministic, no per-slot output buffer, no
+//      separate combine launch.
 // An optional shared expert (graph.json nodes "l3.moe.shared_gate_up",
 // "l3.moe.shared_act", "l3.moe.shared_down"; "l3.moe.blend" takes the routed
 // slots and the shared output) rides in the same two launches: one more
-// gate|up workgroup column streams its rows once for all M tokens, and each
-// token's down dot product runs on over the shared expert's chunks after its
-// routed slots, with coefficient g2s (gate weight 1).
+// gate|up grid row streams its rows once for all M tokens, and each token's
+// down dot product runs on over the shared expert's chunks after its routed
+// slots, with coefficient g2s (gate weight 1).
+// W4A4 routed experts (card.json performance[64], [65]) use the same kernels
+// on activations put on the NVFP4 grid by k_quantize_decode (w4a4.hip), with
+// the static scales folded into the weight scale and the combine weight.
 #include "gemv_core.h"
 #include "internal.h"
 
@@ -33,6 +38,7 @@ namespace nvfp4 {
 constexpr int kMoeWaves = 4;     // wavefronts per workgroup
 constexpr int kDownRows = 2;     // output rows per wavefront in the down pass
 constexpr int kDownUnroll = 2;   // (slot, chunk) pairs in flight per lane
+constexpr int kGateUpSlots = 2;  // slots per pass over an expert's gate|up rows, M >= 2
 
 static inline size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 
@@ -95,6 +101,14 @@ __device__ __forceinline__ void gate_up_rows(const uint8_t* __restrict__ codes,
 // Routed slots read xr with weight scale w13_gscale[e] * *ga (xr = x and
 // ga = NULL for W4A16; the W4A4 activations on the NVFP4 grid and their
 // static scale otherwise); the shared expert always reads x.
+// The shared expert and a routed expert take the same path once their
+// weights, activation rows and slot set are chosen, so the dot-product engine
+// is inlined once per slot-group width: MSX slots per pass over the rows
+// (one pass per slot at MSX = 1, which the launcher uses at M = 1; it keeps
+// the kernel at the register count of one slot and so at 6 wavefronts per
+// SIMD, against 3 when a 4-slot group and a separate shared-expert path were
+// inlined side by side).
+template <int MSX>
 __global__ __launch_bounds__(256) void k_moe_gate_up(
     const uint8_t* __restrict__ w13_codes, const uint8_t* __restrict__ w13_scales,
     const float* __restrict__ w13_gscale, const uint16_t* __restrict__ x,
@@ -102,48 +116,72 @@ __global__ __launch_bounds__(256) void k_moe_gate_up(
     const int32_t* __restrict__ ids, int S, int topk, int64_t E, int64_t H, int64_t I,
     uint16_t* __restrict__ h, const MoeShared sh, int M) {
   // the shared expert (when there is one) is grid row 0, so that its
-  // workgroups, which stream their rows once per 4 tokens, start first
-  const int j = sh.I > 0 ? (blockIdx.y == 0 ? S : (int)blockIdx.y - 1) : (int)blockIdx.y;
+  // workgroups, which serve every token, start first
+  const bool shared_row = sh.I > 0 && blockIdx.y == 0;
+  const int j = sh.I > 0 ? (int)blockIdx.y - 1 : (int)blockIdx.y;   // routed slot
   const int lane = threadIdx.x & 63;
   const int64_t pair =
       (int64_t)blockIdx.x * kMoeWaves + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int64_t r0 = pair * 2;
-  if (j == S) {
+  const uint8_t* codes;
+  const uint8_t* scales;
+  const uint16_t* xs;   // activation rows; slot s reads row s / xdiv
+  uint16_t* hd;         // h rows; slot s writes row s
+  float g;
+  int64_t Iv;
+  int xdiv;
+  uint64_t m0, m1;      // the slots to serve: bit s of m0, bit s - 64 of m1
+  if (shared_row) {
     // the shared expert: its rows once, for all M tokens (its slots)
     if (r0 >= sh.I) return;
-    const float gs = *sh.g13;
-    for (int b = 0; b < M; b += 4) {
-      int slot[4];
-#pragma unroll
-      for (int q = 0; q < 4; ++q) slot[q] = b + q < M ? b + q : b;
-      gate_up_rows<4>(sh.c13, sh.s13, gs, x, H, sh.I, r0, 1, slot, M - b < 4 ? M - b : 4,
-                      sh.h);
+    codes = sh.c13;
+    scales = sh.s13;
+    g = *sh.g13;
+    xs = x;
+    hd = sh.h;
+    Iv = sh.I;
+    xdiv = 1;
+    m0 = (M >= 64) ? ~0ull : ((1ull << M) - 1ull);
+    m1 = 0;
+  } else {
+    if (r0 >= I) return;
+    const int32_t e = ids[j];
+    if (e < 0 || (int64_t)e >= E) return;
+    if constexpr (MSX == 1) {
+      // one token (M = 1): each slot streams its own expert's rows. A
+      // token's top-k names distinct experts; a repeated id is streamed once
+      // per slot, which is still correct.
+      m0 = 1ull << (j & 63);
+      m1 = 0;
+    } else {
+      // lane l looks at slots l and l + 64 (S <= 128)
+      const int32_t a = lane < S ? ids[lane] : -1;
+      const int32_t b = lane + 64 < S ? ids[lane + 64] : -1;
+      const uint64_t earlier =
+          __ballot(a == e && lane < j) | __ballot(b == e && lane + 64 < j);
+      if (earlier) return;   // the workgroup of an earlier slot streams this expert
+      m0 = __ballot(a == e);   // all >= j, j included
+      m1 = __ballot(b == e);
     }
-    return;
+    codes = w13_codes + (int64_t)e * (2 * I) * (H / 2);
+    scales = w13_scales + (int64_t)e * (2 * I) * (H / 16);
+    g = ga ? w13_gscale[e] * *ga : w13_gscale[e];
+    xs = xr;
+    hd = h;
+    Iv = I;
+    xdiv = topk;
   }
-  if (r0 >= I) return;
-  const int32_t e = ids[j];
-  if (e < 0 || (int64_t)e >= E) return;
-  // lane l looks at slots l and l + 64 (S <= 128)
-  const int32_t a = lane < S ? ids[lane] : -1;
-  const int32_t b = lane + 64 < S ? ids[lane + 64] : -1;
-  const uint64_t earlier = __ballot(a == e && lane < j) | __ballot(b == e && lane + 64 < j);
-  if (earlier) return;   // the workgroup of an earlier slot streams this expert
-  uint64_t m0 = __ballot(a == e), m1 = __ballot(b == e);   // all >= j, j included
-
-  const uint8_t* codes = w13_codes + (int64_t)e * (2 * I) * (H / 2);
-  const uint8_t* scales = w13_scales + (int64_t)e * (2 * I) * (H / 16);
-  const float g = ga ? w13_gscale[e] * *ga : w13_gscale[e];
-  if (__popcll(m0) + __popcll(m1) == 1) {
-    const int slot[1] = {j};
-    gate_up_rows<1>(codes, scales, g, xr, H, I, r0, topk, slot, 1, h);
+  if (MSX == 1 || __popcll(m0) + __popcll(m1) == 1) {   // one slot
+    const int slot[1] = {MSX == 1 ? (shared_row ? 0 : j)
+                                  : (m0 ? __builtin_ctzll(m0) : 64 + __builtin_ctzll(m1))};
+    gate_up_rows<1>(codes, scales, g, xs, H, Iv, r0, xdiv, slot, 1, hd);
     return;
   }
   while (m0 | m1) {
-    int slot[4];
+    int slot[MSX];
     int ns = 0;
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
+    for (int q = 0; q < MSX; ++q) {
       if (m0) {
         slot[q] = __builtin_ctzll(m0);
         m0 &= m0 - 1;
@@ -153,10 +191,10 @@ __global__ __launch_bounds__(256) void k_moe_gate_up(
         m1 &= m1 - 1;
         ++ns;
       } else {
-        slot[q] = j;   // unused column (q >= ns)
+        slot[q] = slot[0];   // unused column (q >= ns): any served slot
       }
     }
-    gate_up_rows<4>(codes, scales, g, xr, H, I, r0, topk, slot, ns, h);
+    gate_up_rows<MSX>(codes, scales, g, xs, H, Iv, r0, xdiv, slot, ns, hd);
   }
 }
 
@@ -281,6 +319,170 @@ __global__ __launch_bounds__(256) void k_moe_down(
   }
 }
 
+constexpr int kMaxTok = NVFP4_MAX_M_INTERNAL;     // tokens per call
+constexpr int kMaxSl = NVFP4_MAX_TOPK_INTERNAL;    // slots per token
+constexpr int kSplitRows = 8;                      // k_moe_down_split: rows per workgroup
+constexpr int kSplitWaves = 4;                     //   and wavefronts per workgroup
+
+// The down pass and combine for M >= 2, split over wavefronts. The same
+// dot products as k_moe_down, dealt out differently: a workgroup of NW
+// wavefronts owns R output rows, and the units of work of all its tokens
+// (token m, a block of 64U consecutive (slot, chunk) pairs of that token's
+// valid slots and shared-expert chunks) go to its wavefronts round robin.
+// Each lane keeps one partial per row and token; the wavefronts' sums meet
+// in LDS and are added in wavefront order (deterministic). Compared with one
+// wavefront walking every token's pairs for its rows, this keeps several
+// times more wavefronts, and so more loads, in flight for the same work per
+// weight byte; the slot compaction of every token is built once per
+// workgroup in LDS.
+template <int R, int U, int NW>
+__global__ __launch_bounds__(64 * NW) void k_moe_down_split(
+    const uint8_t* __restrict__ w2_codes, const uint8_t* __restrict__ w2_scales,
+    const float* __restrict__ w2_gscale, const uint16_t* __restrict__ h,
+    const float* __restrict__ ga, const int32_t* __restrict__ ids,
+    const float* __restrict__ gate_w, int M, int topk, int64_t E, int64_t H, int64_t I,
+    float* __restrict__ y, const MoeShared sh) {
+  __shared__ int s_e[kMaxTok][kMaxSl];
+  __shared__ int s_j[kMaxTok][kMaxSl];
+  __shared__ float s_f[kMaxTok][kMaxSl];
+  __shared__ int s_nv[kMaxTok];
+  __shared__ float s_part[NW][R][kMaxTok];
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int64_t n0 = (int64_t)blockIdx.x * R;
+  const int C = (int)(I >> 5);
+  const int64_t cb = I >> 1, sb = I >> 4;
+  const int64_t ecb = H * cb, esb = H * sb;
+  const float invC = 1.0f / (float)C;
+  const int Cs = (int)(sh.I >> 5);
+  const int64_t cbs = sh.I >> 1, sbs = sh.I >> 4;
+  const float gs2 = Cs > 0 ? *sh.g2 : 0.0f;
+  const float gah = ga ? *ga : 1.0f;
+  for (int m = w; m < M; m += NW) {
+    const int jl = m * topk + lane;
+    const int32_t ev = lane < topk ? ids[jl] : -1;
+    const bool valid = lane < topk && ev >= 0 && (int64_t)ev < E;
+    const uint64_t vm = __ballot(valid);
+    const int q = __builtin_amdgcn_mbcnt_hi((uint32_t)(vm >> 32),
+                                            __builtin_amdgcn_mbcnt_lo((uint32_t)vm, 0u));
+    if (valid) {
+      s_e[m][q] = ev;
+      s_j[m][q] = jl;
+      s_f[m][q] = ga ? gate_w[jl] * w2_gscale[ev] * gah : gate_w[jl] * w2_gscale[ev];
+    }
+    if (lane == 0) s_nv[m] = __popcll(vm);
+  }
+  __syncthreads();
+  int64_t rows[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) rows[r] = (n0 + r < H) ? n0 + r : H - 1;
+  float tok[R][kMaxTok];
+#pragma unroll
+  for (int r = 0; r < R; ++r)
+#pragma unroll
+    for (int mm = 0; mm < kMaxTok; ++mm) tok[r][mm] = 0.0f;
+  int unit = 0;
+  for (int m = 0; m < M; ++m) {
+    const int nv = __builtin_amdgcn_readfirstlane(s_nv[m]);
+    const int PR = nv * C;
+    const int P = PR + Cs;
+    const int nb = (P + 64 * U - 1) / (64 * U);
+    for (int b = 0; b < nb; ++b, ++unit) {
+      if (unit % NW != w) continue;
+      u32x4_t qv[U][R];
+      uint32_t sw[U][R];
+      u32x4_t hv[U][4];
+      float cf[U];
+      bool live[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int p = b * 64 * U + lane + 64 * u;
+        live[u] = p < P;
+        const int pc = live[u] ? p : P - 1;
+        const bool shp = pc >= PR;
+        const int pr = shp ? 0 : pc;
+        int qi = (int)(((float)pr + 0.5f) * invC);
+        if (qi * C > pr) --qi;
+        if ((qi + 1) * C <= pr) ++qi;
+        const int c = shp ? pc - PR : pr - qi * C;
+        const int ee = s_e[m][qi];
+        const int jj = s_j[m][qi];
+        const float fr = s_f[m][qi];
+        cf[u] = shp ? gs2 : fr;
+        const uint8_t* cbase = shp ? sh.c2 + (int64_t)c * 16
+                                   : w2_codes + (int64_t)ee * ecb + (int64_t)c * 16;
+        const uint8_t* sbase = shp ? sh.s2 + (int64_t)c * 2
+                                   : w2_scales + (int64_t)ee * esb + (int64_t)c * 2;
+        const int64_t rcb = shp ? cbs : cb, rsb = shp ? sbs : sb;
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+          qv[u][r] = load_stream(cbase + rows[r] * rcb);
+          sw[u][r] = *reinterpret_cast<const uint16_t*>(sbase + rows[r] * rsb);
+        }
+        const uint16_t* hrow = shp ? sh.h + (int64_t)m * sh.I : h + (int64_t)jj * I;
+        const u32x4_t* hp = reinterpret_cast<const u32x4_t*>(hrow + c * 32);
+#pragma unroll
+        for (int t = 0; t < 4; ++t) hv[u][t] = hp[t];
+      }
+      float acc[R];
+#pragma unroll
+      for (int r = 0; r < R; ++r) acc[r] = 0.0f;
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+#pragma unroll
+        for (int b2 = 0; b2 < 2; ++b2) {
+          const u32x4_t xa = hv[u][2 * b2], xb = hv[u][2 * b2 + 1];
+          const bf16x2_t xv[8] = {as_bf16x2(xa.x), as_bf16x2(xa.y), as_bf16x2(xa.z),
+                                  as_bf16x2(xa.w), as_bf16x2(xb.x), as_bf16x2(xb.y),
+                                  as_bf16x2(xb.z), as_bf16x2(xb.w)};
+#pragma unroll
+          for (int r = 0; r < R; ++r) {
+            const uint32_t w0 = b2 ? qv[u][r].z : qv[u][r].x;
+            const uint32_t w1 = b2 ? qv[u][r].w : qv[u][r].y;
+            float p = 0.0f;
+            p = dot2(e2m1x2_to_bf16<0>(w0), xv[0], p);
+            p = dot2(e2m1x2_to_bf16<1>(w0), xv[1], p);
+            p = dot2(e2m1x2_to_bf16<2>(w0), xv[2], p);
+            p = dot2(e2m1x2_to_bf16<3>(w0), xv[3], p);
+            p = dot2(e2m1x2_to_bf16<0>(w1), xv[4], p);
+            p = dot2(e2m1x2_to_bf16<1>(w1), xv[5], p);
+            p = dot2(e2m1x2_to_bf16<2>(w1), xv[6], p);
+            p = dot2(e2m1x2_to_bf16<3>(w1), xv[7], p);
+            const float s = (b2 ? e4m3_to_f32<1>(sw[u][r]) : e4m3_to_f32<0>(sw[u][r])) * cf[u];
+            const float na = __builtin_fmaf(p, s, acc[r]);
+            acc[r] = live[u] ? na : acc[r];
+          }
+        }
+      }
+#pragma unroll
+      for (int mm = 0; mm < kMaxTok; ++mm)
+        if (mm == m) {
+#pragma unroll
+          for (int r = 0; r < R; ++r) tok[r][mm] += acc[r];
+        }
+    }
+  }
+#pragma unroll
+  for (int mm = 0; mm < kMaxTok; ++mm) {
+    if (mm < M) {
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        const float t = wave_sum(tok[r][mm]);
+        if (lane == 0) s_part[w][r][mm] = t;
+      }
+    }
+  }
+  __syncthreads();
+  const int t = threadIdx.x;
+  if (t < R * M) {
+    const int r = t / M, m = t % M;
+    float sum = 0.0f;
+#pragma unroll
+    for (int ww = 0; ww < NW; ++ww) sum += s_part[ww][r][m];
+    if (n0 + r < H) y[(int64_t)m * H + n0 + r] = sum;
+  }
+}
+
 hipError_t launch_moe(const uint8_t* w13_codes, const uint8_t* w13_scales,
                       const float* w13_gscale, const uint8_t* w2_codes,
                       const uint8_t* w2_scales, const float* w2_gscale, const uint16_t* x,
@@ -311,9 +513,13 @@ hipError_t launch_moe(const uint8_t* w13_codes, const uint8_t* w13_scales,
   {
     const int64_t pairs = ((sh.I > I ? sh.I : I) + 1) / 2;
     const int64_t yb = (pairs + kMoeWaves - 1) / kMoeWaves;
-    hipLaunchKernelGGL(k_moe_gate_up, dim3((unsigned)yb, S + (sh.I > 0 ? 1 : 0)), dim3(256), 0,
-                       stream, w13_codes, w13_scales, w13_gscale, x, xr, ga13, ids, S, topk, E,
-                       H, I, h, sh, M);
+    const dim3 grid((unsigned)yb, S + (sh.I > 0 ? 1 : 0));
+    if (M == 1)
+      hipLaunchKernelGGL(k_moe_gate_up<1>, grid, dim3(256), 0, stream, w13_codes, w13_scales,
+                         w13_gscale, x, xr, ga13, ids, S, topk, E, H, I, h, sh, M);
+    else
+      hipLaunchKernelGGL(k_moe_gate_up<kGateUpSlots>, grid, dim3(256), 0, stream, w13_codes,
+                         w13_scales, w13_gscale, x, xr, ga13, ids, S, topk, E, H, I, h, sh, M);
   }
   if (w4a4) {
     // h of every valid slot onto the NVFP4 grid of its static scale
@@ -322,11 +528,16 @@ hipError_t launch_moe(const uint8_t* w13_codes, const uint8_t* w13_scales,
     e = launch_quantize_decode(h, S, I, ga2, ids, E, const_cast<uint16_t*>(hr), stream);
     if (e != hipSuccess) return e;
   }
-  {
+  if (M == 1) {
     const int64_t wgs = (H + kDownRows * kMoeWaves - 1) / (kDownRows * kMoeWaves);
     hipLaunchKernelGGL((k_moe_down<kDownRows, kDownUnroll>), dim3((unsigned)wgs), dim3(256), 0,
                        stream, w2_codes, w2_scales, w2_gscale, hr, ga2, ids, gate_w, M, topk, E,
                        H, I, y, sh);
+  } else {
+    const int64_t wgs = (H + kSplitRows - 1) / kSplitRows;
+    hipLaunchKernelGGL((k_moe_down_split<kSplitRows, 1, kSplitWaves>), dim3((unsigned)wgs),
+                       dim3(64 * kSplitWaves), 0, stream, w2_codes, w2_scales, w2_gscale, hr, ga2,
+                       ids, gate_w, M, topk, E, H, I, y, sh);
   }
   return hipGetLastError();
 }
