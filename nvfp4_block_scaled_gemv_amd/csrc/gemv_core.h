@@ -1,5 +1,6 @@
-// gemv_core.h -- the wavefront-level NVFP4 g16 x bf16 dot-product engine used
-// by the dense GEMV and by both MoE sweeps.
+// gemv_core.h -- the wavefront-level NVFP4 g16 dot-product engine used by the
+// vector-ALU dense GEMV (bf16 activations, and NVFP4 activations for W4A4)
+// and by the MoE gate|up sweep.
 //
 // Layout of the work: one wavefront owns R weight rows at a time. The K axis
 // of a row is cut into 32-element chunks (16 code bytes = one 128-bit load,
@@ -8,7 +9,8 @@
 // decoded once (v_cvt_scalef32_pk_bf16_fp4, exact) and reused for every
 // activation row; per 16-element block and activation row, 8 bf16 pair dots
 // (v_dot2_f32_bf16) give a block partial that is multiplied by the block's
-// E4M3 scale and accumulated in fp32. Lanes are summed at the end.
+// E4M3 scale and accumulated in fp32. Lanes are summed at the end
+// (wave_sum: DPP within 16-lane rows, v_readlane across them).
 #pragma once
 
 #include "device.h"

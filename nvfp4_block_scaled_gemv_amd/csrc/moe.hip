@@ -198,7 +198,7 @@ __global__ __launch_bounds__(256) void k_moe_gate_up(
   }
 }
 
-// grid ceil(H / (R * kMoeWaves)); a wavefront owns output rows n0 .. n0+R-1
+// M = 1. grid ceil(H / (R * kMoeWaves)); a wavefront owns output rows n0 .. n0+R-1
 // for every token. Routed slots read h with coefficient gate_w * g2[e] * *ga
 // (ga = NULL for W4A16; for W4A4, h holds the activations on the NVFP4 grid
 // and ga their static scale).

@@ -1,18 +1,20 @@
 // w4a4.hip -- NVFP4 activations (W4A4) on gfx950.
 //
 // The pages' W4A4 path (card.json "W4A4 NVFP4 x NVFP4 (static input scale)",
-// performance[20] and [24]; graph.json node "l0.mlp.xn_quant", op act_quant,
-// bf16 -> nvfp4/g16):
+// performance[20], [24], [64], [65]; graph.json node "l0.mlp.xn_quant", op
+// act_quant, bf16 -> nvfp4/g16):
 //   k_quantize_act: each row of bf16 x[M, K] is quantized like a weight row,
 //     with the caller's static tensor scale g_x: s = E4M3(amax / (6 g_x)),
-//     code = E2M1(x / (s g_x)), in IEEE fp32 (the same block encoder as pack).
-//   nvfp4_gemv_w4a4: y = g_w g_x sum_k (e2m1_w s_w)(e2m1_x s_x). The
-//     activation values e2m1_x s_x have at most 6 significant bits and lie in
-//     [2^-10, 2688], so they are exact in bf16: k_w4a4_prep writes them to the
-//     workspace as bf16 together with the product scale g_w g_x (one fp32
-//     rounding), and the W4A16 GEMV kernels do the rest (M <= 2 on the vector
-//     ALUs, M >= 3 on the matrix cores). x is at most 8 x K values, so the
-//     extra pass moves kilobytes next to the weight stream.
+//     code = E2M1(x / (s g_x)), in IEEE fp32 (the same encoders as pack).
+//   nvfp4_gemv_w4a4: y = g_w g_x sum_k (e2m1_w s_w)(e2m1_x s_x). At M <= 2
+//     the vector-ALU kernel k_gemv_w4a4 (gemv.hip) decodes both operands in
+//     registers. At M >= 3 the activation values e2m1_x s_x (at most 6
+//     significant bits in [2^-10, 2688], so exact in bf16) are written to the
+//     workspace by k_w4a4_prep with the product scale g_w g_x (one fp32
+//     rounding), and the bf16 MFMA GEMV kernels do the rest; x is at most
+//     8 x K values, so the extra pass moves kilobytes.
+//   k_quantize_decode: the same quantization, written back as the decoded
+//     bf16 values, for the W4A4 MoE (its x before gate|up, its h before down).
 #include "device.h"
 #include "internal.h"
 
