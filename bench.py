@@ -443,11 +443,18 @@ KERNEL_SOURCES = ["gemv.hip", "gemv_core.h", "device.h"]
 
 
 def kernel_source_hash():
+    """Hash of the LM-head kernel's sources with comments and whitespace
+    removed, so that the stored traffic counters stay valid across edits
+    that do not change the code."""
     import hashlib
+    import re
     h = hashlib.sha256()
     for f in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, "nvfp4_block_scaled_gemv_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(ROOT, "nvfp4_block_scaled_gemv_amd", "csrc", f)) as fh:
+            text = fh.read()
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)   # block comments
+        text = re.sub(r"//[^\n]*", " ", text)                  # line comments
+        h.update(f.encode() + b"\0" + " ".join(text.split()).encode())
     return h.hexdigest()[:16]
 
 
