@@ -105,12 +105,14 @@ __global__ __launch_bounds__(256) void k_quantize_decode(const uint16_t* __restr
                                                          uint16_t* __restrict__ out) {
   const size_t t = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (t >= n) return;
+  // the element, the scale and the row's id load together (the element's
+  // address does not depend on the id, which only decides the write)
+  const float g = *gscale;
+  const float w = __uint_as_float((uint32_t)x[t] << 16);   // bf16 -> fp32 is exact
   if (ids) {
     const int32_t e = ids[t / (size_t)K];
     if (e < 0 || (int64_t)e >= E) return;
   }
-  const float g = *gscale;
-  const float w = __uint_as_float((uint32_t)x[t] << 16);   // bf16 -> fp32 is exact
   float ab = fabsf(w);
   ab = fmaxf(ab, dpp_f32<0xB1>(ab));    // quad_perm [1,0,3,2]
   ab = fmaxf(ab, dpp_f32<0x4E>(ab));    // quad_perm [2,3,0,1]
