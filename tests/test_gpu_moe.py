@@ -100,6 +100,23 @@ def test_moe_duplicates_invalid_ids_and_limits():
             assert np.all(y == 0)
 
 
+@pytest.mark.parametrize("M", range(1, 9))
+def test_moe_every_m(M):
+    """Every token count (M = 1 takes the one-slot-per-pass gate|up and the
+    per-wavefront down pass; M >= 2 the slot union and the split down pass),
+    with a repeated id in the first token and 128 slots at M = 8."""
+    E, H, I = 6, 256, 128
+    hw, dw = build_experts(47, 0, E, H, I, range(E))
+    topk = 16 if M == 8 else 4
+    ids = np.random.default_rng(M).integers(0, E, size=(M, topk)).astype(np.int32)
+    ids[0, 1] = ids[0, 0]
+    gw = np.random.default_rng(M + 100).random((M, topk)).astype(np.float32)
+    say(f"[moe] every M: M={M} topk={topk} ids[0]={ids[0].tolist()}")
+    x = workloads.x_bf16(47, M, topk, M, H)
+    y, (y_ref, bound), _ = run_both(hw, dw, x, ids, gw, H, I)
+    check_tol(y, y_ref, bound, f"M={M}")
+
+
 def test_moe_empty_batch():
     E, H, I = 2, 64, 32
     hw, dw = build_experts(42, 0, E, H, I, [])
