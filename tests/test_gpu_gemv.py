@@ -52,13 +52,14 @@ def test_random_storage_shapes(M, N, K):
 
 @pytest.mark.parametrize("M", [3, 6, 8])
 @pytest.mark.parametrize("N,K", [(33, 256), (77, 512), (100, 768), (300, 3840), (50, 4352),
-                                 (4800, 8192)])
+                                 (4800, 8192), (40, 30720), (21, 65536)])
 def test_split_k_shapes(M, N, K):
     """The matrix-core kernel's K splits: one wavefront holding one x slice
     (K = 256) or two (K = 512), three and fifteen wavefronts holding one (odd
     slice counts), one wavefront streaming x over 17 slices (a prime slice
-    count) and eight wavefronts streaming four slices each with several tiles
-    per workgroup (4800 rows); the largest compares a sample of rows, first
+    count), eight wavefronts streaming four slices each with several tiles
+    per workgroup (4800 rows), eight streaming fifteen (K = 30720) and
+    thirty-two (K = 65536); the largest N compares a sample of rows, first
     and last included."""
     say(f"[gemv] split-K M={M} N={N} K={K}")
     codes, scales = workloads.random_nvfp4(9, M, N * 3 + K, N, K)
