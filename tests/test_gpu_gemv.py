@@ -50,6 +50,19 @@ def test_random_storage_shapes(M, N, K):
     check_tol(y, y_ref, ad, f"M={M} N={N} K={K}")
 
 
+@pytest.mark.parametrize("M", [1, 2])
+def test_four_rows_per_wavefront_with_ragged_tail(M):
+    """N >= 32768 takes four rows per wavefront on the vector ALUs; N = 40003
+    leaves a tail of three rows."""
+    N, K = 40003, 64
+    say(f"[gemv] M={M} N={N} K={K}")
+    codes, scales = workloads.random_nvfp4(9, M, 41, N, K)
+    x = workloads.x_bf16(9, M, 41, M, K)
+    y = run_gpu(codes, scales, np.float32(0.02), x)
+    y_ref, ad = oracle.gemv(codes, scales, np.float32(0.02), x)
+    check_tol(y, y_ref, ad, f"M={M} N={N}")
+
+
 @pytest.mark.parametrize("M", [3, 6, 8])
 @pytest.mark.parametrize("N,K", [(33, 256), (77, 512), (100, 768), (300, 3840), (50, 4352),
                                  (4800, 8192), (40, 30720), (21, 65536)])

@@ -117,6 +117,20 @@ def test_moe_every_m(M):
     check_tol(y, y_ref, bound, f"M={M}")
 
 
+@pytest.mark.parametrize("M", [1, 2, 3])
+def test_moe_minimum_sizes(M):
+    """One expert and H = I = 32: one 32-element chunk per slot, so the down
+    pass's (slot, chunk) decode divides by 1, and every slot names expert 0."""
+    E, H, I, topk = 1, 32, 32, 2
+    hw, dw = build_experts(48, M, E, H, I, [0])
+    ids = np.zeros((M, topk), np.int32)
+    gw = np.random.default_rng(M).random((M, topk)).astype(np.float32)
+    x = workloads.x_bf16(48, M, 0, M, H)
+    say(f"[moe] minimum sizes M={M}")
+    y, (y_ref, bound), _ = run_both(hw, dw, x, ids, gw, H, I)
+    check_tol(y, y_ref, bound, f"minimum M={M}")
+
+
 def test_moe_empty_batch():
     E, H, I = 2, 64, 32
     hw, dw = build_experts(42, 0, E, H, I, [])

@@ -66,7 +66,7 @@ def test_moe_shared_workload_4(M):
     check_hs(hs, hs_ref)
 
 
-@pytest.mark.parametrize("Is", [96, 512])
+@pytest.mark.parametrize("Is", [32, 96, 512])
 def test_moe_shared_widths_duplicates_and_invalid_ids(Is):
     E, H, I = 6, 512, 256
     hw, dw = build_experts(43, 0, E, H, I, range(E))
