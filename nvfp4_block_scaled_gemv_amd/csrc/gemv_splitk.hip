@@ -250,10 +250,7 @@ constexpr int kSlots = 4;
 constexpr int kStagePitch = 144;            // bytes per staged row (128 + 16: bank skew)
 constexpr int kStageBytes = 16 * kStagePitch;
 constexpr int kSpinLimit = 1 << 22;         // bound of a slot wait (never reached)
-#ifndef NVFP4_SK_RED_BATCH
-#define NVFP4_SK_RED_BATCH 4
-#endif
-constexpr int kRedBatch = NVFP4_SK_RED_BATCH;   // partial loads in flight in the sum
+constexpr int kRedBatch = 4;                // partial loads in flight in the sum
 
 struct SkShared {
   f32x4_t* part;       // [kSlots][W][32]
