@@ -63,13 +63,18 @@ extern "C" {
 #define NVFP4_MAX_TOPK 16
 /* Largest MoE intermediate size I (down-projection row length) per call. */
 #define NVFP4_MOE_MAX_I (1 << 24)
+/* Largest number of output rows N of one dense GEMV call (of all segments
+   together): every launch grid then stays within 32-bit work-item counts. */
+#define NVFP4_MAX_N (1LL << 30)
+/* Largest MoE hidden size H per call. */
+#define NVFP4_MOE_MAX_H (1 << 24)
 
 typedef enum nvfp4_status {
   NVFP4_OK = 0,
   NVFP4_ERR_NULL = 1,        /* a required pointer is NULL */
   NVFP4_ERR_SHAPE = 2,       /* negative size or a divisibility rule broken */
   NVFP4_ERR_ALIGN = 3,       /* a pointer is not aligned as documented */
-  NVFP4_ERR_UNSUPPORTED = 4, /* M > NVFP4_MAX_M, topk > NVFP4_MAX_TOPK, ... */
+  NVFP4_ERR_UNSUPPORTED = 4, /* a size above its NVFP4_MAX_* / NVFP4_MOE_MAX_* limit */
   NVFP4_ERR_WORKSPACE = 5,   /* workspace NULL or smaller than required */
   NVFP4_ERR_HIP = 6,         /* a HIP call or kernel launch failed */
   NVFP4_ERR_ALIAS = 7        /* an output overlaps an input */
@@ -136,10 +141,10 @@ nvfp4_status nvfp4_dequant(const uint8_t* codes, const uint8_t* scales,
  *   codes   uint8[N, K/2], 16-byte aligned;  scales uint8[N, K/16], 2-byte
  *           aligned;  gscale float[1];
  *   x       bf16[M, K] given as uint16 bit patterns, 16-byte aligned;
- *   M       0 <= M <= NVFP4_MAX_M;  N >= 0;  K >= 0, K % 32 == 0;
+ *   M       0 <= M <= NVFP4_MAX_M;  0 <= N <= NVFP4_MAX_N;  K >= 0, K % 32 == 0;
  *   y       float[M, N] out, 4-byte aligned (M == 0 or N == 0: nothing is
  *           launched; K == 0: y is set to zero).
- * Errors: NULL, SHAPE, ALIGN, UNSUPPORTED (M > 8), ALIAS, HIP.
+ * Errors: NULL, SHAPE, ALIGN, UNSUPPORTED (M > 8 or N > NVFP4_MAX_N), ALIAS, HIP.
  */
 nvfp4_status nvfp4_gemv(const uint8_t* codes, const uint8_t* scales,
                         const float* gscale, const uint16_t* x, int64_t M,
@@ -172,10 +177,11 @@ typedef struct nvfp4_gemv_segment {
  *               only); the pointers inside are device pointers;
  *   n_segments  0 .. NVFP4_MAX_SEGMENTS;
  *   x           bf16[M, K] shared by every segment, 16-byte aligned;
- *   M, K        as for nvfp4_gemv (M <= NVFP4_MAX_M, K % 32 == 0).
+ *   M, K        as for nvfp4_gemv (M <= NVFP4_MAX_M, K % 32 == 0); the
+ *               segments' N together at most NVFP4_MAX_N.
  * No output may overlap any input or another output.
- * Errors: NULL, SHAPE, ALIGN, UNSUPPORTED (n_segments or M too large), ALIAS,
- * HIP.
+ * Errors: NULL, SHAPE, ALIGN, UNSUPPORTED (n_segments, M or the total N too
+ * large), ALIAS, HIP.
  */
 nvfp4_status nvfp4_gemv_segments(const nvfp4_gemv_segment* segs, int64_t n_segments,
                                  const uint16_t* x, int64_t M, int64_t K,
@@ -213,7 +219,7 @@ size_t nvfp4_moe_workspace_bytes(int64_t M, int64_t H, int64_t I, int64_t topk);
  *   x          bf16[M, H] (uint16 bits), 16-byte aligned;
  *   expert_ids int32[M, topk];  gate_w float[M, topk];
  *   M          0 <= M <= NVFP4_MAX_M; 1 <= topk <= NVFP4_MAX_TOPK; E >= 1;
- *              I <= NVFP4_MOE_MAX_I;
+ *              I <= NVFP4_MOE_MAX_I; H <= NVFP4_MOE_MAX_H;
  *              H % 32 == 0, I % 32 == 0, H > 0, I > 0;
  *   y          float[M, H] out, 16-byte aligned;
  *   workspace  device buffer of at least nvfp4_moe_workspace_bytes(M, H, I,
@@ -266,7 +272,7 @@ size_t nvfp4_gemv_w4a4_workspace_bytes(int64_t M, int64_t K);
  *   codes_w, scales_w, gscale_w  the weight, as in nvfp4_gemv;
  *   codes_x   uint8[M, K/2], 16-byte aligned; scales_x uint8[M, K/16], 2-byte
  *             aligned; gscale_x float[1] (from nvfp4_quantize_act);
- *   M         0 <= M <= NVFP4_MAX_M; K % 32 == 0;
+ *   M         0 <= M <= NVFP4_MAX_M; 0 <= N <= NVFP4_MAX_N; K % 32 == 0;
  *   y         float[M, N] out;
  *   workspace at least nvfp4_gemv_w4a4_workspace_bytes(M, K) bytes,
  *             256-byte aligned; overwritten; must not be shared by calls that

@@ -111,8 +111,9 @@ nvfp4_status nvfp4_gemv(const uint8_t* codes, const uint8_t* scales, const float
   if (M < 0 || N < 0 || K < 0 || (K % 32) != 0)
     return fail(NVFP4_ERR_SHAPE, "nvfp4_gemv: need M, N, K >= 0 and K %% 32 == 0 (M=%lld N=%lld K=%lld)",
                 (long long)M, (long long)N, (long long)K);
-  if (M > NVFP4_MAX_M)
-    return fail(NVFP4_ERR_UNSUPPORTED, "nvfp4_gemv: M=%lld exceeds %d", (long long)M, NVFP4_MAX_M);
+  if (M > NVFP4_MAX_M || N > NVFP4_MAX_N)
+    return fail(NVFP4_ERR_UNSUPPORTED, "nvfp4_gemv: M=%lld (max %d), N=%lld (max %lld)",
+                (long long)M, NVFP4_MAX_M, (long long)N, (long long)NVFP4_MAX_N);
   if (M == 0 || N == 0) return NVFP4_OK;
   if (!y) return fail(NVFP4_ERR_NULL, "nvfp4_gemv: y is NULL");
   if (!aligned(y, 4)) return fail(NVFP4_ERR_ALIGN, "nvfp4_gemv: y must be 4-byte aligned");
@@ -147,11 +148,16 @@ nvfp4_status nvfp4_gemv_segments(const nvfp4_gemv_segment* segs, int64_t n_segme
   if (!segs) return fail(NVFP4_ERR_NULL, "nvfp4_gemv_segments: segs is NULL");
   nvfp4::SegDesc d[NVFP4_MAX_SEGMENTS];
   int n = 0;
+  int64_t total_n = 0;
   for (int64_t s = 0; s < n_segments; ++s) {
     const nvfp4_gemv_segment& g = segs[s];
     if (g.N < 0)
       return fail(NVFP4_ERR_SHAPE, "nvfp4_gemv_segments: segment %lld has N=%lld < 0",
                   (long long)s, (long long)g.N);
+    if (g.N > NVFP4_MAX_N - total_n)
+      return fail(NVFP4_ERR_UNSUPPORTED, "nvfp4_gemv_segments: the segments' N exceed %lld",
+                  (long long)NVFP4_MAX_N);
+    total_n += g.N;
     if (g.N == 0) continue;
     if (!g.y) return fail(NVFP4_ERR_NULL, "nvfp4_gemv_segments: segment %lld y is NULL", (long long)s);
     if (!aligned(g.y, 4))
@@ -236,9 +242,9 @@ nvfp4_status nvfp4_gemv_w4a4(const uint8_t* codes_w, const uint8_t* scales_w,
     return fail(NVFP4_ERR_SHAPE,
                 "nvfp4_gemv_w4a4: need M, N, K >= 0 and K %% 32 == 0 (M=%lld N=%lld K=%lld)",
                 (long long)M, (long long)N, (long long)K);
-  if (M > NVFP4_MAX_M)
-    return fail(NVFP4_ERR_UNSUPPORTED, "nvfp4_gemv_w4a4: M=%lld exceeds %d", (long long)M,
-                NVFP4_MAX_M);
+  if (M > NVFP4_MAX_M || N > NVFP4_MAX_N)
+    return fail(NVFP4_ERR_UNSUPPORTED, "nvfp4_gemv_w4a4: M=%lld (max %d), N=%lld (max %lld)",
+                (long long)M, NVFP4_MAX_M, (long long)N, (long long)NVFP4_MAX_N);
   if (M == 0 || N == 0) return NVFP4_OK;
   if (!y) return fail(NVFP4_ERR_NULL, "nvfp4_gemv_w4a4: y is NULL");
   if (!aligned(y, 4)) return fail(NVFP4_ERR_ALIGN, "nvfp4_gemv_w4a4: y must be 4-byte aligned");
@@ -311,11 +317,13 @@ nvfp4_status moe_checked(const char* fn, const uint8_t* w13_codes, const uint8_t
   if (shared && (Is <= 0 || (Is % 32) != 0))
     return fail(NVFP4_ERR_SHAPE, "%s: shared expert width I=%lld must be > 0 and a multiple of 32",
                 fn, (long long)Is);
-  if (M > NVFP4_MAX_M || topk > NVFP4_MAX_TOPK || I > NVFP4_MOE_MAX_I || Is > NVFP4_MOE_MAX_I)
+  if (M > NVFP4_MAX_M || topk > NVFP4_MAX_TOPK || I > NVFP4_MOE_MAX_I || Is > NVFP4_MOE_MAX_I ||
+      H > NVFP4_MOE_MAX_H)
     return fail(NVFP4_ERR_UNSUPPORTED,
-                "%s: M=%lld (max %d), topk=%lld (max %d), I=%lld, shared I=%lld (max %d)", fn,
+                "%s: M=%lld (max %d), topk=%lld (max %d), I=%lld, shared I=%lld (max %d), "
+                "H=%lld (max %d)", fn,
                 (long long)M, NVFP4_MAX_M, (long long)topk, NVFP4_MAX_TOPK, (long long)I,
-                (long long)Is, NVFP4_MOE_MAX_I);
+                (long long)Is, NVFP4_MOE_MAX_I, (long long)H, NVFP4_MOE_MAX_H);
   if (M == 0) return NVFP4_OK;
   if (!w13_codes || !w13_scales || !w13_gscale || !w2_codes || !w2_scales || !w2_gscale || !x ||
       !expert_ids || !gate_w || !y)

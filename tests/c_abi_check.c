@@ -35,6 +35,9 @@ int main(void) {
   expect(nvfp4_gemv(NULL, NULL, NULL, NULL, NVFP4_MAX_M + 1, 4, 32, y, NULL) ==
              NVFP4_ERR_UNSUPPORTED,
          "gemv M above the maximum");
+  expect(nvfp4_gemv(NULL, NULL, NULL, NULL, 1, NVFP4_MAX_N + 1, 32, y, NULL) ==
+             NVFP4_ERR_UNSUPPORTED,
+         "gemv N above the maximum");
   expect(nvfp4_gemv(NULL, NULL, NULL, NULL, 1, 0, 32, y, NULL) == NVFP4_OK,
          "gemv with N = 0 does nothing");
   expect(nvfp4_moe_gemv(NULL, NULL, NULL, NULL, NULL, NULL, NULL, NULL, NULL, 1, 4, 64, 48, 2,

@@ -46,6 +46,25 @@ def test_version_and_status_strings(L):
     assert L.nvfp4_status_string(99) == b"unknown status"
 
 
+def test_binding_limits_match_the_header():
+    text = open(nv.HEADER_PATH).read()
+    defs = dict(re.findall(r"#define (NVFP4_[A-Z_]+) \(?([0-9LU]+(?: << [0-9]+)?)\)?", text))
+
+    def value(name):
+        v = defs[name].replace("LL", "").replace("U", "")
+        if "<<" in v:
+            a, b = v.split("<<")
+            return int(a) << int(b)
+        return int(v)
+
+    assert value("NVFP4_MAX_M") == nv.MAX_M
+    assert value("NVFP4_MAX_TOPK") == nv.MAX_TOPK
+    assert value("NVFP4_MAX_N") == nv.MAX_N
+    assert value("NVFP4_MOE_MAX_I") == nv.MOE_MAX_I
+    assert value("NVFP4_MOE_MAX_H") == nv.MOE_MAX_H
+    assert value("NVFP4_MAX_SEGMENTS") == nv.MAX_SEGMENTS
+
+
 def _err(L):
     return L.nvfp4_last_error().decode()
 
@@ -55,6 +74,8 @@ def test_gemv_rejects_bad_shapes(L):
     assert "K % 32" in _err(L)
     assert L.nvfp4_gemv(A, A, A, A, -1, 16, 64, B, None) == ERR_SHAPE
     assert L.nvfp4_gemv(A, A, A, A, 9, 16, 64, B, None) == ERR_UNSUPPORTED
+    assert L.nvfp4_gemv(A, A, A, A, 1, (1 << 30) + 1, 64, B, None) == ERR_UNSUPPORTED   # N
+    assert "N=" in _err(L)
     assert L.nvfp4_gemv(A, A, A, A, 0, 16, 64, B, None) == OK              # nothing to do
     assert L.nvfp4_gemv(A, A, A, A, 2, 0, 64, B, None) == OK
 
@@ -99,6 +120,8 @@ def test_moe_checks(L):
     assert f(*args, 1, 0, 64, 64, 2, B, B + 0x1000000, ws, None) == ERR_SHAPE
     big_i = (1 << 24) + 32
     assert f(*args, 1, 4, 64, big_i, 2, B, B + 0x1000000, 1 << 40, None) == ERR_UNSUPPORTED
+    big_h = (1 << 24) + 32
+    assert f(*args, 1, 4, big_h, 64, 2, B, B + 0x1000000, 1 << 40, None) == ERR_UNSUPPORTED
     need = nv.moe_workspace_bytes(1, 64, 64, 2)
     assert f(*args, 1, 4, 64, 64, 2, B, B + 0x1000000, need - 1, None) == ERR_WORKSPACE
     assert f(*args, 1, 4, 64, 64, 2, B, None, need, None) == ERR_WORKSPACE
@@ -208,6 +231,7 @@ def test_w4a4_checks(L):
     need = nv.gemv_w4a4_workspace_bytes(2, 64)
     assert f(*w, 2, 16, 48, Y, WS, need, None) == ERR_SHAPE
     assert f(*w, 9, 16, 64, Y, WS, need, None) == ERR_UNSUPPORTED
+    assert f(*w, 2, (1 << 30) + 1, 64, Y, WS, need, None) == ERR_UNSUPPORTED
     assert f(*w, 0, 16, 64, Y, WS, need, None) == OK
     assert f(*w, 2, 16, 64, Y, WS, need - 1, None) == ERR_WORKSPACE
     assert f(*w, 2, 16, 64, Y, None, need, None) == ERR_WORKSPACE
@@ -243,6 +267,9 @@ def test_gemv_segments_checks(L):
     bad = (Seg * 2)(arr[0], arr[1])
     bad[1].N = -1
     assert f(bad, 2, X, 1, 64, None) == ERR_SHAPE
+    bad = (Seg * 2)(arr[0], arr[1])
+    bad[0].N = bad[1].N = (1 << 29) + 1                         # together above 2^30 rows
+    assert f(bad, 2, X, 1, 64, None) == ERR_UNSUPPORTED
     bad = (Seg * 2)(arr[0], arr[1])
     bad[1].y = None
     assert f(bad, 2, X, 1, 64, None) == ERR_NULL
