@@ -106,6 +106,56 @@ def timed_steps(torch, step, steps, warmup):
     return (t1 - t0) * 1e3 / steps, e0.elapsed_time(e1) / steps
 
 
+_SLEEP_CYCLES_PER_MS = None
+
+
+def queued_steps(torch, step, steps, first, wall_ms_per_step):
+    """Device time per step (us) with every launch queued ahead of the GPU.
+    A bounded sleep kernel (torch.cuda._sleep) holds the stream while the
+    host issues the steps; they then run back to back, so host time between
+    launches (the Python binding takes several microseconds per call) is not
+    counted. The events sit after the sleep, around the steps. Returns None
+    when the host did not finish issuing before the sleep ended (the number
+    would include host gaps) or when the sleep kernel is unavailable."""
+    global _SLEEP_CYCLES_PER_MS
+    if not hasattr(torch.cuda, "_sleep"):
+        return None
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    if _SLEEP_CYCLES_PER_MS is None:
+        c0 = 1 << 22
+        torch.cuda.synchronize()
+        e0.record()
+        torch.cuda._sleep(c0)
+        e1.record()
+        torch.cuda.synchronize()
+        _SLEEP_CYCLES_PER_MS = c0 / max(e0.elapsed_time(e1), 1e-3)
+    hold_ms = 2.0 + 2.0 * wall_ms_per_step * steps
+    torch.cuda.synchronize()
+    torch.cuda._sleep(int(hold_ms * _SLEEP_CYCLES_PER_MS))
+    t0 = time.perf_counter()
+    e0.record()
+    for i in range(steps):
+        step(first + i)
+    e1.record()
+    issue_ms = (time.perf_counter() - t0) * 1e3
+    torch.cuda.synchronize()
+    if issue_ms > 0.8 * hold_ms:
+        return None
+    return e0.elapsed_time(e1) / steps * 1e3
+
+
+def back_to_back(torch, step, steps, warmup, wall_ms, nbytes):
+    """The queued measurement as bench fields (at most 100 steps, so that the
+    launches fit in the stream's hardware queue)."""
+    n = min(steps, 100)
+    us = queued_steps(torch, step, n, warmup, wall_ms)
+    if us is None:
+        return {"device_us_back_to_back": None}
+    return {"device_us_back_to_back": us,
+            "frac_of_peak_back_to_back": nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS}
+
+
 # ------------------------------------------------------------------- legs
 
 def leg_lm_head(torch, nv, workloads, traffic, steps, warmup, want_cpu):
@@ -215,6 +265,7 @@ def leg_m8(torch, nv, workloads, traffic, steps, warmup):
             "bytes_per_step": B, "ms_per_step": ms, "step_us_events": kt * 1e3,
             "gbs_wall": B / (ms * 1e-3) / 1e9, "gbs_kernel": B / (kt * 1e-3) / 1e9,
             "frac_of_peak": B / (kt * 1e-3) / 1e9 / HBM_PEAK_GBS,
+            **back_to_back(torch, step, steps, warmup, ms, B),
             "tokens_per_s": M / (ms * 1e-3), "rotate_copies": R}
 
 
@@ -263,11 +314,13 @@ def leg_layer(torch, nv, workloads, traffic, steps, warmup):
             "bytes_per_step": B, "ms_per_step": ms, "step_us_events": kt * 1e3,
             "gbs_wall": B / (ms * 1e-3) / 1e9, "gbs_kernel": B / (kt * 1e-3) / 1e9,
             "frac_of_peak": B / (kt * 1e-3) / 1e9 / HBM_PEAK_GBS,
+            **back_to_back(torch, step, steps, warmup, ms, B),
             "tokens_per_s": M / (ms * 1e-3), "rotate_copies": R,
             "fused": {"launches_per_step": len(groups), "bytes_per_step": Bf,
                       "ms_per_step": msf, "step_us_events": ktf * 1e3,
                       "gbs_kernel": Bf / (ktf * 1e-3) / 1e9,
                       "frac_of_peak": Bf / (ktf * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                      **back_to_back(torch, step_fused, steps, warmup, msf, Bf),
                       "tokens_per_s": M / (msf * 1e-3)}}
 
 
@@ -311,6 +364,7 @@ def leg_w4a4(torch, nv, workloads, traffic, steps, warmup):
             "step_us_events": kms * 1e3, "gbs_wall": B / (ms * 1e-3) / 1e9,
             "gbs_kernel": B / (kms * 1e-3) / 1e9,
             "frac_of_peak": B / (kms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+            **back_to_back(torch, step, steps, warmup, ms, B),
             "tokens_per_s": M / (ms * 1e-3), "rotate_copies": reps}
 
 
@@ -365,6 +419,8 @@ def leg_moe(torch, nv, workloads, traffic, steps, warmup, M):
                 "pass_us": kms * 1e3, "gbs_wall": B / (ms * 1e-3) / 1e9,
                 "gbs_pass": B / (kms * 1e-3) / 1e9,
                 "frac_of_peak": B / (kms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                **back_to_back(torch, step, steps, warmup, ms, float(np.mean(
+                    [nbytes(batches[(warmup + i) % nb][3]) for i in range(min(steps, 100))]))),
                 "tokens_per_s": M / (ms * 1e-3), "rotating_batches": nb}
 
     ws = torch.empty(nv.moe_workspace_bytes(M, H, I, topk), dtype=torch.uint8, device="cuda")
