@@ -126,7 +126,15 @@ def _check(fn: str, status: int) -> None:
         raise Nvfp4Error(fn, status, detail)
 
 
+# The current stream's raw handle for a device index: torch's own accessor
+# when it has one (about 0.06 us a call, against about 1.8 us for building a
+# Stream object through torch.cuda.current_stream).
+_raw_stream = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+
+
 def _stream(t: torch.Tensor) -> int:
+    if _raw_stream is not None:
+        return _raw_stream(t.get_device())
     return torch.cuda.current_stream(t.device).cuda_stream
 
 
