@@ -286,3 +286,28 @@ def test_gemv_segments_checks(L):
     bad[0].y = X                                                # output on x
     assert f(bad, 2, X, 1, 64, None) == ERR_ALIAS
     assert "segment" in L.nvfp4_last_error().decode()
+
+
+def test_last_error_is_per_thread(L):
+    """nvfp4_last_error describes the calling thread's last failure: two
+    threads fail different calls, meet at a barrier, then each reads its own
+    text."""
+    import threading
+    barrier = threading.Barrier(2)
+    seen = {}
+
+    def worker(name, call):
+        for _ in range(200):
+            assert call() != OK
+            barrier.wait()
+            seen.setdefault(name, set()).add(_err(L))
+            barrier.wait()
+
+    t1 = threading.Thread(target=worker, args=(
+        "shape", lambda: L.nvfp4_gemv(A, A, A, A, 1, 16, 48, B, None)))
+    t2 = threading.Thread(target=worker, args=(
+        "unsupported", lambda: L.nvfp4_gemv(A, A, A, A, 9, 16, 64, B, None)))
+    t1.start(), t2.start()
+    t1.join(), t2.join()
+    assert len(seen["shape"]) == 1 and "K % 32" in next(iter(seen["shape"]))
+    assert len(seen["unsupported"]) == 1 and "M=9" in next(iter(seen["unsupported"]))
