@@ -470,7 +470,7 @@ def leg_moe(torch, nv, workloads, traffic, steps, warmup, M):
 
     w4a4 = run(step_w4a4, lambda d: traffic.moe_w4a4_bytes(M, H, I, topk, d, Is),
                f"moe_w4a4_288x(3072x4096,4096x1536)_top8_shared768_m{M}")
-    w4a4["launches_per_step"] = 4
+    w4a4["launches_per_step"] = 3 if M == 1 else 4
     return routed, with_shared, w4a4
 
 

@@ -374,8 +374,9 @@ size_t nvfp4_moe_w4a4_workspace_bytes(int64_t M, int64_t H, int64_t I, int64_t t
  *
  * where Q(v, g) is the quantization of nvfp4_quantize_act (each 16-block:
  * s = E4M3(amax / (6 g)), code = E2M1(v / (s g))) taken back to the values
- * e2m1 * s, which are exact in bf16. Four launches on the stream: quantize
- * x, gate|up (shared expert included), quantize h, down and combine.
+ * e2m1 * s, which are exact in bf16. Launches on the stream: quantize x,
+ * gate|up (shared expert included), quantize h, down and combine; at M == 1
+ * gate|up quantizes h itself (three launches).
  *
  * Arguments as nvfp4_moe_gemv, plus
  *   gscale_x   float[1], > 0 and finite: the static input scale of x,

@@ -29,9 +29,12 @@
 // slots, with coefficient g2s (gate weight 1).
 // W4A4 routed experts (card.json performance[64], [65]) use the same kernels
 // on activations put on the NVFP4 grid by k_quantize_decode (w4a4.hip), with
-// the static scales folded into the weight scale and the combine weight.
+// the static scales folded into the weight scale and the combine weight. At
+// M = 1, k_moe_gate_up_w4a4_1 takes the place of gate|up and of h's
+// quantization pass.
 #include "gemv_core.h"
 #include "internal.h"
+#include "quant.h"
 
 namespace nvfp4 {
 
@@ -195,6 +198,77 @@ __global__ __launch_bounds__(256) void k_moe_gate_up(
       }
     }
     gate_up_rows<MSX>(codes, scales, g, xs, H, Iv, r0, xdiv, slot, ns, hd);
+  }
+}
+
+constexpr int kW4Waves = 8;   // k_moe_gate_up_w4a4_1: 16 gate|up rows per workgroup
+
+// W4A4 at M = 1: gate|up with the quantization of h folded in (three
+// launches per call instead of four). grid (ceil(max(I, Is) / 16), topk
+// [+ 1 for the shared expert, row 0]), kW4Waves wavefronts of one row pair
+// each, so a workgroup holds 16 consecutive rows of one slot's h -- exactly
+// one 16-block, as I is a multiple of 32.
+//   - A routed workgroup streams its 16 rows against x on the NVFP4 grid of
+//     *ga13 (xq, from k_quantize_decode) with weight scale g13[e] * *ga13,
+//     writes their h, and puts the 16 values on the grid of *ga2 (hq) in
+//     wavefront 0, one lane per value, as k_quantize_decode would.
+//   - The shared expert's workgroups (W4A16) read x itself and write hs.
+// A routed workgroup whose id is invalid returns as a whole before the
+// barrier; every other one takes it whole.
+// (Quantizing x inside each workgroup instead, into LDS, measured slower:
+// 30.2 against 27.8 us at 288 experts, top-8, shared expert 768. The
+// quantization sits in front of every workgroup's first weight load.)
+// At most 80 VGPRs (six wavefronts per SIMD): three workgroups per CU, so
+// the M = 1 grid runs in about one round (83 unbounded: two per CU).
+__global__ __launch_bounds__(64 * kW4Waves) __attribute__((amdgpu_waves_per_eu(6)))
+void k_moe_gate_up_w4a4_1(
+    const uint8_t* __restrict__ w13_codes, const uint8_t* __restrict__ w13_scales,
+    const float* __restrict__ w13_gscale, const uint16_t* __restrict__ x,
+    const uint16_t* __restrict__ xq, const float* __restrict__ ga13,
+    const float* __restrict__ ga2, const int32_t* __restrict__ ids, int topk, int64_t E,
+    int64_t H, int64_t I, uint16_t* __restrict__ h, uint16_t* __restrict__ hq,
+    const MoeShared sh) {
+  __shared__ uint16_t s_hb[2 * kW4Waves];   // the workgroup's 16 h values
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int64_t r0 = ((int64_t)blockIdx.x * kW4Waves + w) * 2;
+  if (sh.I > 0 && blockIdx.y == 0) {
+    // the shared expert: W4A16, its rows once for the token
+    if (r0 < sh.I) {
+      const int slot[1] = {0};
+      gate_up_rows<1>(sh.c13, sh.s13, *sh.g13, x, H, sh.I, r0, 1, slot, 1, sh.h);
+    }
+    return;
+  }
+  const int j = sh.I > 0 ? (int)blockIdx.y - 1 : (int)blockIdx.y;
+  if ((int64_t)blockIdx.x * 2 * kW4Waves >= I) return;   // the whole workgroup
+  const int32_t e = ids[j];
+  if (e < 0 || (int64_t)e >= E) return;                   // the whole workgroup
+  // this wavefront's gate rows r0, r0 + 1 and up rows I + r0, I + r0 + 1 (the
+  // workgroup's 16 rows lie below I)
+  {
+    const float g = w13_gscale[e] * *ga13;
+    const int64_t rows[4] = {r0, r0 + 1, I + r0, I + r0 + 1};
+    const uint16_t* xs[1] = {xq};
+    float acc[4][1];
+    wave_row_dots<1, 4>(w13_codes + (int64_t)e * (2 * I) * (H / 2),
+                        w13_scales + (int64_t)e * (2 * I) * (H / 16), H, rows, xs, 1, acc);
+    if (lane < 2) {
+      const float G = g * (lane == 0 ? acc[0][0] : acc[1][0]);
+      const float U = g * (lane == 0 ? acc[2][0] : acc[3][0]);
+      const float act = G / (1.0f + expf(-G)) * U;
+      const uint16_t hb = bf16_rne(act);
+      h[(int64_t)j * I + r0 + lane] = hb;
+      s_hb[2 * w + lane] = hb;
+    }
+  }
+  __syncthreads();
+  // the 16 h values on the grid of g_h: wavefront 0, one lane per value (all
+  // 64 lanes run the row reductions; lanes 0..15 hold the block)
+  if (w == 0) {
+    const uint16_t q =
+        quantize_decode_lane(__uint_as_float((uint32_t)s_hb[lane & 15] << 16), *ga2);
+    if (lane < 16) hq[(int64_t)j * I + (int64_t)blockIdx.x * 2 * kW4Waves + lane] = q;
   }
 }
 
@@ -500,7 +574,22 @@ hipError_t launch_moe(const uint8_t* w13_codes, const uint8_t* w13_scales,
   const uint16_t* hr = h;        // routed down input
   const float* ga13 = nullptr;
   const float* ga2 = nullptr;
-  if (w4a4) {
+  if (w4a4 && M == 1) {
+    // x onto the grid of its static scale, then gate|up, which also puts h
+    // on the grid of its own: three launches
+    uint16_t* hq = reinterpret_cast<uint16_t*>(ws + L.hq_off);
+    uint16_t* xq = reinterpret_cast<uint16_t*>(ws + L.xq_off);
+    hipError_t e = launch_quantize_decode(x, M, H, w4a4->ga13, nullptr, 0, xq, stream);
+    if (e != hipSuccess) return e;
+    const int64_t rows = sh.I > I ? sh.I : I;
+    const int64_t gx = (rows + 2 * kW4Waves - 1) / (2 * kW4Waves);
+    hipLaunchKernelGGL(k_moe_gate_up_w4a4_1, dim3((unsigned)gx, S + (sh.I > 0 ? 1 : 0)),
+                       dim3(64 * kW4Waves), 0, stream, w13_codes, w13_scales, w13_gscale, x, xq,
+                       w4a4->ga13, w4a4->ga2, ids, topk, E, H, I, h, hq, sh);
+    xr = nullptr;   // gate|up is done
+    hr = hq;
+    ga2 = w4a4->ga2;
+  } else if (w4a4) {
     // the token's activations onto the NVFP4 grid of their static scale
     uint16_t* xq = reinterpret_cast<uint16_t*>(ws + L.xq_off);
     hipError_t e = launch_quantize_decode(x, M, H, w4a4->ga13, nullptr, 0, xq, stream);
@@ -510,7 +599,7 @@ hipError_t launch_moe(const uint8_t* w13_codes, const uint8_t* w13_scales,
     ga13 = w4a4->ga13;
     ga2 = w4a4->ga2;
   }
-  {
+  if (xr) {
     const int64_t pairs = ((sh.I > I ? sh.I : I) + 1) / 2;
     const int64_t yb = (pairs + kMoeWaves - 1) / kMoeWaves;
     const dim3 grid((unsigned)yb, S + (sh.I > 0 ? 1 : 0));
@@ -521,7 +610,7 @@ hipError_t launch_moe(const uint8_t* w13_codes, const uint8_t* w13_scales,
       hipLaunchKernelGGL(k_moe_gate_up<kGateUpSlots>, grid, dim3(256), 0, stream, w13_codes,
                          w13_scales, w13_gscale, x, xr, ga13, ids, S, topk, E, H, I, h, sh, M);
   }
-  if (w4a4) {
+  if (w4a4 && xr) {
     // h of every valid slot onto the NVFP4 grid of its static scale
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;

@@ -17,6 +17,7 @@
 //     bf16 values, for the W4A4 MoE (its x before gate|up, its h before down).
 #include "device.h"
 #include "internal.h"
+#include "quant.h"
 
 namespace nvfp4 {
 
@@ -113,16 +114,7 @@ __global__ __launch_bounds__(256) void k_quantize_decode(const uint16_t* __restr
     const int32_t e = ids[t / (size_t)K];
     if (e < 0 || (int64_t)e >= E) return;
   }
-  float ab = fabsf(w);
-  ab = fmaxf(ab, dpp_f32<0xB1>(ab));    // quad_perm [1,0,3,2]
-  ab = fmaxf(ab, dpp_f32<0x4E>(ab));    // quad_perm [2,3,0,1]
-  ab = fmaxf(ab, dpp_f32<0x141>(ab));   // row_half_mirror
-  ab = fmaxf(ab, dpp_f32<0x140>(ab));   // row_mirror: the 16-lane row
-  const float r = ab / (6.0f * g);
-  const float s = e4m3_to_f32<0>(e4m3_encode(r));
-  const uint32_t code = s != 0.0f ? e2m1_encode(w / (s * g)) : 0u;
-  const float v = e2m1x2_to_f32<0>(code).x * s;
-  out[t] = (uint16_t)(__float_as_uint(v) >> 16);
+  out[t] = quantize_decode_lane(w, g);
 }
 
 hipError_t launch_quantize_decode(const uint16_t* x, int64_t rows, int64_t K,

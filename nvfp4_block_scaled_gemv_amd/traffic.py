@@ -50,13 +50,15 @@ def moe_shared_bytes(M: int, H: int, I: int, topk: int, distinct: int, Is: int) 
 
 def moe_w4a4_bytes(M: int, H: int, I: int, topk: int, distinct: int, Is: int = 0) -> int:
     """One W4A4 MoE call: moe_bytes (moe_shared_bytes with a shared expert)
-    plus the two quantization passes, each reading its bf16 input and writing
-    the values on the NVFP4 grid that the next pass reads: x[M, H] (read,
-    write, read) and h[M*topk, I] (read, write, read), and the two static
-    scales."""
+    plus the two quantizations, each writing the values on the NVFP4 grid
+    that the next pass reads, and the two static scales. x[M, H] is read,
+    written and read again by its own pass. h[M*topk, I] is too at M >= 2; at
+    M = 1 gate|up puts h on the grid as it produces it, so h is only written
+    once more."""
     base = (moe_shared_bytes(M, H, I, topk, distinct, Is) if Is
             else moe_bytes(M, H, I, topk, distinct))
-    return base + 2 * M * H * 2 + 2 * M * topk * I * 2 + 8
+    h_extra = (1 if M == 1 else 2) * M * topk * I * 2
+    return base + 2 * M * H * 2 + h_extra + 8
 
 
 def pages_floor_us(M: float, N: int, K: int, experts: float, bits: float,

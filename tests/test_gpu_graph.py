@@ -3,7 +3,8 @@ replayed: each replay, with eager launches and synchronisations between the
 replays and the graph's outputs poisoned before each one, must reproduce the
 eager result bit for bit. Covers the vector-ALU, split-K and other-K MFMA
 GEMV paths, the segmented GEMV, the MoE with and without a shared expert,
-the W4A4 MoE, and the W4A4 quantizer and GEMV (direct and decoded paths).
+the W4A4 MoE (at M = 3 and on the single-token path), and the W4A4
+quantizer and GEMV (direct and decoded paths).
 Nothing here clears memory with hipMemsetAsync, so nothing of the kind is
 recorded into a graph."""
 import numpy as np
@@ -94,14 +95,17 @@ def _shared(H, Is, seed):
             dev(c2), dev(s2), dev(np.array([0.02], np.float32)))
 
 
-@pytest.mark.parametrize("kind", ["routed", "shared", "w4a4", "w4a4_shared"])
+@pytest.mark.parametrize("kind", ["routed", "shared", "w4a4", "w4a4_shared", "w4a4_m1",
+                                  "w4a4_shared_m1"])
 def test_graph_moe(kind):
-    E, H, I, M, topk = 6, 512, 256, 3, 4
+    """M = 3, and M = 1 for W4A4 (the two-launch single-token path)."""
+    E, H, I, topk = 6, 512, 256, 4
+    M = 1 if kind.endswith("_m1") else 3
     w = _experts(E, H, I, 5)
     sh = _shared(H, 96, 5) if "shared" in kind else None
     Is = 96 if sh is not None else 0
     ids, gw = workloads.moe_routing(2, 5, M, E, topk)
-    ids[1, 2] = -1                                   # an invalid slot too
+    ids[M - 1, 2] = -1                               # an invalid slot too
     ids, gw = dev(ids), dev(gw)
     x = dev_x(workloads.x_bf16(2, 5, 0, M, H))
     x2 = dev_x(workloads.x_bf16(2, 6, 0, M, H))

@@ -1,6 +1,7 @@
 """GPU W4A4 MoE (nvfp4_moe_w4a4_gemv) against the oracle: the 288-expert
 workload at M = 1 and M = 8 with and without the W4A16 shared expert, a
-small model with duplicate and invalid ids, and grid activations.
+small model with duplicate and invalid ids, the single-token path (both
+quantizations inside gate|up) and its edges, and grid activations.
 
 What is compared, and how:
   - x on the NVFP4 grid of its static scale (the workspace's xq): bit for bit
@@ -103,6 +104,39 @@ def test_moe_w4a4_duplicates_invalid_ids_and_saturation(Is):
         y = run_w4a4_moe(hw, dw, x, ids, gw, H, I, ga13, 8.0, shared, f"Is={Is} {name}")
         if name == "all_invalid" and not Is:
             assert not y.any()
+
+
+@pytest.mark.parametrize("case", ["dup_invalid", "all_invalid_shared", "shared_wider_than_i",
+                                  "topk16", "h16384", "h16416"])
+def test_moe_w4a4_single_token(case):
+    """M = 1 takes three launches: x onto its grid, then a gate|up launch that
+    also puts each 16-row block of h onto its grid, then down and combine.
+    Covers invalid and duplicate ids, ids that are all invalid (the shared
+    expert alone contributes), a shared expert wider than I, topk = 16, and
+    long rows (H = 16384 and 16416)."""
+    E, H, I, Is = 6, 512, 256, 0
+    ids = np.array([[2, -1, 2, 9]], np.int32)
+    if case == "all_invalid_shared":
+        ids, Is = np.array([[-1, 6]], np.int32), 96
+    elif case == "shared_wider_than_i":
+        E, H, I, Is = 5, 256, 64, 160
+        ids = np.array([[1, 4, 0]], np.int32)
+    elif case == "topk16":
+        E, H, I = 20, 128, 32
+        ids = np.random.default_rng(16).choice(E, 16, replace=False).astype(np.int32)[None]
+    elif case in ("h16384", "h16416"):
+        E, I, Is = 3, 64, 32
+        H = int(case[1:])
+        ids = np.array([[0, 2]], np.int32)
+    hw, dw = build_experts(47, 0, E, H, I, range(E))
+    shared = build_shared(47, 1, H, Is) if Is else None
+    topk = ids.shape[1]
+    gw = np.random.default_rng(topk).random((1, topk)).astype(np.float32)
+    x = workloads.x_bf16(47, 1, H, 1, H)
+    ga13 = np.float32(np.abs(bf16_value(x)).max() / 2688.0 / 4.0)
+    y = run_w4a4_moe(hw, dw, x, ids, gw, H, I, ga13, 2.0, shared, f"M=1 {case}")
+    if case == "all_invalid_shared":
+        assert y.any()
 
 
 def test_moe_w4a4_grid_activations_match_w4a16_h_and_repeat():

@@ -58,3 +58,6 @@ def test_moe_w4a4_bytes_add_the_two_quantization_passes():
     assert q - routed == 2 * 2 * 4096 * 2 + 2 * 16 * 1536 * 2 + 8
     with_shared = traffic.moe_w4a4_bytes(2, 4096, 1536, 8, 14, 768)
     assert with_shared - q == traffic.moe_shared_bytes(2, 4096, 1536, 8, 14, 768) - routed
+    # one token: h goes onto its grid inside gate|up (no second read of h)
+    one = traffic.moe_w4a4_bytes(1, 4096, 1536, 8, 8) - traffic.moe_bytes(1, 4096, 1536, 8, 8)
+    assert one == 2 * 4096 * 2 + 8 * 1536 * 2 + 8
