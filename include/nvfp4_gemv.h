@@ -55,7 +55,7 @@
 extern "C" {
 #endif
 
-#define NVFP4_ABI_VERSION 5
+#define NVFP4_ABI_VERSION 6
 
 /* Largest number of activation rows (tokens) one GEMV / MoE call takes. */
 #define NVFP4_MAX_M 8
@@ -284,6 +284,34 @@ nvfp4_status nvfp4_gemv_w4a4(const uint8_t* codes_w, const uint8_t* scales_w,
                              const uint8_t* scales_x, const float* gscale_x, int64_t M,
                              int64_t N, int64_t K, float* y, void* workspace,
                              size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * nvfp4_gemv_w4a4_segments -- several NVFP4 weight matrices on the same NVFP4
+ * activations (gate|up of the W4A4 dense FFN, card.json performance[20],
+ * [24]), in one launch at M <= 2 (two at M >= 3): for every segment s,
+ *
+ *   y_s = g_s * g_x * decode(W_s) . decode(x)^T
+ *
+ * exactly as n_segments nvfp4_gemv_w4a4 calls would compute it.
+ *
+ *   segs        host array of n_segments descriptors, as for
+ *               nvfp4_gemv_segments (read during the call only);
+ *   n_segments  0 .. NVFP4_MAX_SEGMENTS;
+ *   codes_x, scales_x, gscale_x  the activations, as for nvfp4_gemv_w4a4;
+ *   M, K        0 <= M <= NVFP4_MAX_M, K % 32 == 0; the segments' N together
+ *               at most NVFP4_MAX_N;
+ *   workspace   at least nvfp4_gemv_w4a4_workspace_bytes(M, K) bytes,
+ *               256-byte aligned; overwritten; must not be shared by calls
+ *               that may run concurrently (not needed when K == 0).
+ * No output or the workspace may overlap any input, another output or each
+ * other.
+ * Errors: NULL, SHAPE, ALIGN, UNSUPPORTED, WORKSPACE, ALIAS, HIP.
+ */
+nvfp4_status nvfp4_gemv_w4a4_segments(const nvfp4_gemv_segment* segs, int64_t n_segments,
+                                      const uint8_t* codes_x, const uint8_t* scales_x,
+                                      const float* gscale_x, int64_t M, int64_t K,
+                                      void* workspace, size_t workspace_bytes,
+                                      hipStream_t stream);
 
 /*
  * nvfp4_moe_shared -- the shared expert of a MoE layer: a dense SwiGLU FFN

@@ -98,6 +98,9 @@ def lib() -> ctypes.CDLL:
         L.nvfp4_gemv_w4a4_workspace_bytes.argtypes = [_I64, _I64]
         L.nvfp4_gemv_w4a4.restype = ctypes.c_int
         L.nvfp4_gemv_w4a4.argtypes = [_VP] * 6 + [_I64] * 3 + [_VP, _VP, ctypes.c_size_t, _VP]
+        L.nvfp4_gemv_w4a4_segments.restype = ctypes.c_int
+        L.nvfp4_gemv_w4a4_segments.argtypes = [ctypes.POINTER(GemvSegment), _I64, _VP, _VP, _VP,
+                                               _I64, _I64, _VP, ctypes.c_size_t, _VP]
         L.nvfp4_moe_workspace_bytes.restype = ctypes.c_size_t
         L.nvfp4_moe_workspace_bytes.argtypes = [_I64, _I64, _I64, _I64]
         L.nvfp4_moe_gemv.restype = ctypes.c_int
@@ -301,6 +304,41 @@ def gemv_w4a4(codes, scales, gscale, codes_x, scales_x, gscale_x,
     y = torch.empty((M, codes.shape[0]), dtype=torch.float32, device=codes.device)
     gemv_w4a4_into(codes, scales, gscale, codes_x, scales_x, gscale_x, y, workspace)
     return y
+
+
+def gemv_w4a4_segments_into(mats, codes_x, scales_x, gscale_x, ys, workspace) -> None:
+    """One launch (two at M >= 3) for several weight matrices on the same
+    NVFP4 activations: ys[s] = g_s g_x decode(W_s) . decode(x)^T,
+    mats[s] = (codes, scales, gscale)."""
+    if len(mats) != len(ys):
+        raise ValueError("one output per matrix")
+    if len(mats) > MAX_SEGMENTS:
+        raise ValueError(f"at most {MAX_SEGMENTS} matrices per launch")
+    _dev(codes_x, scales_x, gscale_x, workspace, *ys, *[t for m in mats for t in m])
+    M, K = codes_x.shape[0], codes_x.shape[1] * 2
+    segs = (GemvSegment * max(1, len(mats)))()
+    for i, ((c, sc, g), y) in enumerate(zip(mats, ys)):
+        _dtype(y, torch.float32, name="y")
+        N = c.shape[0]
+        if c.shape[1] * 2 != K or tuple(y.shape) != (M, N):
+            raise ValueError(f"segment {i}: codes {tuple(c.shape)}, codes_x "
+                             f"{tuple(codes_x.shape)}, y {tuple(y.shape)}")
+        segs[i] = GemvSegment(_p(c), _p(sc), _p(g), _p(y), N)
+    _check("nvfp4_gemv_w4a4_segments", lib().nvfp4_gemv_w4a4_segments(
+        segs, len(mats), _p(codes_x), _p(scales_x), _p(gscale_x), M, K, _p(workspace),
+        workspace.numel() * workspace.element_size(), _stream(codes_x)))
+
+
+def gemv_w4a4_segments(mats, codes_x, scales_x, gscale_x, workspace=None):
+    """[y_s] for mats = [(codes, scales, gscale), ...] on the same NVFP4 x."""
+    M, K = codes_x.shape[0], codes_x.shape[1] * 2
+    if workspace is None:
+        workspace = torch.empty(max(gemv_w4a4_workspace_bytes(M, K), 256), dtype=torch.uint8,
+                                device=codes_x.device)
+    ys = [torch.empty((M, c.shape[0]), dtype=torch.float32, device=codes_x.device)
+          for c, _, _ in mats]
+    gemv_w4a4_segments_into(mats, codes_x, scales_x, gscale_x, ys, workspace)
+    return ys
 
 
 # ------------------------------------------------------------------- moe

@@ -276,6 +276,101 @@ nvfp4_status nvfp4_gemv_w4a4(const uint8_t* codes_w, const uint8_t* scales_w,
                     "nvfp4_gemv_w4a4 launch");
 }
 
+nvfp4_status nvfp4_gemv_w4a4_segments(const nvfp4_gemv_segment* segs, int64_t n_segments,
+                                      const uint8_t* codes_x, const uint8_t* scales_x,
+                                      const float* gscale_x, int64_t M, int64_t K,
+                                      void* workspace, size_t workspace_bytes,
+                                      hipStream_t stream) {
+  clear_error();
+  const char* fn = "nvfp4_gemv_w4a4_segments";
+  if (n_segments < 0 || M < 0 || K < 0 || (K % 32) != 0)
+    return fail(NVFP4_ERR_SHAPE, "%s: need n_segments, M, K >= 0 and K %% 32 == 0 "
+                "(n=%lld M=%lld K=%lld)", fn, (long long)n_segments, (long long)M, (long long)K);
+  if (n_segments > NVFP4_MAX_SEGMENTS || M > NVFP4_MAX_M)
+    return fail(NVFP4_ERR_UNSUPPORTED, "%s: n_segments=%lld (max %d), M=%lld (max %d)", fn,
+                (long long)n_segments, NVFP4_MAX_SEGMENTS, (long long)M, NVFP4_MAX_M);
+  if (n_segments == 0 || M == 0) return NVFP4_OK;
+  if (!segs) return fail(NVFP4_ERR_NULL, "%s: segs is NULL", fn);
+  nvfp4::SegDesc d[NVFP4_MAX_SEGMENTS];
+  int n = 0;
+  int64_t total_n = 0;
+  for (int64_t s = 0; s < n_segments; ++s) {
+    const nvfp4_gemv_segment& g = segs[s];
+    if (g.N < 0)
+      return fail(NVFP4_ERR_SHAPE, "%s: segment %lld has N=%lld < 0", fn, (long long)s,
+                  (long long)g.N);
+    if (g.N > NVFP4_MAX_N - total_n)
+      return fail(NVFP4_ERR_UNSUPPORTED, "%s: the segments' N exceed %lld", fn,
+                  (long long)NVFP4_MAX_N);
+    total_n += g.N;
+    if (g.N == 0) continue;
+    if (!g.y) return fail(NVFP4_ERR_NULL, "%s: segment %lld y is NULL", fn, (long long)s);
+    if (!aligned(g.y, 4))
+      return fail(NVFP4_ERR_ALIGN, "%s: segment %lld y must be 4-byte aligned", fn,
+                  (long long)s);
+    if (K > 0) {
+      if (!g.codes || !g.scales || !g.gscale)
+        return fail(NVFP4_ERR_NULL, "%s: segment %lld has a NULL input", fn, (long long)s);
+      if (!aligned(g.codes, 16) || !aligned(g.scales, 2) || !aligned(g.gscale, 4))
+        return fail(NVFP4_ERR_ALIGN, "%s: segment %lld: codes must be 16-byte, scales 2-byte, "
+                    "gscale 4-byte aligned", fn, (long long)s);
+    }
+    d[n++] = {g.codes, g.scales, g.gscale, g.y, g.N};
+  }
+  if (n == 0) return NVFP4_OK;
+  if (K > 0) {
+    if (!codes_x || !scales_x || !gscale_x)
+      return fail(NVFP4_ERR_NULL, "%s: NULL activation input", fn);
+    if (!aligned(codes_x, 16) || !aligned(scales_x, 2) || !aligned(gscale_x, 4))
+      return fail(NVFP4_ERR_ALIGN, "%s: codes_x 16-byte, scales_x 2-byte, gscale_x 4-byte "
+                  "aligned", fn);
+  }
+  const size_t need = nvfp4::w4a4_layout(M, K).total;
+  if (K > 0) {
+    if (!workspace || workspace_bytes < need)
+      return fail(NVFP4_ERR_WORKSPACE, "%s: workspace of %zu bytes needed, %zu given", fn, need,
+                  workspace ? workspace_bytes : (size_t)0);
+    if (!aligned(workspace, 256))
+      return fail(NVFP4_ERR_ALIGN, "%s: workspace must be 256-byte aligned", fn);
+  }
+  // no output (or the workspace) may overlap any input, another output or the workspace
+  const size_t mk = (size_t)M * (size_t)K;
+  for (int a = 0; a < n; ++a) {
+    const size_t ya = (size_t)M * (size_t)d[a].N * 4;
+    if (K > 0 && (overlap(d[a].y, ya, codes_x, mk / 2) || overlap(d[a].y, ya, scales_x, mk / 16) ||
+                  overlap(d[a].y, ya, gscale_x, 4) || overlap(d[a].y, ya, workspace, need)))
+      return fail(NVFP4_ERR_ALIAS, "%s: an output overlaps the activations or the workspace", fn);
+    for (int b = 0; b < n; ++b) {
+      const size_t nk = (size_t)d[b].N * (size_t)K;
+      if (K > 0 && (overlap(d[a].y, ya, d[b].codes, nk / 2) ||
+                    overlap(d[a].y, ya, d[b].scales, nk / 16) ||
+                    overlap(d[a].y, ya, d[b].gscale, 4)))
+        return fail(NVFP4_ERR_ALIAS, "%s: an output overlaps an input", fn);
+      if (K > 0 && (overlap(workspace, need, d[b].codes, nk / 2) ||
+                    overlap(workspace, need, d[b].scales, nk / 16) ||
+                    overlap(workspace, need, d[b].gscale, 4)))
+        return fail(NVFP4_ERR_ALIAS, "%s: the workspace overlaps an input", fn);
+      if (b != a && overlap(d[a].y, ya, d[b].y, (size_t)M * (size_t)d[b].N * 4))
+        return fail(NVFP4_ERR_ALIAS, "%s: two outputs overlap", fn);
+    }
+  }
+  if (K > 0 && (overlap(workspace, need, codes_x, mk / 2) ||
+                overlap(workspace, need, scales_x, mk / 16) || overlap(workspace, need, gscale_x, 4)))
+    return fail(NVFP4_ERR_ALIAS, "%s: the workspace overlaps the activations", fn);
+  if (K == 0) {
+    for (int a = 0; a < n; ++a) {
+      const nvfp4_status st =
+          hip_result(nvfp4::launch_fill_zero(d[a].y, (size_t)M * (size_t)d[a].N, stream),
+                     "nvfp4_gemv_w4a4_segments zero fill");
+      if (st != NVFP4_OK) return st;
+    }
+    return NVFP4_OK;
+  }
+  return hip_result(nvfp4::launch_gemv_w4a4_segments(d, n, codes_x, scales_x, gscale_x, (int)M,
+                                                     K, workspace, stream),
+                    "nvfp4_gemv_w4a4_segments launch");
+}
+
 size_t nvfp4_moe_workspace_bytes(int64_t M, int64_t H, int64_t I, int64_t topk) {
   if (M < 0 || H < 0 || I < 0 || topk < 0) return 0;
   return nvfp4::moe_layout(M, H, I, topk, 0, false).total;

@@ -53,8 +53,8 @@ __global__ __launch_bounds__(256) void k_gemv(const SegTable tab, const uint16_t
 
 // W4A4 at M <= 2: k_gemv's loop with NVFP4 activations read and decoded in
 // place (wave_row_dots_q), and the tensor scale g_w * g_x (one fp32
-// rounding). One matrix.
-template <int M, int R>
+// rounding), over one matrix or the segment table of several.
+template <int M, int R, bool SEG>
 __global__ __launch_bounds__(256) void k_gemv_w4a4(const SegTable tab,
                                                    const uint8_t* __restrict__ codes_x,
                                                    const uint8_t* __restrict__ scales_x,
@@ -72,20 +72,24 @@ __global__ __launch_bounds__(256) void k_gemv_w4a4(const SegTable tab,
     xc[m] = codes_x + (int64_t)m * (K / 2);
     xs[m] = scales_x + (int64_t)m * (K / 16);
   }
-  const float g = *tab.gscale[0] * *gscale_x;
-  const int64_t N = tab.N[0];
+  const float gx = *gscale_x;
+  const float g0 = SEG ? 0.0f : *tab.gscale[0] * gx;
   for (int64_t u = wave; u < units; u += nwaves) {
-    const int64_t n0 = u * R;
+    const Seg sg = SEG ? find_seg(tab, u)
+                       : Seg{tab.codes[0], tab.scales[0], tab.gscale[0], tab.y[0], tab.N[0], u, 0};
+    const float g = SEG ? *sg.gscale * gx : g0;
+    const int64_t N = sg.N;
+    const int64_t n0 = sg.unit * R;
     int64_t rows[R];
 #pragma unroll
     for (int r = 0; r < R; ++r) rows[r] = (n0 + r < N) ? (n0 + r) : (N - 1);
     float acc[R][M];
-    wave_row_dots_q<M, R>(tab.codes[0], tab.scales[0], K, rows, xc, xs, acc);
+    wave_row_dots_q<M, R>(sg.codes, sg.scales, K, rows, xc, xs, acc);
 #pragma unroll
     for (int r = 0; r < R; ++r)
 #pragma unroll
       for (int m = 0; m < M; ++m)
-        if (lane == r * M + m && n0 + r < N) tab.y[0][(int64_t)m * N + n0 + r] = acc[r][m] * g;
+        if (lane == r * M + m && n0 + r < N) sg.y[(int64_t)m * N + n0 + r] = acc[r][m] * g;
   }
 }
 
@@ -149,36 +153,43 @@ hipError_t launch_gemv_segments(const SegDesc* d, int n, const uint16_t* x, int 
 }
 
 template <int M, int R>
-static void launch_w4a4_m(const SegDesc& d, const uint8_t* codes_x, const uint8_t* scales_x,
-                          const float* gscale_x, int64_t K, hipStream_t stream) {
-  const SegTable tab = make_seg_table(&d, 1, R);
+static void launch_w4a4_m(const SegDesc* d, int n, const uint8_t* codes_x,
+                          const uint8_t* scales_x, const float* gscale_x, int64_t K,
+                          hipStream_t stream) {
+  const SegTable tab = make_seg_table(d, n, R);
   const int64_t units = tab.start[kMaxSegments];
   const int64_t want = (units + kWavesPerBlock - 1) / kWavesPerBlock;
   const int64_t cap = (int64_t)1 << 20;
   const unsigned grid = (unsigned)(want < cap ? want : cap);
-  hipLaunchKernelGGL((k_gemv_w4a4<M, R>), dim3(grid), dim3(256), 0, stream, tab, codes_x,
-                     scales_x, gscale_x, K);
+  if (n == 1)
+    hipLaunchKernelGGL((k_gemv_w4a4<M, R, false>), dim3(grid), dim3(256), 0, stream, tab,
+                       codes_x, scales_x, gscale_x, K);
+  else
+    hipLaunchKernelGGL((k_gemv_w4a4<M, R, true>), dim3(grid), dim3(256), 0, stream, tab,
+                       codes_x, scales_x, gscale_x, K);
 }
 
 template <int M>
-static void launch_w4a4_valu(const SegDesc& d, const uint8_t* codes_x, const uint8_t* scales_x,
-                             const float* gscale_x, int64_t K, hipStream_t stream) {
-  if (d.N >= 32768)
-    launch_w4a4_m<M, 4>(d, codes_x, scales_x, gscale_x, K, stream);
-  else if (d.N >= 4096)
-    launch_w4a4_m<M, 2>(d, codes_x, scales_x, gscale_x, K, stream);
+static void launch_w4a4_valu(const SegDesc* d, int n, const uint8_t* codes_x,
+                             const uint8_t* scales_x, const float* gscale_x, int64_t K,
+                             hipStream_t stream) {
+  int64_t rows = 0;
+  for (int s = 0; s < n; ++s) rows += d[s].N;
+  if (rows >= 32768)
+    launch_w4a4_m<M, 4>(d, n, codes_x, scales_x, gscale_x, K, stream);
+  else if (rows >= 4096)
+    launch_w4a4_m<M, 2>(d, n, codes_x, scales_x, gscale_x, K, stream);
   else
-    launch_w4a4_m<M, 1>(d, codes_x, scales_x, gscale_x, K, stream);
+    launch_w4a4_m<M, 1>(d, n, codes_x, scales_x, gscale_x, K, stream);
 }
 
-hipError_t launch_gemv_w4a4_valu(const uint8_t* codes, const uint8_t* scales,
-                                 const float* gscale, const uint8_t* codes_x,
+hipError_t launch_gemv_w4a4_valu(const SegDesc* d, int n, const uint8_t* codes_x,
                                  const uint8_t* scales_x, const float* gscale_x, int M,
-                                 int64_t N, int64_t K, float* y, hipStream_t stream) {
-  const SegDesc d = {codes, scales, gscale, y, N};
+                                 int64_t K, hipStream_t stream) {
+  if (n < 1 || n > kMaxSegments) return hipErrorInvalidValue;
   switch (M) {
-    case 1: launch_w4a4_valu<1>(d, codes_x, scales_x, gscale_x, K, stream); break;
-    case 2: launch_w4a4_valu<2>(d, codes_x, scales_x, gscale_x, K, stream); break;
+    case 1: launch_w4a4_valu<1>(d, n, codes_x, scales_x, gscale_x, K, stream); break;
+    case 2: launch_w4a4_valu<2>(d, n, codes_x, scales_x, gscale_x, K, stream); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

@@ -45,7 +45,7 @@ hipError_t launch_gemv_splitk_shape(const SegDesc* d, int n, const uint16_t* x, 
 // product of the two tensor scales).
 struct W4a4Layout {
   size_t x_off;   // uint16 bf16 x~[M, K]
-  size_t g_off;   // float g_w * g_x
+  size_t g_off;   // float g_w * g_x, one per matrix (up to kMaxSegments)
   size_t total;   // rounded up to 256 bytes
 };
 W4a4Layout w4a4_layout(int64_t M, int64_t K);
@@ -55,11 +55,15 @@ hipError_t launch_gemv_w4a4(const uint8_t* codes_w, const uint8_t* scales_w,
                             const float* gscale_w, const uint8_t* codes_x,
                             const uint8_t* scales_x, const float* gscale_x, int M, int64_t N,
                             int64_t K, float* y, void* workspace, hipStream_t stream);
+// The same over n <= kMaxSegments matrices (all N > 0) sharing the activations;
+// the workspace holds up to kMaxSegments tensor-scale products after x~.
+hipError_t launch_gemv_w4a4_segments(const SegDesc* d, int n, const uint8_t* codes_x,
+                                     const uint8_t* scales_x, const float* gscale_x, int M,
+                                     int64_t K, void* workspace, hipStream_t stream);
 // W4A4 GEMV at M <= 2 on the vector ALUs, activations read as NVFP4.
-hipError_t launch_gemv_w4a4_valu(const uint8_t* codes, const uint8_t* scales,
-                                 const float* gscale, const uint8_t* codes_x,
+hipError_t launch_gemv_w4a4_valu(const SegDesc* d, int n, const uint8_t* codes_x,
                                  const uint8_t* scales_x, const float* gscale_x, int M,
-                                 int64_t N, int64_t K, float* y, hipStream_t stream);
+                                 int64_t K, hipStream_t stream);
 // bf16 rows [rows, K] quantized with the static scale *gscale and written
 // back as the exact bf16 values e2m1 * s (the tensor scale left out). With
 // ids, row r is skipped (not written) when ids[r] is outside [0, E).

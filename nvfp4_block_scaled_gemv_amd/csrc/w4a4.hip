@@ -27,7 +27,7 @@ W4a4Layout w4a4_layout(int64_t M, int64_t K) {
   W4a4Layout L;
   L.x_off = 0;
   L.g_off = align256((size_t)M * (size_t)K * sizeof(uint16_t));
-  L.total = align256(L.g_off + sizeof(float));
+  L.total = align256(L.g_off + kMaxSegments * sizeof(float));
   return L;
 }
 
@@ -60,16 +60,22 @@ __global__ __launch_bounds__(256) void k_quantize_act(const uint16_t* __restrict
   if ((t & 7) == 0) scales[t >> 3] = (uint8_t)sc;
 }
 
+// The tensor scales g_w of up to kMaxSegments matrices.
+struct W4a4Scales {
+  const float* g[kMaxSegments];
+  int n;
+};
+
 // One thread per 32 activation elements (16 code bytes, two blocks): the
-// exact bf16 values e2m1 * s; thread 0 also writes g_w * g_x.
+// exact bf16 values e2m1 * s; thread s < n also writes g_w[s] * g_x.
 __global__ __launch_bounds__(256) void k_w4a4_prep(const uint8_t* __restrict__ codes_x,
                                                    const uint8_t* __restrict__ scales_x,
-                                                   size_t nchunks, const float* __restrict__ g_w,
+                                                   size_t nchunks, const W4a4Scales gw,
                                                    const float* __restrict__ g_x,
                                                    uint16_t* __restrict__ xt,
                                                    float* __restrict__ g_prod) {
   const size_t c = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (c == 0) *g_prod = *g_w * *g_x;
+  if (c < (size_t)gw.n) g_prod[c] = *gw.g[c] * *g_x;
   if (c >= nchunks) return;
   const uint4 q = *reinterpret_cast<const uint4*>(codes_x + c * 16);
   const uint32_t sw = (uint32_t)scales_x[2 * c] | ((uint32_t)scales_x[2 * c + 1] << 8);
@@ -138,23 +144,38 @@ hipError_t launch_quantize_act(const uint16_t* x, int64_t M, int64_t K, const fl
   return hipGetLastError();
 }
 
+hipError_t launch_gemv_w4a4_segments(const SegDesc* d, int n, const uint8_t* codes_x,
+                                     const uint8_t* scales_x, const float* gscale_x, int M,
+                                     int64_t K, void* workspace, hipStream_t stream) {
+  if (n < 1 || n > kMaxSegments) return hipErrorInvalidValue;
+  if (M <= 2)   // the vector-ALU kernel reads the NVFP4 activations directly
+    return launch_gemv_w4a4_valu(d, n, codes_x, scales_x, gscale_x, M, K, stream);
+  const W4a4Layout L = w4a4_layout(M, K);
+  uint16_t* xt = reinterpret_cast<uint16_t*>(static_cast<char*>(workspace) + L.x_off);
+  float* gp = reinterpret_cast<float*>(static_cast<char*>(workspace) + L.g_off);
+  W4a4Scales gw = {};
+  gw.n = n;
+  SegDesc dd[kMaxSegments];
+  for (int s = 0; s < n; ++s) {
+    gw.g[s] = d[s].gscale;
+    dd[s] = d[s];
+    dd[s].gscale = gp + s;   // g_w[s] * g_x, written by the prep pass
+  }
+  const size_t nchunks = (size_t)M * (size_t)K / 32;
+  const size_t threads = nchunks > (size_t)n ? nchunks : (size_t)n;
+  hipLaunchKernelGGL(k_w4a4_prep, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, stream,
+                     codes_x, scales_x, nchunks, gw, gscale_x, xt, gp);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  return launch_gemv_segments(dd, n, xt, M, K, stream);
+}
+
 hipError_t launch_gemv_w4a4(const uint8_t* codes_w, const uint8_t* scales_w,
                             const float* gscale_w, const uint8_t* codes_x,
                             const uint8_t* scales_x, const float* gscale_x, int M, int64_t N,
                             int64_t K, float* y, void* workspace, hipStream_t stream) {
-  if (M <= 2)   // the vector-ALU kernel reads the NVFP4 activations directly
-    return launch_gemv_w4a4_valu(codes_w, scales_w, gscale_w, codes_x, scales_x, gscale_x, M,
-                                 N, K, y, stream);
-  const W4a4Layout L = w4a4_layout(M, K);
-  uint16_t* xt = reinterpret_cast<uint16_t*>(static_cast<char*>(workspace) + L.x_off);
-  float* gp = reinterpret_cast<float*>(static_cast<char*>(workspace) + L.g_off);
-  const size_t nchunks = (size_t)M * (size_t)K / 32;
-  hipLaunchKernelGGL(k_w4a4_prep, dim3((unsigned)((nchunks + 255) / 256 + (nchunks ? 0 : 1))),
-                     dim3(256), 0, stream, codes_x, scales_x, nchunks, gscale_w, gscale_x, xt,
-                     gp);
-  const hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  return launch_gemv(codes_w, scales_w, gp, xt, M, N, K, y, stream);
+  const SegDesc d = {codes_w, scales_w, gscale_w, y, N};
+  return launch_gemv_w4a4_segments(&d, 1, codes_x, scales_x, gscale_x, M, K, workspace, stream);
 }
 
 }  // namespace nvfp4

@@ -32,7 +32,7 @@ def test_exports_every_declared_symbol(L):
     assert {"nvfp4_pack", "nvfp4_dequant", "nvfp4_gemv", "nvfp4_gemv_segments", "nvfp4_moe_gemv",
             "nvfp4_moe_workspace_bytes", "nvfp4_moe_shared_gemv",
             "nvfp4_moe_shared_workspace_bytes", "nvfp4_quantize_act", "nvfp4_gemv_w4a4",
-            "nvfp4_gemv_w4a4_workspace_bytes", "nvfp4_moe_w4a4_gemv",
+            "nvfp4_gemv_w4a4_workspace_bytes", "nvfp4_gemv_w4a4_segments", "nvfp4_moe_w4a4_gemv",
             "nvfp4_moe_w4a4_workspace_bytes", "nvfp4_abi_version", "nvfp4_status_string",
             "nvfp4_last_error"} <= set(names)
     for n in names:
@@ -40,7 +40,7 @@ def test_exports_every_declared_symbol(L):
 
 
 def test_version_and_status_strings(L):
-    assert L.nvfp4_abi_version() == 5
+    assert L.nvfp4_abi_version() == 6
     for s in range(8):
         assert L.nvfp4_status_string(s)
     assert L.nvfp4_status_string(99) == b"unknown status"
@@ -311,3 +311,37 @@ def test_last_error_is_per_thread(L):
     t1.join(), t2.join()
     assert len(seen["shape"]) == 1 and "K % 32" in next(iter(seen["shape"]))
     assert len(seen["unsupported"]) == 1 and "M=9" in next(iter(seen["unsupported"]))
+
+
+def test_gemv_w4a4_segments_checks(L):
+    """Host-side validation of the W4A4 multi-projection call (no launch)."""
+    Seg = nv.GemvSegment
+    arr = (Seg * 9)()
+    for i in range(9):
+        arr[i] = Seg(A + i * 0x100000, A + 0x10000000 + i * 0x10000, A + 0x20000000 + 16 * i,
+                     B + i * 0x100000, 64)
+    f = L.nvfp4_gemv_w4a4_segments
+    CX, SX, GX, WS = A + 0x30000000, A + 0x31000000, A + 0x32000000, B + 0x10000000
+    need = nv.gemv_w4a4_workspace_bytes(2, 64)
+    assert f(arr, 9, CX, SX, GX, 2, 64, WS, need, None) == ERR_UNSUPPORTED     # > 8 segments
+    assert f(arr, 2, CX, SX, GX, 9, 64, WS, need, None) == ERR_UNSUPPORTED     # M > 8
+    assert f(arr, 2, CX, SX, GX, 2, 48, WS, need, None) == ERR_SHAPE           # K % 32
+    assert f(arr, 0, CX, SX, GX, 2, 64, WS, need, None) == OK
+    assert f(arr, 2, CX, SX, GX, 0, 64, WS, need, None) == OK
+    assert f(None, 2, CX, SX, GX, 2, 64, WS, need, None) == ERR_NULL
+    assert f(arr, 2, None, SX, GX, 2, 64, WS, need, None) == ERR_NULL
+    assert f(arr, 2, CX + 8, SX, GX, 2, 64, WS, need, None) == ERR_ALIGN
+    assert f(arr, 2, CX, SX, GX, 2, 64, WS, need - 1, None) == ERR_WORKSPACE
+    assert f(arr, 2, CX, SX, GX, 2, 64, None, need, None) == ERR_WORKSPACE
+    assert f(arr, 2, CX, SX, GX, 2, 64, WS + 64, need, None) == ERR_ALIGN
+    bad = (Seg * 2)(arr[0], arr[1])
+    bad[0].N = bad[1].N = (1 << 29) + 1
+    assert f(bad, 2, CX, SX, GX, 2, 64, WS, need, None) == ERR_UNSUPPORTED
+    bad = (Seg * 2)(arr[0], arr[1])
+    bad[1].y = bad[0].y + 16                                    # outputs overlap
+    assert f(bad, 2, CX, SX, GX, 2, 64, WS, need, None) == ERR_ALIAS
+    bad = (Seg * 2)(arr[0], arr[1])
+    bad[1].y = CX                                               # output on codes_x
+    assert f(bad, 2, CX, SX, GX, 2, 64, WS, need, None) == ERR_ALIAS
+    assert f(arr, 2, CX, SX, GX, 2, 64, arr[0].codes, need, None) == ERR_ALIAS  # workspace on W
+    assert f(arr, 2, CX, SX, GX, 2, 64, arr[1].y, need, None) == ERR_ALIAS      # workspace on y

@@ -4,7 +4,7 @@ replays and the graph's outputs poisoned before each one, must reproduce the
 eager result bit for bit. Covers the vector-ALU, split-K and other-K MFMA
 GEMV paths, the segmented GEMV, the MoE with and without a shared expert,
 the W4A4 MoE (at M = 3 and on the single-token path), and the W4A4
-quantizer and GEMV (direct and decoded paths).
+quantizer and GEMV (direct and decoded paths, one matrix or several).
 Nothing here clears memory with hipMemsetAsync, so nothing of the kind is
 recorded into a graph."""
 import numpy as np
@@ -155,3 +155,20 @@ def test_graph_w4a4(M):
         nv.gemv_w4a4_into(c, s, g, cx2, sx2, gx, y2, ws2)
 
     check_graph(f"w4a4 M={M}", run, [cx, sx, y], disturb)
+
+
+@pytest.mark.parametrize("M", [2, 4])
+def test_graph_w4a4_segments(M):
+    K = 4096
+    mats = [_gemv_case(M, N, K, 400 + i)[:3] for i, N in enumerate((1024, 300))]
+    x = dev_x(workloads.x_bf16(1, 400, 9, M, K))
+    gx = dev(np.array([0.002], np.float32))
+    cx, sx = nv.quantize_act(x, gx)
+    ys = [torch.empty((M, m[0].shape[0]), device="cuda") for m in mats]
+    ws = torch.empty(nv.gemv_w4a4_workspace_bytes(M, K), dtype=torch.uint8, device="cuda")
+    cx2, sx2 = nv.quantize_act(dev_x(workloads.x_bf16(1, 401, 9, M, K)), gx)
+    ys2 = [torch.empty_like(y) for y in ys]
+    ws2 = torch.empty_like(ws)
+    check_graph(f"w4a4 segments M={M}",
+                lambda: nv.gemv_w4a4_segments_into(mats, cx, sx, gx, ys, ws), ys,
+                lambda: nv.gemv_w4a4_segments_into(mats, cx2, sx2, gx, ys2, ws2))

@@ -1,8 +1,9 @@
 """GPU W4A4 against the oracle: activation quantization with a static input
 scale bit for bit (calibrated and saturating scales), and the W4A4 GEMV within
 |y - y_ref| <= 1e-3 sum|w x| + 1e-6 on the pages' W4A4 dense FFN (gate, up,
-down 4096x4096 at M=2) and on shapes that take every GEMV kernel (vector ALU
-for M <= 2, the matrix-core kernels for K % 256 == 0 and otherwise)."""
+down 4096x4096 at M=2), on shapes that take every GEMV kernel (vector ALU
+for M <= 2, the matrix-core kernels for K % 256 == 0 and otherwise), and
+several matrices on the same activations in one call."""
 import numpy as np
 import pytest
 import torch
@@ -85,6 +86,36 @@ def test_w4a4_four_rows_per_wavefront_with_ragged_tail(M):
     x = workloads.x_bf16(6, M, 77, M, K)
     y, (y_ref, ad) = run_w4a4(cw, sw, gw, x, static_scale(6, M, K))
     check_tol(y, y_ref, ad, f"w4a4 M={M} N={N} K={K}")
+
+
+@pytest.mark.parametrize("M,K", [(1, 4096), (2, 4096), (3, 4096), (5, 4096), (8, 4096),
+                                 (2, 1056), (5, 1056)])
+def test_w4a4_segments(M, K):
+    """Several matrices on the same NVFP4 activations in one call (an empty
+    one among them): each output is within tolerance of the oracle's W4A4
+    GEMV of its matrix and equal, bit for bit, to a separate
+    nvfp4_gemv_w4a4 call (K = 1056 takes the other-K kernel at M >= 3)."""
+    say(f"[w4a4] segments M={M} K={K}")
+    Ns = (1000, 0, 37, 4200)
+    x = workloads.x_bf16(6, M, 90 + K, M, K)
+    gx = np.float32(static_scale(6, M, K))
+    cx, sx = oracle.quantize_act(x, gx)
+    cxd, sxd, gxd = dev(cx), dev(sx), dev(np.array([gx], np.float32))
+    host_w, mats = [], []
+    for i, N in enumerate(Ns):
+        cw, sw = workloads.random_nvfp4(6, M, 300 + 10 * i + K, N, K, 0x20, 0x50)
+        gw = np.float32(0.0173 * (i + 1))
+        host_w.append((cw, sw, gw))
+        mats.append((dev(cw), dev(sw), dev(np.array([gw], np.float32))))
+    ys = nv.gemv_w4a4_segments(mats, cxd, sxd, gxd)
+    for i, ((cw, sw, gw), m, y) in enumerate(zip(host_w, mats, ys)):
+        y = host(y)
+        assert y.shape == (M, Ns[i])
+        if Ns[i] == 0:
+            continue
+        y_ref, ad = oracle.gemv_w4a4(cw, sw, gw, cx, sx, gx)
+        check_tol(y, y_ref, ad, f"segment {i} M={M} K={K}")
+        assert np.array_equal(y, host(nv.gemv_w4a4(*m, cxd, sxd, gxd))), f"segment {i}"
 
 
 def test_w4a4_zero_k_and_empty():
