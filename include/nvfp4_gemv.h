@@ -21,8 +21,8 @@
  * Conventions for every entry point:
  *  - every pointer is a DEVICE pointer of the current HIP device; arrays are
  *    row-major and contiguous; the caller owns (allocates and frees) every
- *    buffer. The library allocates no device memory and keeps no mutable
- *    global state.
+ *    buffer. The library allocates no device memory; its only mutable
+ *    global state is the per-thread text of nvfp4_last_error().
  *  - shapes are checked on the host before anything is launched; on a failed
  *    check nothing is launched, the call returns the error code and
  *    nvfp4_last_error() describes it. Device data (ids, scales, the tensor
