@@ -596,8 +596,11 @@ def summarize_stats(stats_csv, cmd, out, top=16):
             rows.append(r)
     rows.sort(key=lambda r: -float(r["TotalDurationNs"]))
     durs = {}
+    # rocprofv3 writes <prefix>_kernel_trace.csv beside <prefix>_kernel_stats.csv
     trace_csv = stats_csv.replace("kernel_stats", "kernel_trace")
-    if os.path.exists(trace_csv):
+    if trace_csv == stats_csv:
+        trace_csv = ""
+    if trace_csv and os.path.exists(trace_csv):
         with open(trace_csv, newline="") as f:
             for r in csv.DictReader(f):
                 durs.setdefault(r["Kernel_Name"], []).append(
@@ -615,7 +618,7 @@ def summarize_stats(stats_csv, cmd, out, top=16):
         lines.append(f"{int(r['Calls']):7d} {float(r['AverageNs']) / 1e3:9.2f} {med:9.2f} "
                      f"{p10:9.2f} {p90:9.2f} {float(r['MinNs']) / 1e3:9.2f} "
                      f"{float(r['MaxNs']) / 1e3:9.2f} {float(r['Percentage']):6.2f}  {short}")
-    if os.path.exists(trace_csv):
+    if trace_csv and os.path.exists(trace_csv):
         lines += moe_pass_sums(trace_csv)
     with open(out, "w") as f:
         f.write("\n".join(lines) + "\n")

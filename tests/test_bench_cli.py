@@ -1,0 +1,72 @@
+"""bench.py's command line on the CPU: more than one GPU is refused with a
+message and exit status 2 before anything touches a device, and the profile
+summaries parse the CSV layout rocprofv3 writes."""
+import os
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.mark.parametrize("args,env", [(["--gpus", "2"], {}), (["--gpus", "8"], {}),
+                                      ([], {"WORLD_SIZE": "2"})])
+def test_more_than_one_gpu_is_refused(args, env):
+    e = dict(os.environ, **env)
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), *args],
+                       capture_output=True, text=True, env=e, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU only" in r.stderr
+    assert r.stdout == ""
+
+
+STATS = (
+    '"Name","Calls","TotalDurationNs","AverageNs","Percentage","MinNs","MaxNs","StdDev"\n'
+    '"void nvfp4::k_gemv<1, 4, false>",3,165000,55000,80.0,54000,56000,800\n'
+    '"nvfp4::k_amax",2,20000,10000,20.0,9000,11000,1000\n')
+TRACE = (
+    '"Kernel_Name","Start_Timestamp","End_Timestamp","Grid_Size_Y"\n'
+    '"void nvfp4::k_gemv<1, 4, false>",0,54000,1\n'
+    '"void nvfp4::k_gemv<1, 4, false>",60000,115000,1\n'
+    '"void nvfp4::k_gemv<1, 4, false>",120000,176000,1\n'
+    '"void nvfp4::k_moe_gate_up<1>",200000,212000,8\n'
+    '"void nvfp4::k_moe_down<2, 2>",212500,222500,1\n')
+
+
+def _summarize(stats, out):
+    return subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--summarize-stats",
+                           str(stats), str(out), "--cmd", "the command"],
+                          capture_output=True, text=True, timeout=120)
+
+
+def test_stats_summary_with_trace(tmp_path):
+    """Medians come from the kernel trace beside the stats file, and the MoE
+    pass sums from its gate|up and down dispatches."""
+    (tmp_path / "b_kernel_stats.csv").write_text(STATS)
+    (tmp_path / "b_kernel_trace.csv").write_text(TRACE)
+    out = tmp_path / "summary.txt"
+    r = _summarize(tmp_path / "b_kernel_stats.csv", out)
+    assert r.returncode == 0, r.stderr
+    text = out.read_text()
+    assert "the command" in text
+    row = [l for l in text.splitlines() if "k_gemv<1, 4, false>" in l][0].split()
+    assert row[0] == "3" and row[2] == "55.00"          # calls, median over the trace
+    assert "gate|up grid.y=8, W4A16, 2 launches" in text
+    line = [l for l in text.splitlines() if "grid.y=8" in l][0].split()
+    assert line[1] == "22.00"                              # 12 + 10 us
+
+
+def test_stats_summary_without_trace(tmp_path):
+    """A stats file with no trace beside it (or not named like rocprofv3's)
+    still gives the table, without medians."""
+    csv = tmp_path / "stats.csv"
+    csv.write_text(
+        '"Name","Calls","TotalDurationNs","AverageNs","Percentage","MinNs","MaxNs","StdDev"\n'
+        '"void nvfp4::k_gemv<1, 4, false>",3,165000,55000,80.0,54000,56000,800\n'
+        '"nvfp4::k_amax",2,20000,10000,20.0,9000,11000,1000\n')
+    out = tmp_path / "summary.txt"
+    r = _summarize(csv, out)
+    assert r.returncode == 0, r.stderr
+    text = out.read_text()
+    assert "the command" in text and "k_gemv<1, 4, false>" in text and "k_amax" in text
