@@ -70,3 +70,38 @@ def test_stats_summary_without_trace(tmp_path):
     assert r.returncode == 0, r.stderr
     text = out.read_text()
     assert "the command" in text and "k_gemv<1, 4, false>" in text and "k_amax" in text
+
+
+def _pmc_csv(path, counter, rows):
+    lines = ['"Dispatch_Id","Kernel_Name","Counter_Name","Counter_Value"']
+    lines += [f'{i},"{k}","{counter}",{v}' for i, (k, v) in enumerate(rows)]
+    path.write_text("\n".join(lines) + "\n")
+
+
+def test_traffic_summary_scales_by_the_copy_kernel(tmp_path):
+    """FETCH_SIZE and WRITE_SIZE of the LM-head kernel are turned into bytes
+    with the bytes per counter unit that the copy kernel of known size (512
+    MiB read and 512 MiB written per launch) gives; the header carries the
+    hash of the kernel sources that stored traffic is keyed on."""
+    lm = "void nvfp4::k_gemv<1, 4, false>(nvfp4::SegTable, unsigned short const*, long)"
+    cp = "void at::native::vectorized_elementwise_kernel<4, at::native::MulFunctor<float>>()"
+    _pmc_csv(tmp_path / "f.csv", "FETCH_SIZE", [(lm, 171000.0), (lm, 171002.0), (cp, 262144.0)])
+    _pmc_csv(tmp_path / "w.csv", "WRITE_SIZE", [(lm, 600.0), (lm, 600.0), (cp, 524288.0)])
+    out = tmp_path / "traffic.txt"
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--summarize-pmc",
+                        str(tmp_path / "f.csv"), str(tmp_path / "w.csv"), str(out),
+                        "--cmd", "pass 1", "--cmd", "pass 2"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 0, r.stderr
+    kv = dict(l.split(":", 1) for l in out.read_text().splitlines()
+              if ":" in l and not l.startswith("#"))
+    kv = {k.strip(): v.strip() for k, v in kv.items()}
+    # 512 MiB over 262144 and over 524288 counter units
+    assert kv["calibration_bytes_per_unit"] == "fetch 2048.00, write 1024.00"
+    kv = {k: v.split()[0] for k, v in kv.items()}
+    assert int(kv["read_bytes_per_launch"]) == 171001 * 2048
+    assert int(kv["write_bytes_per_launch"]) == 600 * 1024
+    assert int(kv["traffic_bytes_per_launch"]) == 171001 * 2048 + 600 * 1024
+    h = subprocess.run([sys.executable, "-c", "import bench; print(bench.kernel_source_hash())"],
+                       capture_output=True, text=True, cwd=ROOT, timeout=120).stdout.strip()
+    assert kv["kernel_source_sha256_16"] == h
