@@ -528,6 +528,24 @@ def _pmc_means(csv_path, counter):
     return {k: (sum(v) / len(v), len(v)) for k, v in acc.items()}
 
 
+def _copy_units(csv_path, counter):
+    """Mean per-dispatch value of `counter` for the copy kernel: among the
+    dispatches whose kernel name contains COPY_KERNEL, those with the largest
+    grid (other legs run the same elementwise kernel on smaller tensors).
+    Returns (mean, dispatches) or None."""
+    import csv
+    rows = []
+    with open(csv_path, newline="") as f:
+        for row in csv.DictReader(f):
+            if row["Counter_Name"] == counter and COPY_KERNEL in row["Kernel_Name"]:
+                rows.append((int(row.get("Grid_Size") or 0), float(row["Counter_Value"])))
+    if not rows:
+        return None
+    top = max(g for g, _ in rows)
+    vals = [v for g, v in rows if g == top]
+    return sum(vals) / len(vals), len(vals)
+
+
 def _pick(means, key):
     hits = [(k, v) for k, v in means.items() if key in k]
     if len(hits) != 1:
@@ -541,9 +559,11 @@ def summarize_pmc(fetch_csv, write_csv, cmd, out):
     the same counter reads for the copy kernel of known size."""
     from nvfp4_block_scaled_gemv_amd import traffic
     f_k, nf = _pick(_pmc_means(fetch_csv, "FETCH_SIZE"), LM_KERNEL)
-    f_c, nfc = _pick(_pmc_means(fetch_csv, "FETCH_SIZE"), COPY_KERNEL)
     w_k, nw = _pick(_pmc_means(write_csv, "WRITE_SIZE"), LM_KERNEL)
-    w_c, nwc = _pick(_pmc_means(write_csv, "WRITE_SIZE"), COPY_KERNEL)
+    fc, wc = _copy_units(fetch_csv, "FETCH_SIZE"), _copy_units(write_csv, "WRITE_SIZE")
+    if fc is None or wc is None:
+        raise SystemExit("no copy kernel dispatches in the counter CSVs")
+    (f_c, nfc), (w_c, nwc) = fc, wc
     copy_bytes = 512 << 20
     fr, fw = copy_bytes / f_c, copy_bytes / w_c        # bytes per counter unit
     read_b, write_b = f_k * fr, w_k * fw
@@ -672,9 +692,9 @@ def summarize_counters(csvs, cmd, out, match="nvfp4::"):
     import csv
     fetch_scale = None
     for path in csvs:
-        means = _pmc_means(path, "FETCH_SIZE")
-        if any(COPY_KERNEL in k for k in means):
-            fetch_scale = (512 << 20) / _pick(means, COPY_KERNEL)[0]
+        fc = _copy_units(path, "FETCH_SIZE")
+        if fc is not None:
+            fetch_scale = (512 << 20) / fc[0]
     vals = {}
     for path in csvs:
         with open(path, newline="") as f:

@@ -73,8 +73,10 @@ def test_stats_summary_without_trace(tmp_path):
 
 
 def _pmc_csv(path, counter, rows):
-    lines = ['"Dispatch_Id","Kernel_Name","Counter_Name","Counter_Value"']
-    lines += [f'{i},"{k}","{counter}",{v}' for i, (k, v) in enumerate(rows)]
+    """rows: (kernel name, counter value[, grid size])."""
+    lines = ['"Dispatch_Id","Grid_Size","Kernel_Name","Counter_Name","Counter_Value"']
+    lines += [f'{i},{r[2] if len(r) > 2 else 1024},"{r[0]}","{counter}",{r[1]}'
+              for i, r in enumerate(rows)]
     path.write_text("\n".join(lines) + "\n")
 
 
@@ -85,8 +87,11 @@ def test_traffic_summary_scales_by_the_copy_kernel(tmp_path):
     hash of the kernel sources that stored traffic is keyed on."""
     lm = "void nvfp4::k_gemv<1, 4, false>(nvfp4::SegTable, unsigned short const*, long)"
     cp = "void at::native::vectorized_elementwise_kernel<4, at::native::MulFunctor<float>>()"
-    _pmc_csv(tmp_path / "f.csv", "FETCH_SIZE", [(lm, 171000.0), (lm, 171002.0), (cp, 262144.0)])
-    _pmc_csv(tmp_path / "w.csv", "WRITE_SIZE", [(lm, 600.0), (lm, 600.0), (cp, 524288.0)])
+    # the same elementwise kernel on a smaller tensor (another leg) is not the copy
+    _pmc_csv(tmp_path / "f.csv", "FETCH_SIZE", [(lm, 171000.0), (lm, 171002.0),
+                                                (cp, 262144.0, 33554432), (cp, 999.0, 4096)])
+    _pmc_csv(tmp_path / "w.csv", "WRITE_SIZE", [(lm, 600.0), (lm, 600.0),
+                                                (cp, 524288.0, 33554432), (cp, 7.0, 4096)])
     out = tmp_path / "traffic.txt"
     r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--summarize-pmc",
                         str(tmp_path / "f.csv"), str(tmp_path / "w.csv"), str(out),
