@@ -1,31 +1,40 @@
 #!/usr/bin/env python3
-"""Benchmark: achieved HBM GB/s and % of the HBM roofline of the NVFP4 g16
-W4A16 GEMV on one MI355X.
+"""Benchmark: achieved HBM GB/s and % of roofline of the NVFP4 g16 W4A16 GEMV
+on one MI355X, for every workload of the method.
 
-Headline leg (``value``): the LM-head-sized GEMV, M=1, N=151936, K=4096 (the
-llama.cpp trace page's output.weight at one token). A step is one GEMV call.
-Secondary legs, measured the same way and reported in the same JSON line:
-  m8    - the stress GEMV pair at M=8 (12288x4096 and 4096x12288, Student-t
-          weights with 1% zero blocks), one step = both calls;
-  layer - the dense decode layer at M=5 (q, k, v, o, gate, up, down), one
-          step = the seven calls;
-  w4a4  - the pages' W4A4 dense FFN at M=2 (gate, up, down 4096x4096): one
-          step = quantizing x with a static input scale and the three calls;
-  moe   - the 288-expert MoE expert-slot pass at M=8 (and M=1), top-8, and
-          the same pass with the pages' shared expert (768 wide) fused in;
-  copy  - a plain fp32 copy kernel of 2 x 512 MiB per launch: the measured
-          bandwidth that the other legs are also reported against, and the
-          calibration of the HBM byte counters.
+Headline (``value``): the LM-head-sized GEMV, M=1, N=151936, K=4096 (the
+llama.cpp trace page's output.weight at one token); a step is one GEMV call.
+Every other workload is measured the same way and reported in the same JSON
+line under ``configs``:
+  1  gemv_m1_1024x4096   - one small GEMV (launch-bound: its HBM time is 0.3 us);
+  2  decode_layer_m5     - q, k, v, o, gate, up, down at M=5, seven calls, and
+                           fused into four launches (q|k|v and gate|up);
+  3  lm_head_m1          - the headline;
+  4  moe_m1, moe_m8      - the 288-expert MoE expert-slot pass, top-8;
+  5  stress_m8           - 12288x4096 and 4096x12288 at M=8, Student-t weights;
+and the wider rows of the method: the LM head at M=8, the stress pair at
+M=16 and M=128, the W4A4 dense FFN, the MoE with the pages' 768-wide shared
+expert, and the W4A4 MoE.
+
 Throughput counts algorithmic bytes (codes + scales + tensor scale + x + y;
 for the MoE every distinct expert's weights once) per second, inputs already
-resident in HBM. Weight copies are rotated so that each call reads memory
-the previous calls did not (the 256 MB MALL cannot serve repeats).
+resident in HBM. Weight copies are rotated so that each call reads memory the
+previous calls did not (the 256 MB MALL cannot serve repeats).
 
-Timing: W warm-up steps, then exactly K steps between two device
-synchronisations (wall clock -> ms_per_step, value). Two HIP events on the
-launch stream bracket the timed launches; their elapsed time over K is the
-kernel's average launch duration (gaps between back-to-back launches
-included) used for ``roofline.achieved``.
+Timing of each leg:
+  * wall: W warm-up steps, then exactly K timed steps between two device
+    synchronisations -> ms_per_step and ``value``;
+  * launches: a fixed window of LAUNCH_WINDOW launches (independent of K),
+    each bracketed by its own pair of HIP events on the launch stream; the
+    mean of those per-launch durations is the kernel's average launch
+    duration, the basis of ``roofline.achieved`` (the rocprofv3 average of
+    the same command agrees with it to within the box's run-to-run spread);
+  * device_us_back_to_back: the steps queued behind a bounded sleep kernel
+    and run back to back (no host time between launches).
+Each leg also carries its parity against the oracle (all outputs of the timed
+configuration), the oracle's own time on the host cores (``cpu``: all threads,
+and one thread on a bounded sample) and the fraction of the measured read
+ceiling (``nvfp4_stream_read``: a pure read of the same byte count).
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--legs ...]
 """
@@ -38,6 +47,7 @@ import platform
 import subprocess
 import sys
 import time
+from concurrent.futures import ThreadPoolExecutor
 
 import numpy as np
 
@@ -46,8 +56,12 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0      # MI355X published HBM3E bandwidth
+BF16_MFMA_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 matrix-core peak
 METRIC = "achieved HBM GB/s and % of roofline, NVFP4 W4A16 GEMV at M=1 and M=8"
 MIN_ROTATION_BYTES = 1 << 30
+LAUNCH_WINDOW = 400        # steps in the issue-gated event window of every leg
+QUEUED_WINDOW = 200        # steps queued back to back behind a sleep kernel
+ALL_LEGS = "lm_head,small,stress,layer,moe,w4a4,wide,copy"
 
 
 def log(*a):
@@ -86,24 +100,42 @@ def cpu_model():
     return platform.processor() or None
 
 
+def oracle_threads():
+    return int(os.environ.get("OMP_NUM_THREADS") or os.cpu_count() or 1)
+
+
+# ------------------------------------------------------------------ timing
+
 def timed_steps(torch, step, steps, warmup):
     """Run `warmup` untimed steps, then exactly `steps` timed ones between two
-    device synchronisations. Two HIP events on the launch stream (torch's
-    current stream, which every call of the library uses) bracket the timed
-    launches. Returns (wall ms per step, event ms per step)."""
+    device synchronisations. Returns the wall ms per step."""
     for i in range(warmup):
         step(i)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        step(warmup + i)
+    torch.cuda.synchronize()
+    return (time.perf_counter() - t0) * 1e3 / steps
+
+
+def launch_window(torch, step, first, n=LAUNCH_WINDOW):
+    """Average device time per step (us) over a fixed window of n steps
+    issued back to back, bracketed by two HIP events on the launch stream
+    (torch's current stream, which the library launches on). While a step
+    takes longer on the GPU than the host needs to issue it, the window is
+    GPU-bound and the first launch's host latency is spread over n steps;
+    for shorter steps the window measures the host, and the queued
+    measurement below is the device time."""
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
-    t0 = time.perf_counter()
     e0.record()
-    for i in range(steps):
-        step(warmup + i)
+    for i in range(n):
+        step(first + i)
     e1.record()
     torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    return (t1 - t0) * 1e3 / steps, e0.elapsed_time(e1) / steps
+    return e0.elapsed_time(e1) / n * 1e3
 
 
 _SLEEP_CYCLES_PER_MS = None
@@ -114,9 +146,8 @@ def queued_steps(torch, step, steps, first, wall_ms_per_step):
     A bounded sleep kernel (torch.cuda._sleep) holds the stream while the
     host issues the steps; they then run back to back, so host time between
     launches (the Python binding takes several microseconds per call) is not
-    counted. The events sit after the sleep, around the steps. Returns None
-    when the host did not finish issuing before the sleep ended (the number
-    would include host gaps) or when the sleep kernel is unavailable."""
+    counted. Returns None when the host did not finish issuing before the
+    sleep ended or when the sleep kernel is unavailable."""
     global _SLEEP_CYCLES_PER_MS
     if not hasattr(torch.cuda, "_sleep"):
         return None
@@ -145,229 +176,505 @@ def queued_steps(torch, step, steps, first, wall_ms_per_step):
     return e0.elapsed_time(e1) / steps * 1e3
 
 
-def back_to_back(torch, step, steps, warmup, wall_ms, nbytes):
-    """The queued measurement as bench fields (at most 100 steps, so that the
-    launches fit in the stream's hardware queue)."""
-    n = min(steps, 100)
-    us = queued_steps(torch, step, n, warmup, wall_ms)
-    if us is None:
-        return {"device_us_back_to_back": None}
-    return {"device_us_back_to_back": us,
-            "frac_of_peak_back_to_back": nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS}
-
-
-# ------------------------------------------------------------------- legs
-
-def leg_lm_head(torch, nv, workloads, traffic, steps, warmup, want_cpu):
-    import oracle
-    M, N, K = 1, 151936, 4096
-    log(f"[bench] lm head: generating W {N}x{K}")
-    W = workloads.dense_weights(3, 0, 0, N, K)
-    Wd = torch.from_numpy(W).cuda()
-    codes, scales, g = nv.pack(Wd)
-    del Wd
-    x_bits = workloads.x_bf16(3, 0, 0, M, K)
-    x = torch.from_numpy(x_bits.view(np.int16)).cuda().view(torch.bfloat16)
-    wbytes = traffic.weight_bytes(N, K)
-    R = max(2, -(-MIN_ROTATION_BYTES // wbytes))
-    copies = [(codes, scales, g)] + [(codes.clone(), scales.clone(), g.clone())
-                                     for _ in range(R - 1)]
-    y = torch.empty((M, N), dtype=torch.float32, device="cuda")
-
-    def step(i):
-        c, s, gg = copies[i % R]
-        nv.gemv_into(c, s, gg, x, y)
-
-    ms, kms = timed_steps(torch, step, steps, warmup)
-    B = traffic.gemv_bytes(M, N, K)
-    out = {
-        "bytes_per_step": B, "ms_per_step": ms, "kernel_us_events": kms * 1e3,
-        "gbs_wall": B / (ms * 1e-3) / 1e9, "gbs_kernel": B / (kms * 1e-3) / 1e9,
-        "tokens_per_s": M / (ms * 1e-3), "rotate_copies": R,
-    }
-    # parity of the timed configuration: pack bit-exact, sampled rows in tolerance
-    log("[bench] lm head: oracle pack + sampled-row parity")
-    t = time.perf_counter()
-    c0, s0, g0 = oracle.pack(W)
-    pack_s = time.perf_counter() - t
-    del W
-    torch.cuda.synchronize()
-    pack_ok = bool(np.array_equal(codes.cpu().numpy(), c0) and
-                   np.array_equal(scales.cpu().numpy(), s0) and
-                   np.float32(g.cpu().numpy()[0]) == g0)
-    nv.gemv_into(codes, scales, g, x, y)
-    yh = y.cpu().numpy()
-    rows = np.random.default_rng(0).choice(N, 2048, replace=False)
-    yr, ad = oracle.gemv(c0, s0, g0, x_bits, rows=rows)
-    worst = float((np.abs(yh[:, rows] - yr) / (1e-3 * ad + 1e-6)).max())
-    out["parity"] = {"pack_bit_exact": pack_ok, "sampled_rows": int(len(rows)),
-                     "max_err_over_tol": worst, "ok": pack_ok and worst <= 1.0}
-    if want_cpu:
-        out["cpu_baseline"] = cpu_baseline(c0, s0, g0, x_bits, B, M)
-        out["cpu_baseline"]["pack_s"] = pack_s
+def measure(torch, step, steps, warmup, nbytes, tokens, launches, ceiling=None):
+    """The timing fields of one leg: wall clock over K steps; device time per
+    step from QUEUED_WINDOW steps queued behind a sleep kernel and run back to
+    back (``step_us``, the basis of every GB/s and fraction below; the
+    issue-gated window of LAUNCH_WINDOW steps stands in where the queue
+    could not be filled in time). `nbytes` = algorithmic bytes per step,
+    `tokens` = activation rows per step, `launches` = kernel launches per
+    step, `ceiling` = pure-read time (us) of the same bytes."""
+    ms = timed_steps(torch, step, steps, warmup)
+    win = launch_window(torch, step, warmup + steps)
+    b2b = queued_steps(torch, step, QUEUED_WINDOW, warmup + steps + LAUNCH_WINDOW, ms)
+    us = b2b if b2b else win
+    out = {"bytes_per_step": nbytes, "launches_per_step": launches, "ms_per_step": ms,
+           "gbs_wall": nbytes / (ms * 1e-3) / 1e9,
+           "step_us": us, "step_us_basis": (f"{QUEUED_WINDOW} steps queued back to back"
+                                            if b2b else f"{LAUNCH_WINDOW}-step event window"),
+           "window_us": win, "device_us_back_to_back": b2b,
+           "gbs": nbytes / (us * 1e-6) / 1e9,
+           "frac_of_peak": nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS,
+           "tokens_per_s": tokens / (ms * 1e-3),
+           "tokens_per_s_device": tokens / (us * 1e-6)}
+    if ceiling:
+        out["read_ceiling_us"] = ceiling
+        out["frac_of_read_ceiling"] = ceiling / us
     return out
 
 
-def cpu_baseline(c0, s0, g0, x_bits, B, M):
-    """The oracle as it stands (fp64, OpenMP over rows) on the host cores:
-    the full 151936 x 4096 M=1 GEMV, repeated until about 10 s have passed."""
-    import oracle
-    threads = int(os.environ.get("OMP_NUM_THREADS") or os.cpu_count() or 1)
+# ----------------------------------------------------------- read ceiling
+
+class ReadCeiling:
+    """Pure-read time of a byte count: nvfp4_stream_read over R buffers of
+    that size (R * size >= 1 GiB, rotated), measured like the legs (launches
+    queued back to back); the mean device time per launch in us."""
+
+    def __init__(self, torch, nv):
+        self.torch, self.nv, self.cache = torch, nv, {}
+        self.sink = torch.zeros(4, dtype=torch.int32, device="cuda")
+
+    def us(self, nbytes):
+        torch = self.torch
+        n16 = -(-int(nbytes) // 16) * 16
+        if n16 not in self.cache:
+            R = max(2, -(-MIN_ROTATION_BYTES // n16))
+            R = min(R, 512)
+            bufs = [torch.empty(n16, dtype=torch.uint8, device="cuda") for _ in range(R)]
+            for b in bufs:
+                b.fill_(0x5A)
+
+            def step(i):
+                self.nv.stream_read(bufs[i % R], self.sink)
+
+            for i in range(10):
+                step(i)
+            ms = timed_steps(torch, step, 20, 0)
+            us = queued_steps(torch, step, QUEUED_WINDOW, 30, ms)
+            self.cache[n16] = us if us else launch_window(torch, step, 30)
+            del bufs
+        return self.cache[n16]
+
+    def table(self):
+        return {str(b): {"us": us, "gbs": b / (us * 1e-6) / 1e9,
+                         "frac_of_peak": b / (us * 1e-6) / 1e9 / HBM_PEAK_GBS}
+                for b, us in sorted(self.cache.items())}
+
+
+# -------------------------------------------------------------- cpu oracle
+
+def cpu_timed(fn, budget_s=3.0, max_runs=20):
+    """Median wall time (s) of fn() on the host, repeated until `budget_s`
+    has passed (at least twice)."""
     times = []
-    t_end = time.perf_counter() + 10.0
-    while len(times) < 2 or (time.perf_counter() < t_end and len(times) < 50):
+    t_end = time.perf_counter() + budget_s
+    while len(times) < 2 or (time.perf_counter() < t_end and len(times) < max_runs):
         t = time.perf_counter()
-        oracle.gemv(c0, s0, g0, x_bits)
+        fn()
         times.append(time.perf_counter() - t)
-    tm = float(np.median(times))
-    out = {"value": B / tm / 1e9, "unit": "GB/s", "cores": threads, "kind": "oracle",
-           "sample": f"full 151936x4096 M=1 GEMV, {len(times)} runs, median {tm:.3f} s",
-           "tokens_per_s": M / tm, "cpu": cpu_model(), "host_cpus": os.cpu_count()}
-    # the same oracle on one thread (one run of the full matrix)
+    return float(np.median(times)), len(times)
+
+
+def one_thread(fn):
+    """Wall time (s) of one call of fn() with the oracle's OpenMP pool cut to
+    one thread (None where libgomp cannot be reached)."""
     try:
         import ctypes
         gomp = ctypes.CDLL("libgomp.so.1")
-        gomp.omp_set_num_threads(1)
-        t = time.perf_counter()
-        oracle.gemv(c0, s0, g0, x_bits)
-        t1 = time.perf_counter() - t
-        gomp.omp_set_num_threads(threads)
-        out["one_thread"] = {"value": B / t1 / 1e9, "unit": "GB/s", "seconds": t1}
     except OSError:
-        pass
+        return None
+    gomp.omp_set_num_threads(1)
+    try:
+        t = time.perf_counter()
+        fn()
+        return time.perf_counter() - t
+    finally:
+        gomp.omp_set_num_threads(oracle_threads())
+
+
+def cpu_baseline(full, nbytes, tokens, what, sample_1t=None, frac_1t=1.0):
+    """The oracle as it stands (fp64, OpenMP over rows) timed on the host
+    cores: `full()` runs the whole step; `sample_1t()` a bounded part of it
+    (fraction `frac_1t` of the work) on one thread, scaled to the whole."""
+    tm, runs = cpu_timed(full)
+    out = {"value": nbytes / tm / 1e9, "unit": "GB/s", "cores": oracle_threads(),
+           "kind": "oracle", "sample": f"{what}: {runs} runs, median {tm:.4f} s",
+           "seconds_per_step": tm, "tokens_per_s": tokens / tm, "cpu": cpu_model(),
+           "host_cpus": os.cpu_count()}
+    t1 = one_thread(sample_1t or full)
+    if t1 is not None:
+        s = t1 / frac_1t
+        out["one_thread"] = {"value": nbytes / s / 1e9, "unit": "GB/s", "cores": 1,
+                             "seconds_per_step": s,
+                             "sample": (f"{frac_1t:.4g} of the step on one thread "
+                                        f"({t1:.3f} s), scaled") if frac_1t != 1.0
+                             else f"the whole step on one thread ({t1:.3f} s)"}
     return out
 
 
-def leg_m8(torch, nv, workloads, traffic, steps, warmup):
-    M = 8
-    mats = [(0, 12288, 4096), (1, 4096, 12288)]
-    packed, B, wb = [], 0, 0
-    for i, N, K in mats:
-        log(f"[bench] m8: generating W {N}x{K} (Student-t)")
-        W = workloads.dense_weights(5, 0, i, N, K)
-        c, s, g = nv.pack(torch.from_numpy(W).cuda())
-        x = torch.from_numpy(workloads.x_bf16(5, 0, i, M, K).view(np.int16)).cuda().view(
-            torch.bfloat16)
-        y = torch.empty((M, N), dtype=torch.float32, device="cuda")
-        packed.append((c, s, g, x, y))
-        B += traffic.gemv_bytes(M, N, K)
-        wb += traffic.weight_bytes(N, K)
-    R = max(2, -(-MIN_ROTATION_BYTES // wb))
-    copies = [packed] + [[(c.clone(), s.clone(), g.clone(), x, y) for c, s, g, x, y in packed]
-                         for _ in range(R - 1)]
+def tol_ratio(y, y_ref, ad):
+    """Largest |y - y_ref| / (1e-3 * sum|w x| + 1e-6) and the count above 1."""
+    r = np.abs(np.asarray(y, np.float64) - y_ref) / (1e-3 * ad + 1e-6)
+    return (float(r.max()) if r.size else 0.0), int((~(r <= 1.0)).sum())
+
+
+def x_dev(torch, bits):
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).cuda().view(
+        torch.bfloat16)
+
+
+# -------------------------------------------------------------- dense legs
+
+class Dense:
+    """Packed matrices of one dense workload on the device, their oracle
+    packs on the host (for parity), and R rotated device copies."""
+
+    def __init__(self, torch, nv, workloads, traffic, wl, mats, M, rep=0, xs_per_mat=True):
+        self.M, self.mats = M, mats
+        self.dev, self.host, self.x, self.xbits = [], [], [], []
+        wb = 0
+        for si, (name, N, K) in enumerate(mats):
+            log(f"[bench] workload {wl}: {name} {N}x{K}")
+            W = workloads.dense_weights(wl, rep, si, N, K)
+            self.dev.append(nv.pack(torch.from_numpy(W).cuda()))
+            self.host.append(_oracle().pack(W))
+            del W
+            xb = workloads.x_bf16(wl, rep, si if xs_per_mat else 0, M, K)
+            self.xbits.append(xb)
+            self.x.append(x_dev(torch, xb))
+            wb += traffic.weight_bytes(N, K)
+        self.R = max(2, -(-MIN_ROTATION_BYTES // wb))
+        self.copies = [self.dev] + [[tuple(t.clone() for t in p) for p in self.dev]
+                                    for _ in range(self.R - 1)]
+        self.y = [torch.empty((M, N), dtype=torch.float32, device="cuda") for _, N, _ in mats]
+        self.bytes = [traffic.gemv_bytes(M, N, K) for _, N, K in mats]
+
+    def pack_exact(self):
+        import torch
+        torch.cuda.synchronize()
+        return all(np.array_equal(d[0].cpu().numpy(), h[0]) and
+                   np.array_equal(d[1].cpu().numpy(), h[1]) and
+                   np.float32(d[2].cpu().numpy()[0]) == h[2]
+                   for d, h in zip(self.dev, self.host))
+
+    def parity(self, ys=None):
+        """All outputs of every matrix against the oracle."""
+        import torch
+        torch.cuda.synchronize()
+        ys = ys or self.y
+        worst, bad, n = 0.0, 0, 0
+        for (c, s, g), xb, y in zip(self.host, self.xbits, ys):
+            yr, ad = _oracle().gemv(c, s, g, xb)
+            w, b = tol_ratio(y.cpu().numpy(), yr, ad)
+            worst, bad, n = max(worst, w), bad + b, n + yr.size
+        return {"outputs": n, "max_err_over_tol": worst, "outside_tol": bad,
+                "ok": bad == 0}
+
+    def oracle_step(self):
+        for (c, s, g), xb in zip(self.host, self.xbits):
+            _oracle().gemv(c, s, g, xb)
+
+    def oracle_sample(self, frac):
+        """The first `frac` of every matrix's rows."""
+        for (c, s, g), xb in zip(self.host, self.xbits):
+            n = max(1, int(round(c.shape[0] * frac)))
+            _oracle().gemv(c, s, g, xb, rows=np.arange(n))
+
+
+def _oracle():
+    import oracle
+    return oracle
+
+
+def dense_leg(torch, nv, D, steps, warmup, ceil, want_cpu, label, segments=None):
+    """One step = every matrix of D, one nvfp4_gemv call each (or, with
+    `segments`, one nvfp4_gemv_segments call per group of matrix indices,
+    the group sharing the first matrix's x)."""
+    M = D.M
+    if segments is None:
+        def step(i):
+            for (c, s, g), x, y in zip(D.copies[i % D.R], D.x, D.y):
+                nv.gemv_into(c, s, g, x, y)
+        nbytes = sum(D.bytes)
+        launches = len(D.mats)
+        ceiling = sum(ceil.us(b) for b in D.bytes)
+    else:
+        def step(i):
+            cp = D.copies[i % D.R]
+            for grp in segments:
+                nv.gemv_segments_into([cp[j] for j in grp], D.x[grp[0]], [D.y[j] for j in grp])
+        K = D.mats[0][2]
+        nbytes = sum(D.bytes) - sum((len(g) - 1) * M * K * 2 for g in segments)
+        launches = len(segments)
+        ceiling = sum(ceil.us(sum(D.bytes[j] for j in g)) for g in segments)
+    out = {"workload": label, "M": M, "rotate_copies": D.R,
+           **measure(torch, step, steps, warmup, nbytes, M, launches, ceiling)}
+    if segments is None:
+        out["parity"] = D.parity()
+    else:
+        # the fused launches read the group's first x: compare against the
+        # oracle on that x
+        step(0)
+        torch.cuda.synchronize()
+        worst, bad, n = 0.0, 0, 0
+        for grp in segments:
+            for j in grp:
+                c, s, g = D.host[j]
+                yr, ad = _oracle().gemv(c, s, g, D.xbits[grp[0]])
+                w, b = tol_ratio(D.y[j].cpu().numpy(), yr, ad)
+                worst, bad, n = max(worst, w), bad + b, n + yr.size
+        out["parity"] = {"outputs": n, "max_err_over_tol": worst, "outside_tol": bad,
+                         "ok": bad == 0}
+    if want_cpu and segments is None:
+        frac = min(1.0, 2.0e8 / max(1, sum(N * K for _, N, K in D.mats) * M))
+        out["cpu"] = cpu_baseline(D.oracle_step, nbytes, M, f"the whole step ({label})",
+                                  lambda: D.oracle_sample(frac), frac)
+    return out
+
+
+# ------------------------------------------------------------------- moe
+
+class Moe:
+    """The 288-expert MoE workload on the device: every expert packed on the
+    GPU from its seeded fp32 stream (workloads.moe_expert_weights), the pages'
+    768-wide shared expert, and rotating batches of routing and x."""
+
+    E, H, I, TOPK, IS = 288, 4096, 1536, 8, 768
+
+    def __init__(self, torch, nv, workloads):
+        self.torch, self.nv, self.wl = torch, nv, workloads
+        E, H, I = self.E, self.H, self.I
+        log(f"[bench] moe: packing {E} experts from their seeded streams")
+        d = "cuda"
+        self.c13 = torch.empty((E, 2 * I, H // 2), dtype=torch.uint8, device=d)
+        self.s13 = torch.empty((E, 2 * I, H // 16), dtype=torch.uint8, device=d)
+        self.g13 = torch.empty((E,), dtype=torch.float32, device=d)
+        self.c2 = torch.empty((E, H, I // 2), dtype=torch.uint8, device=d)
+        self.s2 = torch.empty((E, H, I // 16), dtype=torch.uint8, device=d)
+        self.g2 = torch.empty((E,), dtype=torch.float32, device=d)
+
+        def gen(e):
+            return e, workloads.moe_expert_weights(4, 0, e, H, I, threads=1)
+
+        with ThreadPoolExecutor(max_workers=min(16, os.cpu_count() or 1)) as ex:
+            for c0 in range(0, E, 16):
+                for e, (w13, w2) in ex.map(gen, range(c0, min(E, c0 + 16))):
+                    nv.pack_into(torch.from_numpy(w13).cuda(), self.c13[e], self.s13[e],
+                                 self.g13[e:e + 1])
+                    nv.pack_into(torch.from_numpy(w2).cuda(), self.c2[e], self.s2[e],
+                                 self.g2[e:e + 1])
+        ws13, ws2 = workloads.moe_shared_weights(4, 0, H, self.IS)
+        self.shared_host_w = (ws13, ws2)
+        self.shared = (*nv.pack(torch.from_numpy(ws13).cuda()),
+                       *nv.pack(torch.from_numpy(ws2).cuda()))
+        self.routed = (self.c13, self.s13, self.g13, self.c2, self.s2, self.g2)
+        torch.cuda.synchronize()
+
+    def batches(self, M, nb=16):
+        out = []
+        for b in range(nb):
+            ids, gw = self.wl.moe_routing(4, b, M, self.E, self.TOPK)
+            xb = self.wl.x_bf16(4, b, 0, M, self.H)
+            out.append((self.torch.from_numpy(ids).cuda(), self.torch.from_numpy(gw).cuda(),
+                        x_dev(self.torch, xb), len(set(ids.ravel().tolist())), ids, gw, xb))
+        return out
+
+    def host_stacks(self, ids):
+        """Oracle packs of the experts `ids` names (the rest zero, g = 1),
+        each regenerated from its seeded stream: the oracle's input, built
+        without the GPU."""
+        E, H, I = self.E, self.H, self.I
+        hc13 = np.zeros((E, 2 * I, H // 2), np.uint8)
+        hs13 = np.zeros((E, 2 * I, H // 16), np.uint8)
+        hg13 = np.ones(E, np.float32)
+        hc2 = np.zeros((E, H, I // 2), np.uint8)
+        hs2 = np.zeros((E, H, I // 16), np.uint8)
+        hg2 = np.ones(E, np.float32)
+        for e in sorted(set(int(v) for v in np.ravel(ids) if 0 <= v < E)):
+            w13, w2 = self.wl.moe_expert_weights(4, 0, e, H, I)
+            hc13[e], hs13[e], hg13[e] = _oracle().pack(w13)
+            hc2[e], hs2[e], hg2[e] = _oracle().pack(w2)
+        return hc13, hs13, hg13, hc2, hs2, hg2
+
+    def host_shared(self):
+        ws13, ws2 = self.shared_host_w
+        return (*_oracle().pack(ws13), *_oracle().pack(ws2))
+
+
+def moe_legs(torch, nv, traffic, mo, M, steps, warmup, ceil, want_cpu):
+    """The routed MoE pass at M tokens, the same with the shared expert, and
+    the W4A4 routed experts with the W4A16 shared expert."""
+    E, H, I, topk, Is = mo.E, mo.H, mo.I, mo.TOPK, mo.IS
+    bt = mo.batches(M)
+    nb = len(bt)
+    y = torch.empty((M, H), dtype=torch.float32, device="cuda")
+
+    def mean_bytes(fn, first, n):
+        return float(np.mean([fn(bt[(first + i) % nb][3]) for i in range(n)]))
+
+    def run(step, fn, label, launches):
+        # bytes of the steps timed by the launch window (each step's own
+        # distinct-expert count)
+        first = warmup + steps + LAUNCH_WINDOW
+        nbytes = mean_bytes(fn, first, QUEUED_WINDOW)
+        out = {"workload": label, "M": M, "rotating_batches": nb,
+               "distinct_experts_mean": mean_bytes(lambda d: d, first, QUEUED_WINDOW),
+               **measure(torch, step, steps, warmup, nbytes, M, launches, ceil.us(nbytes))}
+        return out
+
+    # host stacks for the parity batch (batch 0): routed experts + shared
+    ids0, gw0, xb0 = bt[0][4], bt[0][5], bt[0][6]
+    log(f"[bench] moe M={M}: oracle packs of the {bt[0][3]} experts of batch 0")
+    hw = mo.host_stacks(ids0)
+    hsh = mo.host_shared()
+
+    ws = torch.empty(nv.moe_workspace_bytes(M, H, I, topk), dtype=torch.uint8, device="cuda")
 
     def step(i):
-        for c, s, g, x, y in copies[i % R]:
-            nv.gemv_into(c, s, g, x, y)
+        ids, gw, x = bt[i % nb][:3]
+        nv.moe_gemv_into(*mo.routed, x, ids, gw, y, ws)
 
-    ms, kt = timed_steps(torch, step, steps, warmup)
-    return {"workload": "stress_m8_t3 (12288x4096 + 4096x12288)", "M": M,
-            "bytes_per_step": B, "ms_per_step": ms, "step_us_events": kt * 1e3,
-            "gbs_wall": B / (ms * 1e-3) / 1e9, "gbs_kernel": B / (kt * 1e-3) / 1e9,
-            "frac_of_peak": B / (kt * 1e-3) / 1e9 / HBM_PEAK_GBS,
-            **back_to_back(torch, step, steps, warmup, ms, B),
-            "tokens_per_s": M / (ms * 1e-3), "rotate_copies": R}
+    routed = run(step, lambda d: traffic.moe_bytes(M, H, I, topk, d),
+                 f"moe_288x(3072x4096,4096x1536)_top8_m{M}", 2)
+    step(0)
+    yr, bound = _oracle().moe(*hw, xb0, ids0, gw0)
+    w, b = tol_ratio(y.cpu().numpy(), yr, bound)
+    routed["parity"] = {"batch": 0, "outputs": int(yr.size), "max_err_over_tol": w,
+                        "outside_tol": b, "ok": b == 0}
+    if want_cpu:
+        D0 = bt[0][3]
+        # the oracle loops over (token, slot): one token is 1/M of its work
+        routed["cpu"] = cpu_baseline(lambda: _oracle().moe(*hw, xb0, ids0, gw0),
+                                     traffic.moe_bytes(M, H, I, topk, D0), M,
+                                     f"the whole pass of batch 0 ({D0} experts)",
+                                     lambda: _oracle().moe(*hw, xb0[:1], ids0[:1], gw0[:1]),
+                                     1.0 / M)
+
+    wss = torch.empty(nv.moe_shared_workspace_bytes(M, H, I, topk, Is), dtype=torch.uint8,
+                      device="cuda")
+
+    def step_shared(i):
+        ids, gw, x = bt[i % nb][:3]
+        nv.moe_shared_gemv_into(*mo.routed, x, ids, gw, mo.shared, y, wss)
+
+    with_shared = run(step_shared, lambda d: traffic.moe_shared_bytes(M, H, I, topk, d, Is),
+                      f"moe_288x(3072x4096,4096x1536)_top8_shared768_m{M}", 2)
+    step_shared(0)
+    yr, bound = _oracle().moe_shared(*hw, xb0, ids0, gw0, hsh)
+    w, b = tol_ratio(y.cpu().numpy(), yr, bound)
+    with_shared["parity"] = {"batch": 0, "outputs": int(yr.size), "max_err_over_tol": w,
+                             "outside_tol": b, "ok": b == 0}
+
+    # W4A4 routed experts: static input scales for x and h, calibrated on
+    # another batch of the same distributions (batch nb, never timed)
+    xc = mo.wl.x_bf16(4, nb, 0, M, H)
+    gx_v = np.float32(np.abs((xc.astype(np.uint32) << 16).view(np.float32)).max() / 2688.0)
+    idc, gwc = mo.wl.moe_routing(4, nb, M, E, topk)
+    hwc = mo.host_stacks(idc)
+    _, _, hcal = _oracle().moe(*hwc, xc, idc, gwc, want_h=True)
+    hcal_f = (hcal.astype(np.uint32) << 16).view(np.float32)
+    gh_v = np.float32(np.abs(hcal_f).max() / 2688.0)
+    del hwc
+    gx = torch.tensor([gx_v], dtype=torch.float32, device="cuda")
+    gh = torch.tensor([gh_v], dtype=torch.float32, device="cuda")
+    wsq = torch.empty(nv.moe_w4a4_workspace_bytes(M, H, I, topk, Is), dtype=torch.uint8,
+                      device="cuda")
+
+    def step_w4a4(i):
+        ids, gw, x = bt[i % nb][:3]
+        nv.moe_w4a4_gemv_into(*mo.routed, x, gx, gh, ids, gw, y, wsq, shared=mo.shared)
+
+    w4a4 = run(step_w4a4, lambda d: traffic.moe_w4a4_bytes(M, H, I, topk, d, Is),
+               f"moe_w4a4_288x(3072x4096,4096x1536)_top8_shared768_m{M}", 3 if M == 1 else 4)
+    step_w4a4(0)
+    yq = y.cpu().numpy()
+    yr, bound, _, hc, hs = _oracle().moe_w4a4(*hw, xb0, ids0, gw0, gx_v, gh_v, shared=hsh)
+    # tokens whose h landed on the same NVFP4 grid values as the oracle's must
+    # be within tolerance; a token whose gate|up sum (fp32 here, fp64 in the
+    # oracle) rounded one bf16 ulp across a grid decision may differ more
+    lay = nv.moe_w4a4_workspace_layout(M, H, I, topk, Is)
+    hq = wsq[lay["hq"]:lay["hq"] + M * topk * I * 2].view(torch.int16).cpu().numpy()
+    hq = hq.view(np.uint16).reshape(M, topk, I)
+    hq_ref = _oracle_hq_bits(hc, hs).reshape(M, topk, I)
+    valid = (ids0 >= 0) & (ids0 < E)
+    same_tok = np.array([np.array_equal(hq[m][valid[m]], hq_ref[m][valid[m]])
+                         for m in range(M)])
+    r = np.abs(yq.astype(np.float64) - yr) / (1e-3 * bound + 1e-6)
+    w = float(r[same_tok].max()) if same_tok.any() else 0.0
+    b = int((~(r[same_tok] <= 1.0)).sum())
+    w4a4["parity"] = {"batch": 0, "outputs": int(yr.size), "tokens_with_equal_h_grid":
+                      int(same_tok.sum()), "max_err_over_tol_equal_h_grid": w,
+                      "outside_tol_equal_h_grid": b,
+                      "max_err_over_tol_all": float(r.max()), "ok": b == 0}
+    return routed, with_shared, w4a4
 
 
-def leg_layer(torch, nv, workloads, traffic, steps, warmup):
-    """The dense decode layer at M=5: q, k, v, o, gate, up, down, each matrix
-    from its own weight stream. Timed twice: seven separate calls (each with its
-    own x), and fused into four launches (q|k|v and gate|up as one
-    multi-projection call each, sharing the group's x)."""
-    M = 5
-    names = [n for n, _, _ in workloads.DECODE_LAYER]
-    packed, B, wb = {}, 0, 0
-    for si, (name, N, K) in enumerate(workloads.DECODE_LAYER):
-        log(f"[bench] layer: generating {name} {N}x{K}")
-        W = workloads.dense_weights(2, 0, si, N, K)
-        c, s, g = nv.pack(torch.from_numpy(W).cuda())
-        del W
-        x = torch.from_numpy(workloads.x_bf16(2, 0, si, M, K).view(np.int16)).cuda().view(
-            torch.bfloat16)
-        y = torch.empty((M, N), dtype=torch.float32, device="cuda")
-        packed[name] = (c, s, g, x, y)
-        B += traffic.gemv_bytes(M, N, K)
-        wb += traffic.weight_bytes(N, K)
-    R = max(2, -(-MIN_ROTATION_BYTES // wb))
-    copies = [packed] + [{k: (c.clone(), s.clone(), g.clone(), x, y)
-                          for k, (c, s, g, x, y) in packed.items()} for _ in range(R - 1)]
-    groups = [("q", "k", "v"), ("o",), ("gate", "up"), ("down",)]
-    # fused: x read once per launch
-    Bf = B - sum((len(gr) - 1) * M * 4096 * 2 for gr in groups)
-
-    def step(i):
-        cp = copies[i % R]
-        for n in names:
-            c, s, g, x, y = cp[n]
-            nv.gemv_into(c, s, g, x, y)
-
-    def step_fused(i):
-        cp = copies[i % R]
-        for gr in groups:
-            mats = [cp[n][:3] for n in gr]
-            nv.gemv_segments_into(mats, cp[gr[0]][3], [cp[n][4] for n in gr])
-
-    ms, kt = timed_steps(torch, step, steps, warmup)
-    msf, ktf = timed_steps(torch, step_fused, steps, warmup)
-    return {"workload": "decode_layer_m5 (q,k,v,o 4096/1024 x 4096; gate, up 12288x4096; "
-                        "down 4096x12288)", "M": M, "launches_per_step": len(names),
-            "bytes_per_step": B, "ms_per_step": ms, "step_us_events": kt * 1e3,
-            "gbs_wall": B / (ms * 1e-3) / 1e9, "gbs_kernel": B / (kt * 1e-3) / 1e9,
-            "frac_of_peak": B / (kt * 1e-3) / 1e9 / HBM_PEAK_GBS,
-            **back_to_back(torch, step, steps, warmup, ms, B),
-            "tokens_per_s": M / (ms * 1e-3), "rotate_copies": R,
-            "fused": {"launches_per_step": len(groups), "bytes_per_step": Bf,
-                      "ms_per_step": msf, "step_us_events": ktf * 1e3,
-                      "gbs_kernel": Bf / (ktf * 1e-3) / 1e9,
-                      "frac_of_peak": Bf / (ktf * 1e-3) / 1e9 / HBM_PEAK_GBS,
-                      **back_to_back(torch, step_fused, steps, warmup, msf, Bf),
-                      "tokens_per_s": M / (msf * 1e-3)}}
+def _oracle_hq_bits(hc, hs):
+    """bf16 bits of e2m1 * s for quantized rows (codes [R, I/2], scales
+    [R, I/16]) from the oracle's element tables: the values the kernel's
+    quantizer writes to the workspace."""
+    o = _oracle()
+    e2 = np.array([o.e2m1_value(c) for c in range(16)], np.float64)
+    e4 = np.array([o.e4m3_value(b) for b in range(256)], np.float64)
+    lo, hi = hc & 0xF, hc >> 4
+    codes = np.stack([lo, hi], axis=-1).reshape(hc.shape[0], -1)
+    vals = e2[codes] * np.repeat(e4[hs], 16, axis=1)
+    return np.array([o.bf16_from_double(v) for v in vals.ravel()],
+                    np.uint16).reshape(vals.shape)
 
 
-def leg_w4a4(torch, nv, workloads, traffic, steps, warmup):
+# ------------------------------------------------------------------- w4a4
+
+def leg_w4a4(torch, nv, workloads, traffic, steps, warmup, ceil, want_cpu):
     """The pages' W4A4 dense FFN (gate, up, down 4096x4096 at M=2): one step =
     quantizing the activations with a static input scale and the three W4A4
     GEMVs on them, gate|up as one multi-projection call."""
     wl = workloads.WORKLOADS[6]
     M = wl["M"]
-    mats = []
+    mats, host = [], []
     for i, (name, N, K) in enumerate(wl["mats"]):
         log(f"[bench] w4a4: packing {name} {N}x{K}")
-        W = torch.from_numpy(workloads.dense_weights(6, 0, i, N, K)).cuda()
-        mats.append((nv.pack(W), N, K))
+        W = workloads.dense_weights(6, 0, i, N, K)
+        mats.append((nv.pack(torch.from_numpy(W).cuda()), N, K))
+        host.append(_oracle().pack(W))
         del W
     K = wl["mats"][0][2]
     wb = sum(traffic.weight_bytes(N, K) for _, N, K in mats)
     reps = max(2, (1 << 30) // wb + 1)
     copies = [mats] + [[(tuple(t.clone() for t in p), N, K) for p, N, K in mats]
                        for _ in range(reps - 1)]
-    x = torch.from_numpy(workloads.x_bf16(6, 0, 0, M, K).view(np.int16)).cuda().view(
-        torch.bfloat16)
+    xb = workloads.x_bf16(6, 0, 0, M, K)
+    x = x_dev(torch, xb)
     calib = workloads.x_bf16(6, 1, 0, M, K)
-    gx = torch.tensor([np.abs(((calib.astype(np.uint32) << 16).view(np.float32))).max()
-                       / 2688.0], dtype=torch.float32, device="cuda")
+    gx_v = np.float32(np.abs(((calib.astype(np.uint32) << 16).view(np.float32))).max() / 2688.0)
+    gx = torch.tensor([gx_v], dtype=torch.float32, device="cuda")
     cx, sx = nv.quantize_act(x, gx)
     ws = torch.empty(nv.gemv_w4a4_workspace_bytes(M, K), dtype=torch.uint8, device="cuda")
     ys = [torch.empty((M, N), dtype=torch.float32, device="cuda") for _, N, _ in mats]
 
     def step(i):
-        # gate|up share the activations: one multi-projection call; then down
         nv.quantize_act_into(x, gx, cx, sx)
         cp = copies[i % reps]
         nv.gemv_w4a4_segments_into([cp[0][0], cp[1][0]], cx, sx, gx, ys[:2], ws)
         nv.gemv_w4a4_into(*cp[2][0], cx, sx, gx, ys[2], ws)
 
-    ms, kms = timed_steps(torch, step, steps, warmup)
-    B = traffic.quantize_act_bytes(M, K) + sum(traffic.gemv_w4a4_bytes(M, N, K)
-                                               for _, N, K in mats)
-    return {"workload": "w4a4_ffn_m2 (gate, up, down 4096x4096; static input scale)", "M": M,
-            "launches_per_step": 1 + (1 if M <= 2 else 2) * 2, "bytes_per_step": B,
-            "ms_per_step": ms,
-            "step_us_events": kms * 1e3, "gbs_wall": B / (ms * 1e-3) / 1e9,
-            "gbs_kernel": B / (kms * 1e-3) / 1e9,
-            "frac_of_peak": B / (kms * 1e-3) / 1e9 / HBM_PEAK_GBS,
-            **back_to_back(torch, step, steps, warmup, ms, B),
-            "tokens_per_s": M / (ms * 1e-3), "rotate_copies": reps}
+    nbytes = traffic.quantize_act_bytes(M, K) + sum(traffic.gemv_w4a4_bytes(M, N, K)
+                                                    for _, N, K in mats)
+    out = {"workload": "w4a4_ffn_m2 (gate, up, down 4096x4096; static input scale)", "M": M,
+           "rotate_copies": reps,
+           **measure(torch, step, steps, warmup, nbytes, M, 1 + (1 if M <= 2 else 2) * 2,
+                     ceil.us(nbytes))}
+    step(0)
+    torch.cuda.synchronize()
+    hcx, hsx = _oracle().quantize_act(xb, gx_v)
+    q_ok = bool(np.array_equal(cx.cpu().numpy(), hcx) and np.array_equal(sx.cpu().numpy(), hsx))
+    worst, bad, n = 0.0, 0, 0
+    for (c, s, g), yy in zip(host, ys):
+        yr, ad = _oracle().gemv_w4a4(c, s, g, hcx, hsx, gx_v)
+        w, b = tol_ratio(yy.cpu().numpy(), yr, ad)
+        worst, bad, n = max(worst, w), bad + b, n + yr.size
+    out["parity"] = {"quantize_bit_exact": q_ok, "outputs": n, "max_err_over_tol": worst,
+                     "outside_tol": bad, "ok": q_ok and bad == 0}
+    return out
+
+
+# ------------------------------------------------------------------- copy
+
+def leg_copy(torch, steps, warmup):
+    """Calibration for the HBM byte counters: a plain fp32 copy kernel
+    (dst = src * 1) of known size, 512 MiB read and 512 MiB written per
+    launch, two buffer pairs alternating so the MALL cannot serve repeats."""
+    n = (512 << 20) // 4
+    bufs = [(torch.ones(n, device="cuda"), torch.empty(n, device="cuda")) for _ in range(2)]
+
+    def step(i):
+        src, dst = bufs[i % 2]
+        torch.mul(src, 1.0, out=dst)
+
+    timed_steps(torch, step, steps, warmup)
+    us = launch_window(torch, step, warmup + steps, 50)
+    return {"bytes_read": n * 4, "bytes_written": n * 4, "us": us,
+            "gbs": 2 * n * 4 / (us * 1e-6) / 1e9}
 
 
 def gpu_clock_state():
@@ -382,114 +689,6 @@ def gpu_clock_state():
         except OSError:
             pass
     return out or None
-
-
-def leg_moe(torch, nv, workloads, traffic, steps, warmup, M):
-    E, H, I, topk = 288, 4096, 1536, 8
-    log(f"[bench] moe M={M}: generating {E} experts on the device")
-    gen = torch.Generator(device="cuda")
-    gen.manual_seed(4_000 + M)
-    c13 = torch.empty((E, 2 * I, H // 2), dtype=torch.uint8, device="cuda")
-    s13 = torch.empty((E, 2 * I, H // 16), dtype=torch.uint8, device="cuda")
-    g13 = torch.empty((E,), dtype=torch.float32, device="cuda")
-    c2 = torch.empty((E, H, I // 2), dtype=torch.uint8, device="cuda")
-    s2 = torch.empty((E, H, I // 16), dtype=torch.uint8, device="cuda")
-    g2 = torch.empty((E,), dtype=torch.float32, device="cuda")
-    for e in range(E):
-        w = torch.randn((2 * I, H), generator=gen, device="cuda") * 0.02
-        nv.pack_into(w, c13[e], s13[e], g13[e:e + 1])
-        w = torch.randn((H, I), generator=gen, device="cuda") * 0.02
-        nv.pack_into(w, c2[e], s2[e], g2[e:e + 1])
-    del w
-    nb = 16
-    batches = []
-    for b in range(nb):
-        ids, gw = workloads.moe_routing(4, b, M, E, topk)
-        x = torch.from_numpy(workloads.x_bf16(4, b, 0, M, H).view(np.int16)).cuda().view(
-            torch.bfloat16)
-        batches.append((torch.from_numpy(ids).cuda(), torch.from_numpy(gw).cuda(), x,
-                        len(set(ids.ravel().tolist()))))
-    y = torch.empty((M, H), dtype=torch.float32, device="cuda")
-    D = float(np.mean([batches[(warmup + i) % nb][3] for i in range(steps)]))
-
-    def run(step, nbytes, workload):
-        ms, kms = timed_steps(torch, step, steps, warmup)
-        # bytes of the steps actually timed (each step's own distinct-expert count)
-        B = float(np.mean([nbytes(batches[(warmup + i) % nb][3]) for i in range(steps)]))
-        return {"workload": workload, "M": M,
-                "distinct_experts_mean": D, "bytes_per_step": B, "ms_per_step": ms,
-                "pass_us": kms * 1e3, "gbs_wall": B / (ms * 1e-3) / 1e9,
-                "gbs_pass": B / (kms * 1e-3) / 1e9,
-                "frac_of_peak": B / (kms * 1e-3) / 1e9 / HBM_PEAK_GBS,
-                **back_to_back(torch, step, steps, warmup, ms, float(np.mean(
-                    [nbytes(batches[(warmup + i) % nb][3]) for i in range(min(steps, 100))]))),
-                "tokens_per_s": M / (ms * 1e-3), "rotating_batches": nb}
-
-    ws = torch.empty(nv.moe_workspace_bytes(M, H, I, topk), dtype=torch.uint8, device="cuda")
-
-    def step(i):
-        ids, gw, x, _ = batches[i % nb]
-        nv.moe_gemv_into(c13, s13, g13, c2, s2, g2, x, ids, gw, y, ws)
-
-    routed = run(step, lambda d: traffic.moe_bytes(M, H, I, topk, d),
-                 f"moe_288x(3072x4096,4096x1536)_top8_m{M}")
-
-    # the same call with the shared expert of the pages (gate|up 768+768 x
-    # 4096, down 4096 x 768) in the same two launches
-    Is = 768
-    w = torch.randn((2 * Is, H), generator=gen, device="cuda") * 0.02
-    sh13 = nv.pack(w)
-    w = torch.randn((H, Is), generator=gen, device="cuda") * 0.02
-    sh2 = nv.pack(w)
-    del w
-    shared = (*sh13, *sh2)
-    wss = torch.empty(nv.moe_shared_workspace_bytes(M, H, I, topk, Is), dtype=torch.uint8,
-                      device="cuda")
-
-    def step_shared(i):
-        ids, gw, x, _ = batches[i % nb]
-        nv.moe_shared_gemv_into(c13, s13, g13, c2, s2, g2, x, ids, gw, shared, y, wss)
-
-    with_shared = run(step_shared, lambda d: traffic.moe_shared_bytes(M, H, I, topk, d, Is),
-                      f"moe_288x(3072x4096,4096x1536)_top8_shared768_m{M}")
-
-    # W4A4 routed experts (static input scales for x and h, calibrated on
-    # another batch of the same distributions) with the W4A16 shared expert
-    xc = torch.from_numpy(workloads.x_bf16(4, nb, 0, M, H).view(np.int16)).cuda().view(
-        torch.bfloat16)
-    gx = (xc.float().abs().max() / 2688.0).reshape(1)
-    idc, gwc = (torch.from_numpy(a).cuda() for a in workloads.moe_routing(4, nb, M, E, topk))
-    nv.moe_shared_gemv_into(c13, s13, g13, c2, s2, g2, xc, idc, gwc, shared, y, wss)
-    hc = wss[:M * topk * I * 2].view(torch.bfloat16).float()
-    gh = (hc.abs().max() / 2688.0).reshape(1)
-    wsq = torch.empty(nv.moe_w4a4_workspace_bytes(M, H, I, topk, Is), dtype=torch.uint8,
-                      device="cuda")
-
-    def step_w4a4(i):
-        ids, gw, x, _ = batches[i % nb]
-        nv.moe_w4a4_gemv_into(c13, s13, g13, c2, s2, g2, x, gx, gh, ids, gw, y, wsq,
-                              shared=shared)
-
-    w4a4 = run(step_w4a4, lambda d: traffic.moe_w4a4_bytes(M, H, I, topk, d, Is),
-               f"moe_w4a4_288x(3072x4096,4096x1536)_top8_shared768_m{M}")
-    w4a4["launches_per_step"] = 3 if M == 1 else 4
-    return routed, with_shared, w4a4
-
-
-def leg_copy(torch, steps, warmup):
-    """Calibration for the HBM byte counters: a plain fp32 copy kernel
-    (dst = src * 1) of known size, 512 MiB read and 512 MiB written per
-    launch, two buffer pairs alternating so the MALL cannot serve repeats."""
-    n = (512 << 20) // 4
-    bufs = [(torch.ones(n, device="cuda"), torch.empty(n, device="cuda")) for _ in range(2)]
-
-    def step(i):
-        src, dst = bufs[i % 2]
-        torch.mul(src, 1.0, out=dst)
-
-    ms, kms = timed_steps(torch, step, steps, warmup)
-    return {"bytes_read": n * 4, "bytes_written": n * 4, "us_events": kms * 1e3,
-            "gbs": 2 * n * 4 / (kms * 1e-3) / 1e9}
 
 
 # ------------------------------------------------------- profile summaries
@@ -731,12 +930,14 @@ def summarize_counters(csvs, cmd, out, match="nvfp4::"):
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--legs", default="lm_head,m8,layer,w4a4,moe,copy",
-                    help="comma list of lm_head, m8, layer, w4a4, moe, copy (lm_head is the "
-                         "headline; copy is a plain copy kernel: the byte-counter "
-                         "calibration and the measured-bandwidth reference)")
+    ap.add_argument("--legs", default=ALL_LEGS,
+                    help="comma list of lm_head (the headline, config 3), small (config 1), "
+                         "stress (config 5), layer (config 2), moe (config 4 with the shared "
+                         "expert and W4A4 variants), w4a4 (the W4A4 dense FFN), wide (the LM "
+                         "head at M=8 and the stress pair at M=16 and M=128), copy (a plain "
+                         "copy kernel: the byte-counter calibration)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--summarize-pmc", nargs=3, metavar=("FETCH_CSV", "WRITE_CSV", "OUT"),
                     help="write the traffic summary from two rocprofv3 --pmc passes")
@@ -776,60 +977,113 @@ def main():
         sys.exit(1)
     nv.lib()   # fail loudly if the HIP library is not built
     legs = [s.strip() for s in args.legs.split(",") if s.strip()]
+    unknown = set(legs) - set(ALL_LEGS.split(","))
+    if unknown:
+        ap.error(f"unknown legs {sorted(unknown)}")
+    want_cpu = not args.no_cpu_baseline
+    K_, W_ = args.steps, args.warmup
     props = torch.cuda.get_device_properties(0)
+    ceil = ReadCeiling(torch, nv)
     result = {
-        "metric": METRIC, "value": None, "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
-        "warmup": args.warmup, "ms_per_step": None, "higher_is_better": True,
+        "metric": METRIC, "value": None, "unit": "GB/s", "n_gpus": 1, "steps": K_,
+        "warmup": W_, "ms_per_step": None, "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
         "config": {"workload": "lm_head_m1_151936x4096", "M": 1, "N": 151936, "K": 4096,
                    "weights": "nvfp4 g16 from N(0,0.02) fp32, packed on the GPU",
                    "x": "bf16 N(0,1)", "y": "fp32"},
     }
+    configs = {}
     if "lm_head" in legs:
-        lm = leg_lm_head(torch, nv, workloads, traffic, args.steps, args.warmup,
-                         not args.no_cpu_baseline)
+        D = Dense(torch, nv, workloads, traffic, 3, workloads.WORKLOADS[3]["mats"], 1)
+        lm = dense_leg(torch, nv, D, K_, W_, ceil, want_cpu, "lm_head_m1_151936x4096")
+        lm["parity"]["pack_bit_exact"] = D.pack_exact()
+        lm["parity"]["ok"] = lm["parity"]["ok"] and lm["parity"]["pack_bit_exact"]
+        configs["3_lm_head_m1"] = lm
         result["value"] = lm["gbs_wall"]
         result["ms_per_step"] = lm["ms_per_step"]
         result["tokens_per_s"] = lm["tokens_per_s"]
         result["frac_of_peak_wall"] = lm["gbs_wall"] / HBM_PEAK_GBS
-        result["roofline"] = {"bound": "hbm", "achieved": lm["gbs_kernel"],
-                              "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                              "frac": lm["gbs_kernel"] / HBM_PEAK_GBS,
-                              "traffic": read_traffic(),
-                              "kernel": LM_KERNEL,
-                              "kernel_avg_us": lm["kernel_us_events"],
-                              "bytes_per_launch": lm["bytes_per_step"]}
+        result["roofline"] = {
+            "bound": "hbm", "achieved": lm["gbs"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": lm["frac_of_peak"], "traffic": read_traffic(), "kernel": LM_KERNEL,
+            "kernel_avg_us": lm["step_us"],
+            "basis": f"HIP events on the launch stream around {QUEUED_WINDOW} launches queued "
+                     "back to back (a fixed window, independent of --steps)",
+            "kernel_avg_us_event_window": lm["window_us"],
+            "event_window_launches": LAUNCH_WINDOW,
+            "bytes_per_launch": lm["bytes_per_step"],
+            "frac_of_read_ceiling": lm["frac_of_read_ceiling"]}
         result["config"]["rotate_copies"] = lm["rotate_copies"]
         result["parity"] = lm["parity"]
-        if "cpu_baseline" in lm:
-            result["cpu_baseline"] = lm["cpu_baseline"]
-    if "m8" in legs:
-        result["m8"] = leg_m8(torch, nv, workloads, traffic, args.steps, args.warmup)
+        if "cpu" in lm:
+            result["cpu_baseline"] = lm["cpu"]
+        del D
+    if "small" in legs:
+        D = Dense(torch, nv, workloads, traffic, 1, workloads.WORKLOADS[1]["mats"], 1)
+        configs["1_gemv_m1_1024x4096"] = dense_leg(torch, nv, D, K_, W_, ceil, want_cpu,
+                                                   "gemv_m1_1024x4096 (launch-bound)")
+        del D
+    if "stress" in legs:
+        D = Dense(torch, nv, workloads, traffic, 5, workloads.WORKLOADS[5]["mats"], 8)
+        configs["5_stress_m8"] = dense_leg(torch, nv, D, K_, W_, ceil, want_cpu,
+                                           "stress_m8_t3 (12288x4096 + 4096x12288)")
+        del D
     if "layer" in legs:
-        result["layer_m5"] = leg_layer(torch, nv, workloads, traffic, args.steps, args.warmup)
-    if "w4a4" in legs:
-        result["w4a4_ffn_m2"] = leg_w4a4(torch, nv, workloads, traffic, args.steps, args.warmup)
-    if "copy" in legs:
-        cp = leg_copy(torch, min(args.steps, 50), min(args.warmup, 5))
-        result["copy_calibration"] = cp
-        # fractions of the measured copy bandwidth (read + write bytes per second)
-        if result.get("roofline"):
-            result["roofline"]["frac_of_measured_copy"] = result["roofline"]["achieved"] / cp["gbs"]
-        for k in ("m8", "layer_m5", "w4a4_ffn_m2"):
-            if k in result:
-                result[k]["frac_of_measured_copy"] = result[k]["gbs_kernel"] / cp["gbs"]
+        D = Dense(torch, nv, workloads, traffic, 2, workloads.DECODE_LAYER, 5)
+        lay = dense_leg(torch, nv, D, K_, W_, ceil, want_cpu,
+                        "decode_layer_m5 (q,k,v,o 4096/1024 x 4096; gate, up 12288x4096; "
+                        "down 4096x12288), seven calls")
+        lay["fused"] = dense_leg(torch, nv, D, K_, W_, ceil, False,
+                                 "decode_layer_m5, q|k|v and gate|up fused: four launches",
+                                 segments=[(0, 1, 2), (3,), (4, 5), (6,)])
+        configs["2_decode_layer_m5"] = lay
+        del D
     if "moe" in legs:
-        result["moe"], result["moe_shared"], result["moe_w4a4"] = {}, {}, {}
+        mo = Moe(torch, nv, workloads)
+        result["moe_shared"], result["moe_w4a4"] = {}, {}
         for M in (1, 8):
-            routed, with_shared, w4a4 = leg_moe(torch, nv, workloads, traffic, args.steps,
-                                                args.warmup, M)
-            result["moe"][f"m{M}"] = routed
+            routed, with_shared, w4a4 = moe_legs(torch, nv, traffic, mo, M, K_, W_, ceil,
+                                                 want_cpu)
+            configs[f"4_moe_m{M}"] = routed
             result["moe_shared"][f"m{M}"] = with_shared
             result["moe_w4a4"][f"m{M}"] = w4a4
+        del mo
+    if "w4a4" in legs:
+        result["w4a4_ffn_m2"] = leg_w4a4(torch, nv, workloads, traffic, K_, W_, ceil, want_cpu)
+    if "wide" in legs:
+        wide = {}
+        if nv.MAX_M >= 8:
+            D = Dense(torch, nv, workloads, traffic, 3, workloads.WORKLOADS[3]["mats"], 8,
+                      xs_per_mat=False)
+            wide["lm_head_m8"] = dense_leg(torch, nv, D, K_, W_, ceil, False,
+                                           "lm_head_m8_151936x4096")
+            del D
+        for M in (16, 128):
+            if nv.MAX_M >= M:
+                D = Dense(torch, nv, workloads, traffic, 5, workloads.WORKLOADS[5]["mats"], M)
+                leg = dense_leg(torch, nv, D, K_, W_, ceil, False,
+                                f"stress_m{M}_t3 (12288x4096 + 4096x12288)")
+                flops = sum(2 * M * N * K for _, N, K in D.mats)
+                leg["tflops"] = flops / (leg["step_us"] * 1e-6) / 1e12
+                leg["frac_of_bf16_mfma_peak"] = leg["tflops"] / BF16_MFMA_PEAK_TFLOPS
+                wide[f"stress_m{M}"] = leg
+                del D
+        result["wide"] = wide
+    if "copy" in legs:
+        result["copy_calibration"] = leg_copy(torch, min(K_, 50), min(W_, 5))
+    result["configs"] = configs
+    result["read_ceiling"] = ceil.table()
+    result["parity_ok_all"] = all(
+        v["parity"]["ok"] for v in list(configs.values()) +
+        [result.get("w4a4_ffn_m2") or {"parity": {"ok": True}}] +
+        list((result.get("moe_shared") or {}).values()) +
+        list((result.get("moe_w4a4") or {}).values()) +
+        list((result.get("wide") or {}).values()) if "parity" in v)
     result["env"] = {"gpu": props.name, "cus": props.multi_processor_count,
                      "dpm_clocks": gpu_clock_state(),
                      "hip": torch.version.hip, "torch": torch.__version__, "git": git_sha(),
                      "library_sources_sha256_16": library_source_hash(),
+                     "oracle_threads": oracle_threads(), "cpu": cpu_model(),
                      "argv": sys.argv[1:]}
     print(json.dumps(result), flush=True)
 

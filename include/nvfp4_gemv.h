@@ -55,7 +55,7 @@
 extern "C" {
 #endif
 
-#define NVFP4_ABI_VERSION 6
+#define NVFP4_ABI_VERSION 7
 
 /* Largest number of activation rows (tokens) one GEMV / MoE call takes. */
 #define NVFP4_MAX_M 8
@@ -426,6 +426,25 @@ nvfp4_status nvfp4_moe_w4a4_gemv(const uint8_t* w13_codes, const uint8_t* w13_sc
                                  int64_t E, int64_t H, int64_t I, int64_t topk,
                                  const nvfp4_moe_shared* shared, float* y, void* workspace,
                                  size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * nvfp4_stream_read -- measurement aid, not part of the product path: reads
+ * `bytes` of device memory once with the 128-bit non-temporal loads and the
+ * launch shape of the M = 1 GEMV (one wavefront per 4 KiB) and discards the
+ * data. Its throughput is the read bandwidth this device reaches on a pure
+ * stream, the ceiling the weight-streaming kernels are reported against, as
+ * the blueprint's card.json prices each kernel floor at a measured read
+ * bandwidth (performance[*].floor_us at 249 GB/s) next to the nominal one
+ * (hardware.memory_bandwidth_gbps, 273).
+ *
+ *   buf    device memory, 16-byte aligned;  bytes  a multiple of 16;
+ *   sink   uint32[1] device memory, 4-byte aligned: written only when the
+ *          XOR of all words read equals 0x9E3779B9 (it keeps the loads
+ *          alive; the value is of no use), must not overlap buf.
+ * Errors: NULL, SHAPE, ALIGN, ALIAS, HIP.
+ */
+nvfp4_status nvfp4_stream_read(const void* buf, size_t bytes, uint32_t* sink,
+                               hipStream_t stream);
 
 #ifdef __cplusplus
 }

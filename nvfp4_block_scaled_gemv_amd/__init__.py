@@ -17,6 +17,7 @@ Functions (same names as the C entry points, without the prefix):
   moe_gemv(w13..., w2..., x, ids, gate_w[, workspace]) -> y (fp32 [M, H])
   moe_shared_workspace_bytes(M, H, I, topk, I_shared) -> int
   moe_shared_gemv(w13..., w2..., x, ids, gate_w, shared[, workspace]) -> y
+  stream_read(buf, sink)                 (measurement aid: one pure read of buf)
 The ``*_into`` variants write into caller-provided outputs.
 """
 from __future__ import annotations
@@ -117,6 +118,8 @@ def lib() -> ctypes.CDLL:
         L.nvfp4_moe_w4a4_gemv.argtypes = ([_VP] * 11 + [_I64] * 5 +
                                           [ctypes.POINTER(MoeShared), _VP, _VP,
                                            ctypes.c_size_t, _VP])
+        L.nvfp4_stream_read.restype = ctypes.c_int
+        L.nvfp4_stream_read.argtypes = [_VP, ctypes.c_size_t, _VP, _VP]
         _lib = L
     return _lib
 
@@ -200,6 +203,17 @@ def dequant(codes, scales, gscale) -> torch.Tensor:
     out = torch.empty((N, K), dtype=torch.float32, device=codes.device)
     dequant_into(codes, scales, gscale, out)
     return out
+
+
+# ----------------------------------------------------------- measurement
+
+def stream_read(buf: torch.Tensor, sink: torch.Tensor, nbytes: int | None = None) -> None:
+    """Read the first `nbytes` (default: all) bytes of `buf` once on the
+    device (the read-bandwidth ceiling of the benchmark); `sink` is a
+    uint32/int32 [1] device tensor that keeps the loads alive."""
+    _dev(buf, sink)
+    n = buf.numel() * buf.element_size() if nbytes is None else int(nbytes)
+    _check("nvfp4_stream_read", lib().nvfp4_stream_read(_p(buf), n, _p(sink), _stream(buf)))
 
 
 # ------------------------------------------------------------------ gemv

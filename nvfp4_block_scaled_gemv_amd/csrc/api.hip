@@ -371,6 +371,21 @@ nvfp4_status nvfp4_gemv_w4a4_segments(const nvfp4_gemv_segment* segs, int64_t n_
                     "nvfp4_gemv_w4a4_segments launch");
 }
 
+nvfp4_status nvfp4_stream_read(const void* buf, size_t bytes, uint32_t* sink,
+                               hipStream_t stream) {
+  clear_error();
+  if (bytes % 16 != 0)
+    return fail(NVFP4_ERR_SHAPE, "nvfp4_stream_read: bytes=%zu is not a multiple of 16", bytes);
+  if (bytes == 0) return NVFP4_OK;
+  if (!buf || !sink) return fail(NVFP4_ERR_NULL, "nvfp4_stream_read: NULL pointer");
+  if (!aligned(buf, 16) || !aligned(sink, 4))
+    return fail(NVFP4_ERR_ALIGN, "nvfp4_stream_read: buf must be 16-byte, sink 4-byte aligned");
+  if (overlap(sink, 4, buf, bytes))
+    return fail(NVFP4_ERR_ALIAS, "nvfp4_stream_read: sink overlaps buf");
+  return hip_result(nvfp4::launch_stream_read(buf, bytes, sink, stream),
+                    "nvfp4_stream_read launch");
+}
+
 size_t nvfp4_moe_workspace_bytes(int64_t M, int64_t H, int64_t I, int64_t topk) {
   if (M < 0 || H < 0 || I < 0 || topk < 0) return 0;
   return nvfp4::moe_layout(M, H, I, topk, 0, false).total;

@@ -73,6 +73,10 @@ hipError_t launch_quantize_decode(const uint16_t* x, int64_t rows, int64_t K,
 
 hipError_t launch_fill_zero(float* y, size_t n, hipStream_t stream);
 
+// Read `bytes` (a multiple of 16) from buf once; the measurement ceiling.
+hipError_t launch_stream_read(const void* buf, size_t bytes, uint32_t* sink,
+                              hipStream_t stream);
+
 // MoE workspace layout (byte offsets from the workspace base).
 struct MoeLayout {
   size_t h_off;       // uint16 bf16 SwiGLU activations h[M * topk, I]

@@ -34,13 +34,13 @@ def test_exports_every_declared_symbol(L):
             "nvfp4_moe_shared_workspace_bytes", "nvfp4_quantize_act", "nvfp4_gemv_w4a4",
             "nvfp4_gemv_w4a4_workspace_bytes", "nvfp4_gemv_w4a4_segments", "nvfp4_moe_w4a4_gemv",
             "nvfp4_moe_w4a4_workspace_bytes", "nvfp4_abi_version", "nvfp4_status_string",
-            "nvfp4_last_error"} <= set(names)
+            "nvfp4_last_error", "nvfp4_stream_read"} <= set(names)
     for n in names:
         assert hasattr(L, n), n
 
 
 def test_version_and_status_strings(L):
-    assert L.nvfp4_abi_version() == 6
+    assert L.nvfp4_abi_version() == 7
     for s in range(8):
         assert L.nvfp4_status_string(s)
     assert L.nvfp4_status_string(99) == b"unknown status"
@@ -345,3 +345,15 @@ def test_gemv_w4a4_segments_checks(L):
     assert f(bad, 2, CX, SX, GX, 2, 64, WS, need, None) == ERR_ALIAS
     assert f(arr, 2, CX, SX, GX, 2, 64, arr[0].codes, need, None) == ERR_ALIAS  # workspace on W
     assert f(arr, 2, CX, SX, GX, 2, 64, arr[1].y, need, None) == ERR_ALIAS      # workspace on y
+
+
+def test_stream_read_checks(L):
+    """Host-side validation of the read-bandwidth measurement aid (no launch)."""
+    f = L.nvfp4_stream_read
+    assert f(A, 24, B, None) == ERR_SHAPE                       # bytes % 16
+    assert f(A, 0, B, None) == OK                               # nothing to read
+    assert f(None, 64, B, None) == ERR_NULL
+    assert f(A, 64, None, None) == ERR_NULL
+    assert f(A + 8, 64, B, None) == ERR_ALIGN
+    assert f(A, 64, B + 2, None) == ERR_ALIGN
+    assert f(A, 64, A + 32, None) == ERR_ALIAS                  # sink inside buf
