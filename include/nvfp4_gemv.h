@@ -55,7 +55,7 @@
 extern "C" {
 #endif
 
-#define NVFP4_ABI_VERSION 7
+#define NVFP4_ABI_VERSION 8
 
 /* Largest number of activation rows (tokens) one GEMV / MoE call takes. */
 #define NVFP4_MAX_M 8
@@ -426,6 +426,34 @@ nvfp4_status nvfp4_moe_w4a4_gemv(const uint8_t* w13_codes, const uint8_t* w13_sc
                                  int64_t E, int64_t H, int64_t I, int64_t topk,
                                  const nvfp4_moe_shared* shared, float* y, void* workspace,
                                  size_t workspace_bytes, hipStream_t stream);
+
+/* Size of the device array that nvfp4_moe_gemv_noalloc keeps its SwiGLU
+   activations in (one copy per device, held until the process ends). */
+#define NVFP4_NOALLOC_SCRATCH_BYTES (4 << 20)
+
+/*
+ * nvfp4_moe_gemv_noalloc -- nvfp4_moe_gemv for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc): the same computation and kernels, with the bf16
+ * SwiGLU activations h[M * topk, I] kept in a library-owned device array of
+ * NVFP4_NOALLOC_SCRATCH_BYTES bytes (a file-scope __device__ array, one per
+ * device) instead of a caller workspace. Nothing is allocated by the call.
+ *
+ * Arguments as nvfp4_moe_gemv without the workspace. The activations must
+ * fit: nvfp4_moe_workspace_bytes(M, H, I, topk) <= NVFP4_NOALLOC_SCRATCH_BYTES
+ * (else NVFP4_ERR_UNSUPPORTED, nothing launched). Every call on a device
+ * shares that device's array: calls that may overlap on one device (other
+ * streams, other host threads) race on it and must be serialised by the
+ * caller. The array is overwritten by every call; nothing in it needs to
+ * start at zero.
+ * Errors: NULL, SHAPE, ALIGN, UNSUPPORTED, ALIAS, HIP.
+ */
+nvfp4_status nvfp4_moe_gemv_noalloc(const uint8_t* w13_codes, const uint8_t* w13_scales,
+                                    const float* w13_gscale, const uint8_t* w2_codes,
+                                    const uint8_t* w2_scales, const float* w2_gscale,
+                                    const uint16_t* x, const int32_t* expert_ids,
+                                    const float* gate_w, int64_t M, int64_t E, int64_t H,
+                                    int64_t I, int64_t topk, float* y, hipStream_t stream);
 
 /*
  * nvfp4_stream_read -- measurement aid, not part of the product path: reads

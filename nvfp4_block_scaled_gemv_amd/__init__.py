@@ -17,6 +17,7 @@ Functions (same names as the C entry points, without the prefix):
   moe_gemv(w13..., w2..., x, ids, gate_w[, workspace]) -> y (fp32 [M, H])
   moe_shared_workspace_bytes(M, H, I, topk, I_shared) -> int
   moe_shared_gemv(w13..., w2..., x, ids, gate_w, shared[, workspace]) -> y
+  moe_gemv_noalloc_into(w13..., w2..., x, ids, gate_w, y)  (no workspace)
   stream_read(buf, sink)                 (measurement aid: one pure read of buf)
 The ``*_into`` variants write into caller-provided outputs.
 """
@@ -40,6 +41,8 @@ MAX_TOPK = 16
 MAX_N = 1 << 30
 MOE_MAX_I = 1 << 24
 MOE_MAX_H = 1 << 24
+# NVFP4_NOALLOC_SCRATCH_BYTES: the device array of nvfp4_moe_gemv_noalloc.
+NOALLOC_SCRATCH_BYTES = 4 << 20
 
 _VP = ctypes.c_void_p
 _I64 = ctypes.c_int64
@@ -118,6 +121,8 @@ def lib() -> ctypes.CDLL:
         L.nvfp4_moe_w4a4_gemv.argtypes = ([_VP] * 11 + [_I64] * 5 +
                                           [ctypes.POINTER(MoeShared), _VP, _VP,
                                            ctypes.c_size_t, _VP])
+        L.nvfp4_moe_gemv_noalloc.restype = ctypes.c_int
+        L.nvfp4_moe_gemv_noalloc.argtypes = [_VP] * 9 + [_I64] * 5 + [_VP, _VP]
         L.nvfp4_stream_read.restype = ctypes.c_int
         L.nvfp4_stream_read.argtypes = [_VP, ctypes.c_size_t, _VP, _VP]
         _lib = L
@@ -392,6 +397,27 @@ def moe_gemv(w13_codes, w13_scales, w13_gscale, w2_codes, w2_scales, w2_gscale, 
     moe_gemv_into(w13_codes, w13_scales, w13_gscale, w2_codes, w2_scales, w2_gscale, x,
                   expert_ids, gate_w, y, workspace)
     return y
+
+
+def moe_gemv_noalloc_into(w13_codes, w13_scales, w13_gscale, w2_codes, w2_scales, w2_gscale,
+                          x, expert_ids, gate_w, y) -> None:
+    """moe_gemv_into without a workspace: the library's own device array
+    holds the SwiGLU activations (calls on one device must not overlap)."""
+    _dev(w13_codes, w13_scales, w13_gscale, w2_codes, w2_scales, w2_gscale, x,
+         expert_ids, gate_w, y)
+    _dtype(x, torch.bfloat16, torch.int16, torch.uint16, name="x")
+    _dtype(expert_ids, torch.int32, name="expert_ids")
+    _dtype(gate_w, torch.float32, name="gate_w")
+    E, twoI, Hh = w13_codes.shape
+    H, I = Hh * 2, twoI // 2
+    M, topk = expert_ids.shape
+    if tuple(w2_codes.shape) != (E, H, I // 2) or tuple(x.shape) != (M, H) \
+            or tuple(gate_w.shape) != (M, topk) or tuple(y.shape) != (M, H):
+        raise ValueError("inconsistent MoE shapes")
+    _check("nvfp4_moe_gemv_noalloc", lib().nvfp4_moe_gemv_noalloc(
+        _p(w13_codes), _p(w13_scales), _p(w13_gscale), _p(w2_codes), _p(w2_scales),
+        _p(w2_gscale), _p(x), _p(expert_ids), _p(gate_w), M, E, H, I, topk, _p(y),
+        _stream(x)))
 
 
 def moe_workspace_layout(M: int, H: int, I: int, topk: int) -> dict:

@@ -4,6 +4,8 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "nvfp4_gemv.h"
 #include "internal.h"
 
@@ -407,16 +409,23 @@ size_t nvfp4_moe_w4a4_workspace_bytes(int64_t M, int64_t H, int64_t I, int64_t t
 
 namespace {
 
-// Checks and launch shared by nvfp4_moe_gemv, nvfp4_moe_shared_gemv and
-// nvfp4_moe_w4a4_gemv (shared == NULL: no shared expert; w4a4: the routed
-// experts take NVFP4 activations with the static scales ga13 and ga2).
+// The current device's scratch array of nvfp4_moe_gemv_noalloc (defined at
+// the end of this file), or NULL with the error text set.
+void* device_scratch(const char* fn);
+
+// Checks and launch shared by nvfp4_moe_gemv, nvfp4_moe_shared_gemv,
+// nvfp4_moe_w4a4_gemv and nvfp4_moe_gemv_noalloc (shared == NULL: no shared
+// expert; w4a4: the routed experts take NVFP4 activations with the static
+// scales ga13 and ga2; own_ws: the workspace is the library's scratch array,
+// looked up after every host-side check, just before the launch).
 nvfp4_status moe_checked(const char* fn, const uint8_t* w13_codes, const uint8_t* w13_scales,
                          const float* w13_gscale, const uint8_t* w2_codes,
                          const uint8_t* w2_scales, const float* w2_gscale, const uint16_t* x,
                          const int32_t* expert_ids, const float* gate_w, int64_t M, int64_t E,
                          int64_t H, int64_t I, int64_t topk, const nvfp4_moe_shared* shared,
                          bool w4a4, const float* ga13, const float* ga2, float* y,
-                         void* workspace, size_t workspace_bytes, hipStream_t stream) {
+                         void* workspace, size_t workspace_bytes, hipStream_t stream,
+                         bool own_ws = false) {
   clear_error();
   if (M < 0 || E < 1 || H <= 0 || I <= 0 || topk < 1 || (H % 32) != 0 || (I % 32) != 0)
     return fail(NVFP4_ERR_SHAPE,
@@ -443,11 +452,17 @@ nvfp4_status moe_checked(const char* fn, const uint8_t* w13_codes, const uint8_t
     return fail(NVFP4_ERR_NULL, "%s: NULL pointer in the shared expert", fn);
   if (w4a4 && (!ga13 || !ga2)) return fail(NVFP4_ERR_NULL, "%s: NULL static input scale", fn);
   const size_t need = nvfp4::moe_layout(M, H, I, topk, Is, w4a4).total;
-  if (!workspace || workspace_bytes < need)
+  if (own_ws && need > (size_t)NVFP4_NOALLOC_SCRATCH_BYTES)
+    return fail(NVFP4_ERR_UNSUPPORTED,
+                "%s: M * topk * I * 2 = %zu bytes of activations exceed the %d-byte scratch "
+                "array (use nvfp4_moe_gemv with a workspace)",
+                fn, need, NVFP4_NOALLOC_SCRATCH_BYTES);
+  if (!own_ws && (!workspace || workspace_bytes < need))
     return fail(NVFP4_ERR_WORKSPACE, "%s: workspace of %zu bytes needed, %zu given", fn, need,
                 workspace ? workspace_bytes : (size_t)0);
   if (!aligned(w13_codes, 16) || !aligned(w2_codes, 16) || !aligned(w13_scales, 2) ||
-      !aligned(w2_scales, 2) || !aligned(x, 16) || !aligned(y, 16) || !aligned(workspace, 256) ||
+      !aligned(w2_scales, 2) || !aligned(x, 16) || !aligned(y, 16) ||
+      (!own_ws && !aligned(workspace, 256)) ||
       !aligned(expert_ids, 4) || !aligned(gate_w, 4) || !aligned(w13_gscale, 4) ||
       !aligned(w2_gscale, 4))
     return fail(NVFP4_ERR_ALIGN, "%s: alignment rule broken (see nvfp4_gemv.h)", fn);
@@ -469,12 +484,18 @@ nvfp4_status moe_checked(const char* fn, const uint8_t* w13_codes, const uint8_t
   const size_t insz[] = {e13 / 2, e13 / 16, (size_t)E * 4, e2 / 2, e2 / 16, (size_t)E * 4,
                          (size_t)M * (size_t)H * 2, S * 4, S * 4,
                          s13 / 2, s13 / 16, 4, s2 / 2, s2 / 16, 4, 4, 4};
+  // (the library's own scratch array cannot overlap a caller buffer)
   for (int i = 0; i < 17; ++i) {
-    if (overlap(y, yb, ins[i], insz[i]) || overlap(workspace, need, ins[i], insz[i]))
+    if (overlap(y, yb, ins[i], insz[i]) ||
+        (!own_ws && overlap(workspace, need, ins[i], insz[i])))
       return fail(NVFP4_ERR_ALIAS, "%s: y or workspace overlaps input %d", fn, i);
   }
-  if (overlap(y, yb, workspace, need))
+  if (!own_ws && overlap(y, yb, workspace, need))
     return fail(NVFP4_ERR_ALIAS, "%s: y overlaps the workspace", fn);
+  if (own_ws) {
+    workspace = device_scratch(fn);
+    if (!workspace) return NVFP4_ERR_HIP;
+  }
   nvfp4::MoeShared sh = {};
   if (shared) {
     sh.c13 = shared->w13_codes;
@@ -536,6 +557,68 @@ nvfp4_status nvfp4_moe_w4a4_gemv(const uint8_t* w13_codes, const uint8_t* w13_sc
   return moe_checked("nvfp4_moe_w4a4_gemv", w13_codes, w13_scales, w13_gscale, w2_codes,
                      w2_scales, w2_gscale, x, expert_ids, gate_w, M, E, H, I, topk, shared, true,
                      gscale_x, gscale_h, y, workspace, workspace_bytes, stream);
+}
+
+}  // extern "C"
+
+// ---------------------------------------------------------------------------
+// nvfp4_moe_gemv_noalloc: nvfp4_moe_gemv with its workspace (the bf16 SwiGLU
+// activations h) in a file-scope device array instead of caller memory, for
+// callers that cannot allocate. Each device the library runs on holds its own
+// copy of the array until the process ends. In host code `scratch` only names
+// the symbol: its device address is looked up once per device with
+// hipGetSymbolAddress (with that device current) and that address is what
+// the kernels receive.
+
+namespace {
+
+static __device__ __align__(256) unsigned char scratch[NVFP4_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// The current device's address of `scratch` (looked up on the first call on
+// that device), or NULL with the error text set.
+void* device_scratch(const char* fn) {
+  int dev = -1;
+  const hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) {
+    fail(NVFP4_ERR_HIP, "%s: hipGetDevice: %s", fn, hipGetErrorString(e));
+    return nullptr;
+  }
+  if (dev < 0 || dev >= kMaxDevices) {
+    fail(NVFP4_ERR_UNSUPPORTED, "%s: device %d is past the %d devices this entry point serves",
+         fn, dev, kMaxDevices);
+    return nullptr;
+  }
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    const hipError_t r = hipGetSymbolAddress((void**)&ptr, HIP_SYMBOL(scratch));
+    if (r != hipSuccess || !ptr) {
+      fail(NVFP4_ERR_HIP, "%s: hipGetSymbolAddress(scratch) on device %d: %s", fn, dev,
+           hipGetErrorString(r));
+      return nullptr;
+    }
+    g_scratch_ptr[dev] = ptr;
+  }
+  return g_scratch_ptr[dev];
+}
+
+}  // namespace
+
+extern "C" {
+
+nvfp4_status nvfp4_moe_gemv_noalloc(const uint8_t* w13_codes, const uint8_t* w13_scales,
+                                    const float* w13_gscale, const uint8_t* w2_codes,
+                                    const uint8_t* w2_scales, const float* w2_gscale,
+                                    const uint16_t* x, const int32_t* expert_ids,
+                                    const float* gate_w, int64_t M, int64_t E, int64_t H,
+                                    int64_t I, int64_t topk, float* y, hipStream_t stream) {
+  return moe_checked("nvfp4_moe_gemv_noalloc", w13_codes, w13_scales, w13_gscale, w2_codes,
+                     w2_scales, w2_gscale, x, expert_ids, gate_w, M, E, H, I, topk, nullptr,
+                     false, nullptr, nullptr, y, nullptr, 0, stream, /*own_ws=*/true);
 }
 
 }  // extern "C"

@@ -34,13 +34,13 @@ def test_exports_every_declared_symbol(L):
             "nvfp4_moe_shared_workspace_bytes", "nvfp4_quantize_act", "nvfp4_gemv_w4a4",
             "nvfp4_gemv_w4a4_workspace_bytes", "nvfp4_gemv_w4a4_segments", "nvfp4_moe_w4a4_gemv",
             "nvfp4_moe_w4a4_workspace_bytes", "nvfp4_abi_version", "nvfp4_status_string",
-            "nvfp4_last_error", "nvfp4_stream_read"} <= set(names)
+            "nvfp4_last_error", "nvfp4_stream_read", "nvfp4_moe_gemv_noalloc"} <= set(names)
     for n in names:
         assert hasattr(L, n), n
 
 
 def test_version_and_status_strings(L):
-    assert L.nvfp4_abi_version() == 7
+    assert L.nvfp4_abi_version() == 8
     for s in range(8):
         assert L.nvfp4_status_string(s)
     assert L.nvfp4_status_string(99) == b"unknown status"
@@ -63,6 +63,7 @@ def test_binding_limits_match_the_header():
     assert value("NVFP4_MOE_MAX_I") == nv.MOE_MAX_I
     assert value("NVFP4_MOE_MAX_H") == nv.MOE_MAX_H
     assert value("NVFP4_MAX_SEGMENTS") == nv.MAX_SEGMENTS
+    assert value("NVFP4_NOALLOC_SCRATCH_BYTES") == nv.NOALLOC_SCRATCH_BYTES
 
 
 def _err(L):
@@ -357,3 +358,17 @@ def test_stream_read_checks(L):
     assert f(A + 8, 64, B, None) == ERR_ALIGN
     assert f(A, 64, B + 2, None) == ERR_ALIGN
     assert f(A, 64, A + 32, None) == ERR_ALIAS                  # sink inside buf
+
+
+def test_moe_noalloc_refuses_calls_larger_than_its_array(L):
+    """nvfp4_moe_gemv_noalloc checks its size limit before touching a device:
+    M * topk * I * 2 bytes of activations must fit NVFP4_NOALLOC_SCRATCH_BYTES."""
+    assert nv.NOALLOC_SCRATCH_BYTES == 4 << 20
+    args = [A + i * 0x10000000 for i in range(9)]
+    f = L.nvfp4_moe_gemv_noalloc
+    # 8 * 16 * 16416 * 2 bytes: just over 4 MiB
+    assert f(*args, 8, 4, 64, 16416, 16, B, None) == ERR_UNSUPPORTED
+    assert "scratch" in _err(L)
+    assert f(*args, 0, 4, 64, 64, 2, B, None) == OK              # nothing to do
+    assert f(*args, 1, 4, 64, 48, 2, B, None) == ERR_SHAPE       # I % 32, before any device
+    assert f(*args, 9, 4, 64, 64, 2, B, None) == ERR_UNSUPPORTED
