@@ -24,13 +24,14 @@ previous calls did not (the 256 MB MALL cannot serve repeats).
 Timing of each leg:
   * wall: W warm-up steps, then exactly K timed steps between two device
     synchronisations -> ms_per_step and ``value``;
-  * launches: a fixed window of LAUNCH_WINDOW launches (independent of K),
-    each bracketed by its own pair of HIP events on the launch stream; the
-    mean of those per-launch durations is the kernel's average launch
-    duration, the basis of ``roofline.achieved`` (the rocprofv3 average of
-    the same command agrees with it to within the box's run-to-run spread);
-  * device_us_back_to_back: the steps queued behind a bounded sleep kernel
-    and run back to back (no host time between launches).
+  * step_us (the basis of every GB/s and roofline fraction): a fixed number
+    of steps (independent of K) queued on the launch stream behind a busy
+    hold of pure-read launches, then run back to back, bracketed by two HIP
+    events on that stream. The hold keeps the GPU loaded while the host
+    queues: after any idle period the GPU runs its first ~10 ms of kernels
+    up to 15% slower, which an idle hold (a sleep kernel) would fold in;
+  * window_us: LAUNCH_WINDOW steps issued by the host back to back between
+    two events (GPU-bound for long steps, host-bound for short ones).
 Each leg also carries its parity against the oracle (all outputs of the timed
 configuration), the oracle's own time on the host cores (``cpu``: all threads,
 and one thread on a bounded sample) and the fraction of the measured read
@@ -60,8 +61,12 @@ BF16_MFMA_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 matrix-core peak
 METRIC = "achieved HBM GB/s and % of roofline, NVFP4 W4A16 GEMV at M=1 and M=8"
 MIN_ROTATION_BYTES = 1 << 30
 LAUNCH_WINDOW = 400        # steps in the issue-gated event window of every leg
-QUEUED_WINDOW = 200        # steps queued back to back behind a sleep kernel
+QUEUED_WINDOW = 200        # steps queued back to back behind a busy hold
+QUEUED_LAUNCHES = 400      # at most this many launches queued at once
 ALL_LEGS = "lm_head,small,stress,layer,moe,w4a4,wide,copy"
+
+
+HOLD = None               # the BusyHold of this run
 
 
 def log(*a):
@@ -130,40 +135,60 @@ def launch_window(torch, step, first, n=LAUNCH_WINDOW):
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
+    t0 = time.perf_counter()
     e0.record()
     for i in range(n):
         step(first + i)
     e1.record()
+    issue_ms = (time.perf_counter() - t0) * 1e3
     torch.cuda.synchronize()
-    return e0.elapsed_time(e1) / n * 1e3
+    return e0.elapsed_time(e1) / n * 1e3, issue_ms / n
 
 
-_SLEEP_CYCLES_PER_MS = None
+class BusyHold:
+    """Keeps the GPU at full load while the host queues the steps to be
+    timed: pure-read launches over a 1 GiB buffer (nvfp4_stream_read). The
+    GPU runs the first ~10 ms after any idle period up to 15% slower (a
+    clock ramp, seen in rocprofv3 traces after a sleep kernel or a host
+    pause), so an idle hold would bias every queued measurement."""
 
-
-def queued_steps(torch, step, steps, first, wall_ms_per_step):
-    """Device time per step (us) with every launch queued ahead of the GPU.
-    A bounded sleep kernel (torch.cuda._sleep) holds the stream while the
-    host issues the steps; they then run back to back, so host time between
-    launches (the Python binding takes several microseconds per call) is not
-    counted. Returns None when the host did not finish issuing before the
-    sleep ended or when the sleep kernel is unavailable."""
-    global _SLEEP_CYCLES_PER_MS
-    if not hasattr(torch.cuda, "_sleep"):
-        return None
-    e0 = torch.cuda.Event(enable_timing=True)
-    e1 = torch.cuda.Event(enable_timing=True)
-    if _SLEEP_CYCLES_PER_MS is None:
-        c0 = 1 << 22
+    def __init__(self, torch, nv):
+        self.torch, self.nv = torch, nv
+        self.buf = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+        self.buf.fill_(0x3C)
+        self.sink = torch.zeros(4, dtype=torch.int32, device="cuda")
+        for _ in range(5):
+            self.read()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize()
         e0.record()
-        torch.cuda._sleep(c0)
+        for _ in range(20):
+            self.read()
         e1.record()
         torch.cuda.synchronize()
-        _SLEEP_CYCLES_PER_MS = c0 / max(e0.elapsed_time(e1), 1e-3)
-    hold_ms = 2.0 + 2.0 * wall_ms_per_step * steps
+        self.read_ms = e0.elapsed_time(e1) / 20
+
+    def read(self):
+        self.nv.stream_read(self.buf, self.sink)
+
+    def hold(self, ms):
+        """Queue about `ms` of reads; returns the queued hold in ms."""
+        n = max(2, int(np.ceil(ms / self.read_ms)))
+        for _ in range(n):
+            self.read()
+        return n * self.read_ms
+
+
+def queued_steps(torch, hold, step, steps, first, issue_ms_per_step):
+    """Device time per step (us) with the steps queued ahead of the GPU
+    behind a busy hold, so that they run back to back with no host time
+    between launches. Returns None if the host did not finish issuing them
+    before the hold ran out (the number would include host gaps)."""
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
-    torch.cuda._sleep(int(hold_ms * _SLEEP_CYCLES_PER_MS))
+    hold_ms = hold.hold(1.0 + 1.5 * issue_ms_per_step * steps)
     t0 = time.perf_counter()
     e0.record()
     for i in range(steps):
@@ -176,23 +201,26 @@ def queued_steps(torch, step, steps, first, wall_ms_per_step):
     return e0.elapsed_time(e1) / steps * 1e3
 
 
-def measure(torch, step, steps, warmup, nbytes, tokens, launches, ceiling=None):
+def measure(torch, hold, step, steps, warmup, nbytes, tokens, launches, ceiling=None):
     """The timing fields of one leg: wall clock over K steps; device time per
-    step from QUEUED_WINDOW steps queued behind a sleep kernel and run back to
-    back (``step_us``, the basis of every GB/s and fraction below; the
-    issue-gated window of LAUNCH_WINDOW steps stands in where the queue
-    could not be filled in time). `nbytes` = algorithmic bytes per step,
-    `tokens` = activation rows per step, `launches` = kernel launches per
-    step, `ceiling` = pure-read time (us) of the same bytes."""
+    step from a fixed number of steps queued back to back behind a busy hold
+    (``step_us``, the basis of every GB/s and fraction below; the
+    issue-gated window of LAUNCH_WINDOW steps stands in where the host could
+    not queue them in time). `nbytes` = algorithmic bytes per step, `tokens`
+    = activation rows per step, `launches` = kernel launches per step,
+    `ceiling` = pure-read time (us) of the same bytes."""
     ms = timed_steps(torch, step, steps, warmup)
-    win = launch_window(torch, step, warmup + steps)
-    b2b = queued_steps(torch, step, QUEUED_WINDOW, warmup + steps + LAUNCH_WINDOW, ms)
+    win, issue = launch_window(torch, step, warmup + steps)
+    nq = max(40, min(QUEUED_WINDOW, QUEUED_LAUNCHES // launches))
+    b2b = queued_steps(torch, hold, step, nq, warmup + steps + LAUNCH_WINDOW, issue)
     us = b2b if b2b else win
     out = {"bytes_per_step": nbytes, "launches_per_step": launches, "ms_per_step": ms,
            "gbs_wall": nbytes / (ms * 1e-3) / 1e9,
-           "step_us": us, "step_us_basis": (f"{QUEUED_WINDOW} steps queued back to back"
-                                            if b2b else f"{LAUNCH_WINDOW}-step event window"),
-           "window_us": win, "device_us_back_to_back": b2b,
+           "step_us": us, "step_us_basis": (f"{nq} steps queued back to back behind a busy "
+                                            "hold" if b2b else
+                                            f"{LAUNCH_WINDOW}-step event window"),
+           "window_us": win, "host_issue_us_per_step": issue * 1e3,
+           "device_us_back_to_back": b2b,
            "gbs": nbytes / (us * 1e-6) / 1e9,
            "frac_of_peak": nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS,
            "tokens_per_s": tokens / (ms * 1e-3),
@@ -210,8 +238,8 @@ class ReadCeiling:
     that size (R * size >= 1 GiB, rotated), measured like the legs (launches
     queued back to back); the mean device time per launch in us."""
 
-    def __init__(self, torch, nv):
-        self.torch, self.nv, self.cache = torch, nv, {}
+    def __init__(self, torch, nv, hold):
+        self.torch, self.nv, self.hold, self.cache = torch, nv, hold, {}
         self.sink = torch.zeros(4, dtype=torch.int32, device="cuda")
 
     def us(self, nbytes):
@@ -227,11 +255,9 @@ class ReadCeiling:
             def step(i):
                 self.nv.stream_read(bufs[i % R], self.sink)
 
-            for i in range(10):
-                step(i)
-            ms = timed_steps(torch, step, 20, 0)
-            us = queued_steps(torch, step, QUEUED_WINDOW, 30, ms)
-            self.cache[n16] = us if us else launch_window(torch, step, 30)
+            win, issue = launch_window(torch, step, 0, 50)
+            us = queued_steps(torch, self.hold, step, QUEUED_WINDOW, 50, issue)
+            self.cache[n16] = us if us else win
             del bufs
         return self.cache[n16]
 
@@ -388,7 +414,7 @@ def dense_leg(torch, nv, D, steps, warmup, ceil, want_cpu, label, segments=None)
         launches = len(segments)
         ceiling = sum(ceil.us(sum(D.bytes[j] for j in g)) for g in segments)
     out = {"workload": label, "M": M, "rotate_copies": D.R,
-           **measure(torch, step, steps, warmup, nbytes, M, launches, ceiling)}
+           **measure(torch, HOLD, step, steps, warmup, nbytes, M, launches, ceiling)}
     if segments is None:
         out["parity"] = D.parity()
     else:
@@ -499,7 +525,7 @@ def moe_legs(torch, nv, traffic, mo, M, steps, warmup, ceil, want_cpu):
         nbytes = mean_bytes(fn, first, QUEUED_WINDOW)
         out = {"workload": label, "M": M, "rotating_batches": nb,
                "distinct_experts_mean": mean_bytes(lambda d: d, first, QUEUED_WINDOW),
-               **measure(torch, step, steps, warmup, nbytes, M, launches, ceil.us(nbytes))}
+               **measure(torch, HOLD, step, steps, warmup, nbytes, M, launches, ceil.us(nbytes))}
         return out
 
     # host stacks for the parity batch (batch 0): routed experts + shared
@@ -642,7 +668,7 @@ def leg_w4a4(torch, nv, workloads, traffic, steps, warmup, ceil, want_cpu):
                                                     for _, N, K in mats)
     out = {"workload": "w4a4_ffn_m2 (gate, up, down 4096x4096; static input scale)", "M": M,
            "rotate_copies": reps,
-           **measure(torch, step, steps, warmup, nbytes, M, 1 + (1 if M <= 2 else 2) * 2,
+           **measure(torch, HOLD, step, steps, warmup, nbytes, M, 1 + (1 if M <= 2 else 2) * 2,
                      ceil.us(nbytes))}
     step(0)
     torch.cuda.synchronize()
@@ -672,7 +698,7 @@ def leg_copy(torch, steps, warmup):
         torch.mul(src, 1.0, out=dst)
 
     timed_steps(torch, step, steps, warmup)
-    us = launch_window(torch, step, warmup + steps, 50)
+    us, _ = launch_window(torch, step, warmup + steps, 50)
     return {"bytes_read": n * 4, "bytes_written": n * 4, "us": us,
             "gbs": 2 * n * 4 / (us * 1e-6) / 1e9}
 
@@ -983,7 +1009,9 @@ def main():
     want_cpu = not args.no_cpu_baseline
     K_, W_ = args.steps, args.warmup
     props = torch.cuda.get_device_properties(0)
-    ceil = ReadCeiling(torch, nv)
+    global HOLD
+    HOLD = BusyHold(torch, nv)
+    ceil = ReadCeiling(torch, nv, HOLD)
     result = {
         "metric": METRIC, "value": None, "unit": "GB/s", "n_gpus": 1, "steps": K_,
         "warmup": W_, "ms_per_step": None, "higher_is_better": True,
@@ -1007,8 +1035,8 @@ def main():
             "bound": "hbm", "achieved": lm["gbs"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": lm["frac_of_peak"], "traffic": read_traffic(), "kernel": LM_KERNEL,
             "kernel_avg_us": lm["step_us"],
-            "basis": f"HIP events on the launch stream around {QUEUED_WINDOW} launches queued "
-                     "back to back (a fixed window, independent of --steps)",
+            "basis": lm["step_us_basis"] + ": HIP events on the launch stream around a "
+                     "fixed window of launches, independent of --steps",
             "kernel_avg_us_event_window": lm["window_us"],
             "event_window_launches": LAUNCH_WINDOW,
             "bytes_per_launch": lm["bytes_per_step"],

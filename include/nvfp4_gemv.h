@@ -1,8 +1,9 @@
 /*
  * nvfp4_gemv.h -- C ABI of the MI355X (gfx950) NVFP4 g16 W4A16 small-M GEMV
  * library: weight packing, bit-exact dequantisation, the weight-streaming
- * GEMV y[M,N] = x[M,K] . W[N,K]^T for M <= 8, and the MoE expert-slot variant
- * (gather top-k experts by id, SwiGLU, combine by gate weight).
+ * GEMV y[M,N] = x[M,K] . W[N,K]^T for M <= 128 activation rows, and the MoE
+ * expert-slot variant for M <= 8 (gather top-k experts by id, SwiGLU,
+ * combine by gate weight).
  *
  * The operations are the ones the GLM-5.3-Flash-NVFP4 blueprint pages
  * describe for their decode step:
@@ -57,8 +58,11 @@ extern "C" {
 
 #define NVFP4_ABI_VERSION 8
 
-/* Largest number of activation rows (tokens) one GEMV / MoE call takes. */
-#define NVFP4_MAX_M 8
+/* Largest number of activation rows (tokens) one dense GEMV call takes (the
+   blueprint's "multi_seq" plan arm: 2 to 128 rows). */
+#define NVFP4_MAX_M 128
+/* Largest number of tokens one MoE call takes. */
+#define NVFP4_MOE_MAX_M 8
 /* Largest number of expert slots per token in the MoE call. */
 #define NVFP4_MAX_TOPK 16
 /* Largest MoE intermediate size I (down-projection row length) per call. */
@@ -144,7 +148,12 @@ nvfp4_status nvfp4_dequant(const uint8_t* codes, const uint8_t* scales,
  *   M       0 <= M <= NVFP4_MAX_M;  0 <= N <= NVFP4_MAX_N;  K >= 0, K % 32 == 0;
  *   y       float[M, N] out, 4-byte aligned (M == 0 or N == 0: nothing is
  *           launched; K == 0: y is set to zero).
- * Errors: NULL, SHAPE, ALIGN, UNSUPPORTED (M > 8 or N > NVFP4_MAX_N), ALIAS, HIP.
+ * M <= 2 runs on the vector ALUs, 3 <= M <= 8 on the matrix cores with eight
+ * tokens per block half of each MFMA, 9 <= M <= 128 on the matrix cores with
+ * the block scale folded into the decoded weights (blueprint "Plan arms":
+ * multi_seq 2..128 rows; "Planner settings": w4a16_tc=on).
+ * Errors: NULL, SHAPE, ALIGN, UNSUPPORTED (M > NVFP4_MAX_M or N > NVFP4_MAX_N),
+ * ALIAS, HIP.
  */
 nvfp4_status nvfp4_gemv(const uint8_t* codes, const uint8_t* scales,
                         const float* gscale, const uint16_t* x, int64_t M,
@@ -218,7 +227,7 @@ size_t nvfp4_moe_workspace_bytes(int64_t M, int64_t H, int64_t I, int64_t topk);
  *              2-byte aligned; w2_gscale float[E];
  *   x          bf16[M, H] (uint16 bits), 16-byte aligned;
  *   expert_ids int32[M, topk];  gate_w float[M, topk];
- *   M          0 <= M <= NVFP4_MAX_M; 1 <= topk <= NVFP4_MAX_TOPK; E >= 1;
+ *   M          0 <= M <= NVFP4_MOE_MAX_M; 1 <= topk <= NVFP4_MAX_TOPK; E >= 1;
  *              I <= NVFP4_MOE_MAX_I; H <= NVFP4_MOE_MAX_H;
  *              H % 32 == 0, I % 32 == 0, H > 0, I > 0;
  *   y          float[M, H] out, 16-byte aligned;

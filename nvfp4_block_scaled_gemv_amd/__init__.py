@@ -34,9 +34,10 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libnvfp4_gemv.so")
 HEADER_PATH = os.path.join(os.path.dirname(_HERE), "include", "nvfp4_gemv.h")
 
-# The size limits of include/nvfp4_gemv.h (NVFP4_MAX_M, NVFP4_MAX_TOPK,
-# NVFP4_MAX_N, NVFP4_MOE_MAX_I, NVFP4_MOE_MAX_H).
-MAX_M = 8
+# The size limits of include/nvfp4_gemv.h (NVFP4_MAX_M, NVFP4_MOE_MAX_M,
+# NVFP4_MAX_TOPK, NVFP4_MAX_N, NVFP4_MOE_MAX_I, NVFP4_MOE_MAX_H).
+MAX_M = 128
+MOE_MAX_M = 8
 MAX_TOPK = 16
 MAX_N = 1 << 30
 MOE_MAX_I = 1 << 24

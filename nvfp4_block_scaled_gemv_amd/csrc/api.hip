@@ -10,6 +10,7 @@
 #include "internal.h"
 
 static_assert(NVFP4_MAX_M == NVFP4_MAX_M_INTERNAL, "M limit mismatch");
+static_assert(NVFP4_MOE_MAX_M == NVFP4_MOE_MAX_M_INTERNAL, "MoE M limit mismatch");
 static_assert(NVFP4_MAX_TOPK == NVFP4_MAX_TOPK_INTERNAL, "topk limit mismatch");
 
 namespace {
@@ -436,12 +437,12 @@ nvfp4_status moe_checked(const char* fn, const uint8_t* w13_codes, const uint8_t
   if (shared && (Is <= 0 || (Is % 32) != 0))
     return fail(NVFP4_ERR_SHAPE, "%s: shared expert width I=%lld must be > 0 and a multiple of 32",
                 fn, (long long)Is);
-  if (M > NVFP4_MAX_M || topk > NVFP4_MAX_TOPK || I > NVFP4_MOE_MAX_I || Is > NVFP4_MOE_MAX_I ||
+  if (M > NVFP4_MOE_MAX_M || topk > NVFP4_MAX_TOPK || I > NVFP4_MOE_MAX_I || Is > NVFP4_MOE_MAX_I ||
       H > NVFP4_MOE_MAX_H)
     return fail(NVFP4_ERR_UNSUPPORTED,
                 "%s: M=%lld (max %d), topk=%lld (max %d), I=%lld, shared I=%lld (max %d), "
                 "H=%lld (max %d)", fn,
-                (long long)M, NVFP4_MAX_M, (long long)topk, NVFP4_MAX_TOPK, (long long)I,
+                (long long)M, NVFP4_MOE_MAX_M, (long long)topk, NVFP4_MAX_TOPK, (long long)I,
                 (long long)Is, NVFP4_MOE_MAX_I, (long long)H, NVFP4_MOE_MAX_H);
   if (M == 0) return NVFP4_OK;
   if (!w13_codes || !w13_scales || !w13_gscale || !w2_codes || !w2_scales || !w2_gscale || !x ||

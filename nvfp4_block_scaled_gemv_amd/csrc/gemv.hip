@@ -1,6 +1,6 @@
 // gemv.hip -- dense NVFP4 g16 W4A16 GEMV on gfx950, vector-ALU path for
-// M <= 2 activation rows (M >= 3 goes to the matrix-core kernel in
-// gemv_mfma.hip):
+// M <= 2 activation rows (3 <= M <= 8 goes to the matrix-core kernels of
+// gemv_mfma.hip and gemv_splitk.hip, 9 <= M <= 128 to gemv_mt.hip):
 //   y[m, n] = g * sum_k e2m1(c[n,k]) * s[n, k/16] * x[m, k]
 // (graph.json node "l0.kda.q": act bf16, weight nvfp4/g16 -> bf16,
 // accumulate f32, scale f32). Bandwidth-bound: every weight byte is read
@@ -147,7 +147,9 @@ hipError_t launch_gemv_segments(const SegDesc* d, int n, const uint16_t* x, int 
   switch (M) {
     case 1: launch_valu<1>(d, n, rows, x, K, stream); break;
     case 2: launch_valu<2>(d, n, rows, x, K, stream); break;
-    default: return launch_gemv_mfma(d, n, x, M, K, stream);
+    default:
+      if (M > NVFP4_MAX_M_SMALL) return launch_gemv_mt(d, n, x, M, K, stream);
+      return launch_gemv_mfma(d, n, x, M, K, stream);
   }
   return hipGetLastError();
 }

@@ -8,8 +8,12 @@
 #include "segments.h"
 
 // Limits of one call (the public header exports the same values).
-#define NVFP4_MAX_M_INTERNAL 8
+#define NVFP4_MAX_M_INTERNAL 128
+#define NVFP4_MOE_MAX_M_INTERNAL 8
 #define NVFP4_MAX_TOPK_INTERNAL 16
+// The largest M of the vector-ALU and the eight-token matrix-core kernels;
+// above it the many-token kernel (gemv_mt.hip) runs.
+#define NVFP4_MAX_M_SMALL 8
 
 namespace nvfp4 {
 
@@ -29,7 +33,10 @@ hipError_t launch_gemv_segments(const SegDesc* d, int n, const uint16_t* x, int 
                                 hipStream_t stream);
 
 // Matrix-core paths, 3 <= M <= 8 (gemv_mfma.hip routes K % 256 == 0 to
-// gemv_splitk.hip).
+// gemv_splitk.hip), and 9 <= M <= 128 (gemv_mt.hip).
+bool mt_applicable(int M);
+hipError_t launch_gemv_mt(const SegDesc* d, int n, const uint16_t* x, int M, int64_t K,
+                          hipStream_t stream);
 hipError_t launch_gemv_mfma(const SegDesc* d, int n, const uint16_t* x, int M, int64_t K,
                             hipStream_t stream);
 bool splitk_applicable(int M, int64_t K);

@@ -58,6 +58,7 @@ def test_binding_limits_match_the_header():
         return int(v)
 
     assert value("NVFP4_MAX_M") == nv.MAX_M
+    assert value("NVFP4_MOE_MAX_M") == nv.MOE_MAX_M
     assert value("NVFP4_MAX_TOPK") == nv.MAX_TOPK
     assert value("NVFP4_MAX_N") == nv.MAX_N
     assert value("NVFP4_MOE_MAX_I") == nv.MOE_MAX_I
@@ -74,7 +75,7 @@ def test_gemv_rejects_bad_shapes(L):
     assert L.nvfp4_gemv(A, A, A, A, 1, 16, 48, B, None) == ERR_SHAPE       # K % 32
     assert "K % 32" in _err(L)
     assert L.nvfp4_gemv(A, A, A, A, -1, 16, 64, B, None) == ERR_SHAPE
-    assert L.nvfp4_gemv(A, A, A, A, 9, 16, 64, B, None) == ERR_UNSUPPORTED
+    assert L.nvfp4_gemv(A, A, A, A, 129, 16, 64, B, None) == ERR_UNSUPPORTED
     assert L.nvfp4_gemv(A, A, A, A, 1, (1 << 30) + 1, 64, B, None) == ERR_UNSUPPORTED   # N
     assert "N=" in _err(L)
     assert L.nvfp4_gemv(A, A, A, A, 0, 16, 64, B, None) == OK              # nothing to do
@@ -231,7 +232,7 @@ def test_w4a4_checks(L):
     Y, WS = B, B + 0x1000000
     need = nv.gemv_w4a4_workspace_bytes(2, 64)
     assert f(*w, 2, 16, 48, Y, WS, need, None) == ERR_SHAPE
-    assert f(*w, 9, 16, 64, Y, WS, need, None) == ERR_UNSUPPORTED
+    assert f(*w, 129, 16, 64, Y, WS, need, None) == ERR_UNSUPPORTED
     assert f(*w, 2, (1 << 30) + 1, 64, Y, WS, need, None) == ERR_UNSUPPORTED
     assert f(*w, 0, 16, 64, Y, WS, need, None) == OK
     assert f(*w, 2, 16, 64, Y, WS, need - 1, None) == ERR_WORKSPACE
@@ -259,7 +260,7 @@ def test_gemv_segments_checks(L):
     f = L.nvfp4_gemv_segments
     X = A + 0x30000000
     assert f(arr, 9, X, 1, 64, None) == ERR_UNSUPPORTED          # > 8 segments
-    assert f(arr, 2, X, 9, 64, None) == ERR_UNSUPPORTED          # M > 8
+    assert f(arr, 2, X, 129, 64, None) == ERR_UNSUPPORTED        # M > 128
     assert f(arr, 2, X, 1, 48, None) == ERR_SHAPE                # K % 32
     assert f(arr, -1, X, 1, 64, None) == ERR_SHAPE
     assert f(None, 2, X, 1, 64, None) == ERR_NULL
@@ -307,11 +308,11 @@ def test_last_error_is_per_thread(L):
     t1 = threading.Thread(target=worker, args=(
         "shape", lambda: L.nvfp4_gemv(A, A, A, A, 1, 16, 48, B, None)))
     t2 = threading.Thread(target=worker, args=(
-        "unsupported", lambda: L.nvfp4_gemv(A, A, A, A, 9, 16, 64, B, None)))
+        "unsupported", lambda: L.nvfp4_gemv(A, A, A, A, 129, 16, 64, B, None)))
     t1.start(), t2.start()
     t1.join(), t2.join()
     assert len(seen["shape"]) == 1 and "K % 32" in next(iter(seen["shape"]))
-    assert len(seen["unsupported"]) == 1 and "M=9" in next(iter(seen["unsupported"]))
+    assert len(seen["unsupported"]) == 1 and "M=129" in next(iter(seen["unsupported"]))
 
 
 def test_gemv_w4a4_segments_checks(L):
@@ -325,7 +326,7 @@ def test_gemv_w4a4_segments_checks(L):
     CX, SX, GX, WS = A + 0x30000000, A + 0x31000000, A + 0x32000000, B + 0x10000000
     need = nv.gemv_w4a4_workspace_bytes(2, 64)
     assert f(arr, 9, CX, SX, GX, 2, 64, WS, need, None) == ERR_UNSUPPORTED     # > 8 segments
-    assert f(arr, 2, CX, SX, GX, 9, 64, WS, need, None) == ERR_UNSUPPORTED     # M > 8
+    assert f(arr, 2, CX, SX, GX, 129, 64, WS, need, None) == ERR_UNSUPPORTED   # M > 128
     assert f(arr, 2, CX, SX, GX, 2, 48, WS, need, None) == ERR_SHAPE           # K % 32
     assert f(arr, 0, CX, SX, GX, 2, 64, WS, need, None) == OK
     assert f(arr, 2, CX, SX, GX, 0, 64, WS, need, None) == OK

@@ -168,12 +168,12 @@ def test_empty_and_zero_k():
                  torch.zeros((3, 32), dtype=torch.bfloat16, device="cuda"), y)
 
 
-def test_rejects_m9():
+def test_rejects_m129():
     c = torch.zeros((4, 16), dtype=torch.uint8, device="cuda")
     s = torch.zeros((4, 2), dtype=torch.uint8, device="cuda")
     with pytest.raises(nv.Nvfp4Error) as e:
         nv.gemv(c, s, torch.ones(1, device="cuda"),
-                torch.zeros((9, 32), dtype=torch.bfloat16, device="cuda"))
+                torch.zeros((129, 32), dtype=torch.bfloat16, device="cuda"))
     assert e.value.status == 4
 
 

@@ -9,7 +9,8 @@ from refdecode import bf16_value, decode
 ONE_BF16 = 0x3F80
 
 
-@pytest.mark.parametrize("M,N,K", [(1, 7, 32), (3, 16, 64), (8, 33, 96), (5, 64, 48)])
+@pytest.mark.parametrize("M,N,K", [(1, 7, 32), (3, 16, 64), (8, 33, 96), (5, 64, 48),
+                                   (17, 9, 160), (128, 5, 64)])
 def test_gemv_brute_force(oracle, M, N, K):
     W = workloads.normal_weights(1, 10 + M, 0, N, K)
     codes, scales, g = oracle.pack(W)
