@@ -1,0 +1,338 @@
+// gemv_g8.hip -- NVFP4 g16 W4A16 GEMV on the CDNA4 matrix cores for
+// 3 <= M <= 8 activation rows and K a multiple of 256:
+//
+//   y[m, n] = g * sum_k e2m1(c[n,k]) * e4m3(s[n, k/16]) * x[m, k]
+//
+// Work split. A workgroup owns TW tiles of 16 weight rows (of one segment)
+// and all of K; its W wavefronts split K into ranges of S slices of 256 k.
+// Every wavefront issues all of its loads at once (its part of x, then the
+// weights), computes, and the W partial tiles meet once in LDS, summed
+// in wavefront order (deterministic). There is no loop over tiles: workgroups
+// are small and many, and the hardware dispatcher hands them to CUs as CUs
+// free up, which keeps the HBM stream at the rate of a plain read.
+//
+// MFMA layout (v_mfma_f32_16x16x32_bf16; lane l, i = l % 16, g = l / 16: A
+// lane holds A[i][8g .. 8g+7], B lane holds B[8g .. 8g+7][i], D lane holds
+// D[4g + r][i]). Each MFMA multiplies two 16-element blocks of 16 weight
+// rows: A rows 0..7 are the tokens with x at the first block's k (lane
+// groups 0, 1) and zeros elsewhere, A rows 8..15 the tokens with x at the
+// second block's k (lane groups 2, 3). So D rows 0..7 are single-block
+// partials of one block and rows 8..15 of the other, and each lane scales
+// its four D values by the E4M3 scale of its own block before accumulating
+// in fp32; the weights enter as plain E2M1 values (exact in bf16).
+//
+// x in whole cache lines. A window is 64 k (4 blocks, 128 bytes of x per
+// token). One 16-byte load per lane covers a window for all 8 tokens with
+// every line fully used: lane (i, g) reads token i % 8's piece p of the
+// window, p = g, g + 2 (i < 8: g = 0, 1, 2, 3 -> p = 0, 1, 4, 5) and
+// p = g + 6, g (i >= 8: g = 0, 1, 2, 3 -> p = 6, 7, 2, 3), pieces 2b, 2b+1
+// being block b. Then lanes (t, 0..1) hold block 0 and lanes (t + 8, 2..3)
+// block 1: with the other lanes zeroed this is the A operand of the MFMA
+// that pairs blocks 0 and 1. The other lanes hold blocks 2 and 3 in the
+// places the first MFMA uses, one half-wave away: exchanging the halves
+// (v_permlane32_swap) gives the A operand of the MFMA that pairs blocks 2 and
+// 3. The weights follow the same k order: for the first MFMA of a window
+// lane (n, g) feeds dword g of row n's 32 code bytes of the window, for the
+// second dword 4 + g.
+//
+// Weights in whole cache lines. A slice of a tile is 16 rows x 128 code
+// bytes; it is loaded row-major (eight rows of 128 bytes per load) and
+// transposed through a small per-wavefront LDS buffer, together with its 16
+// rows x 16 scale bytes.
+#include "device.h"
+#include "internal.h"
+
+namespace nvfp4 {
+
+namespace {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+constexpr int kG8Slice = 256;                      // k per slice
+constexpr int kG8Pitch = 144;                      // staged code row: 128 bytes + 16 (bank skew)
+constexpr int kG8StageBytes = 16 * kG8Pitch + 16 * 16;   // codes, then scales
+constexpr int kG8MaxWaves = 16;
+
+__device__ __forceinline__ bf16x8_t g8_e2m1x8(uint32_t w) {
+  const bf16x2_t b0 = e2m1x2_to_bf16<0>(w);
+  const bf16x2_t b1 = e2m1x2_to_bf16<1>(w);
+  const bf16x2_t b2 = e2m1x2_to_bf16<2>(w);
+  const bf16x2_t b3 = e2m1x2_to_bf16<3>(w);
+  bf16x8_t r;
+  r[0] = b0[0]; r[1] = b0[1]; r[2] = b1[0]; r[3] = b1[1];
+  r[4] = b2[0]; r[5] = b2[1]; r[6] = b3[0]; r[7] = b3[1];
+  return r;
+}
+
+__device__ __forceinline__ bf16x8_t g8_bf16x8(u32x4_t v) {
+  bf16x8_t r;
+  __builtin_memcpy(&r, &v, 16);
+  return r;
+}
+
+// u[l ^ 32] in every lane (the two half-waves exchanged)
+__device__ __forceinline__ uint32_t g8_swap_halves(uint32_t u, bool low_half) {
+  const auto p = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  // p[0] = {u[0..31], u[0..31]}, p[1] = {u[32..63], u[32..63]}
+  return low_half ? p[1] : p[0];
+}
+
+// v + (v of lane l + 32) in lanes l < 32
+__device__ __forceinline__ f32x4_t g8_add_upper_half(f32x4_t v) {
+  f32x4_t r;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const uint32_t u = __float_as_uint(v[k]);
+    const auto p = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+    r[k] = v[k] + __uint_as_float(p[1]);
+  }
+  return r;
+}
+
+}  // namespace
+
+// TW tiles of 16 rows per workgroup, S slices per wavefront, up to 16
+// wavefronts (128 registers per lane). codes, scales and x are plain loads:
+// the code is straight-line, so the compiler's waits count exactly.
+template <int M, int TW, int S>
+__global__ __launch_bounds__(64 * kG8MaxWaves) void k_gemv_g8(const SegTable tab,
+                                                              const uint16_t* __restrict__ x,
+                                                              int64_t K) {
+  extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int W = blockDim.x >> 6;
+  const int i = lane & 15, g = lane >> 4;
+  const Seg sg = find_seg(tab, blockIdx.x);
+  const int64_t N = sg.N;
+  const int64_t n0 = sg.unit * (16 * TW);
+  const int64_t kw = (int64_t)w * S * kG8Slice;     // this wavefront's first k
+  const int64_t cb = K >> 1, sbytes = K >> 4;
+  unsigned char* const stage = lds + w * kG8StageBytes;
+  f32x4_t* const red = reinterpret_cast<f32x4_t*>(lds + W * kG8StageBytes);   // [slices][TW][32]
+
+  // ---- issue every load: x first (an L2 round trip, needed by the first
+  // MFMA), then the weights slice by slice, so that the waits before slice s
+  // leave the later slices in flight. Every wavefront has exactly S slices
+  // (W S 256 = K) and every lane loads (tokens >= M read token 0's row and
+  // are zeroed after): the code has no branches, and the scheduling barriers
+  // keep the issue order, so the compiler's wait before each slice counts
+  // only the loads issued before it.
+  u32x4_t q[S][TW][2];
+  uint32_t sc[S][TW];
+  u32x4_t xv[S][4];
+  const int rr = lane >> 3;                          // row-major load: row rr, 16 B at 16 (l % 8)
+  const int t = i & 7;
+  const int piece = i < 8 ? (g < 2 ? g : g + 2) : (g < 2 ? g + 6 : g);
+  const bool tok_ok = t < M;
+  const uint16_t* xp = x + (int64_t)(tok_ok ? t : 0) * K + kw + 8 * piece;
+#pragma unroll
+  for (int s = 0; s < S; ++s)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      xv[s][j] = *reinterpret_cast<const u32x4_t*>(xp + s * kG8Slice + 64 * j);
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int s = 0; s < S; ++s) {
+    const int64_t k0 = kw + (int64_t)s * kG8Slice;
+#pragma unroll
+    for (int u = 0; u < TW; ++u) {
+      const int64_t ra = n0 + 16 * u + rr, rb = ra + 8, rs = n0 + 16 * u + (lane >> 2);
+      const uint8_t* cbase = sg.codes + (k0 >> 1) + 16 * (lane & 7);
+      q[s][u][0] = load_stream(cbase + (ra < N ? ra : N - 1) * cb);
+      q[s][u][1] = load_stream(cbase + (rb < N ? rb : N - 1) * cb);
+      sc[s][u] = *reinterpret_cast<const uint32_t*>(sg.scales + (rs < N ? rs : N - 1) * sbytes +
+                                                     (k0 >> 4) + 4 * (lane & 3));
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+
+  // ---- compute
+  const bool live = (i < 8) == (g < 2);   // lanes of the A operand that carry x
+  const bool low_half = lane < 32;
+  const int sh = g < 2 ? 0 : 8;           // the lane's block: first (0) or second (8) byte
+  // one partial per slice and tile: the workgroup sums the slices in slice
+  // order, so the result does not depend on how K is split over wavefronts
+  f32x4_t acc[S][TW];
+#pragma unroll
+  for (int s = 0; s < S; ++s)
+#pragma unroll
+    for (int u = 0; u < TW; ++u) acc[s][u] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  // the staged codes of row i: dwords g, g + 4, g + 8, ... of the slice row
+  const uint32_t* const st_rd = reinterpret_cast<const uint32_t*>(stage + kG8Pitch * i + 4 * g);
+  const u32x4_t* const st_sc = reinterpret_cast<const u32x4_t*>(stage + 16 * kG8Pitch + 16 * i);
+#pragma unroll
+  for (int s = 0; s < S; ++s) {
+    // the A operands of the slice's 8 MFMAs (two per window): prepared once
+    // per slice when several tiles share them, else window by window
+    u32x4_t a[TW > 1 ? 4 : 1][2];
+    auto prep = [&](int j, u32x4_t (&aj)[2]) {
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const uint32_t v = tok_ok ? xv[s][j][c] : 0u;
+        aj[0][c] = live ? v : 0u;
+        aj[1][c] = g8_swap_halves(live ? 0u : v, low_half);
+      }
+    };
+    if constexpr (TW > 1) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) prep(j, a[j]);
+    }
+#pragma unroll
+    for (int u = 0; u < TW; ++u) {
+      // transpose through the stage: rows rr and rr + 8, then the scales
+      *reinterpret_cast<u32x4_t*>(stage + kG8Pitch * rr + 16 * (lane & 7)) = q[s][u][0];
+      *reinterpret_cast<u32x4_t*>(stage + kG8Pitch * (rr + 8) + 16 * (lane & 7)) = q[s][u][1];
+      *reinterpret_cast<uint32_t*>(stage + 16 * kG8Pitch + 16 * (lane >> 2) + 4 * (lane & 3)) =
+          sc[s][u];
+      uint32_t b[4][2];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        b[j][0] = st_rd[8 * j];
+        b[j][1] = st_rd[8 * j + 4];
+      }
+      const u32x4_t sv = *st_sc;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        u32x4_t aj[2];
+        if constexpr (TW > 1) {
+          aj[0] = a[j][0];
+          aj[1] = a[j][1];
+        } else {
+          prep(j, aj);
+        }
+        // window j's block scales: bytes 4j .. 4j + 3; the lane's first or
+        // second block of each pair
+        const uint32_t sw = sv[j] >> sh;
+        const float s01 = e4m3_to_f32<0>(sw), s23 = e4m3_to_f32<2>(sw);
+        const f32x4_t d0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+            g8_bf16x8(aj[0]), g8_e2m1x8(b[j][0]), f32x4_t{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+        const f32x4_t d1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+            g8_bf16x8(aj[1]), g8_e2m1x8(b[j][1]), f32x4_t{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          acc[s][u][r] = __builtin_fmaf(d0[r], s01, acc[s][u][r]);
+          acc[s][u][r] = __builtin_fmaf(d1[r], s23, acc[s][u][r]);
+        }
+      }
+    }
+  }
+
+  // ---- the slice partials of every tile, summed in slice order
+#pragma unroll
+  for (int s = 0; s < S; ++s)
+#pragma unroll
+    for (int u = 0; u < TW; ++u) {
+      const f32x4_t v = g8_add_upper_half(acc[s][u]);   // lanes l and l + 32: the two blocks
+      if (lane < 32) red[((w * S + s) * TW + u) * 32 + lane] = v;
+    }
+  __syncthreads();
+  const float gs = *sg.gscale;
+  const int slices = W * S;
+  // (tile u, lane pair) entries dealt to the wavefronts: 64 per wavefront
+  for (int e = w * 64 + lane; e < TW * 32; e += W * 64) {
+    const int u = e >> 5, l = e & 31;
+    f32x4_t sum = red[u * 32 + l];
+    for (int v = 1; v < slices; ++v) sum += red[(v * TW + u) * 32 + l];
+    const int64_t n = n0 + 16 * u + (l & 15);
+    if (n < N) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int m = 4 * (l >> 4) + r;   // lane (i, g < 2) held D[4g + r][i]
+        if (m < M) sg.y[(int64_t)m * N + n] = sum[r] * gs;
+      }
+    }
+  }
+}
+
+// Whether S slices per wavefront split K evenly over at most 16 wavefronts.
+static bool g8_split_ok(int64_t K, int S) {
+  if (K <= 0 || (K % kG8Slice) != 0 || S < 1 || S > 4) return false;
+  const int64_t slices = K / kG8Slice;
+  return slices % S == 0 && slices / S <= kG8MaxWaves;
+}
+
+bool g8_applicable(int M, int64_t K) {
+  if (M < 3 || M > NVFP4_MAX_M_SMALL) return false;
+  for (int s = 1; s <= 4; ++s)
+    if (g8_split_ok(K, s)) return true;
+  return false;
+}
+
+// Launch shape, from A/B sweeps (1024 .. 151936 rows at K = 4096 and 12288,
+// M = 5 and 8; each choice within a few percent of the best measured):
+// TW tiles per workgroup so that every CU gets one or two workgroups of
+// TW tiles -- 3 from 768 tiles up (12288 rows: 256 workgroups), 2 from 384 --
+// and for very tall matrices (from 3072 tiles) 2 tiles with 2 slices per
+// wavefront (x read once per 32 rows by half as many wavefronts). S: 2 slices
+// per wavefront where K allows it (fewer, fuller wavefronts), 1 with TW >= 2
+// below 3072 tiles, else the smallest split that fits 16 wavefronts. The
+// summation order does not depend on the shape.
+void g8_shape(int64_t rows, int64_t K, int* TW, int* S, int* W) {
+  const int64_t tiles = (rows + 15) / 16;
+  int tw = 1, s = 0;
+  if (tiles >= 3072 && g8_split_ok(K, 2)) {
+    tw = 2;
+    s = 2;
+  } else if (tiles >= 384 && g8_split_ok(K, 1)) {
+    tw = tiles >= 768 ? 3 : 2;
+    s = 1;
+  } else if (g8_split_ok(K, 2)) {
+    s = 2;
+  } else {
+    for (int c = 1; c <= 4 && !s; ++c)
+      if (g8_split_ok(K, c)) s = c;
+  }
+  *TW = tw;
+  *S = s;
+  *W = s ? (int)(K / kG8Slice / s) : 0;
+}
+
+hipError_t launch_gemv_g8_shape(const SegDesc* d, int n, const uint16_t* x, int M, int64_t K,
+                                int TW, int S, hipStream_t stream) {
+  if (M < 3 || M > NVFP4_MAX_M_SMALL || !g8_split_ok(K, S) || n < 1 || n > kMaxSegments)
+    return hipErrorInvalidValue;
+  const int64_t slices = K / kG8Slice;
+  const int64_t W = slices / S;
+  const SegTable tab = make_seg_table(d, n, 16 * TW);
+  const int64_t units = tab.start[kMaxSegments];
+  if (units > 0x7FFFFFFF) return hipErrorInvalidValue;
+  const size_t lds = (size_t)W * kG8StageBytes + (size_t)slices * TW * 32 * sizeof(f32x4_t);
+#define NVFP4_G8(MM, TT, SS)                                                                 \
+  hipLaunchKernelGGL((k_gemv_g8<MM, TT, SS>), dim3((unsigned)units),                         \
+                     dim3(64 * (unsigned)W), lds, stream, tab, x, K)
+#define NVFP4_G8_TS(MM)                                    \
+  switch (TW * 10 + S) {                                   \
+    case 11: NVFP4_G8(MM, 1, 1); break;                    \
+    case 12: NVFP4_G8(MM, 1, 2); break;                    \
+    case 13: NVFP4_G8(MM, 1, 3); break;                    \
+    case 14: NVFP4_G8(MM, 1, 4); break;                    \
+    case 21: NVFP4_G8(MM, 2, 1); break;                    \
+    case 31: NVFP4_G8(MM, 3, 1); break;                    \
+    case 22: NVFP4_G8(MM, 2, 2); break;                    \
+    default: return hipErrorInvalidValue;                  \
+  }
+  switch (M) {
+    case 3: NVFP4_G8_TS(3); break;
+    case 4: NVFP4_G8_TS(4); break;
+    case 5: NVFP4_G8_TS(5); break;
+    case 6: NVFP4_G8_TS(6); break;
+    case 7: NVFP4_G8_TS(7); break;
+    default: NVFP4_G8_TS(8); break;
+  }
+#undef NVFP4_G8_TS
+#undef NVFP4_G8
+  return hipGetLastError();
+}
+
+hipError_t launch_gemv_g8(const SegDesc* d, int n, const uint16_t* x, int M, int64_t K,
+                          hipStream_t stream) {
+  int64_t rows = 0;
+  for (int k = 0; k < n; ++k) rows += d[k].N;
+  int TW, S, W;
+  g8_shape(rows, K, &TW, &S, &W);
+  return launch_gemv_g8_shape(d, n, x, M, K, TW, S, stream);
+}
+
+}  // namespace nvfp4

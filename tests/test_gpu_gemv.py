@@ -87,6 +87,29 @@ def test_split_k_shapes(M, N, K):
     check_tol(y if rows is None else y[:, rows], y_ref, ad, f"M={M} N={N} K={K}")
 
 
+@pytest.mark.parametrize("M", [3, 5, 8])
+@pytest.mark.parametrize("N,K", [(49157, 2048), (12291, 4096), (6150, 2048), (100, 1024),
+                                 (33, 3840), (300, 12288), (50, 16384)])
+def test_matrix_core_launch_shapes(M, N, K):
+    """Every launch shape of the eight-token matrix-core kernel, each with a
+    ragged last tile: two tiles per workgroup with two slices per wavefront
+    (3073 tiles), three and two tiles with one slice (769 and 385 tiles), one
+    tile with two, one (15 wavefronts), three (K = 12288) and four (K = 16384)
+    slices per wavefront. Large N compares a sample of rows, the last
+    included."""
+    say(f"[gemv] matrix-core shape M={M} N={N} K={K}")
+    codes, scales = workloads.random_nvfp4(16, M, N + K, N, K)
+    x = workloads.x_bf16(16, M, N + K, M, K)
+    g = np.float32(0.027)
+    y = run_gpu(codes, scales, g, x)
+    rows = None
+    if N > 2000:
+        rows = np.unique(np.concatenate([[0, 15, 16, 47, 48, N - 17, N - 16, N - 1],
+                                         np.random.default_rng(N).choice(N, 800, replace=False)]))
+    y_ref, ad = oracle.gemv(codes, scales, g, x, rows=rows)
+    check_tol(y if rows is None else y[:, rows], y_ref, ad, f"M={M} N={N} K={K}")
+
+
 @pytest.mark.parametrize("M", [1, 2, 5, 8])
 def test_subnormal_and_max_scales(M):
     N, K = 200, 1024
