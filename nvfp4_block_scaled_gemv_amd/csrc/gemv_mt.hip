@@ -6,31 +6,49 @@
 //   y[m, n] = g * sum_k e2m1(c[n,k]) * e4m3(s[n, k/16]) * x[m, k]
 //
 // Why a kernel of its own. The M <= 8 kernels put two 16-element blocks
-// side by side in one v_mfma_f32_16x16x32_bf16 (eight tokens per block half)
-// and scale the output by the block scale; that spends the instruction's
-// sixteen A rows on two blocks. With more tokens every A row is a token: the
+// side by side in one MFMA (eight tokens per block half) and scale the
+// output by the block scale. With more tokens every A row is a token: the
 // E4M3 block scale is folded into the weights instead (e2m1 * s has at most
-// 6 significant bits in [2^-10, 2688], so it is exact in bf16), the decode of
-// a weight fragment costs about 2 instructions per weight once, and every
-// group of 16 tokens adds one MFMA per fragment with no per-block work.
+// 6 significant bits in [2^-10, 2688], so it is exact in bf16) and every
+// group of 32 tokens adds one v_mfma_f32_32x32x16_bf16 per decoded weight
+// fragment with no per-block work. The decode (about two instructions per
+// weight) is the vector-ALU cost; a wavefront decodes its weights once for
+// all the token groups it holds.
 //
-// Work split. A workgroup is 4 wavefronts and owns T tiles of 16 weight rows
-// (of one segment) and GW groups of 16 tokens; its wavefronts split K into
-// four contiguous ranges of 128-k steps and meet once, at the end, in LDS
-// (their partial tiles summed in wavefront order: deterministic). The
-// token groups of a row block are separate workgroups on the grid's second
-// dimension, mapped so that all of them go to the same XCD (workgroups are
-// dealt to the 8 XCDs round robin in linear order): the weights they share
-// are read from HBM once and served to the others by that XCD's L2.
+// Work split. A workgroup owns R row tiles of 32 rows (one per "row
+// wavefront") of one segment and G <= 2 groups of 32 tokens; its W k-groups
+// of R wavefronts split K into slices of 256 k, slice W r + j going to
+// k-group j in round r. More tokens than G * 32 take several token blocks
+// (separate workgroups); the token blocks of a row block are mapped to the
+// same XCD (workgroups are dealt to the 8 XCDs round robin in linear order),
+// whose L2 then serves the weights they share. The partial tiles of the W
+// k-groups meet in LDS at the end and are summed in k-group order: the
+// result is bit-reproducible for a given launch shape.
 //
-// Operand mapping of v_mfma_f32_16x16x32_bf16 (lane l, i = l % 16,
-// g = l / 16): A (16 x 32) lane holds A[i][8g .. 8g+7], B (32 x 16) lane
-// holds B[8g .. 8g+7][i], D (16 x 16) lane holds D[4g + r][i], r < 4. Step s
-// covers k in [128 s, 128 s + 128): lane (i, g) loads the 16 code bytes of
-// weight row i at k = 128 s + 32 g (two blocks) and MFMA d (d < 4) takes its
-// dword d, k = 128 s + 32 g + 8 d .. +8, as B; A row t of that MFMA is token
-// t's x at the same k. Lanes whose 32 k lie past K (K % 128 != 0) feed zeros
-// on both sides.
+// Memory access. Every load covers whole 128-byte lines where the data
+// allows: the L1 looks up about one line per clock, so a load whose 64
+// lanes touch 32 lines costs four times one that touches 8. Codes are
+// loaded row-major (eight rows of 128 bytes per load) and transposed
+// through a per-wavefront LDS stage; x is loaded by the k-group's threads in
+// whole lines (16 threads per token) into a shared, swizzled LDS buffer that
+// the R row wavefronts read as MFMA A fragments. All loads are bounded
+// buffer loads: rows past N and tokens past M lie past their buffer's bound
+// and read as zeros without touching memory, and pieces past K are sent
+// past it, so nothing is clamped or masked afterwards. x is loaded two
+// halves of a slice ahead (two register sets, two LDS buffers, one barrier
+// per half), the weights one slice ahead, in the order x, weights, x: each
+// wait for x then leaves the newer weight loads in flight. Nothing loaded
+// is used (not even by a select) before it is needed, which would make the
+// wave wait early.
+//
+// Operand mapping (v_mfma_f32_32x32x16_bf16, lane l, n = l % 32,
+// h = l / 32: A lane holds A[n][8h .. 8h+7], B lane holds B[8h .. 8h+7][n],
+// D lane holds D[8(r/4) + 4h + r%4][n] in register r). Within a slice, half
+// h of the MFMA k covers k = 128 h .. 128 h + 127: step s of quarter c reads
+// k = 128 h + 32 c + 8 s .. + 7. So a lane's B words for quarter c are 16
+// staged code bytes of its row (64 h + 16 c), and its scale bytes for the
+// slice are the 8 blocks 8 h .. 8 h + 7 of its row; token t's x for the
+// same step sits at the same k.
 #include "device.h"
 #include "internal.h"
 
@@ -39,9 +57,14 @@ namespace nvfp4 {
 namespace {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
-typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
-constexpr int kMtWaves = 4;
+constexpr int kMtSlice = 256;          // k per slice
+constexpr int kMtTokBytes = 256;       // staged x of one token for half a slice (128 k)
+constexpr int kMtWPitch = 144;         // staged code row: 128 + 16 bytes
+constexpr int kMtWStage = 32 * kMtWPitch;
+constexpr int kMtMaxWaves = 8;         // two per SIMD, 256 registers each
+constexpr int64_t kMtLdsMax = 80 * 1024;   // two workgroups per CU
 
 // bf16x8 of the 8 E2M1 codes of `word` times the block scale s: exact (the
 // products have at most 6 significant bits and lie in bf16's range).
@@ -66,175 +89,336 @@ __device__ __forceinline__ bf16x8_t mt_bf16x8(u32x4_t v) {
   return r;
 }
 
-// The weights of one step for T tiles: lane (i, g)'s 16 code bytes and its
-// two scale bytes (first block in bits 7..0) per tile.
-template <int T>
-struct MtWeights {
-  u32x4_t q[T];
-  uint32_t s[T];
+// A wavefront's weights for one slice as loaded: 32 rows x 128 code bytes
+// row-major (q[i]: row 8 i + l / 8, bytes 16 (l % 8) .. + 15) and the lane's
+// 8 scale bytes (row l % 32, blocks 8 h .. 8 h + 7 of the slice: one 8-byte
+// load, or four 2-byte loads).
+struct MtW {
+  u32x4_t q[4];
+  uint32_t s[4];
 };
+
+// Buffer loads with a byte bound: past it they return zeros and touch no
+// memory. kMtOob is an offset past every bound used here.
+constexpr int kMtOob = 0x7FFFFFF0;
+constexpr uint32_t kMtMaxRecords = 0x7FFFFF00u;
+constexpr int kMtNt = 2;   // cache policy: non-temporal (streamed weights)
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t mt_rsrc(const void* p, int64_t bytes) {
+  const int64_t n = bytes <= 0 ? 0 : (bytes < (int64_t)kMtMaxRecords ? bytes : (int64_t)kMtMaxRecords);
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)n, 0x00020000);
+}
+template <int AUX>
+__device__ __forceinline__ u32x4_t mt_load16(__amdgpu_buffer_rsrc_t r, int off) {
+  return __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, AUX));
+}
 
 }  // namespace
 
-template <int T, int GW>
-__global__ __launch_bounds__(64 * kMtWaves) void k_gemv_mt(const SegTable tab,
-                                                           const uint16_t* __restrict__ x,
-                                                           int M, int64_t K, int64_t units,
-                                                           int groups) {
-  // blockIdx.x -> (row block, token group): the groups of a row block share
-  // the XCD that blockIdx.x % 8 selects
+// KA: K % 128 == 0, so a lane's 8 scale bytes of a slice are one aligned
+// 8-byte load that lies wholly inside or wholly outside K; else four 2-byte
+// loads (rows start 2-byte aligned).
+template <int G, int R, bool KA>
+__global__ __launch_bounds__(64 * kMtMaxWaves) void k_gemv_mt(const SegTable tab,
+                                                              const uint16_t* __restrict__ x,
+                                                              int M, int64_t K, int64_t units,
+                                                              int tblocks, int W) {
+  static_assert((8 * G) % R == 0, "x staging: whole 16-byte pieces per thread");
+  constexpr int P = 8 * G / R;                   // staged pieces per thread per half slice
+  constexpr int kBuf = G * 32 * kMtTokBytes;     // half a slice of x for G * 32 tokens
+
+  // blockIdx.x -> (row block, token block): the token blocks of a row block
+  // share the XCD that blockIdx.x % 8 selects
   const int64_t b = blockIdx.x;
-  const int64_t per = 8 * (int64_t)groups;
+  const int64_t per = 8 * (int64_t)tblocks;
   const int64_t unit = (b / per) * 8 + (b % 8);
-  const int grp = (int)((b % per) / 8);
+  const int tb = (int)((b % per) / 8);
   if (unit >= units) return;   // the same for the whole workgroup
   const Seg sg = find_seg(tab, unit);
-  const uint8_t* __restrict__ codes = sg.codes;
-  const uint8_t* __restrict__ scales = sg.scales;
   const int64_t N = sg.N;
 
-  extern __shared__ __attribute__((aligned(16))) f32x4_t red[];   // [W][T][GW][64]
+  extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int i = lane & 15, g = lane >> 4;
-  const int64_t n0 = sg.unit * (16 * T);
+  const int rw = w % R, kg = w / R;
+  const int n = lane & 31, h = lane >> 5;
+  const int64_t n0 = sg.unit * (32 * R) + 32 * rw;
+  const int tok0 = tb * G * 32;
   const int64_t cb = K >> 1, sbytes = K >> 4;
-  const int64_t S = (K + 127) >> 7;                 // 128-k steps
-  const int64_t s0 = S * w / kMtWaves, s1 = S * (w + 1) / kMtWaves;
-  const int tok0 = grp * 16 * GW;
+  const int64_t slices = (K + kMtSlice - 1) / kMtSlice;
+  const int64_t rounds = (slices + W - 1) / W;
+  unsigned char* const xbuf = lds + kg * 2 * kBuf;
+  unsigned char* const stage = lds + (int64_t)W * 2 * kBuf + w * kMtWStage;
 
-  // this lane's weight rows (a ragged last tile re-reads row N - 1; its
-  // outputs are not stored) and token rows (tokens >= M feed zeros)
-  const uint8_t* cp[T];
-  const uint8_t* sp[T];
+  // Every load is a bounded buffer load, issued unconditionally: rows past N
+  // and tokens past M lie past the bound of their buffer and read as zeros,
+  // and pieces past K are sent past it. Codes go row-major (eight whole
+  // 128-byte lines per load) through the wavefront's LDS stage; each lane
+  // loads its own scale bytes.
+  const __amdgpu_buffer_rsrc_t rc = mt_rsrc(sg.codes + n0 * cb, (N - n0) * cb);
+  const __amdgpu_buffer_rsrc_t rs = mt_rsrc(sg.scales + n0 * sbytes, (N - n0) * sbytes);
+  const __amdgpu_buffer_rsrc_t rx = mt_rsrc(x, (int64_t)M * K * 2);
+  int coff[4];
 #pragma unroll
-  for (int u = 0; u < T; ++u) {
-    const int64_t n = n0 + 16 * u + i;
-    const int64_t row = n < N ? n : N - 1;
-    cp[u] = codes + row * cb + 16 * g;
-    sp[u] = scales + row * sbytes + 2 * g;
+  for (int i = 0; i < 4; ++i) coff[i] = (int)((8 * i + (lane >> 3)) * cb) + 16 * (lane & 7);
+  const int soff = (int)(n * sbytes) + 8 * h;
+  auto load_w = [&](int64_t sl, MtW& wt) {
+    const int64_t k0 = sl * kMtSlice;
+    const bool cok = sl < slices && k0 + 32 * (lane & 7) < K;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) wt.q[i] = mt_load16<kMtNt>(rc, cok ? coff[i] + (int)(k0 >> 1) : kMtOob);
+    if (KA) {
+      const bool v = sl < slices && k0 + 128 * h < K;
+      const uint2 sv = __builtin_bit_cast(
+          uint2, __builtin_amdgcn_raw_buffer_load_b64(rs, v ? soff + (int)(k0 >> 4) : kMtOob, 0, 0));
+      wt.s[0] = sv.x;
+      wt.s[1] = sv.y;
+    } else {
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const bool v = sl < slices && k0 + 128 * h + 32 * c < K;
+        wt.s[c] = __builtin_amdgcn_raw_buffer_load_b16(rs, v ? soff + (int)(k0 >> 4) + 2 * c : kMtOob,
+                                                       0, 0);
+      }
+    }
+  };
+  // the lane's scale bytes of quarters 2 d and 2 d + 1 (one word)
+  auto scale_word = [&](const MtW& wt, int d) -> uint32_t {
+    if (KA) return wt.s[d];
+    return wt.s[2 * d] | (wt.s[2 * d + 1] << 16);
+  };
+  auto store_w = [&](const MtW& wt) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      *reinterpret_cast<u32x4_t*>(stage + (8 * i + (lane >> 3)) * kMtWPitch + 16 * (lane & 7)) =
+          wt.q[i];
+  };
+
+  // x staging: piece e = (thread of the k-group) + 64 R p is token e / 16,
+  // 16-byte chunk j = e % 16 (quarter j / 8 of the half, MFMA half j / 4 % 2,
+  // step j % 4); it goes to LDS byte 256 t + 16 (j ^ (t % 16)). The 16
+  // threads of a token read two whole 128-byte lines.
+  const int tk = rw * 64 + lane;
+  int xsrc[P];
+  int xdst[P];
+  int xk[P];
+#pragma unroll
+  for (int p = 0; p < P; ++p) {
+    const int e = tk + 64 * R * p;
+    const int tt = e >> 4, j = e & 15;
+    xk[p] = 128 * ((j >> 2) & 1) + 32 * (j >> 3);
+    xsrc[p] = (int)((tok0 + tt) * K + xk[p] + 8 * (j & 3)) * 2;
+    xdst[p] = tt * kMtTokBytes + ((j ^ (tt & 15)) << 4);
   }
-  const uint16_t* xp[GW];
-  bool xok[GW];
+  struct XStage {
+    u32x4_t v[P];
+  };
+  // half e of slice sl: quarters 2 e and 2 e + 1
+  auto stage_load = [&](int64_t sl, int e, XStage& xs) {
+    const int64_t k0 = sl * kMtSlice + 64 * e;
 #pragma unroll
-  for (int q = 0; q < GW; ++q) {
-    const int t = tok0 + 16 * q + i;
-    xok[q] = t < M;
-    xp[q] = x + (int64_t)(xok[q] ? t : 0) * K + 32 * g;
-  }
+    for (int p = 0; p < P; ++p) {
+      const bool v = sl < slices && k0 + xk[p] < K;
+      xs.v[p] = mt_load16<0>(rx, v ? xsrc[p] + (int)(k0 * 2) : kMtOob);
+    }
+  };
+  auto stage_store = [&](const XStage& xs, unsigned char* buf) {
+#pragma unroll
+    for (int p = 0; p < P; ++p) *reinterpret_cast<u32x4_t*>(buf + xdst[p]) = xs.v[p];
+  };
 
-  f32x4_t acc[T][GW];
+  // the A fragment of group q, quarter c of a half, step s: token 32 q + n,
+  // chunk 8 c + 4 h + s
+  int xrd[2][4];
 #pragma unroll
-  for (int u = 0; u < T; ++u)
+  for (int c = 0; c < 2; ++c)
 #pragma unroll
-    for (int q = 0; q < GW; ++q) acc[u][q] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int s = 0; s < 4; ++s)
+      xrd[c][s] = n * kMtTokBytes + (((8 * c + 4 * h + s) ^ (n & 15)) << 4);
+  // the B words of quarter c: row n, code bytes 64 h + 16 c .. + 15
+  const unsigned char* const wrd = stage + n * kMtWPitch + 64 * h;
 
-  // the weights of step s (zeros for a lane whose 32 k lie past K)
-  auto load_w = [&](int64_t s, MtWeights<T>& wt) {
-    const bool ok = 128 * s + 32 * g < K;
+  f32x16_t acc[G];
 #pragma unroll
-    for (int u = 0; u < T; ++u) {
-      if (ok) {
-        wt.q[u] = load_stream(cp[u] + 64 * s);
-        wt.s[u] = *reinterpret_cast<const uint16_t*>(sp[u] + 8 * s);
-      } else {
-        wt.q[u] = u32x4_t{0u, 0u, 0u, 0u};
-        wt.s[u] = 0u;
+  for (int q = 0; q < G; ++q)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) acc[q][i] = 0.f;
+
+  // half e of the slice from x buffer buf and the staged codes
+  auto compute = [&](const MtW& wt, const unsigned char* buf, int e) {
+    const uint32_t sw = scale_word(wt, e);
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      const int cq = 2 * e + c;
+      // the quarter's operands first, so that the LDS reads overlap
+      const u32x4_t bq = *reinterpret_cast<const u32x4_t*>(wrd + 16 * cq);
+      u32x4_t a[4][G];
+#pragma unroll
+      for (int s = 0; s < 4; ++s)
+#pragma unroll
+        for (int q = 0; q < G; ++q)
+          a[s][q] = *reinterpret_cast<const u32x4_t*>(buf + q * 32 * kMtTokBytes + xrd[c][s]);
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        // block 8 h + 2 cq + s / 2 of the slice: byte (2 cq + s / 2) % 4 of sw
+        const float sc = ((2 * cq + (s >> 1)) & 3) == 0   ? e4m3_to_f32<0>(sw)
+                         : ((2 * cq + (s >> 1)) & 3) == 1 ? e4m3_to_f32<1>(sw)
+                         : ((2 * cq + (s >> 1)) & 3) == 2 ? e4m3_to_f32<2>(sw)
+                                                           : e4m3_to_f32<3>(sw);
+        const bf16x8_t bw = mt_decode8(bq[s], sc);
+#pragma unroll
+        for (int q = 0; q < G; ++q)
+          acc[q] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(mt_bf16x8(a[s][q]), bw, acc[q], 0, 0, 0);
       }
     }
   };
 
-  if (s0 < s1) {
-    MtWeights<T> cur, nxt;
-    load_w(s0, cur);
-    for (int64_t s = s0; s < s1; ++s) {
-      if (s + 1 < s1) load_w(s + 1, nxt);
-      const bool ok = 128 * s + 32 * g < K;
-      // A operands: 64 bytes of each token row at k = 128 s + 32 g
-      u32x4_t xa[GW][4];
-#pragma unroll
-      for (int q = 0; q < GW; ++q) {
-        const u32x4_t* p = reinterpret_cast<const u32x4_t*>(xp[q] + 128 * s);
-#pragma unroll
-        for (int d = 0; d < 4; ++d)
-          xa[q][d] = (ok && xok[q]) ? p[d] : u32x4_t{0u, 0u, 0u, 0u};
-      }
-#pragma unroll
-      for (int d = 0; d < 4; ++d) {
-        bf16x8_t bw[T];
-#pragma unroll
-        for (int u = 0; u < T; ++u) {
-          const float sc = d < 2 ? e4m3_to_f32<0>(cur.s[u]) : e4m3_to_f32<1>(cur.s[u]);
-          const uint32_t word = d == 0 ? cur.q[u].x : d == 1 ? cur.q[u].y
-                              : d == 2 ? cur.q[u].z : cur.q[u].w;
-          bw[u] = mt_decode8(word, sc);
-        }
-#pragma unroll
-        for (int q = 0; q < GW; ++q)
-#pragma unroll
-          for (int u = 0; u < T; ++u)
-            acc[u][q] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(mt_bf16x8(xa[q][d]), bw[u],
-                                                                acc[u][q], 0, 0, 0);
-      }
-      if (s + 1 < s1) cur = nxt;
-    }
+  // x is loaded two halves ahead of its use (two sets of registers, two LDS
+  // buffers), the weights one slice ahead. Per round the loads go out in the
+  // order x, weights, x, so that each wait for x leaves the newer loads in
+  // flight.
+  unsigned char* const buf0 = xbuf;
+  unsigned char* const buf1 = xbuf + kBuf;
+  MtW wc, wn;
+  XStage xa, xb;
+  load_w(kg, wc);
+  stage_load(kg, 0, xb);
+  stage_load(kg, 1, xa);
+  stage_store(xb, buf0);
+  __syncthreads();
+  for (int64_t r = 0; r < rounds; ++r) {
+    const int64_t sl = r * W + kg;
+    store_w(wc);
+    // first half (x in buf0, the second half's x in xa)
+    stage_load(sl + W, 0, xb);
+    load_w(sl + W, wn);
+    __builtin_amdgcn_sched_barrier(0);
+    compute(wc, buf0, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    stage_store(xa, buf1);
+    __syncthreads();
+    // second half (x in buf1, the next slice's first half in xb)
+    stage_load(sl + W, 1, xa);
+    __builtin_amdgcn_sched_barrier(0);
+    compute(wc, buf1, 1);
+    __builtin_amdgcn_sched_barrier(0);
+    stage_store(xb, buf0);
+    __syncthreads();
+    wc = wn;
   }
 
-  // the four wavefronts' partial tiles, summed in wavefront order
+  // the k-groups' partial tiles, summed in k-group order by k-group 0 (the
+  // loop's last barrier has freed the x buffers and stages)
+  if (W > 1) {
+    float* const red = reinterpret_cast<float*>(lds);   // [W - 1][R][G][16][64]
+    if (kg > 0) {
 #pragma unroll
-  for (int u = 0; u < T; ++u)
+      for (int q = 0; q < G; ++q)
 #pragma unroll
-    for (int q = 0; q < GW; ++q) red[((w * T + u) * GW + q) * 64 + lane] = acc[u][q];
-  __syncthreads();
-  const float gs = *sg.gscale;
-  // pair p = (u, q) is summed and stored by wavefront p % 4
-#pragma unroll
-  for (int p = 0; p < T * GW; ++p) {
-    if (p % kMtWaves != w) continue;
-    const int u = p / GW, q = p % GW;
-    f32x4_t sum = red[((0 * T + u) * GW + q) * 64 + lane];
-#pragma unroll
-    for (int v = 1; v < kMtWaves; ++v) sum += red[((v * T + u) * GW + q) * 64 + lane];
-    const int64_t n = n0 + 16 * u + i;
-    if (n < N) {
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int m = tok0 + 16 * q + 4 * g + r;   // lane (i, g) holds D[4g + r][i]
-        if (m < M) sg.y[(int64_t)m * N + n] = sum[r] * gs;
-      }
+        for (int i = 0; i < 16; ++i)
+          red[((((kg - 1) * R + rw) * G + q) * 16 + i) * 64 + lane] = acc[q][i];
     }
+    __syncthreads();
+    if (kg == 0) {
+      for (int v = 1; v < W; ++v)
+#pragma unroll
+        for (int q = 0; q < G; ++q)
+#pragma unroll
+          for (int i = 0; i < 16; ++i)
+            acc[q][i] += red[((((v - 1) * R + rw) * G + q) * 16 + i) * 64 + lane];
+    }
+  }
+  if (kg == 0 && n0 + n < N) {
+    const float gs = *sg.gscale;
+#pragma unroll
+    for (int q = 0; q < G; ++q)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int m = tok0 + 32 * q + 8 * (i >> 2) + 4 * h + (i & 3);
+        if (m < M) sg.y[(int64_t)m * N + n0 + n] = acc[q][i] * gs;
+      }
   }
 }
 
 bool mt_applicable(int M) { return M > NVFP4_MAX_M_SMALL && M <= NVFP4_MAX_M_INTERNAL; }
 
-// Launch shape: token groups of 16 per workgroup GW (1 up to 32 tokens,
-// 2 above) and tiles per workgroup T (2 when the matrices give at least 8
-// workgroups per CU that way, else 1).
-hipError_t launch_gemv_mt(const SegDesc* d, int n, const uint16_t* x, int M, int64_t K,
-                          hipStream_t stream) {
-  if (!mt_applicable(M) || n < 1 || n > kMaxSegments) return hipErrorInvalidValue;
-  const int GW = M <= 32 ? 1 : 2;
-  const int groups = (M + 16 * GW - 1) / (16 * GW);
-  int64_t rows = 0;
-  for (int s = 0; s < n; ++s) rows += d[s].N;
-  const int T = (rows / 32) * groups >= 8 * 256 ? 2 : 1;
-  const SegTable tab = make_seg_table(d, n, 16 * T);
+int64_t mt_lds_bytes(const MtShape& sh) {
+  const int64_t xb = (int64_t)2 * sh.W * sh.G * 32 * kMtTokBytes + (int64_t)sh.R * sh.W * kMtWStage;
+  const int64_t rb = (int64_t)(sh.W - 1) * sh.R * sh.G * 16 * 64 * 4;
+  return xb > rb ? xb : rb;
+}
+
+MtShape mt_shape(const SegDesc* d, int n, int M, int64_t K) {
+  auto units = [&](int rows) {
+    int64_t u = 0;
+    for (int s = 0; s < n; ++s) u += (d[s].N + rows - 1) / rows;
+    return u;
+  };
+  // Chosen from measured launch-shape sweeps on the stress (12288 x 4096,
+  // 4096 x 12288) and LM-head (151936 x 4096) matrices at 16 and 128 tokens.
+  MtShape sh;
+  const int mg = (M + 31) / 32;
+  // two token groups per workgroup (one decode for both) when the row
+  // blocks of 128 rows still number 192 or more in all, else one
+  sh.G = mg >= 2 && units(128) * ((mg + 1) / 2) >= 192 ? 2 : 1;
+  sh.tblocks = (mg + sh.G - 1) / sh.G;
+  // row wavefronts sharing each staged piece of x: as many as leave 192
+  // workgroups
+  sh.R = units(128) * sh.tblocks >= 192 ? 4 : (units(64) * sh.tblocks >= 192 ? 2 : 1);
+  // k-groups: one with two token groups, else two (three with one row
+  // wavefront), no more than there are slices, within the LDS budget
+  const int64_t slices = (K + kMtSlice - 1) / kMtSlice;
+  const int64_t W = sh.G == 2 ? 1 : (sh.R == 1 ? 3 : 2);
+  sh.W = (int)(W > slices ? slices : W);
+  while (sh.W > 1 && mt_lds_bytes(sh) > kMtLdsMax) --sh.W;
+  return sh;
+}
+
+hipError_t launch_gemv_mt_shape(const SegDesc* d, int n, const uint16_t* x, int M, int64_t K,
+                                const MtShape& sh, hipStream_t stream) {
+  if (!mt_applicable(M) || n < 1 || n > kMaxSegments || K <= 0) return hipErrorInvalidValue;
+  // buffer offsets are 32-bit: the x of a token block and 32 rows of codes
+  // stay far below the bound
+  if (K > (1 << 20)) return hipErrorInvalidValue;
+  if (sh.G < 1 || sh.G > 2 || (sh.R != 1 && sh.R != 2 && sh.R != 4) || (sh.G == 2 && sh.R == 1) ||
+      sh.W < 1 || sh.R * sh.W > kMtMaxWaves || sh.tblocks < 1 ||
+      (int64_t)sh.tblocks * sh.G * 32 < M || mt_lds_bytes(sh) > kMtLdsMax)
+    return hipErrorInvalidValue;
+  const SegTable tab = make_seg_table(d, n, 32 * sh.R);
   const int64_t units = tab.start[kMaxSegments];
+  if (units == 0) return hipSuccess;
   // whole multiples of 8 units so that the XCD mapping stays a bijection
-  const int64_t grid = ((units + 7) / 8) * 8 * groups;
+  const int64_t grid = ((units + 7) / 8) * 8 * sh.tblocks;
   if (grid > 0x7FFFFFFF) return hipErrorInvalidValue;
-  const size_t lds = (size_t)kMtWaves * T * GW * 64 * sizeof(f32x4_t);
-#define NVFP4_MT(TT, GG)                                                                    \
-  hipLaunchKernelGGL((k_gemv_mt<TT, GG>), dim3((unsigned)grid), dim3(64 * kMtWaves), lds, \
-                     stream, tab, x, M, K, units, groups)
-  if (T == 2) {
-    if (GW == 1) NVFP4_MT(2, 1); else NVFP4_MT(2, 2);
-  } else {
-    if (GW == 1) NVFP4_MT(1, 1); else NVFP4_MT(1, 2);
+  const size_t lds = (size_t)mt_lds_bytes(sh);
+  const bool ka = K % 128 == 0;
+#define NVFP4_MT(GG, RR)                                                                      \
+  do {                                                                                        \
+    if (ka)                                                                                   \
+      hipLaunchKernelGGL((k_gemv_mt<GG, RR, true>), dim3((unsigned)grid),                     \
+                         dim3(64 * sh.R * sh.W), lds, stream, tab, x, M, K, units, sh.tblocks, \
+                         sh.W);                                                               \
+    else                                                                                      \
+      hipLaunchKernelGGL((k_gemv_mt<GG, RR, false>), dim3((unsigned)grid),                    \
+                         dim3(64 * sh.R * sh.W), lds, stream, tab, x, M, K, units, sh.tblocks, \
+                         sh.W);                                                               \
+  } while (0)
+  switch (sh.G * 10 + sh.R) {
+    case 11: NVFP4_MT(1, 1); break;
+    case 12: NVFP4_MT(1, 2); break;
+    case 14: NVFP4_MT(1, 4); break;
+    case 22: NVFP4_MT(2, 2); break;
+    case 24: NVFP4_MT(2, 4); break;
+    default: return hipErrorInvalidValue;
   }
 #undef NVFP4_MT
   return hipGetLastError();
+}
+
+hipError_t launch_gemv_mt(const SegDesc* d, int n, const uint16_t* x, int M, int64_t K,
+                          hipStream_t stream) {
+  if (!mt_applicable(M) || n < 1 || n > kMaxSegments || K <= 0) return hipErrorInvalidValue;
+  return launch_gemv_mt_shape(d, n, x, M, K, mt_shape(d, n, M, K), stream);
 }
 
 }  // namespace nvfp4

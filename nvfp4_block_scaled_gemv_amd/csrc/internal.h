@@ -44,8 +44,18 @@ hipError_t launch_gemv_g8(const SegDesc* d, int n, const uint16_t* x, int M, int
                           hipStream_t stream);
 hipError_t launch_gemv_g8_shape(const SegDesc* d, int n, const uint16_t* x, int M, int64_t K,
                                 int TW, int S, hipStream_t stream);
+// 9 <= M <= 128 (gemv_mt.hip): G token groups of 32 per workgroup in
+// `tblocks` token blocks, R row wavefronts of 32 rows sharing staged x, W
+// k-groups splitting K; mt_shape picks one from the rows, M and K.
+struct MtShape {
+  int G, tblocks, R, W;
+};
+MtShape mt_shape(const SegDesc* d, int n, int M, int64_t K);
+int64_t mt_lds_bytes(const MtShape& sh);
 hipError_t launch_gemv_mt(const SegDesc* d, int n, const uint16_t* x, int M, int64_t K,
                           hipStream_t stream);
+hipError_t launch_gemv_mt_shape(const SegDesc* d, int n, const uint16_t* x, int M, int64_t K,
+                                const MtShape& sh, hipStream_t stream);
 hipError_t launch_gemv_mfma(const SegDesc* d, int n, const uint16_t* x, int M, int64_t K,
                             hipStream_t stream);
 bool splitk_applicable(int M, int64_t K);
