@@ -22,8 +22,11 @@
  * Conventions for every entry point:
  *  - every pointer is a DEVICE pointer of the current HIP device; arrays are
  *    row-major and contiguous; the caller owns (allocates and frees) every
- *    buffer. The library allocates no device memory; its only mutable
- *    global state is the per-thread text of nvfp4_last_error().
+ *    buffer. The library allocates no device memory. Its mutable global
+ *    state: the per-thread text of nvfp4_last_error(), the fixed array of
+ *    nvfp4_moe_gemv_noalloc, one fault word per device (see
+ *    nvfp4_check_device_faults) and the wait bound of
+ *    nvfp4_debug_set_wait_limit.
  *  - shapes are checked on the host before anything is launched; on a failed
  *    check nothing is launched, the call returns the error code and
  *    nvfp4_last_error() describes it. Device data (ids, scales, the tensor
@@ -56,7 +59,7 @@
 extern "C" {
 #endif
 
-#define NVFP4_ABI_VERSION 8
+#define NVFP4_ABI_VERSION 9
 
 /* Largest number of activation rows (tokens) one dense GEMV call takes (the
    blueprint's "multi_seq" plan arm: 2 to 128 rows). */
@@ -72,6 +75,10 @@ extern "C" {
 #define NVFP4_MAX_N (1LL << 30)
 /* Largest MoE hidden size H per call. */
 #define NVFP4_MOE_MAX_H (1 << 24)
+/* Largest K (inputs per row) of one dense or W4A4 GEMV call: the many-token
+   kernel addresses a token block's x and a row tile's codes with 32-bit
+   offsets. */
+#define NVFP4_MAX_K (1LL << 20)
 
 typedef enum nvfp4_status {
   NVFP4_OK = 0,
@@ -482,6 +489,31 @@ nvfp4_status nvfp4_moe_gemv_noalloc(const uint8_t* w13_codes, const uint8_t* w13
  */
 nvfp4_status nvfp4_stream_read(const void* buf, size_t bytes, uint32_t* sink,
                                hipStream_t stream);
+
+/*
+ * nvfp4_check_device_faults -- diagnostic: waits for `stream`, then reads and
+ * clears the current device's fault word. A kernel sets it when it gives up
+ * a bounded internal wait: the split-K GEMV (3 <= M <= 8, K a multiple of 256
+ * that the 16-wavefront kernel cannot split) sums a tile's partials once all
+ * wavefronts of its workgroup have delivered them, and a wavefront that is
+ * four tiles ahead waits for a free slot; after about 4M polls it records
+ * the fault and delivers a NaN partial. The results of a call that set the
+ * fault are invalid (tiles summed from that partial hold NaN; others may be
+ * wrong without showing it). Not seen in normal operation. Synchronises
+ * the stream; not for use under graph capture.
+ * Returns NVFP4_OK, or NVFP4_ERR_HIP (also on a HIP failure) with
+ * nvfp4_last_error() naming the fault.
+ */
+nvfp4_status nvfp4_check_device_faults(hipStream_t stream);
+
+/*
+ * nvfp4_debug_set_wait_limit -- test hook: the number of polls after which
+ * the split-K slot wait gives up (0 restores the default of 1 << 22; a
+ * negative value makes every tile give up at once, to exercise the fault
+ * path). Process-wide and not synchronised with other host threads; applies
+ * to launches made after the call.
+ */
+void nvfp4_debug_set_wait_limit(int polls);
 
 #ifdef __cplusplus
 }

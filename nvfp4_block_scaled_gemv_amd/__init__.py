@@ -35,11 +35,12 @@ LIB_PATH = os.path.join(_HERE, "libnvfp4_gemv.so")
 HEADER_PATH = os.path.join(os.path.dirname(_HERE), "include", "nvfp4_gemv.h")
 
 # The size limits of include/nvfp4_gemv.h (NVFP4_MAX_M, NVFP4_MOE_MAX_M,
-# NVFP4_MAX_TOPK, NVFP4_MAX_N, NVFP4_MOE_MAX_I, NVFP4_MOE_MAX_H).
+# NVFP4_MAX_TOPK, NVFP4_MAX_N, NVFP4_MAX_K, NVFP4_MOE_MAX_I, NVFP4_MOE_MAX_H).
 MAX_M = 128
 MOE_MAX_M = 8
 MAX_TOPK = 16
 MAX_N = 1 << 30
+MAX_K = 1 << 20
 MOE_MAX_I = 1 << 24
 MOE_MAX_H = 1 << 24
 # NVFP4_NOALLOC_SCRATCH_BYTES: the device array of nvfp4_moe_gemv_noalloc.
@@ -126,6 +127,10 @@ def lib() -> ctypes.CDLL:
         L.nvfp4_moe_gemv_noalloc.argtypes = [_VP] * 9 + [_I64] * 5 + [_VP, _VP]
         L.nvfp4_stream_read.restype = ctypes.c_int
         L.nvfp4_stream_read.argtypes = [_VP, ctypes.c_size_t, _VP, _VP]
+        L.nvfp4_check_device_faults.restype = ctypes.c_int
+        L.nvfp4_check_device_faults.argtypes = [_VP]
+        L.nvfp4_debug_set_wait_limit.restype = None
+        L.nvfp4_debug_set_wait_limit.argtypes = [ctypes.c_int]
         _lib = L
     return _lib
 
@@ -220,6 +225,22 @@ def stream_read(buf: torch.Tensor, sink: torch.Tensor, nbytes: int | None = None
     _dev(buf, sink)
     n = buf.numel() * buf.element_size() if nbytes is None else int(nbytes)
     _check("nvfp4_stream_read", lib().nvfp4_stream_read(_p(buf), n, _p(sink), _stream(buf)))
+
+
+# ------------------------------------------------------------ diagnostics
+
+def check_device_faults(stream=None) -> None:
+    """Wait for `stream` (default: torch's current stream) and raise if a
+    kernel gave up a bounded internal wait since the last check (the fault
+    word is cleared by the read)."""
+    s = torch.cuda.current_stream() if stream is None else stream
+    _check("nvfp4_check_device_faults", lib().nvfp4_check_device_faults(s.cuda_stream))
+
+
+def debug_set_wait_limit(polls: int) -> None:
+    """Test hook: polls before the split-K slot wait gives up (0: default,
+    negative: give up at once)."""
+    lib().nvfp4_debug_set_wait_limit(int(polls))
 
 
 # ------------------------------------------------------------------ gemv

@@ -114,9 +114,11 @@ nvfp4_status nvfp4_gemv(const uint8_t* codes, const uint8_t* scales, const float
   if (M < 0 || N < 0 || K < 0 || (K % 32) != 0)
     return fail(NVFP4_ERR_SHAPE, "nvfp4_gemv: need M, N, K >= 0 and K %% 32 == 0 (M=%lld N=%lld K=%lld)",
                 (long long)M, (long long)N, (long long)K);
-  if (M > NVFP4_MAX_M || N > NVFP4_MAX_N)
-    return fail(NVFP4_ERR_UNSUPPORTED, "nvfp4_gemv: M=%lld (max %d), N=%lld (max %lld)",
-                (long long)M, NVFP4_MAX_M, (long long)N, (long long)NVFP4_MAX_N);
+  if (M > NVFP4_MAX_M || N > NVFP4_MAX_N || K > NVFP4_MAX_K)
+    return fail(NVFP4_ERR_UNSUPPORTED,
+                "nvfp4_gemv: M=%lld (max %d), N=%lld (max %lld), K=%lld (max %lld)",
+                (long long)M, NVFP4_MAX_M, (long long)N, (long long)NVFP4_MAX_N, (long long)K,
+                (long long)NVFP4_MAX_K);
   if (M == 0 || N == 0) return NVFP4_OK;
   if (!y) return fail(NVFP4_ERR_NULL, "nvfp4_gemv: y is NULL");
   if (!aligned(y, 4)) return fail(NVFP4_ERR_ALIGN, "nvfp4_gemv: y must be 4-byte aligned");
@@ -143,10 +145,11 @@ nvfp4_status nvfp4_gemv_segments(const nvfp4_gemv_segment* segs, int64_t n_segme
                 "nvfp4_gemv_segments: need n_segments, M, K >= 0 and K %% 32 == 0 "
                 "(n=%lld M=%lld K=%lld)",
                 (long long)n_segments, (long long)M, (long long)K);
-  if (n_segments > NVFP4_MAX_SEGMENTS || M > NVFP4_MAX_M)
+  if (n_segments > NVFP4_MAX_SEGMENTS || M > NVFP4_MAX_M || K > NVFP4_MAX_K)
     return fail(NVFP4_ERR_UNSUPPORTED,
-                "nvfp4_gemv_segments: n_segments=%lld (max %d), M=%lld (max %d)",
-                (long long)n_segments, NVFP4_MAX_SEGMENTS, (long long)M, NVFP4_MAX_M);
+                "nvfp4_gemv_segments: n_segments=%lld (max %d), M=%lld (max %d), K=%lld (max %lld)",
+                (long long)n_segments, NVFP4_MAX_SEGMENTS, (long long)M, NVFP4_MAX_M,
+                (long long)K, (long long)NVFP4_MAX_K);
   if (n_segments == 0 || M == 0) return NVFP4_OK;
   if (!segs) return fail(NVFP4_ERR_NULL, "nvfp4_gemv_segments: segs is NULL");
   nvfp4::SegDesc d[NVFP4_MAX_SEGMENTS];
@@ -245,9 +248,11 @@ nvfp4_status nvfp4_gemv_w4a4(const uint8_t* codes_w, const uint8_t* scales_w,
     return fail(NVFP4_ERR_SHAPE,
                 "nvfp4_gemv_w4a4: need M, N, K >= 0 and K %% 32 == 0 (M=%lld N=%lld K=%lld)",
                 (long long)M, (long long)N, (long long)K);
-  if (M > NVFP4_MAX_M || N > NVFP4_MAX_N)
-    return fail(NVFP4_ERR_UNSUPPORTED, "nvfp4_gemv_w4a4: M=%lld (max %d), N=%lld (max %lld)",
-                (long long)M, NVFP4_MAX_M, (long long)N, (long long)NVFP4_MAX_N);
+  if (M > NVFP4_MAX_M || N > NVFP4_MAX_N || K > NVFP4_MAX_K)
+    return fail(NVFP4_ERR_UNSUPPORTED,
+                "nvfp4_gemv_w4a4: M=%lld (max %d), N=%lld (max %lld), K=%lld (max %lld)",
+                (long long)M, NVFP4_MAX_M, (long long)N, (long long)NVFP4_MAX_N, (long long)K,
+                (long long)NVFP4_MAX_K);
   if (M == 0 || N == 0) return NVFP4_OK;
   if (!y) return fail(NVFP4_ERR_NULL, "nvfp4_gemv_w4a4: y is NULL");
   if (!aligned(y, 4)) return fail(NVFP4_ERR_ALIGN, "nvfp4_gemv_w4a4: y must be 4-byte aligned");
@@ -289,9 +294,10 @@ nvfp4_status nvfp4_gemv_w4a4_segments(const nvfp4_gemv_segment* segs, int64_t n_
   if (n_segments < 0 || M < 0 || K < 0 || (K % 32) != 0)
     return fail(NVFP4_ERR_SHAPE, "%s: need n_segments, M, K >= 0 and K %% 32 == 0 "
                 "(n=%lld M=%lld K=%lld)", fn, (long long)n_segments, (long long)M, (long long)K);
-  if (n_segments > NVFP4_MAX_SEGMENTS || M > NVFP4_MAX_M)
-    return fail(NVFP4_ERR_UNSUPPORTED, "%s: n_segments=%lld (max %d), M=%lld (max %d)", fn,
-                (long long)n_segments, NVFP4_MAX_SEGMENTS, (long long)M, NVFP4_MAX_M);
+  if (n_segments > NVFP4_MAX_SEGMENTS || M > NVFP4_MAX_M || K > NVFP4_MAX_K)
+    return fail(NVFP4_ERR_UNSUPPORTED, "%s: n_segments=%lld (max %d), M=%lld (max %d), K=%lld (max %lld)",
+                fn, (long long)n_segments, NVFP4_MAX_SEGMENTS, (long long)M, NVFP4_MAX_M,
+                (long long)K, (long long)NVFP4_MAX_K);
   if (n_segments == 0 || M == 0) return NVFP4_OK;
   if (!segs) return fail(NVFP4_ERR_NULL, "%s: segs is NULL", fn);
   nvfp4::SegDesc d[NVFP4_MAX_SEGMENTS];
@@ -388,6 +394,23 @@ nvfp4_status nvfp4_stream_read(const void* buf, size_t bytes, uint32_t* sink,
   return hip_result(nvfp4::launch_stream_read(buf, bytes, sink, stream),
                     "nvfp4_stream_read launch");
 }
+
+nvfp4_status nvfp4_check_device_faults(hipStream_t stream) {
+  clear_error();
+  uint32_t fault = 0u;
+  const hipError_t e = nvfp4::splitk_take_fault(stream, &fault);
+  if (e != hipSuccess)
+    return fail(NVFP4_ERR_HIP, "nvfp4_check_device_faults: %s (%s)", hipGetErrorName(e),
+                hipGetErrorString(e));
+  if (fault != 0u)
+    return fail(NVFP4_ERR_HIP,
+                "nvfp4_check_device_faults: a split-K GEMV slot wait gave up (fault word %#x); "
+                "the tiles concerned hold NaN",
+                fault);
+  return NVFP4_OK;
+}
+
+void nvfp4_debug_set_wait_limit(int polls) { nvfp4::splitk_set_spin_limit(polls); }
 
 size_t nvfp4_moe_workspace_bytes(int64_t M, int64_t H, int64_t I, int64_t topk) {
   if (M < 0 || H < 0 || I < 0 || topk < 0) return 0;

@@ -1,6 +1,7 @@
 // gemv_mfma.hip -- NVFP4 g16 W4A16 GEMV on the CDNA4 matrix cores, for
 // 3 <= M <= 8 activation rows (the instruction has room for 16) and K not a
-// multiple of 256 (those go to gemv_splitk.hip).
+// multiple of 256 (multiples of 256 go to gemv_g8.hip, or to gemv_splitk.hip
+// where their slices do not split evenly over 16 wavefronts).
 //
 // Why MFMA here: at M rows the plain VALU path spends about 0.5 + M/2
 // instructions per weight (one bf16 pair dot per two weights per row), which
@@ -83,7 +84,7 @@ struct Chunk {
 // offset) and at its row's scale bytes; t_last is the last iteration whose
 // codes this lane may load (its own last in-range iteration), g_sb its scale
 // byte offset inside an iteration (2g, or 0 for a lane group wholly past K).
-template <int T, bool FULL>
+template <int T>
 __device__ __forceinline__ void load_chunk_regs(Chunk<T>& ch, const uint8_t* const (&cp)[T],
                                                 const uint8_t* const (&sp)[T], int64_t t0,
                                                 int64_t t_last, int64_t sb, int g_sb) {
@@ -95,16 +96,7 @@ __device__ __forceinline__ void load_chunk_regs(Chunk<T>& ch, const uint8_t* con
       ch.q[u][j] = load_stream(cp[u] + t * 64);
     }
   }
-  if (FULL) {
-    // K % 512 == 0: whole chunks only; a chunk past the wavefront's range is
-    // clamped to the last one (its data is not used)
-    const int64_t tc = t0 < t_last ? t0 : t_last - (kChunkIters - 1);
-#pragma unroll
-    for (int u = 0; u < T; ++u) {
-      ch.s[u][0] = load_stream(sp[u] + tc * 8);
-      ch.s[u][1] = load_stream(sp[u] + tc * 8 + 16);
-    }
-  } else if (8 * t0 + 32 <= sb) {
+  if (8 * t0 + 32 <= sb) {
     // the chunk's 32 scale bytes of each row lie inside the row
 #pragma unroll
     for (int u = 0; u < T; ++u) {
@@ -191,7 +183,7 @@ __device__ __forceinline__ void compute_iter(const Chunk<T>& ch, int j, uint32_t
 // One pipeline step: wait for chunk c (registers `cur`, x in the LDS buffer
 // at byte address xread), issue x(c+1) into xload and regs(c+2) into `ld`,
 // then decode and multiply chunk c.
-template <int T, bool FULL>
+template <int T>
 __device__ __forceinline__ void mfma_step(const Chunk<T>& cur, Chunk<T>& ld, uint32_t xread,
                                           unsigned char* xload, int64_t c, int64_t nch,
                                           int64_t tb, int64_t te, int64_t t_last,
@@ -201,27 +193,16 @@ __device__ __forceinline__ void mfma_step(const Chunk<T>& cur, Chunk<T>& ld, uin
                                           int lane, int g, f32x4_t (&acc)[T]) {
   __builtin_amdgcn_s_waitcnt(kWaitBase | (6 * T));
   const int64_t t0 = tb + c * kChunkIters;
-  if (FULL) {
-    // the x prefetch past the range reloads this wavefront's last chunk
-    const int64_t tx = c + 1 < nch ? t0 + kChunkIters : t0;
-    load_chunk_x(xload, x, M, K, tx * 128, lane);
-  } else if (c + 1 < nch) {
-    load_chunk_x(xload, x, M, K, (t0 + kChunkIters) * 128, lane);
-  }
-  load_chunk_regs<T, FULL>(ld, cp, sp, t0 + 2 * kChunkIters, t_last, sb, g_sb);
+  if (c + 1 < nch) load_chunk_x(xload, x, M, K, (t0 + kChunkIters) * 128, lane);
+  load_chunk_regs<T>(ld, cp, sp, t0 + 2 * kChunkIters, t_last, sb, g_sb);
   __builtin_amdgcn_sched_barrier(0);  // keep the prefetch ahead of the math
-  if (FULL) {
 #pragma unroll
-    for (int j = 0; j < kChunkIters; ++j) compute_iter<T>(cur, j, xread, g, true, false, acc);
-  } else {
-#pragma unroll
-    for (int j = 0; j < kChunkIters; ++j)
-      if (t0 + j < te)
-        compute_iter<T>(cur, j, xread, g, t0 + j < t_gvalid_end, 8 * t0 + 32 > sb, acc);
-  }
+  for (int j = 0; j < kChunkIters; ++j)
+    if (t0 + j < te)
+      compute_iter<T>(cur, j, xread, g, t0 + j < t_gvalid_end, 8 * t0 + 32 > sb, acc);
 }
 
-template <int T, bool FULL>
+template <int T>
 __global__ __launch_bounds__(64 * kMfmaMaxWaves) void k_gemv_mfma(
     const SegTable tab, const uint16_t* __restrict__ x, int M, int64_t K) {
   // workgroup = one unit of 16T rows of one segment
@@ -292,21 +273,21 @@ __global__ __launch_bounds__(64 * kMfmaMaxWaves) void k_gemv_mfma(
     // track the DMA's writes. regs(c+2) past this wavefront's range repeat
     // clamped in-range addresses (cache hits), so the count never changes.
     Chunk<T> S0, S1, S2;
-    load_chunk_regs<T, FULL>(S0, cp, sp, tb, t_last, sb, g_sb);
+    load_chunk_regs<T>(S0, cp, sp, tb, t_last, sb, g_sb);
     load_chunk_x(xl0, x, M, K, tb * 128, lane);
-    load_chunk_regs<T, FULL>(S1, cp, sp, tb + kChunkIters, t_last, sb, g_sb);
+    load_chunk_regs<T>(S1, cp, sp, tb + kChunkIters, t_last, sb, g_sb);
     for (int64_t c = 0;;) {
-      mfma_step<T, FULL>(S0, S2, xa0, xl1, c, nch, tb, te, t_last, t_gvalid_end, cp, sp, sb, g_sb, x, M, K, lane, g, acc);
+      mfma_step<T>(S0, S2, xa0, xl1, c, nch, tb, te, t_last, t_gvalid_end, cp, sp, sb, g_sb, x, M, K, lane, g, acc);
       if (++c >= nch) break;
-      mfma_step<T, FULL>(S1, S0, xa1, xl0, c, nch, tb, te, t_last, t_gvalid_end, cp, sp, sb, g_sb, x, M, K, lane, g, acc);
+      mfma_step<T>(S1, S0, xa1, xl0, c, nch, tb, te, t_last, t_gvalid_end, cp, sp, sb, g_sb, x, M, K, lane, g, acc);
       if (++c >= nch) break;
-      mfma_step<T, FULL>(S2, S1, xa0, xl1, c, nch, tb, te, t_last, t_gvalid_end, cp, sp, sb, g_sb, x, M, K, lane, g, acc);
+      mfma_step<T>(S2, S1, xa0, xl1, c, nch, tb, te, t_last, t_gvalid_end, cp, sp, sb, g_sb, x, M, K, lane, g, acc);
       if (++c >= nch) break;
-      mfma_step<T, FULL>(S0, S2, xa1, xl0, c, nch, tb, te, t_last, t_gvalid_end, cp, sp, sb, g_sb, x, M, K, lane, g, acc);
+      mfma_step<T>(S0, S2, xa1, xl0, c, nch, tb, te, t_last, t_gvalid_end, cp, sp, sb, g_sb, x, M, K, lane, g, acc);
       if (++c >= nch) break;
-      mfma_step<T, FULL>(S1, S0, xa0, xl1, c, nch, tb, te, t_last, t_gvalid_end, cp, sp, sb, g_sb, x, M, K, lane, g, acc);
+      mfma_step<T>(S1, S0, xa0, xl1, c, nch, tb, te, t_last, t_gvalid_end, cp, sp, sb, g_sb, x, M, K, lane, g, acc);
       if (++c >= nch) break;
-      mfma_step<T, FULL>(S2, S1, xa1, xl0, c, nch, tb, te, t_last, t_gvalid_end, cp, sp, sb, g_sb, x, M, K, lane, g, acc);
+      mfma_step<T>(S2, S1, xa1, xl0, c, nch, tb, te, t_last, t_gvalid_end, cp, sp, sb, g_sb, x, M, K, lane, g, acc);
       if (++c >= nch) break;
     }
   }
@@ -363,12 +344,8 @@ hipError_t launch_gemv_mfma_shape(const SegDesc* d, int n, const uint16_t* x, in
   const SegTable tab = make_seg_table(d, n, 16);
   const int64_t wgs = tab.start[kMaxSegments];
   const size_t lds = (size_t)2 * W * M * kXRowStride + (size_t)W * 32 * 4 * sizeof(float);
-  const bool full = (K % (128 * kChunkIters)) == 0;
-#define NVFP4_LAUNCH_MFMA(TT, FF)                                                        \
-  hipLaunchKernelGGL((k_gemv_mfma<TT, FF>), dim3((unsigned)wgs), dim3(64 * W), lds, stream, \
-                     tab, x, M, K)
-  if (full) NVFP4_LAUNCH_MFMA(1, true); else NVFP4_LAUNCH_MFMA(1, false);
-#undef NVFP4_LAUNCH_MFMA
+  hipLaunchKernelGGL((k_gemv_mfma<1>), dim3((unsigned)wgs), dim3(64 * W), lds, stream, tab, x, M,
+                     K);
   return hipGetLastError();
 }
 

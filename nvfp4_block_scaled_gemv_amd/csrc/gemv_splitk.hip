@@ -56,6 +56,7 @@
 // final sum.
 #include "device.h"
 #include "internal.h"
+#include "splitk_slots.h"
 
 namespace nvfp4 {
 
@@ -246,10 +247,14 @@ struct SkEngine {
 
 // LDS of a workgroup: partial-tile slots, per-wavefront transpose buffers and
 // the slots' arrival and release counters.
-constexpr int kSlots = 4;
+constexpr int kSlots = kSkSlots;
 constexpr int kStagePitch = 144;            // bytes per staged row (128 + 16: bank skew)
 constexpr int kStageBytes = 16 * kStagePitch;
 constexpr int kSpinLimit = 1 << 22;         // bound of a slot wait (never reached)
+
+// Set (bit 0) by a wavefront that gave up a slot wait; read and cleared by
+// splitk_take_fault. One word per device (this file's code object).
+__device__ uint32_t g_splitk_fault = 0u;
 constexpr int kRedBatch = 4;                // partial loads in flight in the sum
 
 struct SkShared {
@@ -269,20 +274,25 @@ static size_t splitk_lds(int W) {
 template <int M, int WMAX>
 __device__ __forceinline__ void sk_finish(const SkCursor& cs, int64_t tile, int tl, f32x4_t& acc,
                                           uint32_t done_seen, const SkShared& sh, int w, int W,
-                                          int lane) {
+                                          int lane, int spin_limit) {
   // lanes l and l + 32 hold the two block halves of the same outputs
   acc = sk_add_upper_half(acc);
-  const int s = tl % kSlots;
-  const uint32_t round = (uint32_t)(tl / kSlots);
+  const int s = sk_slot(tl);
+  const uint32_t round = sk_round(tl);
   // the slot's previous round must have been summed (it normally has been
   // long ago; the wait only holds a wavefront kSlots tiles ahead). done_seen
-  // is the slot's release count read before this tile's math.
-  if (done_seen < round) {
-    for (int spin = 0; spin < kSpinLimit; ++spin) {
-      if (__hip_atomic_load(&sh.done[s], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) >= round)
-        break;
-      __builtin_amdgcn_s_sleep(1);
-    }
+  // is the slot's release count read before this tile's math. A negative
+  // limit (a test of the fault path) gives up at once.
+  bool free = spin_limit >= 0 && sk_slot_free(done_seen, round);
+  for (int spin = 0; !free && spin < spin_limit; ++spin) {
+    __builtin_amdgcn_s_sleep(1);
+    free = sk_slot_free(
+        __hip_atomic_load(&sh.done[s], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP), round);
+  }
+  if (!free) {
+    // give up: record the fault and arrive with a NaN partial
+    if (lane == 0) atomicOr(&g_splitk_fault, 1u);
+    acc = f32x4_t{__builtin_nanf(""), __builtin_nanf(""), __builtin_nanf(""), __builtin_nanf("")};
   }
   f32x4_t* slot = sh.part + s * (W * 32);
   if (lane < 32) slot[w * 32 + lane] = acc;
@@ -293,7 +303,7 @@ __device__ __forceinline__ void sk_finish(const SkCursor& cs, int64_t tile, int 
   if (lane == 0) old = atomicAdd(&sh.cnt[s], 1u);
   old = __builtin_amdgcn_readfirstlane(old);
   asm volatile("" ::: "memory");
-  if (old == round * (uint32_t)W + (uint32_t)(W - 1)) {
+  if (sk_last_arrival(old, round, W)) {
     // lane l < 32 sums partials 0 .. h-1 of entry l, lane l + 32 partials
     // h .. W-1 (h = ceil(W / 2)); the loads are unconditional (clamped to a
     // valid partial) so that they are all in flight before the first add
@@ -337,7 +347,7 @@ __device__ __forceinline__ void sk_finish(const SkCursor& cs, int64_t tile, int 
 // the ring's loads across its ordering points.
 template <int M, int XS, int D>
 __global__ __launch_bounds__(64 * sk_max_waves(XS)) void
-k_gemv_splitk(const SegTable tab, const uint16_t* x, int64_t K, int KS) {
+k_gemv_splitk(const SegTable tab, const uint16_t* x, int64_t K, int KS, int spin_limit) {
   constexpr bool WX = XS == 0;
   constexpr int kSl = SkStage<XS>::kSl;
   constexpr int kIssue = 3 * kSl + (WX ? 8 : 0);   // vector-memory instructions per item
@@ -452,7 +462,7 @@ k_gemv_splitk(const SegTable tab, const uint16_t* x, int64_t K, int KS) {
     }
     if (++csl == ipt) {
       sk_finish<M, sk_max_waves(XS)>(cf, ctile, (int)(ctile - t0), acc, done_seen, sh, w, W,
-                                     lane);
+                                     lane, spin_limit);
       csl = 0;
       if (++ctile < t0 + nt && cf.seek(tab, ctile)) cf.load_gs();
     }
@@ -491,6 +501,23 @@ k_gemv_splitk(const SegTable tab, const uint16_t* x, int64_t K, int KS) {
       if (++c >= n) break;
     }
   }
+}
+
+// The slot-wait bound the launches pass (a test may lower it, or make it
+// negative to force the fault path).
+static int g_splitk_spin_limit = kSpinLimit;
+
+void splitk_set_spin_limit(int limit) { g_splitk_spin_limit = limit == 0 ? kSpinLimit : limit; }
+
+hipError_t splitk_take_fault(hipStream_t stream, uint32_t* fault) {
+  hipError_t e = hipStreamSynchronize(stream);
+  if (e != hipSuccess) return e;
+  e = hipMemcpyFromSymbol(fault, HIP_SYMBOL(g_splitk_fault), sizeof(uint32_t), 0,
+                          hipMemcpyDeviceToHost);
+  if (e != hipSuccess || *fault == 0u) return e;
+  const uint32_t zero = 0u;
+  return hipMemcpyToSymbol(HIP_SYMBOL(g_splitk_fault), &zero, sizeof(uint32_t), 0,
+                           hipMemcpyHostToDevice);
 }
 
 bool splitk_applicable(int M, int64_t K) {
@@ -541,7 +568,7 @@ hipError_t launch_gemv_splitk_shape(const SegDesc* d, int n, const uint16_t* x, 
   const size_t lds = splitk_lds(W);
 #define NVFP4_SK(MM, XX, DD)                                                              \
   hipLaunchKernelGGL((k_gemv_splitk<MM, XX, DD>), dim3((unsigned)grid), dim3(64 * W), lds, \
-                     stream, tab, x, K, KS)
+                     stream, tab, x, K, KS, g_splitk_spin_limit)
 #define NVFP4_SKM(MM)                    \
   if (XS == 1) {                         \
     NVFP4_SK(MM, 1, 3);                  \

@@ -59,6 +59,10 @@ hipError_t launch_gemv_mt_shape(const SegDesc* d, int n, const uint16_t* x, int 
 hipError_t launch_gemv_mfma(const SegDesc* d, int n, const uint16_t* x, int M, int64_t K,
                             hipStream_t stream);
 bool splitk_applicable(int M, int64_t K);
+// the slot-wait bound of later split-K launches (0: the default; negative:
+// give up at once) and the read-and-clear of this device's fault word
+void splitk_set_spin_limit(int limit);
+hipError_t splitk_take_fault(hipStream_t stream, uint32_t* fault);
 void splitk_default_shape(int64_t K, int* KS, int* XS, int* D);
 hipError_t launch_gemv_splitk(const SegDesc* d, int n, const uint16_t* x, int M, int64_t K,
                               hipStream_t stream);

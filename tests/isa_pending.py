@@ -9,6 +9,10 @@ load whose result is never consumed is the typical way to break it, since the
 compiler then hands its registers to another value. The walk is linear over
 the function body (branches are ignored, so both sides of an if/else apply
 their waits); every global_load* counts as one vmcnt event, in issue order.
+A load whose destination overlaps a pending load's is not a violation: loads
+return in issue order, so the later one's data lands last (the two sides of
+an if/else that load the same registers look like this to a linear walk);
+its address operands are checked like any other read.
 """
 import re
 
@@ -38,12 +42,16 @@ def violations(body_lines):
                 pending = pending[len(pending) - n:] if 0 < n < len(pending) else (
                     [] if n == 0 else pending)
             continue
-        touched = _regs(t[len(op):])
+        is_load = op.startswith("global_load") or op.startswith("buffer_load")
+        operands = t[len(op):]
+        if is_load and "lds" not in op and "," in operands:
+            operands = operands.split(",", 1)[1]   # the destination is a write
+        touched = _regs(operands)
         for pk, dest in pending:
             if dest and touched & dest:
                 found.append((k, t, pk))
                 break
-        if op.startswith("global_load") or op.startswith("buffer_load"):
+        if is_load:
             dst = None if "lds" in op else _regs(t[len(op):].split(",")[0])
             pending.append((k, dst))
     return found

@@ -34,13 +34,14 @@ def test_exports_every_declared_symbol(L):
             "nvfp4_moe_shared_workspace_bytes", "nvfp4_quantize_act", "nvfp4_gemv_w4a4",
             "nvfp4_gemv_w4a4_workspace_bytes", "nvfp4_gemv_w4a4_segments", "nvfp4_moe_w4a4_gemv",
             "nvfp4_moe_w4a4_workspace_bytes", "nvfp4_abi_version", "nvfp4_status_string",
-            "nvfp4_last_error", "nvfp4_stream_read", "nvfp4_moe_gemv_noalloc"} <= set(names)
+            "nvfp4_last_error", "nvfp4_stream_read", "nvfp4_moe_gemv_noalloc",
+            "nvfp4_check_device_faults", "nvfp4_debug_set_wait_limit"} <= set(names)
     for n in names:
         assert hasattr(L, n), n
 
 
 def test_version_and_status_strings(L):
-    assert L.nvfp4_abi_version() == 8
+    assert L.nvfp4_abi_version() == 9
     for s in range(8):
         assert L.nvfp4_status_string(s)
     assert L.nvfp4_status_string(99) == b"unknown status"
@@ -61,6 +62,7 @@ def test_binding_limits_match_the_header():
     assert value("NVFP4_MOE_MAX_M") == nv.MOE_MAX_M
     assert value("NVFP4_MAX_TOPK") == nv.MAX_TOPK
     assert value("NVFP4_MAX_N") == nv.MAX_N
+    assert value("NVFP4_MAX_K") == nv.MAX_K
     assert value("NVFP4_MOE_MAX_I") == nv.MOE_MAX_I
     assert value("NVFP4_MOE_MAX_H") == nv.MOE_MAX_H
     assert value("NVFP4_MAX_SEGMENTS") == nv.MAX_SEGMENTS
@@ -69,6 +71,14 @@ def test_binding_limits_match_the_header():
 
 def _err(L):
     return L.nvfp4_last_error().decode()
+
+
+def test_gemv_rejects_k_past_its_limit(L):
+    """K above NVFP4_MAX_K is refused on the host by every GEMV entry point."""
+    K = nv.MAX_K + 32
+    assert L.nvfp4_gemv(A, A, A, A, 9, 16, K, B, None) == ERR_UNSUPPORTED
+    assert "K=" in _err(L)
+    assert L.nvfp4_gemv_w4a4(A, A, A, A, A, A, 1, 16, K, B, A, 1 << 30, None) == ERR_UNSUPPORTED
 
 
 def test_gemv_rejects_bad_shapes(L):

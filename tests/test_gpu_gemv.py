@@ -214,3 +214,32 @@ def test_deterministic_and_on_side_stream():
     assert np.array_equal(host(y1), host(y2))
     y_ref, ad = oracle.gemv(codes, scales, 0.5, x)
     check_tol(host(y2), y_ref, ad, "side stream")
+
+
+def test_splitk_fault_path_is_reported_and_cleared():
+    """The split-K kernel's bounded slot wait, forced to give up from the host
+    (a negative wait bound: every tile gives up at once, no wait at all): the
+    kernel still ends normally, its outputs are NaN, the fault is reported by
+    nvfp4_check_device_faults and cleared by the read; with the default bound
+    the same call is correct again and reports nothing. K = 17 slices of 256
+    takes the split-K kernel (the 16-wavefront kernel cannot split 17)."""
+    M, N, K = 5, 256, 256 * 17
+    codes, scales = workloads.random_nvfp4(40, M, 1, N, K)
+    x = workloads.x_bf16(40, M, 1, M, K)
+    g = np.float32(0.02)
+    args = (dev(codes), dev(scales), dev(np.array([g], np.float32)), dev_x(x))
+    say("[fault] forced give-up of the split-K slot wait")
+    try:
+        nv.debug_set_wait_limit(-1)
+        y_bad = host(nv.gemv(*args))
+        with pytest.raises(nv.Nvfp4Error) as err:
+            nv.check_device_faults()
+        assert "slot wait" in str(err.value)
+        assert np.isnan(y_bad).all()
+        nv.check_device_faults()   # cleared by the first read
+    finally:
+        nv.debug_set_wait_limit(0)
+    y = host(nv.gemv(*args))
+    nv.check_device_faults()
+    y_ref, ad = oracle.gemv(codes, scales, g, x)
+    check_tol(y, y_ref, ad, "after the fault path")

@@ -29,6 +29,14 @@ def test_walker_flags_a_touch_before_the_wait():
           "s_waitcnt vmcnt(1)",
           "v_add_u32_e32 v5, v5, v2"]
     assert violations(ok) == []
+    # a load into registers another load still has pending is a write after
+    # write (returns are in order), but its address must not be pending
+    waw = ["global_load_dwordx4 v[40:43], v[0:1], off",
+           "global_load_ushort v40, v[4:5], off"]
+    assert violations(waw) == []
+    raw = ["global_load_dwordx4 v[40:43], v[0:1], off",
+           "global_load_ushort v50, v[40:41], off"]
+    assert [f[0] for f in violations(raw)] == [1]
 
 
 @pytest.mark.skipif(not os.path.exists(HIPCC), reason="hipcc not installed")
@@ -51,4 +59,27 @@ def test_splitk_kernels_leave_pending_loads_alone(tmp_path):
     for n in (3, 12, 11, 22):   # (ring - 2) x loads per item of each variant
         assert f"vmcnt({n})" in text, n
     # no spills: a spilled ring register would be stored while its load is pending
+    assert "scratch_" not in text
+
+
+# The other kernel with hand-placed waits: the matrix-core GEMV for K not a
+# multiple of 256 copies x into LDS by DMA and reads it with inline-asm LDS
+# reads, ordered by an explicit vmcnt wait. (The remaining kernels issue
+# every load through the compiler, whose own wait insertion tracks them; the
+# walk is linear and would see the two sides of their branches as one path.)
+@pytest.mark.skipif(not os.path.exists(HIPCC), reason="hipcc not installed")
+def test_mfma_kernel_leaves_pending_loads_alone(tmp_path):
+    out = tmp_path / "mfma.s"
+    cmd = [HIPCC, "--offload-arch=gfx950", "-O3", "-std=c++17", "-ffp-contract=off",
+           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+           "-I", os.path.join(ROOT, "include"), "--cuda-device-only", "-S",
+           "-o", str(out), os.path.join(CSRC, "gemv_mfma.hip")]
+    subprocess.run(cmd, check=True, capture_output=True, timeout=600)
+    text = out.read_text()
+    res = check_asm(text, r"_Z\S*k_gemv_mfma\S*")
+    assert len(res) == 1, sorted(res)
+    bad = {k: v[:3] for k, v in res.items() if v}
+    assert not bad, bad
+    # the x copies go by LDS DMA and the A operands come from asm LDS reads
+    assert "global_load_lds_dwordx4" in text and "ds_read_b128" in text
     assert "scratch_" not in text
