@@ -393,7 +393,7 @@ __global__ __launch_bounds__(256) void k_moe_down(
   }
 }
 
-constexpr int kMaxTok = NVFP4_MAX_M_INTERNAL;     // tokens per call
+constexpr int kMaxTok = NVFP4_MOE_MAX_M_INTERNAL;  // tokens per call
 constexpr int kMaxSl = NVFP4_MAX_TOPK_INTERNAL;    // slots per token
 constexpr int kSplitRows = 8;                      // k_moe_down_split: rows per workgroup
 constexpr int kSplitWaves = 4;                     //   and wavefronts per workgroup

@@ -83,3 +83,36 @@ def test_mfma_kernel_leaves_pending_loads_alone(tmp_path):
     # the x copies go by LDS DMA and the A operands come from asm LDS reads
     assert "global_load_lds_dwordx4" in text and "ds_read_b128" in text
     assert "scratch_" not in text
+
+
+KERNEL_FILES = ["gemv.hip", "gemv_g8.hip", "gemv_mfma.hip", "gemv_splitk.hip", "gemv_mt.hip",
+                "moe.hip", "w4a4.hip", "pack.hip", "stream_read.hip"]
+
+
+@pytest.mark.skipif(not os.path.exists(HIPCC), reason="hipcc not installed")
+def test_no_kernel_spills_registers(tmp_path):
+    """Every kernel fits its registers: no VGPR spills and no private
+    (scratch) memory. A spill costs a round trip to memory per use; a size
+    bound shared between kernels once grew a per-token array of the MoE down
+    pass to 128 entries and spilled it whole."""
+    import re
+    procs = {}
+    for f in KERNEL_FILES:
+        out = tmp_path / (f + ".s")
+        cmd = [HIPCC, "--offload-arch=gfx950", "-O3", "-std=c++17", "-ffp-contract=off",
+               "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+               "-I", os.path.join(ROOT, "include"), "--cuda-device-only", "-S",
+               "-o", str(out), os.path.join(CSRC, f)]
+        procs[f] = (subprocess.Popen(cmd, stdout=subprocess.DEVNULL, stderr=subprocess.PIPE), out)
+    kernels = 0
+    for f, (p, out) in procs.items():
+        _, err = p.communicate(timeout=900)
+        assert p.returncode == 0, (f, err[-2000:])
+        text = out.read_text()
+        for block in text.split("- .agpr_count:")[1:]:
+            name = re.search(r"\.name:\s+(\S+)", block).group(1)
+            spill = int(re.search(r"\.vgpr_spill_count:\s+(\d+)", block).group(1))
+            priv = int(re.search(r"\.private_segment_fixed_size:\s+(\d+)", block).group(1))
+            assert spill == 0 and priv == 0, (f, name, spill, priv)
+            kernels += 1
+    assert kernels >= 40, kernels
