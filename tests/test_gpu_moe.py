@@ -138,3 +138,33 @@ def test_moe_empty_batch():
                     torch.zeros((0, 2), dtype=torch.int32, device="cuda"),
                     torch.zeros((0, 2), dtype=torch.float32, device="cuda"))
     assert y.shape == (0, H)
+
+
+@pytest.mark.parametrize("case", ["one_expert_all_tokens", "same_experts_all_tokens"])
+def test_moe_skewed_routing(case):
+    """Skewed routing at M = 8, full per-expert size: one expert named by all
+    eight tokens (slot 0 of every token; the other slots distinct), or all
+    tokens naming the same eight experts (in permuted slot order, different
+    gate weights). The gate|up pass streams a shared expert's rows for all
+    its slots and the down pass reads them per token (the L2 serves the
+    repeats); the result is checked against the oracle."""
+    E, H, I, topk, M = 288, 4096, 1536, 8, 8
+    rng = np.random.default_rng(77)
+    if case == "one_expert_all_tokens":
+        ids, gw = workloads.moe_routing(4, 3, M, E, topk)
+        ids = ids.copy()
+        for m in range(M):
+            row = [e for e in ids[m] if e != 7][:topk - 1]
+            while len(row) < topk - 1:
+                row.append(int(rng.integers(8, E)))
+            ids[m] = [7] + row
+    else:
+        ids = np.stack([rng.permutation(np.arange(40, 48)) for _ in range(M)]).astype(np.int32)
+        gw = rng.random((M, topk)).astype(np.float32)
+    ids = ids.astype(np.int32)
+    say(f"[moe] skewed routing {case}: distinct experts={len(set(ids.ravel()))}")
+    hw, dw = build_experts(4, 3, E, H, I, ids.ravel())
+    x = workloads.x_bf16(4, 3, 1, M, H)
+    y, (y_ref, bound), _ = run_both(hw, dw, x, ids, gw, H, I)
+    r = check_tol(y, y_ref, bound, f"moe {case}")
+    say(f"  max err / tol = {r:.3e}")
