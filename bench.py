@@ -63,7 +63,7 @@ MIN_ROTATION_BYTES = 1 << 30
 LAUNCH_WINDOW = 400        # steps in the issue-gated event window of every leg
 QUEUED_WINDOW = 200        # steps queued back to back behind a busy hold
 QUEUED_LAUNCHES = 400      # at most this many launches queued at once
-ALL_LEGS = "lm_head,small,stress,layer,moe,w4a4,wide,copy"
+ALL_LEGS = "lm_head,small,stress,layer,moe,moe_skew,w4a4,wide,copy"
 
 
 HOLD = None               # the BusyHold of this run
@@ -615,6 +615,69 @@ def moe_legs(torch, nv, traffic, mo, M, steps, warmup, ceil, want_cpu):
     return routed, with_shared, w4a4
 
 
+def skewed_routing(ids, case, b, E):
+    """Skewed variants of a routing batch (ids int32[M, topk]): case
+    "one_expert_all_tokens" puts expert b % E in slot 0 of every token (the
+    token's other slots keep their distinct experts); "same_experts_all_tokens"
+    has every token name the same topk experts, each token in its own order."""
+    M, topk = ids.shape
+    r = np.random.default_rng(1000 + b)
+    if case == "one_expert_all_tokens":
+        e0 = b % E
+        out = np.empty_like(ids)
+        for m in range(M):
+            rest = [int(e) for e in ids[m] if e != e0][:topk - 1]
+            while len(rest) < topk - 1:
+                c = int(r.integers(0, E))
+                if c != e0 and c not in rest:
+                    rest.append(c)
+            out[m] = [e0] + rest
+        return out.astype(np.int32)
+    base = (topk * b + np.arange(topk)) % E
+    return np.stack([r.permutation(base) for _ in range(M)]).astype(np.int32)
+
+
+def moe_skew_legs(torch, nv, traffic, mo, steps, warmup, ceil):
+    """The routed MoE pass at M = 8 under skewed routing (skewed_routing):
+    the weights each distinct expert contributes are what the bytes count, so
+    a pass that re-read a shared expert's rows per token would show here as
+    a lower fraction of the read ceiling. Parity on batch 0 of each case."""
+    E, H, I, topk, M = mo.E, mo.H, mo.I, mo.TOPK, 8
+    y = torch.empty((M, H), dtype=torch.float32, device="cuda")
+    ws = torch.empty(nv.moe_workspace_bytes(M, H, I, topk), dtype=torch.uint8, device="cuda")
+    out = {}
+    for case in ("one_expert_all_tokens", "same_experts_all_tokens"):
+        bt = []
+        for b in range(16):
+            ids, gw = mo.wl.moe_routing(4, 100 + b, M, E, topk)
+            ids = skewed_routing(ids, case, b, E)
+            xb = mo.wl.x_bf16(4, 100 + b, 0, M, H)
+            bt.append((torch.from_numpy(ids).cuda(), torch.from_numpy(gw).cuda(),
+                       x_dev(torch, xb), len(set(ids.ravel().tolist())), ids, gw, xb))
+        nb = len(bt)
+
+        def step(i, bt=bt):
+            ids, gw, x = bt[i % nb][:3]
+            nv.moe_gemv_into(*mo.routed, x, ids, gw, y, ws)
+
+        first = warmup + steps + LAUNCH_WINDOW
+        ds = [bt[(first + i) % nb][3] for i in range(QUEUED_WINDOW)]
+        nbytes = float(np.mean([traffic.moe_bytes(M, H, I, topk, d) for d in ds]))
+        res = {"workload": f"moe_288x(3072x4096,4096x1536)_top8_m8_{case}", "M": M,
+               "rotating_batches": nb, "distinct_experts_mean": float(np.mean(ds)),
+               **measure(torch, HOLD, step, steps, warmup, nbytes, M, 2, ceil.us(nbytes))}
+        ids0, gw0, xb0 = bt[0][4], bt[0][5], bt[0][6]
+        hw = mo.host_stacks(ids0)
+        step(0)
+        yr, bound = _oracle().moe(*hw, xb0, ids0, gw0)
+        w, bo = tol_ratio(y.cpu().numpy(), yr, bound)
+        res["parity"] = {"batch": 0, "outputs": int(yr.size), "max_err_over_tol": w,
+                         "outside_tol": bo, "ok": bo == 0}
+        del hw
+        out[case] = res
+    return out
+
+
 def _oracle_hq_bits(hc, hs):
     """bf16 bits of e2m1 * s for quantized rows (codes [R, I/2], scales
     [R, I/16]) from the oracle's element tables: the values the kernel's
@@ -1066,15 +1129,18 @@ def main():
                                  segments=[(0, 1, 2), (3,), (4, 5), (6,)])
         configs["2_decode_layer_m5"] = lay
         del D
-    if "moe" in legs:
+    if "moe" in legs or "moe_skew" in legs:
         mo = Moe(torch, nv, workloads)
-        result["moe_shared"], result["moe_w4a4"] = {}, {}
-        for M in (1, 8):
-            routed, with_shared, w4a4 = moe_legs(torch, nv, traffic, mo, M, K_, W_, ceil,
-                                                 want_cpu)
-            configs[f"4_moe_m{M}"] = routed
-            result["moe_shared"][f"m{M}"] = with_shared
-            result["moe_w4a4"][f"m{M}"] = w4a4
+        if "moe" in legs:
+            result["moe_shared"], result["moe_w4a4"] = {}, {}
+            for M in (1, 8):
+                routed, with_shared, w4a4 = moe_legs(torch, nv, traffic, mo, M, K_, W_, ceil,
+                                                     want_cpu)
+                configs[f"4_moe_m{M}"] = routed
+                result["moe_shared"][f"m{M}"] = with_shared
+                result["moe_w4a4"][f"m{M}"] = w4a4
+        if "moe_skew" in legs:
+            result["moe_skew"] = moe_skew_legs(torch, nv, traffic, mo, K_, W_, ceil)
         del mo
     if "w4a4" in legs:
         result["w4a4_ffn_m2"] = leg_w4a4(torch, nv, workloads, traffic, K_, W_, ceil, want_cpu)
@@ -1106,6 +1172,7 @@ def main():
         [result.get("w4a4_ffn_m2") or {"parity": {"ok": True}}] +
         list((result.get("moe_shared") or {}).values()) +
         list((result.get("moe_w4a4") or {}).values()) +
+        list((result.get("moe_skew") or {}).values()) +
         list((result.get("wide") or {}).values()) if "parity" in v)
     result["env"] = {"gpu": props.name, "cus": props.multi_processor_count,
                      "dpm_clocks": gpu_clock_state(),
