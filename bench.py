@@ -1160,6 +1160,13 @@ def main():
                 flops = sum(2 * M * N * K for _, N, K in D.mats)
                 leg["tflops"] = flops / (leg["step_us"] * 1e-6) / 1e12
                 leg["frac_of_bf16_mfma_peak"] = leg["tflops"] / BF16_MFMA_PEAK_TFLOPS
+                # which roof binds: the weight bytes at the HBM peak or the
+                # bf16 products at the dense matrix-core peak
+                hbm_us = leg["bytes_per_step"] / (HBM_PEAK_GBS * 1e3)
+                mfma_us = flops / (BF16_MFMA_PEAK_TFLOPS * 1e6)
+                leg["roof"] = {"hbm_us": hbm_us, "mfma_us": mfma_us,
+                               "bound": "mfma" if mfma_us > hbm_us else "hbm",
+                               "frac_of_bound": max(hbm_us, mfma_us) / leg["step_us"]}
                 wide[f"stress_m{M}"] = leg
                 del D
         result["wide"] = wide
