@@ -64,6 +64,8 @@ LAUNCH_WINDOW = 400        # steps in the issue-gated event window of every leg
 QUEUED_WINDOW = 200        # steps queued back to back behind a busy hold
 QUEUED_LAUNCHES = 400      # at most this many launches queued at once
 ALL_LEGS = "lm_head,small,stress,layer,moe,moe_skew,w4a4,wide,copy"
+# legs that only run when named: one skewed-routing case each (for counters)
+EXTRA_LEGS = "moe_skew_one,moe_skew_same"
 
 
 HOLD = None               # the BusyHold of this run
@@ -637,7 +639,8 @@ def skewed_routing(ids, case, b, E):
     return np.stack([r.permutation(base) for _ in range(M)]).astype(np.int32)
 
 
-def moe_skew_legs(torch, nv, traffic, mo, steps, warmup, ceil):
+def moe_skew_legs(torch, nv, traffic, mo, steps, warmup, ceil,
+                  cases=("one_expert_all_tokens", "same_experts_all_tokens")):
     """The routed MoE pass at M = 8 under skewed routing (skewed_routing):
     the weights each distinct expert contributes are what the bytes count, so
     a pass that re-read a shared expert's rows per token would show here as
@@ -646,7 +649,7 @@ def moe_skew_legs(torch, nv, traffic, mo, steps, warmup, ceil):
     y = torch.empty((M, H), dtype=torch.float32, device="cuda")
     ws = torch.empty(nv.moe_workspace_bytes(M, H, I, topk), dtype=torch.uint8, device="cuda")
     out = {}
-    for case in ("one_expert_all_tokens", "same_experts_all_tokens"):
+    for case in cases:
         bt = []
         for b in range(16):
             ids, gw = mo.wl.moe_routing(4, 100 + b, M, E, topk)
@@ -920,7 +923,8 @@ def summarize_stats(stats_csv, cmd, out, top=16):
              f"{'max':>9} {'pct':>6}  kernel"]
     for r in rows[:top]:
         name = r["Name"]
-        short = name.split("(")[0] if name.startswith(("nvfp4", "void nvfp4")) else name[:90]
+        bare = name.replace("(anonymous namespace)::", "")
+        short = bare.split("(")[0] if bare.startswith(("nvfp4", "void nvfp4")) else name[:90]
         d = np.sort(np.array(durs.get(name, [float("nan")])))
         med, p10, p90 = (float(np.percentile(d, q)) for q in (50, 10, 90))
         lines.append(f"{int(r['Calls']):7d} {float(r['AverageNs']) / 1e3:9.2f} {med:9.2f} "
@@ -990,7 +994,7 @@ def summarize_counters(csvs, cmd, out, match="nvfp4::"):
                 name = r["Kernel_Name"]
                 if match not in name:
                     continue
-                short = name.split("(")[0].replace("void ", "")
+                short = name.replace("(anonymous namespace)::", "").split("(")[0].replace("void ", "")
                 vals.setdefault(short, {}).setdefault(r["Counter_Name"], []).append(
                     float(r["Counter_Value"]))
     lines = ["# rocprofv3 --pmc counter means per dispatch (one pass per command)",
@@ -1066,7 +1070,7 @@ def main():
         sys.exit(1)
     nv.lib()   # fail loudly if the HIP library is not built
     legs = [s.strip() for s in args.legs.split(",") if s.strip()]
-    unknown = set(legs) - set(ALL_LEGS.split(","))
+    unknown = set(legs) - set(ALL_LEGS.split(",")) - set(EXTRA_LEGS.split(","))
     if unknown:
         ap.error(f"unknown legs {sorted(unknown)}")
     want_cpu = not args.no_cpu_baseline
@@ -1129,7 +1133,10 @@ def main():
                                  segments=[(0, 1, 2), (3,), (4, 5), (6,)])
         configs["2_decode_layer_m5"] = lay
         del D
-    if "moe" in legs or "moe_skew" in legs:
+    skew_cases = tuple(c for leg, c in (("moe_skew_one", "one_expert_all_tokens"),
+                                        ("moe_skew_same", "same_experts_all_tokens"))
+                       if "moe_skew" in legs or leg in legs)
+    if "moe" in legs or skew_cases:
         mo = Moe(torch, nv, workloads)
         if "moe" in legs:
             result["moe_shared"], result["moe_w4a4"] = {}, {}
@@ -1139,8 +1146,8 @@ def main():
                 configs[f"4_moe_m{M}"] = routed
                 result["moe_shared"][f"m{M}"] = with_shared
                 result["moe_w4a4"][f"m{M}"] = w4a4
-        if "moe_skew" in legs:
-            result["moe_skew"] = moe_skew_legs(torch, nv, traffic, mo, K_, W_, ceil)
+        if skew_cases:
+            result["moe_skew"] = moe_skew_legs(torch, nv, traffic, mo, K_, W_, ceil, skew_cases)
         del mo
     if "w4a4" in legs:
         result["w4a4_ffn_m2"] = leg_w4a4(torch, nv, workloads, traffic, K_, W_, ceil, want_cpu)
