@@ -17,6 +17,30 @@ __device__ __forceinline__ u32x4_t load_stream(const void* p) {
   return __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
 }
 
+// Buffer loads with a byte bound (raw buffer resource, no stride): a lane
+// whose offset lies past the bound reads zeros and touches no memory. Kernels
+// send masked lanes to kBufOob, past every bound used here, instead of
+// clamping addresses or selecting after the load (a select right after a
+// load makes the wavefront wait for it). AUX is the cache policy: kBufNt for
+// streamed weights, 0 for data that other workgroups read again.
+constexpr int kBufOob = 0x7FFFFFF0;
+constexpr uint32_t kBufMaxRecords = 0x7FFFFF00u;
+constexpr int kBufNt = 2;
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void* p, int64_t bytes) {
+  const int64_t n =
+      bytes <= 0 ? 0 : (bytes < (int64_t)kBufMaxRecords ? bytes : (int64_t)kBufMaxRecords);
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)n, 0x00020000);
+}
+template <int AUX>
+__device__ __forceinline__ u32x4_t buf_load16(__amdgpu_buffer_rsrc_t r, int off) {
+  return __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, AUX));
+}
+template <int AUX>
+__device__ __forceinline__ uint32_t buf_load4(__amdgpu_buffer_rsrc_t r, int off) {
+  return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, AUX);
+}
+
 // ------------------------------------------------------------------ decode
 
 // Two E2M1 codes (byte `sel` of `word`; low nibble -> .x) to bf16. The scale

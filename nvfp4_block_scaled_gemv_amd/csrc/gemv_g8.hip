@@ -22,23 +22,25 @@
 // in fp32; the weights enter as plain E2M1 values (exact in bf16).
 //
 // x in whole cache lines. A window is 64 k (4 blocks, 128 bytes of x per
-// token). One 16-byte load per lane covers a window for all 8 tokens with
-// every line fully used: lane (i, g) reads token i % 8's piece p of the
-// window, p = g, g + 2 (i < 8: g = 0, 1, 2, 3 -> p = 0, 1, 4, 5) and
-// p = g + 6, g (i >= 8: g = 0, 1, 2, 3 -> p = 6, 7, 2, 3), pieces 2b, 2b+1
-// being block b. Then lanes (t, 0..1) hold block 0 and lanes (t + 8, 2..3)
-// block 1: with the other lanes zeroed this is the A operand of the MFMA
-// that pairs blocks 0 and 1. The other lanes hold blocks 2 and 3 in the
-// places the first MFMA uses, one half-wave away: exchanging the halves
-// (v_permlane32_swap) gives the A operand of the MFMA that pairs blocks 2 and
-// 3. The weights follow the same k order: for the first MFMA of a window
-// lane (n, g) feeds dword g of row n's 32 code bytes of the window, for the
-// second dword 4 + g.
+// token, pieces 2b and 2b+1 of 16 bytes being block b). One 16-byte load per
+// lane covers a window for all 8 tokens with every line fully used. The
+// lanes that carry x in an A operand ("live": rows i < 8 in lane groups 0
+// and 1, rows i >= 8 in groups 2 and 3) load token i % 8's piece g, which is
+// exactly the A operand of the MFMA pairing blocks 0 and 1 once the other
+// lanes are zeroed. The other lanes load piece 4 + g of the same token: that
+// is what the live lane i ^ 8 of the same 16-lane row needs for the MFMA
+// pairing blocks 2 and 3, so a DPP row rotation by 8 folded into the
+// zeroing select builds that operand. Tokens past M lie past the bound of
+// x's buffer resource and load as zeros. The weights follow the same k
+// order: for the first MFMA of a window lane (n, g) feeds dword g of row
+// n's 32 code bytes of the window, for the second dword 4 + g.
 //
 // Weights in whole cache lines. A slice of a tile is 16 rows x 128 code
 // bytes; it is loaded row-major (eight rows of 128 bytes per load) and
 // transposed through a small per-wavefront LDS buffer, together with its 16
-// rows x 16 scale bytes.
+// rows x 16 scale bytes. All loads are bounded buffer loads from resources
+// based at the workgroup's first row: rows past N read as zeros, so no
+// address is clamped.
 #include "device.h"
 #include "internal.h"
 
@@ -71,11 +73,9 @@ __device__ __forceinline__ bf16x8_t g8_bf16x8(u32x4_t v) {
   return r;
 }
 
-// u[l ^ 32] in every lane (the two half-waves exchanged)
-__device__ __forceinline__ uint32_t g8_swap_halves(uint32_t u, bool low_half) {
-  const auto p = __builtin_amdgcn_permlane32_swap(u, u, false, false);
-  // p[0] = {u[0..31], u[0..31]}, p[1] = {u[32..63], u[32..63]}
-  return low_half ? p[1] : p[0];
+// v of lane l ^ 8 (the other half of the lane's 16-lane row)
+__device__ __forceinline__ uint32_t g8_row_ror8(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x128, 0xF, 0xF, false);   // row_ror:8
 }
 
 // v + (v of lane l + 32) in lanes l < 32
@@ -115,43 +115,48 @@ __global__ __launch_bounds__(64 * kG8MaxWaves) void k_gemv_g8(const SegTable tab
   // ---- issue every load: x first (an L2 round trip, needed by the first
   // MFMA), then the weights slice by slice, so that the waits before slice s
   // leave the later slices in flight. Every wavefront has exactly S slices
-  // (W S 256 = K) and every lane loads (tokens >= M read token 0's row and
-  // are zeroed after): the code has no branches, and the scheduling barriers
-  // keep the issue order, so the compiler's wait before each slice counts
-  // only the loads issued before it.
+  // (W S 256 = K) and every lane loads: the code has no branches, and the
+  // scheduling barriers keep the issue order, so the compiler's wait before
+  // each slice counts only the loads issued before it.
   u32x4_t q[S][TW][2];
   uint32_t sc[S][TW];
   u32x4_t xv[S][4];
-  const int rr = lane >> 3;                          // row-major load: row rr, 16 B at 16 (l % 8)
+  const bool live = (i < 8) == (g < 2);    // lanes of the A operands that carry x
   const int t = i & 7;
-  const int piece = i < 8 ? (g < 2 ? g : g + 2) : (g < 2 ? g + 6 : g);
-  const bool tok_ok = t < M;
-  const uint16_t* xp = x + (int64_t)(tok_ok ? t : 0) * K + kw + 8 * piece;
+  const __amdgpu_buffer_rsrc_t rx = buf_rsrc(x, (int64_t)M * K * 2);
+  const __amdgpu_buffer_rsrc_t rc = buf_rsrc(sg.codes + n0 * cb, (N - n0) * cb);
+  const __amdgpu_buffer_rsrc_t rs = buf_rsrc(sg.scales + n0 * sbytes, (N - n0) * sbytes);
+  // byte offsets (unsigned: an out-of-bound base plus a window offset stays
+  // past the bound and below 2^32)
+  const uint32_t xoff =
+      t < M ? (uint32_t)((t * K + kw + 8 * (live ? g : 4 + g)) * 2) : (uint32_t)kBufOob;
+  const int rr = lane >> 3;                          // row-major load: row rr, 16 B at 16 (l % 8)
+  const uint32_t coff = (uint32_t)(rr * cb + (kw >> 1)) + 16u * (lane & 7);
+  const uint32_t soff = (uint32_t)((lane >> 2) * sbytes + (kw >> 4)) + 4u * (lane & 3);
 #pragma unroll
   for (int s = 0; s < S; ++s)
 #pragma unroll
     for (int j = 0; j < 4; ++j)
-      xv[s][j] = *reinterpret_cast<const u32x4_t*>(xp + s * kG8Slice + 64 * j);
+      xv[s][j] = buf_load16<0>(rx, (int)(xoff + 2u * (s * kG8Slice + 64 * j)));
   __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
   for (int s = 0; s < S; ++s) {
-    const int64_t k0 = kw + (int64_t)s * kG8Slice;
 #pragma unroll
     for (int u = 0; u < TW; ++u) {
-      const int64_t ra = n0 + 16 * u + rr, rb = ra + 8, rs = n0 + 16 * u + (lane >> 2);
-      const uint8_t* cbase = sg.codes + (k0 >> 1) + 16 * (lane & 7);
-      q[s][u][0] = load_stream(cbase + (ra < N ? ra : N - 1) * cb);
-      q[s][u][1] = load_stream(cbase + (rb < N ? rb : N - 1) * cb);
-      sc[s][u] = *reinterpret_cast<const uint32_t*>(sg.scales + (rs < N ? rs : N - 1) * sbytes +
-                                                     (k0 >> 4) + 4 * (lane & 3));
+      const uint32_t cu = coff + (uint32_t)(16 * u * cb) + 128u * s;
+      q[s][u][0] = buf_load16<kBufNt>(rc, (int)cu);
+      q[s][u][1] = buf_load16<kBufNt>(rc, (int)(cu + (uint32_t)(8 * cb)));
+      sc[s][u] = buf_load4<0>(rs, (int)(soff + (uint32_t)(16 * u * sbytes) + 16u * s));
     }
     __builtin_amdgcn_sched_barrier(0);
   }
 
   // ---- compute
-  const bool live = (i < 8) == (g < 2);   // lanes of the A operand that carry x
-  const bool low_half = lane < 32;
-  const int sh = g < 2 ? 0 : 8;           // the lane's block: first (0) or second (8) byte
+  const int sh = g < 2 ? 0 : 8;
+  // all ones in the live lanes, zero elsewhere: an AND, not a select, so
+  // that the row rotation is never moved under a lane mask (a DPP read from
+  // a lane outside the mask would not see its value)
+  const uint32_t keep = live ? 0xFFFFFFFFu : 0u;           // the lane's block: first (0) or second (8) byte
   // one partial per slice and tile: the workgroup sums the slices in slice
   // order, so the result does not depend on how K is split over wavefronts
   f32x4_t acc[S][TW];
@@ -170,9 +175,9 @@ __global__ __launch_bounds__(64 * kG8MaxWaves) void k_gemv_g8(const SegTable tab
     auto prep = [&](int j, u32x4_t (&aj)[2]) {
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
-        const uint32_t v = tok_ok ? xv[s][j][c] : 0u;
-        aj[0][c] = live ? v : 0u;
-        aj[1][c] = g8_swap_halves(live ? 0u : v, low_half);
+        const uint32_t v = xv[s][j][c];
+        aj[0][c] = v & keep;
+        aj[1][c] = g8_row_ror8(v) & keep;
       }
     };
     if constexpr (TW > 1) {

@@ -98,21 +98,6 @@ struct MtW {
   uint32_t s[4];
 };
 
-// Buffer loads with a byte bound: past it they return zeros and touch no
-// memory. kMtOob is an offset past every bound used here.
-constexpr int kMtOob = 0x7FFFFFF0;
-constexpr uint32_t kMtMaxRecords = 0x7FFFFF00u;
-constexpr int kMtNt = 2;   // cache policy: non-temporal (streamed weights)
-
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t mt_rsrc(const void* p, int64_t bytes) {
-  const int64_t n = bytes <= 0 ? 0 : (bytes < (int64_t)kMtMaxRecords ? bytes : (int64_t)kMtMaxRecords);
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)n, 0x00020000);
-}
-template <int AUX>
-__device__ __forceinline__ u32x4_t mt_load16(__amdgpu_buffer_rsrc_t r, int off) {
-  return __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, AUX));
-}
-
 }  // namespace
 
 // KA: K % 128 == 0, so a lane's 8 scale bytes of a slice are one aligned
@@ -155,9 +140,9 @@ __global__ __launch_bounds__(64 * kMtMaxWaves) void k_gemv_mt(const SegTable tab
   // and pieces past K are sent past it. Codes go row-major (eight whole
   // 128-byte lines per load) through the wavefront's LDS stage; each lane
   // loads its own scale bytes.
-  const __amdgpu_buffer_rsrc_t rc = mt_rsrc(sg.codes + n0 * cb, (N - n0) * cb);
-  const __amdgpu_buffer_rsrc_t rs = mt_rsrc(sg.scales + n0 * sbytes, (N - n0) * sbytes);
-  const __amdgpu_buffer_rsrc_t rx = mt_rsrc(x, (int64_t)M * K * 2);
+  const __amdgpu_buffer_rsrc_t rc = buf_rsrc(sg.codes + n0 * cb, (N - n0) * cb);
+  const __amdgpu_buffer_rsrc_t rs = buf_rsrc(sg.scales + n0 * sbytes, (N - n0) * sbytes);
+  const __amdgpu_buffer_rsrc_t rx = buf_rsrc(x, (int64_t)M * K * 2);
   int coff[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) coff[i] = (int)((8 * i + (lane >> 3)) * cb) + 16 * (lane & 7);
@@ -166,18 +151,18 @@ __global__ __launch_bounds__(64 * kMtMaxWaves) void k_gemv_mt(const SegTable tab
     const int64_t k0 = sl * kMtSlice;
     const bool cok = sl < slices && k0 + 32 * (lane & 7) < K;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) wt.q[i] = mt_load16<kMtNt>(rc, cok ? coff[i] + (int)(k0 >> 1) : kMtOob);
+    for (int i = 0; i < 4; ++i) wt.q[i] = buf_load16<kBufNt>(rc, cok ? coff[i] + (int)(k0 >> 1) : kBufOob);
     if (KA) {
       const bool v = sl < slices && k0 + 128 * h < K;
       const uint2 sv = __builtin_bit_cast(
-          uint2, __builtin_amdgcn_raw_buffer_load_b64(rs, v ? soff + (int)(k0 >> 4) : kMtOob, 0, 0));
+          uint2, __builtin_amdgcn_raw_buffer_load_b64(rs, v ? soff + (int)(k0 >> 4) : kBufOob, 0, 0));
       wt.s[0] = sv.x;
       wt.s[1] = sv.y;
     } else {
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
         const bool v = sl < slices && k0 + 128 * h + 32 * c < K;
-        wt.s[c] = __builtin_amdgcn_raw_buffer_load_b16(rs, v ? soff + (int)(k0 >> 4) + 2 * c : kMtOob,
+        wt.s[c] = __builtin_amdgcn_raw_buffer_load_b16(rs, v ? soff + (int)(k0 >> 4) + 2 * c : kBufOob,
                                                        0, 0);
       }
     }
@@ -219,7 +204,7 @@ __global__ __launch_bounds__(64 * kMtMaxWaves) void k_gemv_mt(const SegTable tab
 #pragma unroll
     for (int p = 0; p < P; ++p) {
       const bool v = sl < slices && k0 + xk[p] < K;
-      xs.v[p] = mt_load16<0>(rx, v ? xsrc[p] + (int)(k0 * 2) : kMtOob);
+      xs.v[p] = buf_load16<0>(rx, v ? xsrc[p] + (int)(k0 * 2) : kBufOob);
     }
   };
   auto stage_store = [&](const XStage& xs, unsigned char* buf) {

@@ -89,8 +89,13 @@ struct SegCursor {
 };
 
 #if defined(__HIPCC__) || defined(__HIP__)
-// The segment of work unit u (wavefront-uniform) with its pointers; a scan with
-// constant indices so that the table stays in kernel-argument (scalar) memory.
+// The segment of work unit u (wavefront-uniform) with its pointers. The scan
+// reads only start[] (start is non-decreasing, so the segment is the number
+// of later starts at or below u, empty segments included), then the entry is
+// read with that index straight from the kernel arguments: a scan that
+// carried every field through a chain of selects held the whole table in
+// scalar registers, which overflowed into vector-register lanes (a few
+// hundred v_writelane/v_readlane per wavefront).
 struct Seg {
   const uint8_t* codes;
   const uint8_t* scales;
@@ -102,20 +107,10 @@ struct Seg {
 };
 
 __device__ __forceinline__ Seg find_seg(const SegTable& t, int64_t u) {
-  Seg s = {t.codes[0], t.scales[0], t.gscale[0], t.y[0], t.N[0], u, 0};
+  int k = 0;
 #pragma unroll
-  for (int k = 1; k < kMaxSegments; ++k) {
-    if (k < t.n && u >= t.start[k]) {
-      s.codes = t.codes[k];
-      s.scales = t.scales[k];
-      s.gscale = t.gscale[k];
-      s.y = t.y[k];
-      s.N = t.N[k];
-      s.unit = u - t.start[k];
-      s.index = k;
-    }
-  }
-  return s;
+  for (int j = 1; j < kMaxSegments; ++j) k += (j < t.n && u >= t.start[j]) ? 1 : 0;
+  return Seg{t.codes[k], t.scales[k], t.gscale[k], t.y[k], t.N[k], u - t.start[k], k};
 }
 #endif
 
