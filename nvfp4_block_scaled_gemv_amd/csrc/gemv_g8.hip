@@ -50,6 +50,7 @@ namespace {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
 
 constexpr int kG8Slice = 256;                      // k per slice
 constexpr int kG8Pitch = 144;                      // staged code row: 128 bytes + 16 (bank skew)
@@ -75,17 +76,23 @@ __device__ __forceinline__ bf16x8_t g8_bf16x8(u32x4_t v) {
 
 // v of lane l ^ 8 (the other half of the lane's 16-lane row)
 __device__ __forceinline__ uint32_t g8_row_ror8(uint32_t v) {
-  return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x128, 0xF, 0xF, false);   // row_ror:8
+  return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x128, 0xF, 0xF, true);   // row_ror:8
 }
 
-// v + (v of lane l + 32) in lanes l < 32
-__device__ __forceinline__ f32x4_t g8_add_upper_half(f32x4_t v) {
-  f32x4_t r;
+// The two blocks' halves of a tile partial added: lanes l and l + 32 hold the
+// same (token, row) for the two blocks of each MFMA. One half-wave exchange
+// per pair of registers: lanes < 32 receive registers 0 and 2 (tokens
+// 4 g + 0, 4 g + 2), lanes >= 32 registers 1 and 3 (tokens 4 (g - 2) + 1,
+// 4 (g - 2) + 3); each sum is (first block) + (second block).
+__device__ __forceinline__ f32x2_t g8_merge_halves(f32x4_t v) {
+  f32x2_t r;
 #pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    const uint32_t u = __float_as_uint(v[k]);
-    const auto p = __builtin_amdgcn_permlane32_swap(u, u, false, false);
-    r[k] = v[k] + __uint_as_float(p[1]);
+  for (int k = 0; k < 2; ++k) {
+    const auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(v[2 * k]),
+                                                    __float_as_uint(v[2 * k + 1]), false, false);
+    // p[0] = {v[2k] of lanes 0..31, v[2k+1] of lanes 0..31},
+    // p[1] = {v[2k] of lanes 32..63, v[2k+1] of lanes 32..63}
+    r[k] = __uint_as_float(p[0]) + __uint_as_float(p[1]);
   }
   return r;
 }
@@ -96,7 +103,7 @@ __device__ __forceinline__ f32x4_t g8_add_upper_half(f32x4_t v) {
 // wavefronts (128 registers per lane). codes, scales and x are plain loads:
 // the code is straight-line, so the compiler's waits count exactly.
 template <int M, int TW, int S>
-__global__ __launch_bounds__(64 * kG8MaxWaves) void k_gemv_g8(const SegTable tab,
+__global__ __launch_bounds__(64 * kG8MaxWaves) __attribute__((amdgpu_waves_per_eu(S == 1 && TW <= 2 ? 8 : 1))) void k_gemv_g8(const SegTable tab,
                                                               const uint16_t* __restrict__ x,
                                                               int64_t K) {
   extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
@@ -104,13 +111,13 @@ __global__ __launch_bounds__(64 * kG8MaxWaves) void k_gemv_g8(const SegTable tab
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int W = blockDim.x >> 6;
   const int i = lane & 15, g = lane >> 4;
-  const Seg sg = find_seg(tab, blockIdx.x);
+  const Seg sg = find_seg32(tab, (int)blockIdx.x);
   const int64_t N = sg.N;
   const int64_t n0 = sg.unit * (16 * TW);
   const int64_t kw = (int64_t)w * S * kG8Slice;     // this wavefront's first k
   const int64_t cb = K >> 1, sbytes = K >> 4;
   unsigned char* const stage = lds + w * kG8StageBytes;
-  f32x4_t* const red = reinterpret_cast<f32x4_t*>(lds + W * kG8StageBytes);   // [slices][TW][32]
+  f32x2_t* const red = reinterpret_cast<f32x2_t*>(lds + W * kG8StageBytes);   // [slices][TW][64]
 
   // ---- issue every load: x first (an L2 round trip, needed by the first
   // MFMA), then the weights slice by slice, so that the waits before slice s
@@ -126,13 +133,15 @@ __global__ __launch_bounds__(64 * kG8MaxWaves) void k_gemv_g8(const SegTable tab
   const __amdgpu_buffer_rsrc_t rx = buf_rsrc(x, (int64_t)M * K * 2);
   const __amdgpu_buffer_rsrc_t rc = buf_rsrc(sg.codes + n0 * cb, (N - n0) * cb);
   const __amdgpu_buffer_rsrc_t rs = buf_rsrc(sg.scales + n0 * sbytes, (N - n0) * sbytes);
-  // byte offsets (unsigned: an out-of-bound base plus a window offset stays
-  // past the bound and below 2^32)
+  // byte offsets, 32-bit (K <= 16384 keeps every offset below 2^20), and
+  // unsigned: an out-of-bound base plus a window offset stays past the bound
+  // and below 2^32
+  const uint32_t Ku = (uint32_t)K, cbu = (uint32_t)cb, sbu = (uint32_t)sbytes, kwu = (uint32_t)kw;
   const uint32_t xoff =
-      t < M ? (uint32_t)((t * K + kw + 8 * (live ? g : 4 + g)) * 2) : (uint32_t)kBufOob;
+      t < M ? (t * Ku + kwu + 8u * (live ? g : 4 + g)) * 2u : (uint32_t)kBufOob;
   const int rr = lane >> 3;                          // row-major load: row rr, 16 B at 16 (l % 8)
-  const uint32_t coff = (uint32_t)(rr * cb + (kw >> 1)) + 16u * (lane & 7);
-  const uint32_t soff = (uint32_t)((lane >> 2) * sbytes + (kw >> 4)) + 4u * (lane & 3);
+  const uint32_t coff = rr * cbu + (kwu >> 1) + 16u * (lane & 7);
+  const uint32_t soff = (lane >> 2) * sbu + (kwu >> 4) + 4u * (lane & 3);
 #pragma unroll
   for (int s = 0; s < S; ++s)
 #pragma unroll
@@ -143,10 +152,10 @@ __global__ __launch_bounds__(64 * kG8MaxWaves) void k_gemv_g8(const SegTable tab
   for (int s = 0; s < S; ++s) {
 #pragma unroll
     for (int u = 0; u < TW; ++u) {
-      const uint32_t cu = coff + (uint32_t)(16 * u * cb) + 128u * s;
+      const uint32_t cu = coff + 16u * u * cbu + 128u * s;
       q[s][u][0] = buf_load16<kBufNt>(rc, (int)cu);
-      q[s][u][1] = buf_load16<kBufNt>(rc, (int)(cu + (uint32_t)(8 * cb)));
-      sc[s][u] = buf_load4<0>(rs, (int)(soff + (uint32_t)(16 * u * sbytes) + 16u * s));
+      q[s][u][1] = buf_load16<kBufNt>(rc, (int)(cu + 8u * cbu));
+      sc[s][u] = buf_load4<0>(rs, (int)(soff + 16u * u * sbu + 16u * s));
     }
     __builtin_amdgcn_sched_barrier(0);
   }
@@ -155,8 +164,11 @@ __global__ __launch_bounds__(64 * kG8MaxWaves) void k_gemv_g8(const SegTable tab
   const int sh = g < 2 ? 0 : 8;
   // all ones in the live lanes, zero elsewhere: an AND, not a select, so
   // that the row rotation is never moved under a lane mask (a DPP read from
-  // a lane outside the mask would not see its value)
-  const uint32_t keep = live ? 0xFFFFFFFFu : 0u;           // the lane's block: first (0) or second (8) byte
+  // a lane outside the mask would not see its value) and folds into it
+  // (v_and_b32 with a DPP source). The empty asm hides the value, which
+  // would otherwise turn the AND back into a select.
+  uint32_t keep = live ? 0xFFFFFFFFu : 0u;
+  asm volatile("" : "+v"(keep));           // the lane's block: first (0) or second (8) byte
   // one partial per slice and tile: the workgroup sums the slices in slice
   // order, so the result does not depend on how K is split over wavefronts
   f32x4_t acc[S][TW];
@@ -228,25 +240,20 @@ __global__ __launch_bounds__(64 * kG8MaxWaves) void k_gemv_g8(const SegTable tab
 #pragma unroll
   for (int s = 0; s < S; ++s)
 #pragma unroll
-    for (int u = 0; u < TW; ++u) {
-      const f32x4_t v = g8_add_upper_half(acc[s][u]);   // lanes l and l + 32: the two blocks
-      if (lane < 32) red[((w * S + s) * TW + u) * 32 + lane] = v;
-    }
+    for (int u = 0; u < TW; ++u) red[((w * S + s) * TW + u) * 64 + lane] = g8_merge_halves(acc[s][u]);
   __syncthreads();
   const float gs = *sg.gscale;
   const int slices = W * S;
-  // (tile u, lane pair) entries dealt to the wavefronts: 64 per wavefront
-  for (int e = w * 64 + lane; e < TW * 32; e += W * 64) {
-    const int u = e >> 5, l = e & 31;
-    f32x4_t sum = red[u * 32 + l];
-    for (int v = 1; v < slices; ++v) sum += red[(v * TW + u) * 32 + l];
+  // (tile u, lane) entries dealt to the wavefronts: 64 per wavefront
+  for (int e = w * 64 + lane; e < TW * 64; e += W * 64) {
+    const int u = e >> 6, l = e & 63;
+    f32x2_t sum = red[u * 64 + l];
+    for (int v = 1; v < slices; ++v) sum += red[(v * TW + u) * 64 + l];
     const int64_t n = n0 + 16 * u + (l & 15);
+    const int m0 = 4 * ((l >> 4) & 1) + (l >> 5);   // tokens m0 and m0 + 2
     if (n < N) {
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int m = 4 * (l >> 4) + r;   // lane (i, g < 2) held D[4g + r][i]
-        if (m < M) sg.y[(int64_t)m * N + n] = sum[r] * gs;
-      }
+      if (m0 < M) sg.y[(int64_t)m0 * N + n] = sum[0] * gs;
+      if (m0 + 2 < M) sg.y[(int64_t)(m0 + 2) * N + n] = sum[1] * gs;
     }
   }
 }
@@ -266,30 +273,24 @@ bool g8_applicable(int M, int64_t K) {
 }
 
 // Launch shape, from A/B sweeps (1024 .. 151936 rows at K = 4096 and 12288,
-// M = 5 and 8; each choice within a few percent of the best measured):
-// TW tiles per workgroup so that every CU gets one or two workgroups of
-// TW tiles -- 3 from 768 tiles up (12288 rows: 256 workgroups), 2 from 384 --
-// and for very tall matrices (from 3072 tiles) 2 tiles with 2 slices per
-// wavefront (x read once per 32 rows by half as many wavefronts). S: 2 slices
-// per wavefront where K allows it (fewer, fuller wavefronts), 1 with TW >= 2
-// below 3072 tiles, else the smallest split that fits 16 wavefronts. The
-// summation order does not depend on the shape.
+// M = 5 and 8): TW tiles per workgroup so that every CU gets one or two
+// workgroups of TW tiles -- 3 from 768 tiles up to 3072 (12288 rows: 256
+// workgroups), 2 from 384 and from 3072 up (the LM head: many rounds of
+// smaller workgroups balance better), one tile where K needs more than one
+// slice per wavefront -- and S, the slices per wavefront, as small as 16
+// wavefronts allow: one slice per wavefront at K = 4096 keeps
+// the registers at about 64, so each CU holds 32 wavefronts (two
+// workgroups) where two slices per wavefront held 16 (LM head at M = 8:
+// 74.7 against 85.9 us; 4096 and 1024 rows: 5.3 against 5.8 us and 5.1
+// against 5.5 us). The summation order does not depend on the shape.
 void g8_shape(int64_t rows, int64_t K, int* TW, int* S, int* W) {
   const int64_t tiles = (rows + 15) / 16;
-  int tw = 1, s = 0;
-  if (tiles >= 3072 && g8_split_ok(K, 2)) {
-    tw = 2;
-    s = 2;
-  } else if (tiles >= 384 && g8_split_ok(K, 1)) {
-    tw = tiles >= 768 ? 3 : 2;
-    s = 1;
-  } else if (g8_split_ok(K, 2)) {
-    s = 2;
-  } else {
-    for (int c = 1; c <= 4 && !s; ++c)
-      if (g8_split_ok(K, c)) s = c;
-  }
-  *TW = tw;
+  int s = 0;
+  for (int c = 1; c <= 4 && !s; ++c)
+    if (g8_split_ok(K, c)) s = c;
+  // several tiles per workgroup only with one slice per wavefront (the
+  // registers of more slices and tiles would not fit)
+  *TW = s != 1 ? 1 : (tiles >= 768 && tiles < 3072) ? 3 : (tiles >= 384 ? 2 : 1);
   *S = s;
   *W = s ? (int)(K / kG8Slice / s) : 0;
 }
@@ -303,7 +304,7 @@ hipError_t launch_gemv_g8_shape(const SegDesc* d, int n, const uint16_t* x, int 
   const SegTable tab = make_seg_table(d, n, 16 * TW);
   const int64_t units = tab.start[kMaxSegments];
   if (units > 0x7FFFFFFF) return hipErrorInvalidValue;
-  const size_t lds = (size_t)W * kG8StageBytes + (size_t)slices * TW * 32 * sizeof(f32x4_t);
+  const size_t lds = (size_t)W * kG8StageBytes + (size_t)slices * TW * 64 * sizeof(f32x2_t);
 #define NVFP4_G8(MM, TT, SS)                                                                 \
   hipLaunchKernelGGL((k_gemv_g8<MM, TT, SS>), dim3((unsigned)units),                         \
                      dim3(64 * (unsigned)W), lds, stream, tab, x, K)
@@ -315,7 +316,6 @@ hipError_t launch_gemv_g8_shape(const SegDesc* d, int n, const uint16_t* x, int 
     case 14: NVFP4_G8(MM, 1, 4); break;                    \
     case 21: NVFP4_G8(MM, 2, 1); break;                    \
     case 31: NVFP4_G8(MM, 3, 1); break;                    \
-    case 22: NVFP4_G8(MM, 2, 2); break;                    \
     default: return hipErrorInvalidValue;                  \
   }
   switch (M) {

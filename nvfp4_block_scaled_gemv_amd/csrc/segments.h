@@ -112,6 +112,15 @@ __device__ __forceinline__ Seg find_seg(const SegTable& t, int64_t u) {
   for (int j = 1; j < kMaxSegments; ++j) k += (j < t.n && u >= t.start[j]) ? 1 : 0;
   return Seg{t.codes[k], t.scales[k], t.gscale[k], t.y[k], t.N[k], u - t.start[k], k};
 }
+
+// The same for a launch whose units number below 2^31 (its launcher checks):
+// the comparisons are 32-bit and stay on the scalar unit.
+__device__ __forceinline__ Seg find_seg32(const SegTable& t, int u) {
+  int k = 0;
+#pragma unroll
+  for (int j = 1; j < kMaxSegments; ++j) k += (j < t.n && u >= (int)t.start[j]) ? 1 : 0;
+  return Seg{t.codes[k], t.scales[k], t.gscale[k], t.y[k], t.N[k], (int64_t)(u - (int)t.start[k]), k};
+}
 #endif
 
 }  // namespace nvfp4

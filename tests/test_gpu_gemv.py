@@ -89,14 +89,14 @@ def test_split_k_shapes(M, N, K):
 
 @pytest.mark.parametrize("M", [3, 5, 8])
 @pytest.mark.parametrize("N,K", [(49157, 2048), (12291, 4096), (6150, 2048), (100, 1024),
-                                 (33, 3840), (300, 12288), (50, 16384)])
+                                 (33, 3840), (70, 8192), (300, 12288), (50, 16384)])
 def test_matrix_core_launch_shapes(M, N, K):
     """Every launch shape of the eight-token matrix-core kernel, each with a
-    ragged last tile: two tiles per workgroup with two slices per wavefront
-    (3073 tiles), three and two tiles with one slice (769 and 385 tiles), one
-    tile with two, one (15 wavefronts), three (K = 12288) and four (K = 16384)
-    slices per wavefront. Large N compares a sample of rows, the last
-    included."""
+    ragged last tile: two tiles per workgroup from 3073 tiles up, three from
+    769 and two from 385 tiles (one slice per wavefront), one tile with one
+    slice (4 and 15 wavefronts), two (K = 8192), three (K = 12288) and four
+    (K = 16384) slices per wavefront. Large N compares a sample of rows, the
+    last included."""
     say(f"[gemv] matrix-core shape M={M} N={N} K={K}")
     codes, scales = workloads.random_nvfp4(16, M, N + K, N, K)
     x = workloads.x_bf16(16, M, N + K, M, K)
