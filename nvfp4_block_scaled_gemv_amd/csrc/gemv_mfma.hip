@@ -351,6 +351,7 @@ hipError_t launch_gemv_mfma_shape(const SegDesc* d, int n, const uint16_t* x, in
 
 hipError_t launch_gemv_mfma(const SegDesc* d, int n, const uint16_t* x, int M, int64_t K,
                             hipStream_t stream) {
+  if (g8r_applicable(M, n, n == 1 ? d[0].N : 0, K)) return launch_gemv_g8r(d[0], x, M, K, stream);
   if (g8_applicable(M, K)) return launch_gemv_g8(d, n, x, M, K, stream);
   if (splitk_applicable(M, K)) return launch_gemv_splitk(d, n, x, M, K, stream);
   int64_t tiles = 0;

@@ -44,6 +44,12 @@ hipError_t launch_gemv_g8(const SegDesc* d, int n, const uint16_t* x, int M, int
                           hipStream_t stream);
 hipError_t launch_gemv_g8_shape(const SegDesc* d, int n, const uint16_t* x, int M, int64_t K,
                                 int TW, int S, hipStream_t stream);
+// 3 <= M <= 8 on one very tall matrix (2^17 rows and more, K % 256 == 0,
+// K <= 4096; gemv_g8r.hip): wavefronts split the rows, x held once per
+// workgroup in LDS
+bool g8r_applicable(int M, int n, int64_t N, int64_t K);
+hipError_t launch_gemv_g8r(const SegDesc& d, const uint16_t* x, int M, int64_t K,
+                           hipStream_t stream);
 // 9 <= M <= 128 (gemv_mt.hip): G token groups of 32 per workgroup in
 // `tblocks` token blocks, R row wavefronts of 32 rows sharing staged x, W
 // k-groups splitting K; mt_shape picks one from the rows, M and K.

@@ -1,0 +1,82 @@
+"""GPU GEMV at 3 <= M <= 8 on very tall single matrices (2^17 rows and more,
+K a multiple of 256 up to 4096), where the wavefronts split the rows and x
+sits once per workgroup in LDS, against the oracle within
+|y - y_ref| <= 1e-3 sum|w x| + 1e-6: the LM head at every token count, and
+ragged shapes whose rows per wavefront leave a partial last tile, fill
+exactly two or three tiles, or need more than one workgroup per CU. Rows are
+sampled at the first and last rows, around the first wavefronts' row
+boundaries and at random."""
+import numpy as np
+import pytest
+
+import oracle
+import workloads
+import nvfp4_block_scaled_gemv_amd as nv
+from gpu_util import check_tol, dev, dev_x, host, say
+
+pytestmark = pytest.mark.gpu
+
+
+def rows_per_wave(N):
+    """The launch's rows per wavefront: 16 wavefronts per workgroup, at least
+    256 workgroups, at most 48 rows per wavefront."""
+    grid = max(256, -(-N // (16 * 48)))
+    return -(-N // (grid * 16))
+
+
+def sample_rows(N, n, seed):
+    rpw = rows_per_wave(N)
+    fixed = [0, 1, 15, 16, 31, 32]
+    for b in (rpw, 2 * rpw, 3 * rpw, 100 * rpw):
+        fixed += [b - 1, b, b + 1, b + 15, b + 16]
+    fixed += [N - 17, N - 16, N - 2, N - 1]
+    fixed = [r for r in fixed if 0 <= r < N]
+    return np.unique(np.concatenate([fixed, np.random.default_rng(seed).choice(N, n, replace=False)]))
+
+
+def compare(y, c, s, g, x, rows, what):
+    y_ref, ad = oracle.gemv(c, s, g, x, rows=rows)
+    r = check_tol(y[:, rows], y_ref, ad, what)
+    say(f"  {what}: max err / tol = {r:.3e}")
+
+
+@pytest.fixture(scope="module")
+def lm_head_packed():
+    W = workloads.dense_weights(3, 0, 0, 151936, 4096)
+    return oracle.pack(W), nv.pack(dev(W))
+
+
+@pytest.mark.parametrize("M", [3, 4, 5, 6, 7, 8])
+def test_lm_head_up_to_eight_tokens(lm_head_packed, M):
+    N, K = 151936, 4096
+    say(f"[gemv-tall] LM head {N}x{K} M={M}")
+    (c0, s0, g0), (c1, s1, g1) = lm_head_packed
+    x = workloads.x_bf16(3, 3, M, M, K)
+    y = host(nv.gemv(c1, s1, g1, dev_x(x)))
+    compare(y, c0, s0, g0, x, sample_rows(N, 800, M), f"LM head M={M}")
+    assert np.all(np.isfinite(y))
+
+
+@pytest.mark.parametrize("M,N,K", [(8, 131072, 256), (3, 131073, 1024), (5, 200003, 4096),
+                                   (8, 393217, 512), (7, 150001, 2304)])
+def test_tall_ragged_shapes(M, N, K):
+    """Rows per wavefront 32 (two whole tiles), 33 (a third tile of one
+    row), 48 (three whole tiles, 261 workgroups), 48 over 513 workgroups
+    (two per CU and more), and K = 2304 (9 slices: the ring's last round
+    half empty)."""
+    say(f"[gemv-tall] ragged M={M} N={N} K={K}")
+    codes, scales = workloads.random_nvfp4(17, M, N % 1000 + K, N, K)
+    x = workloads.x_bf16(17, M, N % 1000 + K, M, K)
+    g = np.float32(0.0123)
+    y = host(nv.gemv(dev(codes), dev(scales), dev(np.array([g], np.float32)), dev_x(x)))
+    compare(y, codes, scales, g, x, sample_rows(N, 600, N), f"{N}x{K} M={M}")
+    assert np.all(np.isfinite(y))
+
+
+def test_tall_deterministic(lm_head_packed):
+    """Two calls give the same bits."""
+    _, (c1, s1, g1) = lm_head_packed
+    x = dev_x(workloads.x_bf16(3, 4, 0, 8, 4096))
+    a = host(nv.gemv(c1, s1, g1, x))
+    b = host(nv.gemv(c1, s1, g1, x))
+    assert np.array_equal(a.view(np.uint32), b.view(np.uint32))

@@ -85,7 +85,7 @@ def test_mfma_kernel_leaves_pending_loads_alone(tmp_path):
     assert "scratch_" not in text
 
 
-KERNEL_FILES = ["gemv.hip", "gemv_g8.hip", "gemv_mfma.hip", "gemv_splitk.hip", "gemv_mt.hip",
+KERNEL_FILES = ["gemv.hip", "gemv_g8.hip", "gemv_g8r.hip", "gemv_mfma.hip", "gemv_splitk.hip", "gemv_mt.hip",
                 "moe.hip", "w4a4.hip", "pack.hip", "stream_read.hip"]
 
 
