@@ -395,15 +395,19 @@ __global__ __launch_bounds__(256) void k_moe_down(
 
 constexpr int kMaxTok = NVFP4_MOE_MAX_M_INTERNAL;  // tokens per call
 constexpr int kMaxSl = NVFP4_MAX_TOPK_INTERNAL;    // slots per token
-constexpr int kSplitRows = 8;                      // k_moe_down_split: rows per workgroup
-constexpr int kSplitWaves = 4;                     //   and wavefronts per workgroup
+constexpr int kSplitRows = 8;                      // k_moe_down_split: rows per workgroup,
+constexpr int kSplitUnroll = 2;                    //   (slot, chunk) pairs in flight per lane
+constexpr int kSplitWaves = 8;                     //   and wavefronts per workgroup
 
 // The down pass and combine for M >= 2, split over wavefronts. The same
 // dot products as k_moe_down, dealt out differently: a workgroup of NW
 // wavefronts owns R output rows, and the units of work of all its tokens
 // (token m, a block of 64U consecutive (slot, chunk) pairs of that token's
 // valid slots and shared-expert chunks) go to its wavefronts round robin.
-// Each lane keeps one partial per row and token; the wavefronts' sums meet
+// Units are numbered token by token, so a wavefront finishes its units of
+// one token before it starts the next: each lane keeps one partial per row
+// of the current token only (R registers, not R per token), and the
+// wavefront sums them into LDS when it moves on. The wavefronts' sums meet
 // in LDS and are added in wavefront order (deterministic). Compared with one
 // wavefront walking every token's pairs for its rows, this keeps several
 // times more wavefronts, and so more loads, in flight for the same work per
@@ -450,19 +454,20 @@ __global__ __launch_bounds__(64 * NW) void k_moe_down_split(
   int64_t rows[R];
 #pragma unroll
   for (int r = 0; r < R; ++r) rows[r] = (n0 + r < H) ? n0 + r : H - 1;
-  float tok[R][kMaxTok];
-#pragma unroll
-  for (int r = 0; r < R; ++r)
-#pragma unroll
-    for (int mm = 0; mm < kMaxTok; ++mm) tok[r][mm] = 0.0f;
   int unit = 0;
   for (int m = 0; m < M; ++m) {
+    // the lane's partials of token m: only the current token's are live
+    float tok[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) tok[r] = 0.0f;
+    bool any = false;
     const int nv = __builtin_amdgcn_readfirstlane(s_nv[m]);
     const int PR = nv * C;
     const int P = PR + Cs;
     const int nb = (P + 64 * U - 1) / (64 * U);
     for (int b = 0; b < nb; ++b, ++unit) {
       if (unit % NW != w) continue;
+      any = true;
       u32x4_t qv[U][R];
       uint32_t sw[U][R];
       u32x4_t hv[U][4];
@@ -529,21 +534,13 @@ __global__ __launch_bounds__(64 * NW) void k_moe_down_split(
         }
       }
 #pragma unroll
-      for (int mm = 0; mm < kMaxTok; ++mm)
-        if (mm == m) {
-#pragma unroll
-          for (int r = 0; r < R; ++r) tok[r][mm] += acc[r];
-        }
+      for (int r = 0; r < R; ++r) tok[r] += acc[r];
     }
-  }
+    // the wave's sums of token m (zero when it took none of its units)
 #pragma unroll
-  for (int mm = 0; mm < kMaxTok; ++mm) {
-    if (mm < M) {
-#pragma unroll
-      for (int r = 0; r < R; ++r) {
-        const float t = wave_sum(tok[r][mm]);
-        if (lane == 0) s_part[w][r][mm] = t;
-      }
+    for (int r = 0; r < R; ++r) {
+      const float t = any ? wave_sum(tok[r]) : 0.0f;
+      if (lane == 0) s_part[w][r][m] = t;
     }
   }
   __syncthreads();
@@ -624,7 +621,7 @@ hipError_t launch_moe(const uint8_t* w13_codes, const uint8_t* w13_scales,
                        H, I, y, sh);
   } else {
     const int64_t wgs = (H + kSplitRows - 1) / kSplitRows;
-    hipLaunchKernelGGL((k_moe_down_split<kSplitRows, 1, kSplitWaves>), dim3((unsigned)wgs),
+    hipLaunchKernelGGL((k_moe_down_split<kSplitRows, kSplitUnroll, kSplitWaves>), dim3((unsigned)wgs),
                        dim3(64 * kSplitWaves), 0, stream, w2_codes, w2_scales, w2_gscale, hr, ga2,
                        ids, gate_w, M, topk, E, H, I, y, sh);
   }
