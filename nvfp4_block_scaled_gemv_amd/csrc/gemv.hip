@@ -148,7 +148,8 @@ hipError_t launch_gemv_segments(const SegDesc* d, int n, const uint16_t* x, int 
     case 1: launch_valu<1>(d, n, rows, x, K, stream); break;
     case 2: launch_valu<2>(d, n, rows, x, K, stream); break;
     default:
-      if (M > NVFP4_MAX_M_SMALL) return launch_gemv_mt(d, n, x, M, K, stream);
+      if (M > NVFP4_MAX_M_SMALL && !g8_groups_applicable(d, n, M, K))
+        return launch_gemv_mt(d, n, x, M, K, stream);
       return launch_gemv_mfma(d, n, x, M, K, stream);
   }
   return hipGetLastError();

@@ -1,5 +1,6 @@
 // gemv_g8.hip -- NVFP4 g16 W4A16 GEMV on the CDNA4 matrix cores for
-// 3 <= M <= 8 activation rows and K a multiple of 256:
+// 3 <= M <= 8 activation rows (9 to 16 as two groups of 8) and K a multiple
+// of 256:
 //
 //   y[m, n] = g * sum_k e2m1(c[n,k]) * e4m3(s[n, k/16]) * x[m, k]
 //
@@ -47,20 +48,35 @@
 namespace nvfp4 {
 
 constexpr int kG8MaxWaves = 16;
+// tokens per call: groups of 8 (9..16 tokens run as two groups; past that the
+// many-token kernel of gemv_mt.hip decodes each weight once for 32 tokens)
+constexpr int kG8MaxTokens = 16;
 
 // TW tiles of 16 rows per workgroup, S slices per wavefront, up to 16
 // wavefronts (128 registers per lane). codes, scales and x are plain loads:
 // the code is straight-line, so the compiler's waits count exactly.
+// Tokens come in groups of at most 8 (M is the group size; Mt tokens in
+// all, ng = ceil(Mt / 8) groups): the ng workgroups of a unit read the same
+// weights for different tokens. Their workgroup indices differ by multiples
+// of 8, so they are dealt to the same XCD (workgroups go to the 8 XCDs
+// round robin in linear order) close together in time, and the later ones
+// find the weights in that XCD's L2.
 template <int M, int TW, int S>
 __global__ __launch_bounds__(64 * kG8MaxWaves) __attribute__((amdgpu_waves_per_eu(S == 1 && TW <= 2 ? 8 : 1))) void k_gemv_g8(const SegTable tab,
                                                               const uint16_t* __restrict__ x,
-                                                              int64_t K) {
+                                                              int64_t K, int Mt, int ng,
+                                                              int units) {
   extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int W = blockDim.x >> 6;
   const int i = lane & 15, g = lane >> 4;
-  const Seg sg = find_seg32(tab, (int)blockIdx.x);
+  const int b = (int)blockIdx.x;
+  const int grp = (b >> 3) % ng;                      // token group
+  const int unit = (b >> 3) / ng * 8 + (b & 7);
+  if (unit >= units) return;                          // the whole workgroup
+  const int Mq = Mt - 8 * grp < M ? Mt - 8 * grp : M; // tokens of this group
+  const Seg sg = find_seg32(tab, unit);
   const int64_t N = sg.N;
   const int64_t n0 = sg.unit * (16 * TW);
   const int64_t kw = (int64_t)w * S * kG8Slice;     // this wavefront's first k
@@ -79,7 +95,8 @@ __global__ __launch_bounds__(64 * kG8MaxWaves) __attribute__((amdgpu_waves_per_e
   u32x4_t xv[S][4];
   const bool live = (i < 8) == (g < 2);    // lanes of the A operands that carry x
   const int t = i & 7;
-  const __amdgpu_buffer_rsrc_t rx = buf_rsrc(x, (int64_t)M * K * 2);
+  // tokens of the group past Mq lie past the bound and read as zeros
+  const __amdgpu_buffer_rsrc_t rx = buf_rsrc(x + (int64_t)8 * grp * K, (int64_t)Mq * K * 2);
   const __amdgpu_buffer_rsrc_t rc = buf_rsrc(sg.codes + n0 * cb, (N - n0) * cb);
   const __amdgpu_buffer_rsrc_t rs = buf_rsrc(sg.scales + n0 * sbytes, (N - n0) * sbytes);
   // byte offsets, 32-bit (K <= 16384 keeps every offset below 2^20), and
@@ -201,8 +218,9 @@ __global__ __launch_bounds__(64 * kG8MaxWaves) __attribute__((amdgpu_waves_per_e
     const int64_t n = n0 + 16 * u + (l & 15);
     const int m0 = 4 * ((l >> 4) & 1) + (l >> 5);   // tokens m0 and m0 + 2
     if (n < N) {
-      if (m0 < M) sg.y[(int64_t)m0 * N + n] = sum[0] * gs;
-      if (m0 + 2 < M) sg.y[(int64_t)(m0 + 2) * N + n] = sum[1] * gs;
+      float* const yq = sg.y + (int64_t)8 * grp * N;
+      if (m0 < Mq) yq[(int64_t)m0 * N + n] = sum[0] * gs;
+      if (m0 + 2 < Mq) yq[(int64_t)(m0 + 2) * N + n] = sum[1] * gs;
     }
   }
 }
@@ -215,10 +233,22 @@ static bool g8_split_ok(int64_t K, int S) {
 }
 
 bool g8_applicable(int M, int64_t K) {
-  if (M < 3 || M > NVFP4_MAX_M_SMALL) return false;
+  if (M < 3 || M > kG8MaxTokens) return false;
   for (int s = 1; s <= 4; ++s)
     if (g8_split_ok(K, s)) return true;
   return false;
+}
+
+// 9 <= M <= 16 as two token groups, where that beats the many-token kernel
+// (one decode per weight for 32 tokens): on 12288 x 4096, 4096 x 12288 and
+// 4096 x 4096 (13.3 / 19.7 / 7.4 us against 15.0 / 28.8 / 13.3 at M = 9 to
+// 16) but not on the 151936-row LM head (128 against 82 us), where the
+// second group's reads of the weights miss the L2.
+bool g8_groups_applicable(const SegDesc* d, int n, int M, int64_t K) {
+  if (M <= NVFP4_MAX_M_SMALL || M > kG8MaxTokens || !g8_applicable(M, K)) return false;
+  int64_t rows = 0;
+  for (int k = 0; k < n; ++k) rows += d[k].N;
+  return rows < 131072;
 }
 
 // Launch shape, from A/B sweeps (1024 .. 151936 rows at K = 4096 and 12288,
@@ -246,17 +276,19 @@ void g8_shape(int64_t rows, int64_t K, int* TW, int* S, int* W) {
 
 hipError_t launch_gemv_g8_shape(const SegDesc* d, int n, const uint16_t* x, int M, int64_t K,
                                 int TW, int S, hipStream_t stream) {
-  if (M < 3 || M > NVFP4_MAX_M_SMALL || !g8_split_ok(K, S) || n < 1 || n > kMaxSegments)
+  if (M < 3 || M > kG8MaxTokens || !g8_split_ok(K, S) || n < 1 || n > kMaxSegments)
     return hipErrorInvalidValue;
   const int64_t slices = K / kG8Slice;
   const int64_t W = slices / S;
   const SegTable tab = make_seg_table(d, n, 16 * TW);
   const int64_t units = tab.start[kMaxSegments];
-  if (units > 0x7FFFFFFF) return hipErrorInvalidValue;
+  const int ng = (M + 7) / 8;
+  const int64_t grid = (units + 7) / 8 * 8 * ng;
+  if (grid > 0x7FFFFFFF) return hipErrorInvalidValue;
   const size_t lds = (size_t)W * kG8StageBytes + (size_t)slices * TW * 64 * sizeof(f32x2_t);
 #define NVFP4_G8(MM, TT, SS)                                                                 \
-  hipLaunchKernelGGL((k_gemv_g8<MM, TT, SS>), dim3((unsigned)units),                         \
-                     dim3(64 * (unsigned)W), lds, stream, tab, x, K)
+  hipLaunchKernelGGL((k_gemv_g8<MM, TT, SS>), dim3((unsigned)grid), dim3(64 * (unsigned)W),  \
+                     lds, stream, tab, x, K, M, ng, (int)units)
 #define NVFP4_G8_TS(MM)                                    \
   switch (TW * 10 + S) {                                   \
     case 11: NVFP4_G8(MM, 1, 1); break;                    \
@@ -273,7 +305,7 @@ hipError_t launch_gemv_g8_shape(const SegDesc* d, int n, const uint16_t* x, int 
     case 5: NVFP4_G8_TS(5); break;
     case 6: NVFP4_G8_TS(6); break;
     case 7: NVFP4_G8_TS(7); break;
-    default: NVFP4_G8_TS(8); break;
+    default: NVFP4_G8_TS(8); break;   // 8 tokens, or groups of 8
   }
 #undef NVFP4_G8_TS
 #undef NVFP4_G8

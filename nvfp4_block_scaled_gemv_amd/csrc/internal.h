@@ -35,10 +35,12 @@ hipError_t launch_gemv_segments(const SegDesc* d, int n, const uint16_t* x, int 
 // Matrix-core paths, 3 <= M <= 8 (gemv_mfma.hip routes K % 256 == 0 to
 // gemv_splitk.hip), and 9 <= M <= 128 (gemv_mt.hip).
 bool mt_applicable(int M);
-// 3 <= M <= 8, K % 256 == 0 and K / 256 splitting evenly over at most 16
-// wavefronts of up to 4 slices (gemv_g8.hip): one launch shape per row count and K
-// (g8_shape), or an explicit one
+// 3 <= M <= 16 (groups of 8 tokens), K % 256 == 0 and K / 256 splitting
+// evenly over at most 16 wavefronts of up to 4 slices (gemv_g8.hip): one
+// launch shape per row count and K (g8_shape), or an explicit one
 bool g8_applicable(int M, int64_t K);
+// 9 <= M <= 16: the same kernel in two groups of 8 tokens (below 2^17 rows)
+bool g8_groups_applicable(const SegDesc* d, int n, int M, int64_t K);
 void g8_shape(int64_t rows, int64_t K, int* TW, int* S, int* W);
 hipError_t launch_gemv_g8(const SegDesc* d, int n, const uint16_t* x, int M, int64_t K,
                           hipStream_t stream);

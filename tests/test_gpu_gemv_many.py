@@ -1,5 +1,7 @@
-"""GPU GEMV at 9 <= M <= 128 tokens (the many-token matrix-core kernel)
-against the oracle within |y - y_ref| <= 1e-3 sum|w x| + 1e-6: the stress and
+"""GPU GEMV at 9 <= M <= 128 tokens (the many-token matrix-core kernel; at
+9 <= M <= 16 below 2^17 rows with K a multiple of 256, the eight-token
+kernel in two token groups) against the oracle within
+|y - y_ref| <= 1e-3 sum|w x| + 1e-6: the stress and
 LM-head shapes at M in {9, 12, 16, 24, 32, 64, 128} (sampled rows where the
 oracle would take long), ragged token counts, rows and K, arbitrary codes and
 scales, segments, the W4A4 path at many tokens, and determinism."""
