@@ -1,11 +1,10 @@
 """GPU GEMV at 3 <= M <= 8 on very tall single matrices (2^17 rows and more,
-K a multiple of 256 up to 4096), where the wavefronts split the rows and x
-sits once per workgroup in LDS, against the oracle within
-|y - y_ref| <= 1e-3 sum|w x| + 1e-6: the LM head at every token count, and
-ragged shapes whose rows per wavefront leave a partial last tile, fill
-exactly two or three tiles, or need more than one workgroup per CU. Rows are
-sampled at the first and last rows, around the first wavefronts' row
-boundaries and at random."""
+K a multiple of 256 up to 4096), where the wavefronts split the rows (two or
+three whole 16-row tiles each) and x sits once per workgroup in LDS, against
+the oracle within |y - y_ref| <= 1e-3 sum|w x| + 1e-6: the LM head at every
+token count, and ragged shapes whose last tile is partial or whose launch
+needs more than one workgroup per CU. Rows are sampled at the first and last
+rows, around the first wavefronts' row boundaries and at random."""
 import numpy as np
 import pytest
 
@@ -17,17 +16,19 @@ from gpu_util import check_tol, dev, dev_x, host, say
 pytestmark = pytest.mark.gpu
 
 
-def rows_per_wave(N):
-    """The launch's rows per wavefront: 16 wavefronts per workgroup, at least
-    256 workgroups, at most 48 rows per wavefront."""
-    grid = max(256, -(-N // (16 * 48)))
-    return -(-N // (grid * 16))
+def wave_first_rows(N, waves):
+    """First rows of wavefronts 0 .. waves - 1 in the launch: 16 wavefronts
+    per workgroup, at least 256 workgroups, at most three tiles per
+    wavefront; wavefront v takes tiles [v T / W, (v + 1) T / W)."""
+    T = -(-N // 16)
+    grid = max(256, -(-T // 48))
+    W = 16 * grid
+    return [16 * (v * T // W) for v in range(waves)]
 
 
 def sample_rows(N, n, seed):
-    rpw = rows_per_wave(N)
     fixed = [0, 1, 15, 16, 31, 32]
-    for b in (rpw, 2 * rpw, 3 * rpw, 100 * rpw):
+    for b in wave_first_rows(N, 6)[1:] + wave_first_rows(N, 300)[-2:]:
         fixed += [b - 1, b, b + 1, b + 15, b + 16]
     fixed += [N - 17, N - 16, N - 2, N - 1]
     fixed = [r for r in fixed if 0 <= r < N]
@@ -60,10 +61,10 @@ def test_lm_head_up_to_eight_tokens(lm_head_packed, M):
 @pytest.mark.parametrize("M,N,K", [(8, 131072, 256), (3, 131073, 1024), (5, 200003, 4096),
                                    (8, 393217, 512), (7, 150001, 2304)])
 def test_tall_ragged_shapes(M, N, K):
-    """Rows per wavefront 32 (two whole tiles), 33 (a third tile of one
-    row), 48 (three whole tiles, 261 workgroups), 48 over 513 workgroups
-    (two per CU and more), and K = 2304 (9 slices: the ring's last round
-    half empty)."""
+    """Two tiles per wavefront exactly (131072 rows), a last tile of one row
+    (131073, 150001), 261 workgroups at 2.99 tiles per wavefront (200003),
+    513 workgroups (two per CU and more), and K = 2304 (9 slices: the ring's
+    last round half empty)."""
     say(f"[gemv-tall] ragged M={M} N={N} K={K}")
     codes, scales = workloads.random_nvfp4(17, M, N % 1000 + K, N, K)
     x = workloads.x_bf16(17, M, N % 1000 + K, M, K)
