@@ -65,6 +65,8 @@ constexpr int kMtWPitch = 144;         // staged code row: 128 + 16 bytes
 constexpr int kMtWStage = 32 * kMtWPitch;
 constexpr int kMtMaxWaves = 8;         // two per SIMD, 256 registers each
 constexpr int64_t kMtLdsMax = 80 * 1024;   // two workgroups per CU
+constexpr int64_t kMtLdsOne = 160 * 1024;  // one workgroup per CU (all of its LDS)
+constexpr int64_t kMtOneRound = 256;       // workgroups that one per CU runs in one round
 
 // bf16x8 of the 8 E2M1 codes of `word` times the block scale s: exact (the
 // products have at most 6 significant bits and lie in bf16's range).
@@ -350,12 +352,25 @@ MtShape mt_shape(const SegDesc* d, int n, int M, int64_t K) {
   // row wavefronts sharing each staged piece of x: as many as leave 192
   // workgroups
   sh.R = units(128) * sh.tblocks >= 192 ? 4 : (units(64) * sh.tblocks >= 192 ? 2 : 1);
-  // k-groups: one with two token groups, else two (three with one row
-  // wavefront), no more than there are slices, within the LDS budget
+  // k-groups. Where the grid fits on the CUs one workgroup each, LDS for a
+  // second workgroup per CU buys nothing: up to 4 k-groups (8 wavefronts)
+  // within all of the CU's LDS, since with one or two wavefronts per SIMD
+  // the weight stream waits on load latency and more k-groups keep more
+  // slices in flight (warm same-process A/B: 4096 x 12288 at 128 tokens
+  // 36.0 -> 33.0 us; 12288 x 4096 at 128 tokens 28.6 -> 28.3 us, and at 32
+  // tokens 15.6 -> 15.4 and 29.1 -> 28.8 us). Otherwise one with two token
+  // groups, else two (three with one row wavefront), within half of it.
+  // Never more than there are slices.
   const int64_t slices = (K + kMtSlice - 1) / kMtSlice;
-  const int64_t W = sh.G == 2 ? 1 : (sh.R == 1 ? 3 : 2);
+  const bool one_round = units(32 * sh.R) * sh.tblocks <= kMtOneRound;
+  const int64_t budget = one_round ? kMtLdsOne : kMtLdsMax;
+  int64_t W;
+  if (one_round)
+    W = kMtMaxWaves / sh.R < 4 ? kMtMaxWaves / sh.R : 4;
+  else
+    W = sh.G == 2 ? 1 : (sh.R == 1 ? 3 : 2);
   sh.W = (int)(W > slices ? slices : W);
-  while (sh.W > 1 && mt_lds_bytes(sh) > kMtLdsMax) --sh.W;
+  while (sh.W > 1 && mt_lds_bytes(sh) > budget) --sh.W;
   return sh;
 }
 
@@ -367,7 +382,7 @@ hipError_t launch_gemv_mt_shape(const SegDesc* d, int n, const uint16_t* x, int 
   if (K > (1 << 20)) return hipErrorInvalidValue;
   if (sh.G < 1 || sh.G > 2 || (sh.R != 1 && sh.R != 2 && sh.R != 4) || (sh.G == 2 && sh.R == 1) ||
       sh.W < 1 || sh.R * sh.W > kMtMaxWaves || sh.tblocks < 1 ||
-      (int64_t)sh.tblocks * sh.G * 32 < M || mt_lds_bytes(sh) > kMtLdsMax)
+      (int64_t)sh.tblocks * sh.G * 32 < M || mt_lds_bytes(sh) > kMtLdsOne)
     return hipErrorInvalidValue;
   const SegTable tab = make_seg_table(d, n, 32 * sh.R);
   const int64_t units = tab.start[kMaxSegments];
