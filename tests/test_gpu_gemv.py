@@ -156,19 +156,17 @@ def test_workload_5_stress_m8(i, N, K):
     check_tol(y, y_ref, ad, f"stress {N}x{K}")
 
 
-def test_workload_3_lm_head_sampled_rows():
-    """Full 151936 x 4096 at M=1, in the launch the benchmark times; the
-    oracle computes a sample of rows (first, last, random) one by one."""
+def test_workload_3_lm_head_all_rows():
+    """Full 151936 x 4096 at M=1, in the launch the benchmark times, every
+    output against the oracle."""
     N, K = 151936, 4096
     W = workloads.dense_weights(3, 0, 0, N, K)
     (c0, s0, g0), (c1, s1, g1) = packed_pair(W)
     del W
     x = workloads.x_bf16(3, 0, 0, 1, K)
     y = host(nv.gemv(c1, s1, g1, dev_x(x)))
-    rows = np.unique(np.concatenate([[0, 1, N - 2, N - 1],
-                                     np.random.default_rng(5).choice(N, 3000, replace=False)]))
-    y_ref, ad = oracle.gemv(c0, s0, g0, x, rows=rows)
-    check_tol(y[:, rows], y_ref, ad, "lm head")
+    y_ref, ad = oracle.gemv(c0, s0, g0, x)
+    check_tol(y, y_ref, ad, "lm head")
     assert np.all(np.isfinite(y))
 
 
