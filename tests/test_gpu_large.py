@@ -75,6 +75,29 @@ def test_large_gemv_vector_alu_and_split_k(big_k256, M):
     assert bool(torch.isfinite(y).all())
 
 
+@pytest.mark.parametrize("M", [3, 8])
+def test_large_tall_eight_tokens(M):
+    """2.2 M rows x K = 4096 (4.5 GB of codes): the row-split matrix-core
+    kernel for 3 <= M <= 8, whose wavefronts take two or three whole tiles
+    from 45840 (2865 workgroups), with rows on both sides of the 2^31 and
+    2^32 byte offsets of the codes."""
+    N, K = 2_200_000, 4096
+    say(f"[large] tall gemv M={M} N={N} K={K}")
+    c, s = device_nvfp4(13, N, K)
+    rows = sample_rows(N, K, 7)
+    hc, hs = rows_to_host(c, rows), rows_to_host(s, rows)
+    g = np.float32(0.0077)
+    x = workloads.x_bf16(9, 600 + M, 0, M, K)
+    y = nv.gemv(c, s, dev(np.array([g], np.float32)), dev_x(x))
+    y_rows = host(y[:, torch.from_numpy(rows).to("cuda")])
+    finite = bool(torch.isfinite(y).all())
+    del c, s, y
+    release()
+    y_ref, ad = oracle.gemv(hc, hs, g, x)
+    check_tol(y_rows, y_ref, ad, f"large tall gemv M={M}")
+    assert finite
+
+
 @pytest.mark.parametrize("M", [2, 5])
 def test_large_segments(big_k256, M):
     """The large matrix as the second segment of one launch."""
