@@ -1,6 +1,8 @@
 // gemv.hip -- dense NVFP4 g16 W4A16 GEMV on gfx950, vector-ALU path for
-// M <= 2 activation rows (3 <= M <= 8 goes to the matrix-core kernels of
-// gemv_mfma.hip and gemv_splitk.hip, 9 <= M <= 128 to gemv_mt.hip):
+// M = 1, and for M = 2 on small matrices or K that the matrix-core kernels
+// do not split (M = 2 from 4096 rows with K % 256 == 0, and 3 <= M <= 8, go
+// to the matrix-core kernels of gemv_g8.hip, gemv_g8r.hip, gemv_splitk.hip
+// and gemv_mfma.hip; 9 <= M <= 128 to gemv_mt.hip):
 //   y[m, n] = g * sum_k e2m1(c[n,k]) * s[n, k/16] * x[m, k]
 // (graph.json node "l0.kda.q": act bf16, weight nvfp4/g16 -> bf16,
 // accumulate f32, scale f32). Bandwidth-bound: every weight byte is read
@@ -11,6 +13,7 @@
 namespace nvfp4 {
 
 constexpr int kWavesPerBlock = 4;
+constexpr int64_t kM2MatrixCoreRows = 4096;   // M = 2 takes the matrix cores from here
 
 // Each wavefront takes groups of R consecutive rows of one segment, striding
 // over the groups of all segments.
@@ -146,7 +149,17 @@ hipError_t launch_gemv_segments(const SegDesc* d, int n, const uint16_t* x, int 
   for (int s = 0; s < n; ++s) rows += d[s].N;
   switch (M) {
     case 1: launch_valu<1>(d, n, rows, x, K, stream); break;
-    case 2: launch_valu<2>(d, n, rows, x, K, stream); break;
+    case 2:
+      // Two tokens on the matrix cores from 4096 rows (same-process A/B at
+      // K = 4096 and 12288: 4096 x 4096 5.60 -> 5.09 us, 12288 x 4096
+      // 10.06 -> 8.31, 4096 x 12288 12.15 -> 9.28, the 151936-row LM head
+      // 78.7 -> 57.1); at 1024 rows the vector ALUs stay faster (3.95
+      // against 4.63 us).
+      if (rows >= kM2MatrixCoreRows &&
+          (g8r_applicable(M, n, n == 1 ? d[0].N : 0, K) || g8_applicable(M, K)))
+        return launch_gemv_mfma(d, n, x, M, K, stream);
+      launch_valu<2>(d, n, rows, x, K, stream);
+      break;
     default:
       if (M > NVFP4_MAX_M_SMALL && !g8_groups_applicable(d, n, M, K))
         return launch_gemv_mt(d, n, x, M, K, stream);

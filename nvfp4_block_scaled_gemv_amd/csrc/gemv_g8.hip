@@ -1,5 +1,5 @@
 // gemv_g8.hip -- NVFP4 g16 W4A16 GEMV on the CDNA4 matrix cores for
-// 3 <= M <= 8 activation rows (9 to 16 as two groups of 8) and K a multiple
+// 2 <= M <= 8 activation rows (9 to 16 as two groups of 8) and K a multiple
 // of 256:
 //
 //   y[m, n] = g * sum_k e2m1(c[n,k]) * e4m3(s[n, k/16]) * x[m, k]
@@ -233,7 +233,7 @@ static bool g8_split_ok(int64_t K, int S) {
 }
 
 bool g8_applicable(int M, int64_t K) {
-  if (M < 3 || M > kG8MaxTokens) return false;
+  if (M < 2 || M > kG8MaxTokens) return false;
   for (int s = 1; s <= 4; ++s)
     if (g8_split_ok(K, s)) return true;
   return false;
@@ -276,7 +276,7 @@ void g8_shape(int64_t rows, int64_t K, int* TW, int* S, int* W) {
 
 hipError_t launch_gemv_g8_shape(const SegDesc* d, int n, const uint16_t* x, int M, int64_t K,
                                 int TW, int S, hipStream_t stream) {
-  if (M < 3 || M > kG8MaxTokens || !g8_split_ok(K, S) || n < 1 || n > kMaxSegments)
+  if (M < 2 || M > kG8MaxTokens || !g8_split_ok(K, S) || n < 1 || n > kMaxSegments)
     return hipErrorInvalidValue;
   const int64_t slices = K / kG8Slice;
   const int64_t W = slices / S;
@@ -300,6 +300,7 @@ hipError_t launch_gemv_g8_shape(const SegDesc* d, int n, const uint16_t* x, int 
     default: return hipErrorInvalidValue;                  \
   }
   switch (M) {
+    case 2: NVFP4_G8_TS(2); break;
     case 3: NVFP4_G8_TS(3); break;
     case 4: NVFP4_G8_TS(4); break;
     case 5: NVFP4_G8_TS(5); break;

@@ -1,5 +1,5 @@
 // gemv_g8r.hip -- NVFP4 g16 W4A16 GEMV on the CDNA4 matrix cores for
-// 3 <= M <= 8 activation rows and very tall matrices (an LM head: 2^17 rows
+// 2 <= M <= 8 activation rows and very tall matrices (an LM head: 2^17 rows
 // and more, K a multiple of 256 up to 4096, one matrix per call):
 //
 //   y[m, n] = g * sum_k e2m1(c[n,k]) * e4m3(s[n, k/16]) * x[m, k]
@@ -278,7 +278,7 @@ __global__ __launch_bounds__(64 * kRWaves) void k_gemv_g8r(
 }
 
 bool g8r_applicable(int M, int n, int64_t N, int64_t K) {
-  return M >= 3 && M <= NVFP4_MAX_M_SMALL && n == 1 && N >= kRMinRows && K > 0 &&
+  return M >= 2 && M <= NVFP4_MAX_M_SMALL && n == 1 && N >= kRMinRows && K > 0 &&
          K % kG8Slice == 0 && K <= kRMaxK;
 }
 
@@ -295,6 +295,7 @@ hipError_t launch_gemv_g8r(const SegDesc& d, const uint16_t* x, int M, int64_t K
   hipLaunchKernelGGL((k_gemv_g8r<MM>), dim3((unsigned)grid), dim3(64 * kRWaves), lds, stream, \
                      d.codes, d.scales, d.gscale, x, d.y, d.N, K, T)
   switch (M) {
+    case 2: NVFP4_G8R(2); break;
     case 3: NVFP4_G8R(3); break;
     case 4: NVFP4_G8R(4); break;
     case 5: NVFP4_G8R(5); break;

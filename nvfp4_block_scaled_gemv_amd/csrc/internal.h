@@ -32,10 +32,11 @@ hipError_t launch_gemv(const uint8_t* codes, const uint8_t* scales, const float*
 hipError_t launch_gemv_segments(const SegDesc* d, int n, const uint16_t* x, int M, int64_t K,
                                 hipStream_t stream);
 
-// Matrix-core paths, 3 <= M <= 8 (gemv_mfma.hip routes K % 256 == 0 to
-// gemv_splitk.hip), and 9 <= M <= 128 (gemv_mt.hip).
+// Matrix-core paths, 2 <= M <= 8 (gemv_mfma.hip routes K % 256 == 0 to
+// gemv_g8r.hip, gemv_g8.hip or gemv_splitk.hip; M = 2 only where those two
+// apply), and 9 <= M <= 128 (gemv_mt.hip).
 bool mt_applicable(int M);
-// 3 <= M <= 16 (groups of 8 tokens), K % 256 == 0 and K / 256 splitting
+// 2 <= M <= 16 (groups of 8 tokens), K % 256 == 0 and K / 256 splitting
 // evenly over at most 16 wavefronts of up to 4 slices (gemv_g8.hip): one
 // launch shape per row count and K (g8_shape), or an explicit one
 bool g8_applicable(int M, int64_t K);
@@ -46,7 +47,7 @@ hipError_t launch_gemv_g8(const SegDesc* d, int n, const uint16_t* x, int M, int
                           hipStream_t stream);
 hipError_t launch_gemv_g8_shape(const SegDesc* d, int n, const uint16_t* x, int M, int64_t K,
                                 int TW, int S, hipStream_t stream);
-// 3 <= M <= 8 on one very tall matrix (2^17 rows and more, K % 256 == 0,
+// 2 <= M <= 8 on one very tall matrix (2^17 rows and more, K % 256 == 0,
 // K <= 4096; gemv_g8r.hip): wavefronts split the rows, x held once per
 // workgroup in LDS
 bool g8r_applicable(int M, int n, int64_t N, int64_t K);

@@ -63,6 +63,22 @@ def test_four_rows_per_wavefront_with_ragged_tail(M):
     check_tol(y, y_ref, ad, f"M={M} N={N}")
 
 
+@pytest.mark.parametrize("N,K", [(4095, 4096), (4096, 4096), (6001, 512), (12288, 4096),
+                                 (4096, 12288), (8000, 2304)])
+def test_two_tokens_on_the_matrix_cores(N, K):
+    """M = 2 from 4096 rows with K % 256 == 0 runs on the matrix-core kernels
+    (below that, and for other K, on the vector ALUs): both sides of the
+    switch, a ragged last tile (6001 rows), tall K, and K = 2304 (9 slices)."""
+    M = 2
+    say(f"[gemv] two tokens N={N} K={K}")
+    codes, scales = workloads.random_nvfp4(9, M, N + K, N, K)
+    x = workloads.x_bf16(9, M, N + K, M, K)
+    g = np.float32(0.017)
+    y = run_gpu(codes, scales, g, x)
+    y_ref, ad = oracle.gemv(codes, scales, g, x)
+    check_tol(y, y_ref, ad, f"M=2 N={N} K={K}")
+
+
 @pytest.mark.parametrize("M", [3, 6, 8])
 @pytest.mark.parametrize("N,K", [(33, 256), (77, 512), (100, 768), (300, 3840), (50, 4352),
                                  (4800, 8192), (40, 30720), (21, 65536)])

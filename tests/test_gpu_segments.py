@@ -44,7 +44,7 @@ def test_ragged_segments(M, Ns, K):
     run_and_check(mats, x, f"M={M} K={K}")
 
 
-@pytest.mark.parametrize("M", [1, 5, 8])
+@pytest.mark.parametrize("M", [1, 2, 5, 8])
 def test_decode_layer_groups(M):
     """q|k|v (4096 + 1024 + 1024 rows) and gate|up (2 x 12288 rows), K = 4096,
     packed from the decode-layer workload's weights."""

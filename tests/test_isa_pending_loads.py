@@ -126,4 +126,4 @@ def test_no_kernel_spills_registers(tmp_path):
                 assert vgpr <= 64, (name, vgpr)
                 g8_one_slice += 1
     assert kernels >= 40, kernels
-    assert g8_one_slice == 12, g8_one_slice
+    assert g8_one_slice == 14, g8_one_slice   # M = 2 .. 8, one or two tiles
