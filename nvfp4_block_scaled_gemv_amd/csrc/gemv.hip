@@ -16,15 +16,24 @@ constexpr int kWavesPerBlock = 4;
 constexpr int64_t kM2MatrixCoreRows = 4096;   // M = 2 takes the matrix cores from here
 
 // Each wavefront takes groups of R consecutive rows of one segment, striding
-// over the groups of all segments.
+// over the groups of all segments. The nblk workgroups are numbered so that
+// each XCD streams a contiguous eighth of the rows: workgroups are dealt to
+// the 8 XCDs round robin in launch order, so launch index b runs workgroup
+// (b % 8) * ceil(nblk / 8) + b / 8 (the grid is rounded up to a multiple of
+// 8; the extra workgroups exit). Against the plain order, same-process A/B:
+// LM head 50.7 -> 50.4 us, 4096 x 4096 4.74 -> 4.67 us, 12288 x 4096 at M =
+// 2 10.08 -> 9.97 us (a pure read stream: 6.95 -> 7.05 TB/s).
 template <int M, int R, bool SEG>
 __global__ __launch_bounds__(256) void k_gemv(const SegTable tab, const uint16_t* __restrict__ x,
-                                              int64_t K) {
+                                              int64_t K, unsigned nblk) {
   const int lane = threadIdx.x & 63;
+  const unsigned per = (nblk + 7) / 8;
+  const unsigned blk = (blockIdx.x & 7) * per + (blockIdx.x >> 3);
+  if (blk >= nblk) return;
   // wavefront index, made provably uniform so loop control stays scalar
   const int64_t wave =
-      (int64_t)blockIdx.x * kWavesPerBlock + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int64_t nwaves = (int64_t)gridDim.x * kWavesPerBlock;
+      (int64_t)blk * kWavesPerBlock + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int64_t nwaves = (int64_t)nblk * kWavesPerBlock;
   const int64_t units = tab.start[kMaxSegments];
   const uint16_t* xs[M];
 #pragma unroll
@@ -124,11 +133,12 @@ static void launch_m(const SegDesc* d, int n, const uint16_t* x, int64_t K,
   const int64_t units = tab.start[kMaxSegments];
   const int64_t want = (units + kWavesPerBlock - 1) / kWavesPerBlock;
   const int64_t cap = (int64_t)1 << 20;
-  const unsigned grid = (unsigned)(want < cap ? want : cap);
+  const unsigned nblk = (unsigned)(want < cap ? want : cap);
+  const unsigned grid = (nblk + 7) / 8 * 8;
   if (n == 1)
-    hipLaunchKernelGGL((k_gemv<M, R, false>), dim3(grid), dim3(256), 0, stream, tab, x, K);
+    hipLaunchKernelGGL((k_gemv<M, R, false>), dim3(grid), dim3(256), 0, stream, tab, x, K, nblk);
   else
-    hipLaunchKernelGGL((k_gemv<M, R, true>), dim3(grid), dim3(256), 0, stream, tab, x, K);
+    hipLaunchKernelGGL((k_gemv<M, R, true>), dim3(grid), dim3(256), 0, stream, tab, x, K, nblk);
 }
 
 template <int M>
