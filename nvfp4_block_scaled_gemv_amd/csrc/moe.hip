@@ -42,6 +42,8 @@ constexpr int kMoeWaves = 4;     // wavefronts per workgroup
 constexpr int kDownRows = 2;     // output rows per wavefront in the down pass
 constexpr int kDownUnroll = 2;   // (slot, chunk) pairs in flight per lane
 constexpr int kGateUpSlots = 2;  // slots per pass over an expert's gate|up rows, M >= 2
+// wavefronts that six per SIMD hold at once on the 256 CUs of an MI355X
+constexpr int64_t kOneRoundWaves6 = 6 * 4 * 256;
 
 static inline size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 
@@ -111,8 +113,13 @@ __device__ __forceinline__ void gate_up_rows(const uint8_t* __restrict__ codes,
 // the kernel at the register count of one slot and so at 6 wavefronts per
 // SIMD, against 3 when a 4-slot group and a separate shared-expert path were
 // inlined side by side).
-template <int MSX>
-__global__ __launch_bounds__(256) void k_moe_gate_up(
+// W7 caps the registers for seven wavefronts per SIMD. The launcher takes it
+// at M = 1 when the grid holds more wavefronts than six per SIMD run in one
+// round (the 768-wide shared expert's grid row makes 6912 for 6144 places):
+// with the shared expert, 25.7 -> 24.2 us; without it (exactly one round at
+// six) the uncapped kernel stays faster, 21.5 against 21.9 us.
+template <int MSX, bool W7>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(W7 ? 7 : 1))) void k_moe_gate_up(
     const uint8_t* __restrict__ w13_codes, const uint8_t* __restrict__ w13_scales,
     const float* __restrict__ w13_gscale, const uint16_t* __restrict__ x,
     const uint16_t* __restrict__ xr, const float* __restrict__ ga,
@@ -219,8 +226,11 @@ constexpr int kW4Waves = 8;   // k_moe_gate_up_w4a4_1: 16 gate|up rows per workg
 // 30.2 against 27.8 us at 288 experts, top-8, shared expert 768. The
 // quantization sits in front of every workgroup's first weight load.)
 // At most 80 VGPRs (six wavefronts per SIMD): three workgroups per CU, so
-// the M = 1 grid runs in about one round (83 unbounded: two per CU).
-__global__ __launch_bounds__(64 * kW4Waves) __attribute__((amdgpu_waves_per_eu(6)))
+// the M = 1 grid runs in about one round (83 unbounded: two per CU); W7
+// caps them for seven, taken when the grid holds more wavefronts than one
+// round at six (the shared expert's grid row), as for k_moe_gate_up.
+template <bool W7>
+__global__ __launch_bounds__(64 * kW4Waves) __attribute__((amdgpu_waves_per_eu(W7 ? 7 : 6)))
 void k_moe_gate_up_w4a4_1(
     const uint8_t* __restrict__ w13_codes, const uint8_t* __restrict__ w13_scales,
     const float* __restrict__ w13_gscale, const uint16_t* __restrict__ x,
@@ -580,9 +590,15 @@ hipError_t launch_moe(const uint8_t* w13_codes, const uint8_t* w13_scales,
     if (e != hipSuccess) return e;
     const int64_t rows = sh.I > I ? sh.I : I;
     const int64_t gx = (rows + 2 * kW4Waves - 1) / (2 * kW4Waves);
-    hipLaunchKernelGGL(k_moe_gate_up_w4a4_1, dim3((unsigned)gx, S + (sh.I > 0 ? 1 : 0)),
-                       dim3(64 * kW4Waves), 0, stream, w13_codes, w13_scales, w13_gscale, x, xq,
-                       w4a4->ga13, w4a4->ga2, ids, topk, E, H, I, h, hq, sh);
+    const dim3 grid((unsigned)gx, S + (sh.I > 0 ? 1 : 0));
+    if ((int64_t)grid.x * grid.y * kW4Waves > kOneRoundWaves6)
+      hipLaunchKernelGGL(k_moe_gate_up_w4a4_1<true>, grid, dim3(64 * kW4Waves), 0, stream,
+                         w13_codes, w13_scales, w13_gscale, x, xq, w4a4->ga13, w4a4->ga2, ids,
+                         topk, E, H, I, h, hq, sh);
+    else
+      hipLaunchKernelGGL(k_moe_gate_up_w4a4_1<false>, grid, dim3(64 * kW4Waves), 0, stream,
+                         w13_codes, w13_scales, w13_gscale, x, xq, w4a4->ga13, w4a4->ga2, ids,
+                         topk, E, H, I, h, hq, sh);
     xr = nullptr;   // gate|up is done
     hr = hq;
     ga2 = w4a4->ga2;
@@ -600,12 +616,16 @@ hipError_t launch_moe(const uint8_t* w13_codes, const uint8_t* w13_scales,
     const int64_t pairs = ((sh.I > I ? sh.I : I) + 1) / 2;
     const int64_t yb = (pairs + kMoeWaves - 1) / kMoeWaves;
     const dim3 grid((unsigned)yb, S + (sh.I > 0 ? 1 : 0));
-    if (M == 1)
-      hipLaunchKernelGGL(k_moe_gate_up<1>, grid, dim3(256), 0, stream, w13_codes, w13_scales,
-                         w13_gscale, x, xr, ga13, ids, S, topk, E, H, I, h, sh, M);
-    else
-      hipLaunchKernelGGL(k_moe_gate_up<kGateUpSlots>, grid, dim3(256), 0, stream, w13_codes,
+    if (M == 1 && (int64_t)grid.x * grid.y * kMoeWaves > kOneRoundWaves6)
+      hipLaunchKernelGGL((k_moe_gate_up<1, true>), grid, dim3(256), 0, stream, w13_codes,
                          w13_scales, w13_gscale, x, xr, ga13, ids, S, topk, E, H, I, h, sh, M);
+    else if (M == 1)
+      hipLaunchKernelGGL((k_moe_gate_up<1, false>), grid, dim3(256), 0, stream, w13_codes,
+                         w13_scales, w13_gscale, x, xr, ga13, ids, S, topk, E, H, I, h, sh, M);
+    else
+      hipLaunchKernelGGL((k_moe_gate_up<kGateUpSlots, false>), grid, dim3(256), 0, stream,
+                         w13_codes, w13_scales, w13_gscale, x, xr, ga13, ids, S, topk, E, H, I,
+                         h, sh, M);
   }
   if (w4a4 && xr) {
     // h of every valid slot onto the NVFP4 grid of its static scale
