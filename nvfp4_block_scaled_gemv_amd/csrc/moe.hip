@@ -208,6 +208,156 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(W7 ? 7 : 1)
   }
 }
 
+// One token (M = 1), H = 2048 or 4096 (CL = H / 2048 chunks per lane; more
+// would spill): the gate|up pieces of k_moe_gate_up_1x. They compute the rows of wave_row_dots<1, 4> in the
+// same per-lane order of (chunk, block) products, so the same h bit for bit,
+// with two changes to the memory side:
+//  - every slot multiplies the same activation row, so each workgroup
+//    stages it once in LDS (8 KB at H = 4096) instead of every wavefront
+//    reading all of it through the L1;
+//  - each lane issues the loads of all CL of its chunks before the first
+//    product, so a wavefront waits for one HBM round trip, not CL.
+// LDS layout: 16-byte unit u holds x[8u .. 8u+7]; chunk c (32 elements) is
+// units 4c .. 4c+3, its quarter q stored at unit 4c + (q ^ ((c >> 2) & 3)).
+// Lane l reads chunk l (+64 cl), so the 16 lanes of one 128-bit LDS read
+// cover 16 consecutive chunks, and the swizzle puts them on distinct banks.
+__device__ __forceinline__ int x1x_unit(int u) {
+  const int c = u >> 2;
+  return 4 * c + ((u & 3) ^ ((c >> 2) & 3));
+}
+
+// the H / 8 units of x, UPT per thread of NT (surplus threads repeat the last)
+template <int NT, int UPT>
+__device__ __forceinline__ void x1x_load(const uint16_t* __restrict__ xs, int64_t H,
+                                         u32x4_t (&xv)[UPT]) {
+  const int nu = (int)(H >> 3);
+#pragma unroll
+  for (int k = 0; k < UPT; ++k) {
+    const int u0 = (int)threadIdx.x + NT * k;
+    xv[k] = reinterpret_cast<const u32x4_t*>(xs)[u0 < nu ? u0 : nu - 1];
+  }
+}
+template <int NT, int UPT>
+__device__ __forceinline__ void x1x_store(u32x4_t* xl, int64_t H, const u32x4_t (&xv)[UPT]) {
+  const int nu = (int)(H >> 3);
+#pragma unroll
+  for (int k = 0; k < UPT; ++k) {
+    const int u0 = (int)threadIdx.x + NT * k;
+    xl[x1x_unit(u0 < nu ? u0 : nu - 1)] = xv[k];
+  }
+}
+
+// the codes and scales of rows[0..3] at the lane's CL chunks
+template <int CL>
+__device__ __forceinline__ void gate_up_loads_1x(const uint8_t* __restrict__ codes,
+                                                 const uint8_t* __restrict__ scales, int64_t H,
+                                                 const int64_t (&rows)[4], u32x4_t (&q)[CL][4],
+                                                 uint32_t (&sw)[CL][4]) {
+  const int lane = threadIdx.x & 63;
+  const int64_t cb = H >> 1, sbytes = H >> 4;
+#pragma unroll
+  for (int cl = 0; cl < CL; ++cl)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int64_t c = lane + 64 * cl;
+      q[cl][r] = load_stream(codes + rows[r] * cb + c * 16);
+      sw[cl][r] = *reinterpret_cast<const uint16_t*>(scales + rows[r] * sbytes + c * 2);
+    }
+}
+
+// acc[r] = the wavefront's dot of row r with the staged x (every lane)
+template <int CL>
+__device__ __forceinline__ void gate_up_dots_1x(const u32x4_t (&q)[CL][4],
+                                                const uint32_t (&sw)[CL][4],
+                                                const u32x4_t* xl, float (&acc)[4]) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) acc[r] = 0.0f;
+#pragma unroll
+  for (int cl = 0; cl < CL; ++cl) {
+    const int c = lane + 64 * cl;
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+      const u32x4_t xa = xl[x1x_unit(4 * c + 2 * b)];
+      const u32x4_t xb = xl[x1x_unit(4 * c + 2 * b + 1)];
+      const bf16x2_t xq[8] = {as_bf16x2(xa.x), as_bf16x2(xa.y), as_bf16x2(xa.z),
+                              as_bf16x2(xa.w), as_bf16x2(xb.x), as_bf16x2(xb.y),
+                              as_bf16x2(xb.z), as_bf16x2(xb.w)};
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const uint32_t w0 = b ? q[cl][r].z : q[cl][r].x;
+        const uint32_t w1 = b ? q[cl][r].w : q[cl][r].y;
+        const bf16x2_t wd[8] = {e2m1x2_to_bf16<0>(w0), e2m1x2_to_bf16<1>(w0),
+                                e2m1x2_to_bf16<2>(w0), e2m1x2_to_bf16<3>(w0),
+                                e2m1x2_to_bf16<0>(w1), e2m1x2_to_bf16<1>(w1),
+                                e2m1x2_to_bf16<2>(w1), e2m1x2_to_bf16<3>(w1)};
+        const float sc = b ? e4m3_to_f32<1>(sw[cl][r]) : e4m3_to_f32<0>(sw[cl][r]);
+        float p = 0.0f;
+#pragma unroll
+        for (int t = 0; t < 8; ++t) p = dot2(wd[t], xq[t], p);
+        acc[r] = __builtin_fmaf(p, sc, acc[r]);
+      }
+    }
+  }
+#pragma unroll
+  for (int r = 0; r < 4; ++r) acc[r] = wave_sum(acc[r]);
+}
+
+// W4A16 gate|up at one token with the pieces above: grid and outputs as
+// k_moe_gate_up<1, W7>, dynamic LDS 2 H bytes.
+template <int CL, bool W7>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(W7 ? 7 : 6))) void k_moe_gate_up_1x(
+    const uint8_t* __restrict__ w13_codes, const uint8_t* __restrict__ w13_scales,
+    const float* __restrict__ w13_gscale, const uint16_t* __restrict__ x,
+    const uint16_t* __restrict__ xr, const float* __restrict__ ga,
+    const int32_t* __restrict__ ids, int64_t E, int64_t H, int64_t I,
+    uint16_t* __restrict__ h, const MoeShared sh) {
+  extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
+  u32x4_t* const xl = reinterpret_cast<u32x4_t*>(lds);
+  const bool shared_row = sh.I > 0 && blockIdx.y == 0;
+  const int j = sh.I > 0 ? (int)blockIdx.y - 1 : (int)blockIdx.y;   // routed slot
+  const int lane = threadIdx.x & 63;
+  const int64_t r0 =
+      ((int64_t)blockIdx.x * kMoeWaves + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6)) * 2;
+  int32_t e = 0;
+  bool ok = true;
+  const uint8_t* codes = sh.c13;
+  const uint8_t* scales = sh.s13;
+  const uint16_t* xs = x;
+  uint16_t* hd = sh.h;
+  int64_t Iv = sh.I;
+  if (!shared_row) {
+    e = ids[j];
+    ok = e >= 0 && (int64_t)e < E;
+    codes = w13_codes + (int64_t)(ok ? e : 0) * (2 * I) * (H / 2);
+    scales = w13_scales + (int64_t)(ok ? e : 0) * (2 * I) * (H / 16);
+    xs = xr;
+    hd = h + (int64_t)j * I;
+    Iv = I;
+  }
+  const bool act = ok && r0 < Iv;   // the whole wavefront
+  u32x4_t xv[CL];
+  x1x_load<256, CL>(xs, H, xv);
+  const int64_t r1 = (r0 + 1 < Iv) ? r0 + 1 : r0;
+  const int64_t rows[4] = {r0, r1, Iv + r0, Iv + r1};
+  u32x4_t q[CL][4];
+  uint32_t sw[CL][4];
+  if (act) gate_up_loads_1x<CL>(codes, scales, H, rows, q, sw);
+  x1x_store<256, CL>(xl, H, xv);
+  __syncthreads();
+  if (!act) return;
+  float acc[4];
+  gate_up_dots_1x<CL>(q, sw, xl, acc);
+  const float g = shared_row ? *sh.g13 : (ga ? w13_gscale[e] * *ga : w13_gscale[e]);
+#pragma unroll
+  for (int p = 0; p < 2; ++p)
+    if (lane == p && r0 + p < Iv) {
+      const float G = g * acc[p], U = g * acc[2 + p];
+      const float a = G / (1.0f + expf(-G)) * U;
+      hd[r0 + p] = bf16_rne(a);
+    }
+}
+
 constexpr int kW4Waves = 8;   // k_moe_gate_up_w4a4_1: 16 gate|up rows per workgroup
 
 // W4A4 at M = 1: gate|up with the quantization of h folded in (three
@@ -400,6 +550,164 @@ __global__ __launch_bounds__(256) void k_moe_down(
       const float t = wave_sum(acc[r]);
       if (lane == r && n0 + r < H) y[(int64_t)m * H + n0 + r] = t;
     }
+  }
+}
+
+// One token (M = 1): the products of k_moe_down<R, U> in the same per-lane
+// order (lane l takes pairs l, l + 64, l + 128, ... of the token's routed
+// then shared (slot, chunk) pairs), so the same y bit for bit, with the
+// memory side rearranged as in k_moe_gate_up_1x:
+//  - each lane issues the loads of all KP of its pairs before the first
+//    product (one HBM round trip per wavefront instead of one per U pairs);
+//  - the h chunks of all pairs (every valid slot's h row, then the shared
+//    expert's) are staged once per workgroup in LDS, pair p's 64 bytes at
+//    units 4p .. 4p+3, quarter q at unit 4p + (q ^ ((p >> 2) & 3)) so that
+//    16 lanes reading 16 consecutive pairs hit distinct banks. Every
+//    wavefront used to read all of h through the L1.
+// Needs P = (valid slots) I/32 + Is/32 <= 64 KP; the launcher checks the
+// bound for topk valid slots.
+template <int R, int KP>
+__global__ __launch_bounds__(256) void k_moe_down_1x(
+    const uint8_t* __restrict__ w2_codes, const uint8_t* __restrict__ w2_scales,
+    const float* __restrict__ w2_gscale, const uint16_t* __restrict__ h,
+    const float* __restrict__ ga, const int32_t* __restrict__ ids,
+    const float* __restrict__ gate_w, int topk, int64_t E, int64_t H, int64_t I,
+    float* __restrict__ y, const MoeShared sh) {
+  extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
+  u32x4_t* const hl = reinterpret_cast<u32x4_t*>(lds);
+  const int lane = threadIdx.x & 63;
+  const int64_t n0 =
+      ((int64_t)blockIdx.x * kMoeWaves + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6)) * R;
+  const int C = (int)(I >> 5);
+  const int64_t cb = I >> 1, sb = I >> 4;
+  const int64_t ecb = H * cb, esb = H * sb;
+  const float invC = 1.0f / (float)C;
+  const int Cs = (int)(sh.I >> 5);
+  const int64_t cbs = sh.I >> 1, sbs = sh.I >> 4;
+  const float gs2 = Cs > 0 ? *sh.g2 : 0.0f;
+  const float gah = ga ? *ga : 1.0f;
+  int64_t rows[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) rows[r] = (n0 + r < H) ? n0 + r : H - 1;
+  // the token's valid slots compacted into lanes 0 .. nv-1, in slot order
+  // (every wavefront of the workgroup builds the same table)
+  const int32_t ev = lane < topk ? ids[lane] : -1;
+  const bool valid = lane < topk && ev >= 0 && (int64_t)ev < E;
+  const uint64_t vm = __ballot(valid);
+  const int nv = __popcll(vm);
+  float coef = 0.0f;
+  if (valid) coef = ga ? gate_w[lane] * w2_gscale[ev] * gah : gate_w[lane] * w2_gscale[ev];
+  const int qv_ = __builtin_amdgcn_mbcnt_hi((uint32_t)(vm >> 32),
+                                            __builtin_amdgcn_mbcnt_lo((uint32_t)vm, 0u));
+  const int dst = (valid ? qv_ : 63) * 4;   // lane 63 is never read (nv <= 16)
+  const int e_c = __builtin_amdgcn_ds_permute(dst, ev);
+  const int j_c = __builtin_amdgcn_ds_permute(dst, lane);
+  const int f_c = __builtin_amdgcn_ds_permute(dst, __float_as_int(coef));
+  const int PR = nv * C;
+  const int P = PR + Cs;
+  if (P == 0) {   // no valid slot and no shared expert: y = 0 (the whole workgroup)
+    if (lane < R && n0 + lane < H) y[n0 + lane] = 0.0f;
+    return;
+  }
+  // the pair of an index: (slot q, chunk c) for routed pairs, chunk c of the
+  // shared expert otherwise
+  auto pair_of = [&](int pc, bool& shp, int& qi, int& c) {
+    shp = pc >= PR;
+    const int pr = shp ? 0 : pc;
+    qi = (int)(((float)pr + 0.5f) * invC);
+    if (qi * C > pr) --qi;
+    if ((qi + 1) * C <= pr) ++qi;
+    c = shp ? pc - PR : pr - qi * C;
+  };
+  // h units to stage: KP per thread (P <= 64 KP pairs of 4 units); the
+  // surplus threads repeat the last unit
+  u32x4_t hs[KP];
+#pragma unroll
+  for (int k = 0; k < KP; ++k) {
+    const int u0 = (int)threadIdx.x + 256 * k;
+    const int u = u0 < 4 * P ? u0 : 4 * P - 1;
+    bool shp;
+    int qi, c;
+    pair_of(u >> 2, shp, qi, c);
+    const int jj = __shfl(j_c, qi, 64);
+    const uint16_t* src = shp ? sh.h + (int64_t)c * 32 : h + (int64_t)jj * I + c * 32;
+    hs[k] = reinterpret_cast<const u32x4_t*>(src)[u & 3];
+  }
+  // every pair's weights
+  u32x4_t qw[KP][R];
+  uint32_t sw[KP][R];
+  float cf[KP];
+  bool live[KP];
+  int pcs[KP];
+#pragma unroll
+  for (int k = 0; k < KP; ++k) {
+    const int p = lane + 64 * k;
+    live[k] = p < P;
+    const int pc = live[k] ? p : P - 1;
+    pcs[k] = pc;
+    bool shp;
+    int qi, c;
+    pair_of(pc, shp, qi, c);
+    const int ee = __shfl(e_c, qi, 64);
+    const float fr = __int_as_float(__shfl(f_c, qi, 64));
+    cf[k] = shp ? gs2 : fr;
+    const uint8_t* cbase = shp ? sh.c2 + (int64_t)c * 16
+                               : w2_codes + (int64_t)ee * ecb + (int64_t)c * 16;
+    const uint8_t* sbase = shp ? sh.s2 + (int64_t)c * 2
+                               : w2_scales + (int64_t)ee * esb + (int64_t)c * 2;
+    const int64_t rcb = shp ? cbs : cb, rsb = shp ? sbs : sb;
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      qw[k][r] = load_stream(cbase + rows[r] * rcb);
+      sw[k][r] = *reinterpret_cast<const uint16_t*>(sbase + rows[r] * rsb);
+    }
+  }
+#pragma unroll
+  for (int k = 0; k < KP; ++k) {
+    const int u0 = (int)threadIdx.x + 256 * k;
+    const int u = u0 < 4 * P ? u0 : 4 * P - 1;
+    const int pp = u >> 2;
+    hl[4 * pp + ((u & 3) ^ ((pp >> 2) & 3))] = hs[k];
+  }
+  __syncthreads();
+  if (n0 >= H) return;
+  float acc[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) acc[r] = 0.0f;
+#pragma unroll
+  for (int k = 0; k < KP; ++k) {
+    const int pc = pcs[k];
+    const int sz = (pc >> 2) & 3;
+#pragma unroll
+    for (int b2 = 0; b2 < 2; ++b2) {
+      const u32x4_t xa = hl[4 * pc + ((2 * b2) ^ sz)];
+      const u32x4_t xb = hl[4 * pc + ((2 * b2 + 1) ^ sz)];
+      const bf16x2_t xv[8] = {as_bf16x2(xa.x), as_bf16x2(xa.y), as_bf16x2(xa.z),
+                              as_bf16x2(xa.w), as_bf16x2(xb.x), as_bf16x2(xb.y),
+                              as_bf16x2(xb.z), as_bf16x2(xb.w)};
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        const uint32_t w0 = b2 ? qw[k][r].z : qw[k][r].x;
+        const uint32_t w1 = b2 ? qw[k][r].w : qw[k][r].y;
+        float p = 0.0f;
+        p = dot2(e2m1x2_to_bf16<0>(w0), xv[0], p);
+        p = dot2(e2m1x2_to_bf16<1>(w0), xv[1], p);
+        p = dot2(e2m1x2_to_bf16<2>(w0), xv[2], p);
+        p = dot2(e2m1x2_to_bf16<3>(w0), xv[3], p);
+        p = dot2(e2m1x2_to_bf16<0>(w1), xv[4], p);
+        p = dot2(e2m1x2_to_bf16<1>(w1), xv[5], p);
+        p = dot2(e2m1x2_to_bf16<2>(w1), xv[6], p);
+        p = dot2(e2m1x2_to_bf16<3>(w1), xv[7], p);
+        const float s = (b2 ? e4m3_to_f32<1>(sw[k][r]) : e4m3_to_f32<0>(sw[k][r])) * cf[k];
+        const float na = __builtin_fmaf(p, s, acc[r]);
+        acc[r] = live[k] ? na : acc[r];
+      }
+    }
+  }
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const float t = wave_sum(acc[r]);
+    if (lane == r && n0 + r < H) y[n0 + r] = t;
   }
 }
 
@@ -616,7 +924,24 @@ hipError_t launch_moe(const uint8_t* w13_codes, const uint8_t* w13_scales,
     const int64_t pairs = ((sh.I > I ? sh.I : I) + 1) / 2;
     const int64_t yb = (pairs + kMoeWaves - 1) / kMoeWaves;
     const dim3 grid((unsigned)yb, S + (sh.I > 0 ? 1 : 0));
-    if (M == 1 && (int64_t)grid.x * grid.y * kMoeWaves > kOneRoundWaves6)
+    const bool w7 = (int64_t)grid.x * grid.y * kMoeWaves > kOneRoundWaves6;
+    const int cl = H == 2048 ? 1 : H == 4096 ? 2 : 0;
+    if (M == 1 && cl) {
+      const size_t lds = (size_t)H * sizeof(uint16_t);
+#define NVFP4_GU1X(CC)                                                                        \
+  if (w7)                                                                                     \
+    hipLaunchKernelGGL((k_moe_gate_up_1x<CC, true>), grid, dim3(256), lds, stream, w13_codes, \
+                       w13_scales, w13_gscale, x, xr, ga13, ids, E, H, I, h, sh);            \
+  else                                                                                        \
+    hipLaunchKernelGGL((k_moe_gate_up_1x<CC, false>), grid, dim3(256), lds, stream, w13_codes,\
+                       w13_scales, w13_gscale, x, xr, ga13, ids, E, H, I, h, sh)
+      if (cl == 1) {
+        NVFP4_GU1X(1);
+      } else {
+        NVFP4_GU1X(2);
+      }
+#undef NVFP4_GU1X
+    } else if (M == 1 && w7)
       hipLaunchKernelGGL((k_moe_gate_up<1, true>), grid, dim3(256), 0, stream, w13_codes,
                          w13_scales, w13_gscale, x, xr, ga13, ids, S, topk, E, H, I, h, sh, M);
     else if (M == 1)
@@ -634,7 +959,22 @@ hipError_t launch_moe(const uint8_t* w13_codes, const uint8_t* w13_scales,
     e = launch_quantize_decode(h, S, I, ga2, ids, E, const_cast<uint16_t*>(hr), stream);
     if (e != hipSuccess) return e;
   }
-  if (M == 1) {
+  const int64_t pmax = (int64_t)topk * (I >> 5) + (sh.I >> 5);   // pairs with every slot valid
+  if (M == 1 && pmax >= 1 && pmax <= 64 * 8) {
+    const int64_t wgs = (H + kDownRows * kMoeWaves - 1) / (kDownRows * kMoeWaves);
+    const int kp = (int)((pmax + 63) / 64);
+    const size_t lds = (size_t)pmax * 64;
+#define NVFP4_DOWN1X(KK)                                                                  \
+  hipLaunchKernelGGL((k_moe_down_1x<kDownRows, KK>), dim3((unsigned)wgs), dim3(256), lds, \
+                     stream, w2_codes, w2_scales, w2_gscale, hr, ga2, ids, gate_w, topk, E, H, \
+                     I, y, sh)
+    if (kp <= 2) NVFP4_DOWN1X(2);
+    else if (kp <= 4) NVFP4_DOWN1X(4);
+    else if (kp <= 6) NVFP4_DOWN1X(6);
+    else if (kp <= 7) NVFP4_DOWN1X(7);
+    else NVFP4_DOWN1X(8);
+#undef NVFP4_DOWN1X
+  } else if (M == 1) {
     const int64_t wgs = (H + kDownRows * kMoeWaves - 1) / (kDownRows * kMoeWaves);
     hipLaunchKernelGGL((k_moe_down<kDownRows, kDownUnroll>), dim3((unsigned)wgs), dim3(256), 0,
                        stream, w2_codes, w2_scales, w2_gscale, hr, ga2, ids, gate_w, M, topk, E,

@@ -64,6 +64,37 @@ def test_moe_workload_4_full_size(M):
     assert same > 0.999
 
 
+@pytest.mark.parametrize("H, I, topk", [(2048, 1024, 16), (2048, 768, 8), (6144, 256, 8)])
+def test_moe_one_token_shapes(H, I, topk):
+    """One token across the launch variants of its two passes: x staged in
+    LDS for gate|up at H = 2048 (one chunk per lane; H = 6144 keeps the
+    unstaged kernel), and the down pass with all of a lane's (slot, chunk)
+    pairs in flight at once: 512 pairs (8 per lane: 16 slots of I = 1024)
+    and 192 (3 per lane, run as 4). The slot ids hold a repeat and two
+    invalid ids; y and the valid slots' h against the oracle."""
+    E = 20
+    rng = np.random.default_rng(H + I + topk)
+    row = rng.choice(E, size=topk, replace=False).astype(np.int32)
+    row[1] = row[0]
+    row[2] = -1
+    row[topk - 1] = E + 3
+    ids = row.reshape(1, topk)
+    gw = rng.random((1, topk)).astype(np.float32)
+    say(f"[moe] one token H={H} I={I} topk={topk} ids={row.tolist()}")
+    valid = (row >= 0) & (row < E)
+    hw, dw = build_experts(49, 0, E, H, I, row[valid])
+    x = workloads.x_bf16(49, 1, topk, 1, H)
+    y, (y_ref, bound, h_ref), ws = run_both(hw, dw, x, ids, gw, H, I, want_h=True)
+    check_tol(y, y_ref, bound, f"moe one token H={H} I={I} topk={topk}")
+    lay = nv.moe_workspace_layout(1, H, I, topk)
+    h = host(ws[lay["h"]:lay["h"] + topk * I * 2].view(torch.int16)).view(np.uint16)
+    h = h.reshape(topk, I)[valid]
+    hr = np.asarray(h_ref).reshape(topk, I)[valid]
+    ulp = np.abs(h.astype(np.int32) - hr.astype(np.int32))
+    say(f"  h bit-equal fraction {np.mean(ulp == 0):.6f}, max ulp diff {ulp.max()}")
+    assert ulp.max() <= 1 and np.mean(ulp == 0) > 0.99
+
+
 def test_moe_shared_experts_union():
     """All 8 rows route to the same 8 experts (each expert streamed once for
     8 slots), in different slot orders."""

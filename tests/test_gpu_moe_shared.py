@@ -66,6 +66,23 @@ def test_moe_shared_workload_4(M):
     check_hs(hs, hs_ref)
 
 
+def test_moe_shared_one_token_staged():
+    """One token with a shared expert at H = 2048: the staged gate|up, shared
+    row included, and the down pass over 136 pairs (8 slots of I = 512, then
+    the shared expert's 8 chunks), 3 per lane run as 4."""
+    E, H, I, topk, Is = 12, 2048, 512, 8, 256
+    rng = np.random.default_rng(5)
+    ids = rng.choice(E, size=(1, topk), replace=False).astype(np.int32)
+    gw = rng.random((1, topk)).astype(np.float32)
+    say(f"[moe shared] one token H={H} I={I} Is={Is} ids={ids[0].tolist()}")
+    hw, dw = build_experts(50, 0, E, H, I, ids.ravel())
+    hsw, dsw = build_shared(50, 0, H, Is)
+    x = workloads.x_bf16(50, 1, topk, 1, H)
+    y, y_ref, bound, hs, hs_ref = run_shared(hw, dw, hsw, dsw, x, ids, gw, H, I)
+    check_tol(y, y_ref, bound, "moe shared one token H=2048")
+    check_hs(hs, hs_ref)
+
+
 @pytest.mark.parametrize("Is", [32, 96, 512])
 def test_moe_shared_widths_duplicates_and_invalid_ids(Is):
     E, H, I = 6, 512, 256
