@@ -63,6 +63,111 @@ __global__ __launch_bounds__(256) void k_gemv(const SegTable tab, const uint16_t
   }
 }
 
+// Below 32768 rows with K = 2048 CL (launched for K = 4096, CL = 2): each wavefront has
+// exactly one group of R rows (the grid covers every group), so its loads
+// can all be issued at once. The workgroup stages x (M rows, x1x_unit
+// layout) in LDS while the weights are in flight; every lane then issues
+// the codes and scales of all CL of its chunks before the first product,
+// and reads x from LDS. The products and their order per lane are those of
+// wave_row_dots<M, R>, so y is the same bit for bit; the memory side waits
+// for one HBM round trip per wavefront instead of CL, and x crosses the L1
+// once per workgroup instead of once per wavefront. Same-process A/B at M = 1
+// (calls queued back to back): 1024 x 4096 3.47 -> 3.22 us, 4096 x 4096
+// 4.70 -> 4.45, 16384 x 4096 9.24 -> 8.63, 24576 x 4096 12.3 -> 11.0; at
+// M = 2, 1024 x 4096 3.95 -> 3.57 and 2048 x 4096 5.02 -> 4.02. At K = 2048
+// (one chunk per lane) it was slower (2048 x 2048 2.96 -> 3.08 us), so that
+// K keeps k_gemv.
+template <int M, int R, int CL, bool SEG>
+__global__ __launch_bounds__(256) void k_gemv_1x(const SegTable tab, const uint16_t* __restrict__ x,
+                                                 int64_t K, unsigned nblk) {
+  extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
+  u32x4_t* const xl = reinterpret_cast<u32x4_t*>(lds);
+  const int lane = threadIdx.x & 63;
+  const unsigned per = (nblk + 7) / 8;
+  const unsigned blk = (blockIdx.x & 7) * per + (blockIdx.x >> 3);
+  if (blk >= nblk) return;   // the whole workgroup
+  const int64_t u =
+      (int64_t)blk * kWavesPerBlock + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int64_t units = tab.start[kMaxSegments];
+  const bool act = u < units;   // the whole wavefront
+  const int nu = (int)(M * (K >> 3));
+  u32x4_t xv[M * CL];
+  x1x_load<256, M * CL>(x, nu, xv);
+  const Seg sg = SEG ? find_seg(tab, act ? u : 0)
+                     : Seg{tab.codes[0], tab.scales[0], tab.gscale[0], tab.y[0], tab.N[0], u, 0};
+  const int64_t N = sg.N;
+  const int64_t n0 = sg.unit * R;
+  const int64_t cb = K >> 1, sbytes = K >> 4;
+  u32x4_t q[CL][R];
+  uint32_t sw[CL][R];
+  if (act) {
+#pragma unroll
+    for (int cl = 0; cl < CL; ++cl)
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        const int64_t row = (n0 + r < N) ? (n0 + r) : (N - 1);
+        const int64_t c = lane + 64 * cl;
+        q[cl][r] = load_stream(sg.codes + row * cb + c * 16);
+        sw[cl][r] = *reinterpret_cast<const uint16_t*>(sg.scales + row * sbytes + c * 2);
+      }
+  }
+  x1x_store<256, M * CL>(xl, nu, xv);
+  __syncthreads();
+  if (!act) return;
+  const float g = *sg.gscale;
+  float acc[R][M];
+#pragma unroll
+  for (int r = 0; r < R; ++r)
+#pragma unroll
+    for (int m = 0; m < M; ++m) acc[r][m] = 0.0f;
+  const int ku = (int)(K >> 3);   // units per row of x
+#pragma unroll
+  for (int cl = 0; cl < CL; ++cl) {
+    const int c = lane + 64 * cl;
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+      bf16x2_t wd[R][8];
+      float s[R];
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        const uint32_t w0 = b ? q[cl][r].z : q[cl][r].x;
+        const uint32_t w1 = b ? q[cl][r].w : q[cl][r].y;
+        wd[r][0] = e2m1x2_to_bf16<0>(w0);
+        wd[r][1] = e2m1x2_to_bf16<1>(w0);
+        wd[r][2] = e2m1x2_to_bf16<2>(w0);
+        wd[r][3] = e2m1x2_to_bf16<3>(w0);
+        wd[r][4] = e2m1x2_to_bf16<0>(w1);
+        wd[r][5] = e2m1x2_to_bf16<1>(w1);
+        wd[r][6] = e2m1x2_to_bf16<2>(w1);
+        wd[r][7] = e2m1x2_to_bf16<3>(w1);
+        s[r] = b ? e4m3_to_f32<1>(sw[cl][r]) : e4m3_to_f32<0>(sw[cl][r]);
+      }
+#pragma unroll
+      for (int m = 0; m < M; ++m) {
+        const u32x4_t xa = xl[x1x_unit(m * ku + 4 * c + 2 * b)];
+        const u32x4_t xb = xl[x1x_unit(m * ku + 4 * c + 2 * b + 1)];
+        const bf16x2_t xq[8] = {as_bf16x2(xa.x), as_bf16x2(xa.y), as_bf16x2(xa.z),
+                                as_bf16x2(xa.w), as_bf16x2(xb.x), as_bf16x2(xb.y),
+                                as_bf16x2(xb.z), as_bf16x2(xb.w)};
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+          float p = 0.0f;
+#pragma unroll
+          for (int j = 0; j < 8; ++j) p = dot2(wd[r][j], xq[j], p);
+          acc[r][m] = __builtin_fmaf(p, s[r], acc[r][m]);
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int r = 0; r < R; ++r)
+#pragma unroll
+    for (int m = 0; m < M; ++m) {
+      const float t = wave_sum(acc[r][m]);
+      if (lane == r * M + m && n0 + r < N) sg.y[(int64_t)m * N + n0 + r] = t * g;
+    }
+}
+
 // W4A4 at M <= 2: k_gemv's loop with NVFP4 activations read and decoded in
 // place (wave_row_dots_q), and the tensor scale g_w * g_x (one fp32
 // rounding), over one matrix or the segment table of several.
@@ -135,6 +240,19 @@ static void launch_m(const SegDesc* d, int n, const uint16_t* x, int64_t K,
   const int64_t cap = (int64_t)1 << 20;
   const unsigned nblk = (unsigned)(want < cap ? want : cap);
   const unsigned grid = (nblk + 7) / 8 * 8;
+  if constexpr (R <= 2) {
+    if (K == 4096 && want <= cap) {
+      // one row group per wavefront: the staged kernel, two chunks per lane
+      const size_t lds = (size_t)M * K * sizeof(uint16_t);
+      if (n == 1)
+        hipLaunchKernelGGL((k_gemv_1x<M, R, 2, false>), dim3(grid), dim3(256), lds, stream, tab,
+                           x, K, nblk);
+      else
+        hipLaunchKernelGGL((k_gemv_1x<M, R, 2, true>), dim3(grid), dim3(256), lds, stream, tab,
+                           x, K, nblk);
+      return;
+    }
+  }
   if (n == 1)
     hipLaunchKernelGGL((k_gemv<M, R, false>), dim3(grid), dim3(256), 0, stream, tab, x, K, nblk);
   else

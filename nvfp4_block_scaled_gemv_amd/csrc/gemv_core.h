@@ -17,6 +17,39 @@
 
 namespace nvfp4 {
 
+// Activations staged in LDS (kernels where every wavefront of a workgroup
+// reads the same rows of x): 16-byte unit u holds x[8u .. 8u+7] of the
+// row-major [M, K] array; chunk c (32 elements) is units 4c .. 4c+3, its
+// quarter q stored at unit 4c + (q ^ ((c >> 2) & 3)). A lane reads one
+// chunk per 128-bit load pair and 16 lanes read 16 consecutive chunks, which
+// the swizzle puts on distinct banks (K a multiple of 512 keeps the pattern
+// the same in every row).
+__device__ __forceinline__ int x1x_unit(int u) {
+  const int c = u >> 2;
+  return 4 * c + ((u & 3) ^ ((c >> 2) & 3));
+}
+
+// the nu units of x, UPT per thread of NT (surplus threads repeat the last):
+// loaded into registers first, so that other loads can be issued before the
+// LDS stores wait for them
+template <int NT, int UPT>
+__device__ __forceinline__ void x1x_load(const uint16_t* __restrict__ xs, int nu,
+                                         u32x4_t (&xv)[UPT]) {
+#pragma unroll
+  for (int k = 0; k < UPT; ++k) {
+    const int u0 = (int)threadIdx.x + NT * k;
+    xv[k] = reinterpret_cast<const u32x4_t*>(xs)[u0 < nu ? u0 : nu - 1];
+  }
+}
+template <int NT, int UPT>
+__device__ __forceinline__ void x1x_store(u32x4_t* xl, int nu, const u32x4_t (&xv)[UPT]) {
+#pragma unroll
+  for (int k = 0; k < UPT; ++k) {
+    const int u0 = (int)threadIdx.x + NT * k;
+    xl[x1x_unit(u0 < nu ? u0 : nu - 1)] = xv[k];
+  }
+}
+
 // out[r][m] = sum_k e2m1(c[row_r, k]) * s[row_r, k/16] * x_m[k]  (no tensor
 // scale), for r < R and m < ns (ns <= MS; entries m >= ns are left at 0).
 // Every lane of the wavefront receives the totals. `rows[r]` must be valid

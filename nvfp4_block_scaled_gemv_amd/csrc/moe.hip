@@ -208,8 +208,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(W7 ? 7 : 1)
   }
 }
 
-// One token (M = 1), H = 2048 or 4096 (CL = H / 2048 chunks per lane; more
-// would spill): the gate|up pieces of k_moe_gate_up_1x. They compute the rows of wave_row_dots<1, 4> in the
+// One token (M = 1), H = 2048 CL (launched for H = 4096, CL = 2: more chunks
+// per lane would spill, and one chunk per lane was slower in the dense
+// GEMV's version of this kernel): the gate|up pieces of k_moe_gate_up_1x. They compute the rows of wave_row_dots<1, 4> in the
 // same per-lane order of (chunk, block) products, so the same h bit for bit,
 // with two changes to the memory side:
 //  - every slot multiplies the same activation row, so each workgroup
@@ -217,36 +218,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(W7 ? 7 : 1)
 //    reading all of it through the L1;
 //  - each lane issues the loads of all CL of its chunks before the first
 //    product, so a wavefront waits for one HBM round trip, not CL.
-// LDS layout: 16-byte unit u holds x[8u .. 8u+7]; chunk c (32 elements) is
-// units 4c .. 4c+3, its quarter q stored at unit 4c + (q ^ ((c >> 2) & 3)).
-// Lane l reads chunk l (+64 cl), so the 16 lanes of one 128-bit LDS read
-// cover 16 consecutive chunks, and the swizzle puts them on distinct banks.
-__device__ __forceinline__ int x1x_unit(int u) {
-  const int c = u >> 2;
-  return 4 * c + ((u & 3) ^ ((c >> 2) & 3));
-}
-
-// the H / 8 units of x, UPT per thread of NT (surplus threads repeat the last)
-template <int NT, int UPT>
-__device__ __forceinline__ void x1x_load(const uint16_t* __restrict__ xs, int64_t H,
-                                         u32x4_t (&xv)[UPT]) {
-  const int nu = (int)(H >> 3);
-#pragma unroll
-  for (int k = 0; k < UPT; ++k) {
-    const int u0 = (int)threadIdx.x + NT * k;
-    xv[k] = reinterpret_cast<const u32x4_t*>(xs)[u0 < nu ? u0 : nu - 1];
-  }
-}
-template <int NT, int UPT>
-__device__ __forceinline__ void x1x_store(u32x4_t* xl, int64_t H, const u32x4_t (&xv)[UPT]) {
-  const int nu = (int)(H >> 3);
-#pragma unroll
-  for (int k = 0; k < UPT; ++k) {
-    const int u0 = (int)threadIdx.x + NT * k;
-    xl[x1x_unit(u0 < nu ? u0 : nu - 1)] = xv[k];
-  }
-}
-
+// LDS layout: x1x_unit (gemv_core.h).
 // the codes and scales of rows[0..3] at the lane's CL chunks
 template <int CL>
 __device__ __forceinline__ void gate_up_loads_1x(const uint8_t* __restrict__ codes,
@@ -337,13 +309,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(W7 ? 7 : 6)
   }
   const bool act = ok && r0 < Iv;   // the whole wavefront
   u32x4_t xv[CL];
-  x1x_load<256, CL>(xs, H, xv);
+  x1x_load<256, CL>(xs, (int)(H >> 3), xv);
   const int64_t r1 = (r0 + 1 < Iv) ? r0 + 1 : r0;
   const int64_t rows[4] = {r0, r1, Iv + r0, Iv + r1};
   u32x4_t q[CL][4];
   uint32_t sw[CL][4];
   if (act) gate_up_loads_1x<CL>(codes, scales, H, rows, q, sw);
-  x1x_store<256, CL>(xl, H, xv);
+  x1x_store<256, CL>(xl, (int)(H >> 3), xv);
   __syncthreads();
   if (!act) return;
   float acc[4];
@@ -560,10 +532,10 @@ __global__ __launch_bounds__(256) void k_moe_down(
 //  - each lane issues the loads of all KP of its pairs before the first
 //    product (one HBM round trip per wavefront instead of one per U pairs);
 //  - the h chunks of all pairs (every valid slot's h row, then the shared
-//    expert's) are staged once per workgroup in LDS, pair p's 64 bytes at
-//    units 4p .. 4p+3, quarter q at unit 4p + (q ^ ((p >> 2) & 3)) so that
-//    16 lanes reading 16 consecutive pairs hit distinct banks. Every
-//    wavefront used to read all of h through the L1.
+//    expert's) are staged once per workgroup in LDS, pair p's 64 bytes
+//    where x1x_unit puts chunk p, so that 16 lanes reading 16 consecutive
+//    pairs hit distinct banks. Every wavefront used to read all of h
+//    through the L1.
 // Needs P = (valid slots) I/32 + Is/32 <= 64 KP; the launcher checks the
 // bound for topk valid slots.
 template <int R, int KP>
@@ -666,8 +638,7 @@ __global__ __launch_bounds__(256) void k_moe_down_1x(
   for (int k = 0; k < KP; ++k) {
     const int u0 = (int)threadIdx.x + 256 * k;
     const int u = u0 < 4 * P ? u0 : 4 * P - 1;
-    const int pp = u >> 2;
-    hl[4 * pp + ((u & 3) ^ ((pp >> 2) & 3))] = hs[k];
+    hl[x1x_unit(u)] = hs[k];
   }
   __syncthreads();
   if (n0 >= H) return;
@@ -677,11 +648,10 @@ __global__ __launch_bounds__(256) void k_moe_down_1x(
 #pragma unroll
   for (int k = 0; k < KP; ++k) {
     const int pc = pcs[k];
-    const int sz = (pc >> 2) & 3;
 #pragma unroll
     for (int b2 = 0; b2 < 2; ++b2) {
-      const u32x4_t xa = hl[4 * pc + ((2 * b2) ^ sz)];
-      const u32x4_t xb = hl[4 * pc + ((2 * b2 + 1) ^ sz)];
+      const u32x4_t xa = hl[x1x_unit(4 * pc + 2 * b2)];
+      const u32x4_t xb = hl[x1x_unit(4 * pc + 2 * b2 + 1)];
       const bf16x2_t xv[8] = {as_bf16x2(xa.x), as_bf16x2(xa.y), as_bf16x2(xa.z),
                               as_bf16x2(xa.w), as_bf16x2(xb.x), as_bf16x2(xb.y),
                               as_bf16x2(xb.z), as_bf16x2(xb.w)};
@@ -925,22 +895,14 @@ hipError_t launch_moe(const uint8_t* w13_codes, const uint8_t* w13_scales,
     const int64_t yb = (pairs + kMoeWaves - 1) / kMoeWaves;
     const dim3 grid((unsigned)yb, S + (sh.I > 0 ? 1 : 0));
     const bool w7 = (int64_t)grid.x * grid.y * kMoeWaves > kOneRoundWaves6;
-    const int cl = H == 2048 ? 1 : H == 4096 ? 2 : 0;
-    if (M == 1 && cl) {
+    if (M == 1 && H == 4096) {
       const size_t lds = (size_t)H * sizeof(uint16_t);
-#define NVFP4_GU1X(CC)                                                                        \
-  if (w7)                                                                                     \
-    hipLaunchKernelGGL((k_moe_gate_up_1x<CC, true>), grid, dim3(256), lds, stream, w13_codes, \
-                       w13_scales, w13_gscale, x, xr, ga13, ids, E, H, I, h, sh);            \
-  else                                                                                        \
-    hipLaunchKernelGGL((k_moe_gate_up_1x<CC, false>), grid, dim3(256), lds, stream, w13_codes,\
-                       w13_scales, w13_gscale, x, xr, ga13, ids, E, H, I, h, sh)
-      if (cl == 1) {
-        NVFP4_GU1X(1);
-      } else {
-        NVFP4_GU1X(2);
-      }
-#undef NVFP4_GU1X
+      if (w7)
+        hipLaunchKernelGGL((k_moe_gate_up_1x<2, true>), grid, dim3(256), lds, stream, w13_codes,
+                           w13_scales, w13_gscale, x, xr, ga13, ids, E, H, I, h, sh);
+      else
+        hipLaunchKernelGGL((k_moe_gate_up_1x<2, false>), grid, dim3(256), lds, stream, w13_codes,
+                           w13_scales, w13_gscale, x, xr, ga13, ids, E, H, I, h, sh);
     } else if (M == 1 && w7)
       hipLaunchKernelGGL((k_moe_gate_up<1, true>), grid, dim3(256), 0, stream, w13_codes,
                          w13_scales, w13_gscale, x, xr, ga13, ids, S, topk, E, H, I, h, sh, M);

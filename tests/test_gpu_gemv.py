@@ -50,6 +50,22 @@ def test_random_storage_shapes(M, N, K):
     check_tol(y, y_ref, ad, f"M={M} N={N} K={K}")
 
 
+@pytest.mark.parametrize("M,N", [(1, 4097), (1, 32767), (2, 4095), (1, 1), (2, 130)])
+def test_staged_vector_alu_shapes(M, N):
+    """K = 4096 below 32768 rows: one row group per wavefront with x staged in
+    LDS, two rows per wavefront from 4096 rows and one below (M = 2 stays on
+    the vector ALUs below 4096 rows); ragged last groups, the largest row
+    count of the kernel and a one-row matrix, every output compared."""
+    K = 4096
+    say(f"[gemv] staged vector-ALU shape M={M} N={N} K={K}")
+    codes, scales = workloads.random_nvfp4(9, M, 3 * N + 1, N, K)
+    x = workloads.x_bf16(9, M, 3 * N + 1, M, K)
+    g = np.float32(0.0211)
+    y = run_gpu(codes, scales, g, x)
+    y_ref, ad = oracle.gemv(codes, scales, g, x)
+    check_tol(y, y_ref, ad, f"M={M} N={N} K={K}")
+
+
 @pytest.mark.parametrize("M", [1, 2])
 def test_four_rows_per_wavefront_with_ragged_tail(M):
     """N >= 32768 takes four rows per wavefront on the vector ALUs; N = 40003

@@ -66,12 +66,12 @@ def test_moe_workload_4_full_size(M):
 
 @pytest.mark.parametrize("H, I, topk", [(2048, 1024, 16), (2048, 768, 8), (6144, 256, 8)])
 def test_moe_one_token_shapes(H, I, topk):
-    """One token across the launch variants of its two passes: x staged in
-    LDS for gate|up at H = 2048 (one chunk per lane; H = 6144 keeps the
-    unstaged kernel), and the down pass with all of a lane's (slot, chunk)
-    pairs in flight at once: 512 pairs (8 per lane: 16 slots of I = 1024)
-    and 192 (3 per lane, run as 4). The slot ids hold a repeat and two
-    invalid ids; y and the valid slots' h against the oracle."""
+    """One token across the launch variants of its two passes: gate|up at
+    H other than 4096 (the kernel without x staged in LDS), the down pass
+    with all of a lane's (slot, chunk) pairs in flight at once: 512 pairs
+    (8 per lane: 16 slots of I = 1024), 192 (3 per lane, run as 4) and 64.
+    The slot ids hold a repeat and two invalid ids; y and the valid slots'
+    h against the oracle."""
     E = 20
     rng = np.random.default_rng(H + I + topk)
     row = rng.choice(E, size=topk, replace=False).astype(np.int32)

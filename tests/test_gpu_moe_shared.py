@@ -67,9 +67,9 @@ def test_moe_shared_workload_4(M):
 
 
 def test_moe_shared_one_token_staged():
-    """One token with a shared expert at H = 2048: the staged gate|up, shared
-    row included, and the down pass over 136 pairs (8 slots of I = 512, then
-    the shared expert's 8 chunks), 3 per lane run as 4."""
+    """One token with a shared expert at H = 2048 (gate|up without x staged
+    in LDS) and the down pass over 136 pairs (8 slots of I = 512, then the
+    shared expert's 8 chunks), 3 per lane run as 4."""
     E, H, I, topk, Is = 12, 2048, 512, 8, 256
     rng = np.random.default_rng(5)
     ids = rng.choice(E, size=(1, topk), replace=False).astype(np.int32)
