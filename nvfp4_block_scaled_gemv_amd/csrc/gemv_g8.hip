@@ -252,24 +252,44 @@ bool g8_groups_applicable(const SegDesc* d, int n, int M, int64_t K) {
 }
 
 // Launch shape, from A/B sweeps (1024 .. 151936 rows at K = 4096 and 12288,
-// M = 5 and 8): TW tiles per workgroup so that every CU gets one or two
-// workgroups of TW tiles -- 3 from 768 tiles up to 3072 (12288 rows: 256
-// workgroups), 2 from 384 and from 3072 up (the LM head: many rounds of
-// smaller workgroups balance better), one tile where K needs more than one
-// slice per wavefront -- and S, the slices per wavefront, as small as 16
-// wavefronts allow: one slice per wavefront at K = 4096 keeps
-// the registers at about 64, so each CU holds 32 wavefronts (two
-// workgroups) where two slices per wavefront held 16 (LM head at M = 8:
-// 74.7 against 85.9 us; 4096 and 1024 rows: 5.3 against 5.8 us and 5.1
-// against 5.5 us). The summation order does not depend on the shape.
-void g8_shape(int64_t rows, int64_t K, int* TW, int* S, int* W) {
+// M = 2, 5 and 8). S, the slices per wavefront, as small as 16 wavefronts
+// allow: one slice per wavefront at K = 4096 keeps the registers at about
+// 64, so each CU holds 32 wavefronts (two workgroups) where two slices per
+// wavefront held 16 (LM head at M = 8: 74.7 against 85.9 us; 4096 and 1024
+// rows: 5.3 against 5.8 us and 5.1 against 5.5 us). TW, the tiles per
+// workgroup, with one slice per wavefront (the registers of more slices and
+// tiles would not fit; one tile otherwise):
+//   - 3 where the three-tile grid is one round of one workgroup per CU
+//     (744 .. 768 tiles; the three-tile kernel runs one workgroup per CU):
+//     12288 rows at M = 8, 8.8 us against 10.3 with TW = 2;
+//   - 2 from 384 tiles otherwise: a three-tile grid past one round leaves
+//     most CUs idle in its last round (16384 rows at M = 8: 14.5 us with
+//     TW = 3, 10.6 with TW = 2; 30000 rows 21.0 against 17.9; 24576 rows at
+//     M = 5 14.7 against 13.8);
+//   - 1 below 384 tiles;
+//   - at M = 2 from 1280 tiles (20480 rows), one tile with two slices per
+//     wavefront (8 wavefronts): 20480, 24576, 30000 and 49152 rows 11.3,
+//     12.7, 14.8 and 21.7 us against 12.5, 13.3, 15.6 and 22.7 with TW = 2.
+// Token groups (9 <= M <= 16) keep the rule of the first sweeps: TW = 3
+// from 768 up to 3072 tiles. The summation order does not depend on the
+// shape.
+void g8_shape(int64_t rows, int64_t K, int M, int* TW, int* S, int* W) {
   const int64_t tiles = (rows + 15) / 16;
   int s = 0;
   for (int c = 1; c <= 4 && !s; ++c)
     if (g8_split_ok(K, c)) s = c;
-  // several tiles per workgroup only with one slice per wavefront (the
-  // registers of more slices and tiles would not fit)
-  *TW = s != 1 ? 1 : (tiles >= 768 && tiles < 3072) ? 3 : (tiles >= 384 ? 2 : 1);
+  int tw;
+  if (s != 1) {
+    tw = 1;
+  } else if (M == 2 && tiles >= 1280 && g8_split_ok(K, 2)) {
+    tw = 1;
+    s = 2;
+  } else if (M > 8) {
+    tw = (tiles >= 768 && tiles < 3072) ? 3 : (tiles >= 384 ? 2 : 1);
+  } else {
+    tw = (tiles >= 744 && tiles <= 768) ? 3 : (tiles >= 384 ? 2 : 1);
+  }
+  *TW = tw;
   *S = s;
   *W = s ? (int)(K / kG8Slice / s) : 0;
 }
@@ -318,7 +338,7 @@ hipError_t launch_gemv_g8(const SegDesc* d, int n, const uint16_t* x, int M, int
   int64_t rows = 0;
   for (int k = 0; k < n; ++k) rows += d[k].N;
   int TW, S, W;
-  g8_shape(rows, K, &TW, &S, &W);
+  g8_shape(rows, K, M, &TW, &S, &W);
   return launch_gemv_g8_shape(d, n, x, M, K, TW, S, stream);
 }
 

@@ -42,7 +42,7 @@ bool mt_applicable(int M);
 bool g8_applicable(int M, int64_t K);
 // 9 <= M <= 16: the same kernel in two groups of 8 tokens (below 2^17 rows)
 bool g8_groups_applicable(const SegDesc* d, int n, int M, int64_t K);
-void g8_shape(int64_t rows, int64_t K, int* TW, int* S, int* W);
+void g8_shape(int64_t rows, int64_t K, int M, int* TW, int* S, int* W);
 hipError_t launch_gemv_g8(const SegDesc* d, int n, const uint16_t* x, int M, int64_t K,
                           hipStream_t stream);
 hipError_t launch_gemv_g8_shape(const SegDesc* d, int n, const uint16_t* x, int M, int64_t K,
