@@ -260,8 +260,9 @@ bool g8_groups_applicable(const SegDesc* d, int n, int M, int64_t K) {
 // workgroup, with one slice per wavefront (the registers of more slices and
 // tiles would not fit; one tile otherwise):
 //   - 3 where the three-tile grid is one round of one workgroup per CU
-//     (744 .. 768 tiles; the three-tile kernel runs one workgroup per CU):
-//     12288 rows at M = 8, 8.8 us against 10.3 with TW = 2;
+//     (248 .. 256 workgroups; the three-tile kernel runs one workgroup per
+//     CU): 12288 rows at M = 8, 8.8 us against 10.3 with TW = 2; 6144 rows
+//     at M = 12 and 16 (two token groups), 7.6 / 7.8 us against 9.4 / 9.5;
 //   - 2 from 384 tiles otherwise: a three-tile grid past one round leaves
 //     most CUs idle in its last round (16384 rows at M = 8: 14.5 us with
 //     TW = 3, 10.6 with TW = 2; 30000 rows 21.0 against 17.9; 24576 rows at
@@ -270,9 +271,10 @@ bool g8_groups_applicable(const SegDesc* d, int n, int M, int64_t K) {
 //   - at M = 2 from 1280 tiles (20480 rows), one tile with two slices per
 //     wavefront (8 wavefronts): 20480, 24576, 30000 and 49152 rows 11.3,
 //     12.7, 14.8 and 21.7 us against 12.5, 13.3, 15.6 and 22.7 with TW = 2.
-// Token groups (9 <= M <= 16) keep the rule of the first sweeps: TW = 3
-// from 768 up to 3072 tiles. The summation order does not depend on the
-// shape.
+// With two token groups two tiles also won from 8192 rows up (M = 16:
+// 16384 / 20480 / 24576 rows 16.8 / 20.5 / 23.8 us against 18.9 / 24.2 /
+// 24.9 with TW = 3; 12288 rows 13.4 against 13.5). The summation order does
+// not depend on the shape.
 void g8_shape(int64_t rows, int64_t K, int M, int* TW, int* S, int* W) {
   const int64_t tiles = (rows + 15) / 16;
   int s = 0;
@@ -284,10 +286,10 @@ void g8_shape(int64_t rows, int64_t K, int M, int* TW, int* S, int* W) {
   } else if (M == 2 && tiles >= 1280 && g8_split_ok(K, 2)) {
     tw = 1;
     s = 2;
-  } else if (M > 8) {
-    tw = (tiles >= 768 && tiles < 3072) ? 3 : (tiles >= 384 ? 2 : 1);
   } else {
-    tw = (tiles >= 744 && tiles <= 768) ? 3 : (tiles >= 384 ? 2 : 1);
+    // workgroups of the three-tile grid: one per (unit, token group)
+    const int64_t g3 = (tiles + 2) / 3 * (M > 8 ? 2 : 1);
+    tw = (g3 >= 248 && g3 <= 256) ? 3 : (tiles >= 384 ? 2 : 1);
   }
   *TW = tw;
   *S = s;
