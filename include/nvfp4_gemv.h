@@ -155,8 +155,9 @@ nvfp4_status nvfp4_dequant(const uint8_t* codes, const uint8_t* scales,
  *   M       0 <= M <= NVFP4_MAX_M;  0 <= N <= NVFP4_MAX_N;  K >= 0, K % 32 == 0;
  *   y       float[M, N] out, 4-byte aligned (M == 0 or N == 0: nothing is
  *           launched; K == 0: y is set to zero).
- * M <= 2 runs on the vector ALUs, 3 <= M <= 8 on the matrix cores with eight
- * tokens per block half of each MFMA, 9 <= M <= 128 on the matrix cores with
+ * M <= 2 runs on the vector ALUs (and 3 <= M <= 5 when N <= 1024 and K =
+ * 4096), 3 <= M <= 8 otherwise on the matrix cores with eight tokens per
+ * block half of each MFMA, 9 <= M <= 128 on the matrix cores with
  * the block scale folded into the decoded weights (blueprint "Plan arms":
  * multi_seq 2..128 rows; "Planner settings": w4a16_tc=on).
  * Errors: NULL, SHAPE, ALIGN, UNSUPPORTED (M > NVFP4_MAX_M or N > NVFP4_MAX_N),

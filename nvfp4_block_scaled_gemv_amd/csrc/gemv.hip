@@ -1,8 +1,9 @@
 // gemv.hip -- dense NVFP4 g16 W4A16 GEMV on gfx950, vector-ALU path for
-// M = 1, and for M = 2 on small matrices or K that the matrix-core kernels
-// do not split (M = 2 from 4096 rows with K % 256 == 0, and 3 <= M <= 8, go
-// to the matrix-core kernels of gemv_g8.hip, gemv_g8r.hip, gemv_splitk.hip
-// and gemv_mfma.hip; 9 <= M <= 128 to gemv_mt.hip):
+// M = 1, for M = 2 on small matrices or K that the matrix-core kernels do
+// not split, and for 3 <= M <= 5 on matrices of at most 1024 rows at K =
+// 4096 (M = 2 from 4096 rows with K % 256 == 0, and 3 <= M <= 8 otherwise,
+// go to the matrix-core kernels of gemv_g8.hip, gemv_g8r.hip,
+// gemv_splitk.hip and gemv_mfma.hip; 9 <= M <= 128 to gemv_mt.hip):
 //   y[m, n] = g * sum_k e2m1(c[n,k]) * s[n, k/16] * x[m, k]
 // (graph.json node "l0.kda.q": act bf16, weight nvfp4/g16 -> bf16,
 // accumulate f32, scale f32). Bandwidth-bound: every weight byte is read
@@ -14,6 +15,7 @@ namespace nvfp4 {
 
 constexpr int kWavesPerBlock = 4;
 constexpr int64_t kM2MatrixCoreRows = 4096;   // M = 2 takes the matrix cores from here
+constexpr int64_t kStagedManyRows = 1024;     // 3 <= M <= 5 on the vector ALUs up to here
 
 // Each wavefront takes groups of R consecutive rows of one segment, striding
 // over the groups of all segments. The nblk workgroups are numbered so that
@@ -259,6 +261,28 @@ static void launch_m(const SegDesc* d, int n, const uint16_t* x, int64_t K,
     hipLaunchKernelGGL((k_gemv<M, R, true>), dim3(grid), dim3(256), 0, stream, tab, x, K, nblk);
 }
 
+// 3 <= M <= 5 on matrices of at most 1024 rows at K = 4096: the staged
+// kernel, one row per wavefront. There the matrix-core kernel has only 64
+// workgroups of 16 tiles; same-process A/B (calls queued back to back), 1024
+// x 4096: M = 3 4.92 -> 3.86 us, M = 5 5.09 -> 4.51 us. At M = 8 (5.34
+// against 5.52 us) and from 2048 rows (M = 5: 5.17 against 5.57 us) the
+// matrix cores stay ahead.
+template <int M, int R>
+static void launch_staged(const SegDesc* d, int n, const uint16_t* x, int64_t K,
+                          hipStream_t stream) {
+  const SegTable tab = make_seg_table(d, n, R);
+  const int64_t units = tab.start[kMaxSegments];
+  const unsigned nblk = (unsigned)((units + kWavesPerBlock - 1) / kWavesPerBlock);
+  const unsigned grid = (nblk + 7) / 8 * 8;
+  const size_t lds = (size_t)M * K * sizeof(uint16_t);
+  if (n == 1)
+    hipLaunchKernelGGL((k_gemv_1x<M, R, 2, false>), dim3(grid), dim3(256), lds, stream, tab, x,
+                       K, nblk);
+  else
+    hipLaunchKernelGGL((k_gemv_1x<M, R, 2, true>), dim3(grid), dim3(256), lds, stream, tab, x,
+                       K, nblk);
+}
+
 template <int M>
 static void launch_valu(const SegDesc* d, int n, int64_t rows, const uint16_t* x, int64_t K,
                         hipStream_t stream) {
@@ -289,6 +313,12 @@ hipError_t launch_gemv_segments(const SegDesc* d, int n, const uint16_t* x, int 
       launch_valu<2>(d, n, rows, x, K, stream);
       break;
     default:
+      if (M <= 5 && K == 4096 && rows <= kStagedManyRows) {
+        if (M == 3) launch_staged<3, 1>(d, n, x, K, stream);
+        else if (M == 4) launch_staged<4, 1>(d, n, x, K, stream);
+        else launch_staged<5, 1>(d, n, x, K, stream);
+        break;
+      }
       if (M > NVFP4_MAX_M_SMALL && !g8_groups_applicable(d, n, M, K))
         return launch_gemv_mt(d, n, x, M, K, stream);
       return launch_gemv_mfma(d, n, x, M, K, stream);

@@ -50,12 +50,14 @@ def test_random_storage_shapes(M, N, K):
     check_tol(y, y_ref, ad, f"M={M} N={N} K={K}")
 
 
-@pytest.mark.parametrize("M,N", [(1, 4097), (1, 32767), (2, 4095), (1, 1), (2, 130)])
+@pytest.mark.parametrize("M,N", [(1, 4097), (1, 32767), (2, 4095), (1, 1), (2, 130),
+                                 (3, 1024), (4, 1), (5, 1024), (5, 1025)])
 def test_staged_vector_alu_shapes(M, N):
     """K = 4096 below 32768 rows: one row group per wavefront with x staged in
     LDS, two rows per wavefront from 4096 rows and one below (M = 2 stays on
-    the vector ALUs below 4096 rows); ragged last groups, the largest row
-    count of the kernel and a one-row matrix, every output compared."""
+    the vector ALUs below 4096 rows, 3 <= M <= 5 up to 1024 rows; 1025 rows
+    at M = 5 is the matrix cores' again); ragged last groups, the largest row
+    counts and a one-row matrix, every output compared."""
     K = 4096
     say(f"[gemv] staged vector-ALU shape M={M} N={N} K={K}")
     codes, scales = workloads.random_nvfp4(9, M, 3 * N + 1, N, K)
