@@ -167,7 +167,12 @@ hipError_t launch_gemv_w4a4_segments(const SegDesc* d, int n, const uint8_t* cod
                      codes_x, scales_x, nchunks, gw, gscale_x, xt, gp);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  return launch_gemv_segments(dd, n, xt, M, K, stream);
+  // the matrix-core kernels at every row count (not the dense route's
+  // vector-ALU kernel for small matrices), so that one segments call and
+  // separate calls sum in the same order
+  if (M > NVFP4_MAX_M_SMALL && !g8_groups_applicable(dd, n, M, K))
+    return launch_gemv_mt(dd, n, xt, M, K, stream);
+  return launch_gemv_mfma(dd, n, xt, M, K, stream);
 }
 
 hipError_t launch_gemv_w4a4(const uint8_t* codes_w, const uint8_t* scales_w,

@@ -88,6 +88,32 @@ def test_w4a4_four_rows_per_wavefront_with_ragged_tail(M):
     check_tol(y, y_ref, ad, f"w4a4 M={M} N={N} K={K}")
 
 
+@pytest.mark.parametrize("M", [1, 2])
+def test_w4a4_scales_off_16_byte_alignment(M):
+    """Activation scales 2-byte but not 16-byte aligned (the least the
+    boundary accepts): the oracle's result within tolerance, and the same
+    bits as with aligned scales."""
+    N, K = 3001, 4096
+    say(f"[w4a4] misaligned activation scales M={M} N={N} K={K}")
+    cw, sw = workloads.random_nvfp4(6, M, 4242, N, K, 0x20, 0x50)
+    gw = np.float32(0.0173)
+    x = workloads.x_bf16(6, M, 4242, M, K)
+    gx = np.float32(static_scale(6, M, K))
+    cx, sx = oracle.quantize_act(x, gx)
+    flat = np.zeros(sx.size + 16, np.uint8)
+    flat[2:2 + sx.size] = sx.ravel()
+    big = dev(flat)
+    sx_off = big[2:2 + sx.size].reshape(sx.shape)
+    assert sx_off.data_ptr() % 16 == (big.data_ptr() + 2) % 16 != 0
+    m = (dev(cw), dev(sw), dev(np.array([gw], np.float32)))
+    cxd, gxd = dev(cx), dev(np.array([gx], np.float32))
+    y_off = host(nv.gemv_w4a4(*m, cxd, sx_off, gxd))
+    y_al = host(nv.gemv_w4a4(*m, cxd, dev(sx), gxd))
+    y_ref, ad = oracle.gemv_w4a4(cw, sw, gw, cx, sx, gx)
+    check_tol(y_off, y_ref, ad, f"w4a4 misaligned scales M={M}")
+    assert np.array_equal(y_off, y_al)
+
+
 @pytest.mark.parametrize("M,K", [(1, 4096), (2, 4096), (3, 4096), (5, 4096), (8, 4096),
                                  (2, 1056), (5, 1056)])
 def test_w4a4_segments(M, K):
