@@ -95,6 +95,42 @@ def test_moe_one_token_shapes(H, I, topk):
     assert ulp.max() <= 1 and np.mean(ulp == 0) > 0.99
 
 
+@pytest.mark.parametrize("case", ["same_8_experts", "one_expert_all_tokens", "odd_tokens"])
+def test_moe_gate_up_passes_at_h4096(case):
+    """H = 4096 at M >= 2 loads a wavefront's gate|up weights once for all
+    its passes of two slots and stages each pass's activation rows in LDS:
+    experts named by 8 slots (four passes), one expert named by every token,
+    and 5 tokens on the same experts (a last pass with a lone slot); y and
+    every valid h against the oracle."""
+    E, H, I, topk = 16, 4096, 256, 8
+    rng = np.random.default_rng(len(case))
+    if case == "same_8_experts":
+        M = 8
+        ids = np.tile(rng.choice(E, size=topk, replace=False).astype(np.int32), (M, 1))
+    elif case == "one_expert_all_tokens":
+        M = 8
+        ids = np.stack([rng.choice(E, size=topk, replace=False) for _ in range(M)]).astype(np.int32)
+        ids[:, 0] = 3
+        for m in range(M):   # keep a token's experts distinct
+            row = ids[m]
+            dup = np.flatnonzero(row[1:] == 3) + 1
+            row[dup] = [e for e in range(E) if e not in row][:len(dup)]
+    else:
+        M = 5
+        ids = np.tile(np.arange(topk, dtype=np.int32), (M, 1))
+    gw = rng.random((M, topk)).astype(np.float32)
+    say(f"[moe] gate|up passes at H=4096: {case} M={M} ids[0]={ids[0].tolist()}")
+    hw, dw = build_experts(51, 0, E, H, I, ids.ravel())
+    x = workloads.x_bf16(51, M, len(case), M, H)
+    y, (y_ref, bound, h_ref), ws = run_both(hw, dw, x, ids, gw, H, I, want_h=True)
+    check_tol(y, y_ref, bound, f"moe {case}")
+    lay = nv.moe_workspace_layout(M, H, I, topk)
+    h = host(ws[lay["h"]:lay["h"] + M * topk * I * 2].view(torch.int16)).view(np.uint16)
+    ulp = np.abs(h.reshape(M * topk, I).astype(np.int32) - h_ref.astype(np.int32))
+    say(f"  h bit-equal fraction {np.mean(ulp == 0):.6f}, max ulp diff {ulp.max()}")
+    assert ulp.max() <= 1 and np.mean(ulp == 0) > 0.99
+
+
 def test_moe_shared_experts_union():
     """All 8 rows route to the same 8 experts (each expert streamed once for
     8 slots), in different slot orders."""
