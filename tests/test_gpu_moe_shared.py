@@ -83,6 +83,32 @@ def test_moe_shared_one_token_staged():
     check_hs(hs, hs_ref)
 
 
+@pytest.mark.parametrize("M,Is", [(3, 512), (2, 64)])
+def test_moe_shared_h4096_widths(M, Is):
+    """H = 4096 at M >= 2 (the gate|up kernel that loads a wavefront's
+    weights once for all passes): a shared expert wider than the routed one
+    (routed wavefronts past I idle through the passes) and a narrower one,
+    with a repeated expert across tokens and an invalid id."""
+    E, H, I, topk = 8, 4096, 256, 4
+    rng = np.random.default_rng(M * 7 + Is)
+    ids = np.stack([rng.choice(E, size=topk, replace=False) for _ in range(M)]).astype(np.int32)
+    ids[:, 0] = 5
+    for m in range(M):
+        row = ids[m]
+        dup = np.flatnonzero(row[1:] == 5) + 1
+        row[dup] = [e for e in range(E) if e not in row][:len(dup)]
+    ids[M - 1, topk - 1] = -1
+    gw = rng.random((M, topk)).astype(np.float32)
+    say(f"[moe shared] H=4096 M={M} I={I} Is={Is} ids={ids.tolist()}")
+    valid = ids[(ids >= 0) & (ids < E)]
+    hw, dw = build_experts(52, 0, E, H, I, valid)
+    hsw, dsw = build_shared(52, Is, H, Is)
+    x = workloads.x_bf16(52, M, Is, M, H)
+    y, y_ref, bound, hs, hs_ref = run_shared(hw, dw, hsw, dsw, x, ids, gw, H, I)
+    check_tol(y, y_ref, bound, f"moe shared H=4096 M={M} Is={Is}")
+    check_hs(hs, hs_ref)
+
+
 @pytest.mark.parametrize("Is", [32, 96, 512])
 def test_moe_shared_widths_duplicates_and_invalid_ids(Is):
     E, H, I = 6, 512, 256
